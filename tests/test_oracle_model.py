@@ -1,0 +1,171 @@
+"""Whole-decoder pins of the oracle.
+
+* incremental KV-cache decode equals the model recomputed from scratch over
+  the whole prefix (a different loop order with its own K/V storage);
+* an independent fp64 model assembled from library routines (torch's
+  rms_norm, scaled_dot_product_attention with grouped-query heads, silu,
+  softmax, topk) gives the same logits -- this pins the block structure,
+  residual placement, head-to-group map and the MoE weighting;
+* grouped-query attention with duplicated K/V heads equals plain multi-head
+  attention;
+* MoE with identical experts reduces to one expert scaled by the summed
+  top-k router probabilities.
+"""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from persistent_resident_execution_amd import synth
+
+
+def _model(oracle_lib, cfg, seed=0):
+    W = synth.gen_weights(cfg, seed=seed, device="cpu")
+    return W, oracle_lib.OracleModel(cfg, synth.weights_to_numpy(W))
+
+
+def _dequant(q, s, m, k):
+    sc = s.double().repeat_interleave(128, -2).repeat_interleave(128, -1)[..., :m, :k]
+    return q.to(torch.float64) * sc
+
+
+def _rope_t(x, pos, theta):
+    # x [n, H, d]; rotate-half pairs (i, i + d/2) at per-row positions
+    d = x.shape[-1]
+    inv = theta ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = pos[:, None].double() * inv[None]
+    c, s = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+    a, b = x[..., : d // 2], x[..., d // 2:]
+    return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+
+def library_forward(cfg, W, tokens):
+    """The decoder written with torch library routines in fp64 (all positions)."""
+    n, h, d = len(tokens), cfg.hidden, cfg.head_dim
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    pos = torch.arange(n)
+    x = W["embed"][torch.as_tensor(tokens, dtype=torch.long)].double()
+    for L in W["layers"]:
+        a = F.rms_norm(x, (h,), weight=L["attn_norm"].double(), eps=cfg.rms_eps)
+        q = (a @ L["wq"].double().T).view(n, Hq, d)
+        k = (a @ L["wk"].double().T).view(n, Hkv, d)
+        v = (a @ L["wv"].double().T).view(n, Hkv, d)
+        q, k = _rope_t(q, pos, cfg.rope_theta), _rope_t(k, pos, cfg.rope_theta)
+        k = k.float().to(torch.bfloat16).double()
+        v = v.float().to(torch.bfloat16).double()
+        o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                           is_causal=True, enable_gqa=True)
+        x = x + o.transpose(0, 1).reshape(n, Hq * d) @ L["wo"].double().T
+        b = F.rms_norm(x, (h,), weight=L["ffn_norm"].double(), eps=cfg.rms_eps)
+        if cfg.is_moe:
+            f = cfg.expert_ffn
+            p = torch.softmax(b @ L["router"].double().T, dim=-1)
+            delta = torch.zeros_like(x)
+
+            def expert(wg, sg, wu, su, wd, sd, e):
+                Wg, Wu = _dequant(wg[e], sg[e], f, h), _dequant(wu[e], su[e], f, h)
+                Wd = _dequant(wd[e], sd[e], h, f)
+                return (F.silu(b @ Wg.T) * (b @ Wu.T)) @ Wd.T
+
+            for s in range(cfg.n_shared):
+                delta += expert(L["s_wg"], L["s_sg"], L["s_wu"], L["s_su"], L["s_wd"], L["s_sd"], s)
+            topv, topi = torch.topk(p, cfg.top_k, dim=-1)
+            for t in range(n):
+                for j in range(cfg.top_k):
+                    e = int(topi[t, j])
+                    y = expert(L["e_wg"], L["e_sg"], L["e_wu"], L["e_su"], L["e_wd"], L["e_sd"], e)
+                    delta[t] += topv[t, j] * y[t]
+            x = x + delta
+        else:
+            x = x + (F.silu(b @ L["wg"].double().T) * (b @ L["wu"].double().T)) @ L["wd"].double().T
+    y = F.rms_norm(x, (h,), weight=W["final_norm"].double(), eps=cfg.rms_eps)
+    return y @ W["lm_head"].double().T, x
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, synth.SMALL_DENSE], ids=lambda c: c.name)
+def test_incremental_decode_equals_full_forward(oracle_lib, cfg):
+    W, m = _model(oracle_lib, cfg)
+    toks = synth.gen_tokens(cfg.vocab, 24, seed=3).numpy()
+    tok_full, lg_full, hd_full = m.forward_full(toks)
+    kc, vc = m.new_cache()
+    for t, tok in enumerate(toks):
+        nxt, lg, hd = m.decode_step(kc, vc, int(tok), t)
+        assert np.array_equal(lg, lg_full[t]), f"position {t}"
+        assert np.array_equal(hd, hd_full[t])
+    assert nxt == tok_full == int(np.argmax(lg_full[-1]))
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, synth.SMALL_DENSE, synth.SMALL_MOE], ids=lambda c: c.name)
+def test_oracle_matches_library_model(oracle_lib, cfg):
+    W, m = _model(oracle_lib, cfg, seed=1)
+    toks = synth.gen_tokens(cfg.vocab, 12, seed=4).numpy()
+    _, lg, hd = m.forward_full(toks)
+    ref_lg, ref_x = library_forward(cfg, W, toks)
+    np.testing.assert_allclose(hd, ref_x.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(lg, ref_lg.numpy(), rtol=1e-9, atol=1e-10)
+
+
+def test_gqa_with_duplicated_kv_heads_equals_mha(oracle_lib):
+    cfg = replace(synth.TINY, n_q_heads=4, n_kv_heads=2, n_layers=2)
+    W, m = _model(oracle_lib, cfg, seed=2)
+    mha = replace(cfg, n_kv_heads=4)
+    Wm = {k: v for k, v in W.items()}
+    Wm["layers"] = []
+    d, h = cfg.head_dim, cfg.hidden
+    for L in W["layers"]:
+        L2 = dict(L)
+        for n in ("wk", "wv"):  # MHA head j uses the rows of GQA group j // 2
+            L2[n] = L[n].view(2, d, h).repeat_interleave(2, dim=0).reshape(4 * d, h).contiguous()
+        Wm["layers"].append(L2)
+    mm = oracle_lib.OracleModel(mha, synth.weights_to_numpy(Wm))
+    toks = synth.gen_tokens(cfg.vocab, 10, seed=5).numpy()
+    _, lg_g, _ = m.forward_full(toks)
+    _, lg_m, _ = mm.forward_full(toks)
+    assert np.array_equal(lg_g, lg_m)
+
+
+def test_moe_identical_experts_reduce_to_one(oracle_lib):
+    cfg = synth.SMALL_MOE
+    W, _ = _model(oracle_lib, cfg, seed=6)
+    L = W["layers"][0]
+    for n in ("e_wg", "e_sg", "e_wu", "e_su", "e_wd", "e_sd"):
+        L[n] = L[n][:1].expand_as(L[n]).contiguous()  # every routed expert = expert 0
+    m = oracle_lib.OracleModel(cfg, synth.weights_to_numpy(W))
+    b = np.random.default_rng(8).normal(size=cfg.hidden)
+    delta, sel, selw = m.moe_ffn(0, b)
+    # shared expert alone, and shared + one routed expert with weight 1
+    shared_only = oracle_lib.OracleModel(replace(cfg, top_k=0), synth.weights_to_numpy(W))
+    d_sh, _, _ = shared_only.moe_ffn(0, b)
+    one = replace(cfg, n_experts=1, top_k=1)
+    W1 = dict(W)
+    W1["layers"] = [dict(L, router=L["router"][:1].contiguous(),
+                         **{n: L[n][:1].contiguous() for n in ("e_wg", "e_sg", "e_wu", "e_su",
+                                                               "e_wd", "e_sd")})]
+    W1["layers"] += W["layers"][1:]
+    d_one, _, w1 = oracle_lib.OracleModel(one, synth.weights_to_numpy(W1)).moe_ffn(0, b)
+    assert w1[0] == 1.0  # softmax over a single expert
+    np.testing.assert_allclose(delta - d_sh, selw.sum() * (d_one - d_sh), rtol=1e-10, atol=1e-13)
+    # the weights are the router's softmax probabilities of the chosen experts, unrenormalised
+    p = torch.softmax(torch.from_numpy(b) @ L["router"].double().T, 0).numpy()
+    assert list(sel) == list(np.argsort(-p, kind="stable")[: cfg.top_k])
+    np.testing.assert_allclose(selw, p[sel], rtol=1e-12)
+    assert selw.sum() < 1.0
+
+
+def test_prefill_then_decode_matches_full(oracle_lib):
+    cfg = synth.TINY
+    W, m = _model(oracle_lib, cfg, seed=9)
+    prompt = synth.gen_tokens(cfg.vocab, 16, seed=9).numpy()
+    kc, vc = m.new_cache()
+    g0 = m.prefill(kc, vc, prompt)
+    seq = list(prompt) + [g0]
+    tok = g0
+    for s in range(4):
+        tok, _, _ = m.decode_step(kc, vc, tok, len(prompt) + s)
+        seq.append(tok)
+    # the greedy continuation recomputed from scratch
+    for j in range(len(prompt), len(seq) - 1):
+        assert m.forward_full(np.array(seq[: j + 1], np.int32))[0] == seq[j + 1]
