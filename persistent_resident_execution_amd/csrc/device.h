@@ -1,0 +1,171 @@
+// Device-side primitives for gfx950 (CDNA4): buffer loads/stores with
+// explicit cache-scope bits, device-scope flag access, DPP wavefront
+// reductions and bf16 / fp8 unpacking.
+//
+// Visibility between workgroups inside one resident kernel.  The eight XCDs
+// of the chip each have a private L2 that is not kept coherent with the
+// others (persistent-execution survey, section 1; Fleet's two-level event
+// sync relies on CDNA cache-scope modifiers, section 7.2).  Everything one
+// workgroup hands to another therefore goes through device-scope ("sc1")
+// accesses: producers write activations with sc1 stores (written through
+// past the private L2), wait for those stores to complete (s_waitcnt), and
+// only then store the ready flag with an sc1 store; consumers poll the flag
+// with sc1 loads and read the activations with sc1 loads, which are not
+// served from a stale private line.  No cache-wide write-back or invalidate
+// is issued on the hot path.  Weights are only read, so they use ordinary
+// (or streaming) loads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pre {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Cache-policy operand of the buffer intrinsics on gfx94x/gfx950:
+// bit 0 = sc0, bit 1 = nt, bit 4 = sc1.
+constexpr int CP_DEF = 0;
+constexpr int CP_NT = 2;
+constexpr int CP_SC1 = 16;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Raw buffer over [p, p + bytes): loads past the end return 0, stores past
+// the end are dropped.  Word 3 is the gfx9 data-format default.
+__device__ __forceinline__ Rsrc mkbuf(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int CP>
+__device__ __forceinline__ v4i ld128(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ float ldf(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP));
+}
+template <int CP>
+__device__ __forceinline__ void stf(Rsrc r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st128(Rsrc r, uint32_t off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st16(Rsrc r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, CP);
+}
+
+// Device-scope 32-bit accesses at per-lane addresses (global_load/store sc1).
+__device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_sc1(const float *p) {
+  return __builtin_bit_cast(float, ld_flag(reinterpret_cast<const uint32_t *>(p)));
+}
+__device__ __forceinline__ void st_sc1(float *p, float v) {
+  st_flag(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v));
+}
+
+// Wait until every memory operation this thread issued has completed.
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---- wavefront reductions (DPP) ------------------------------------------
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROWMASK, 0xf, false));
+}
+// Sum over each group of 8 lanes, result in every lane of the group.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  return v;
+}
+// Sum over each row of 16 lanes, result in every lane of the row.
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+// Sum over the 64 lanes, wave-uniform result.  Fixed order: deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  v += dpp<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp<0x143, 0xc>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ---- unpacking -----------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Eight bf16 weights (one 16-byte load) dotted with eight fp32 activations.
+__device__ __forceinline__ float dot8_bf16(v4i w, const float4 a, const float4 b, float acc) {
+  acc = fmaf(bf_lo(w.x), a.x, acc);
+  acc = fmaf(bf_hi(w.x), a.y, acc);
+  acc = fmaf(bf_lo(w.y), a.z, acc);
+  acc = fmaf(bf_hi(w.y), a.w, acc);
+  acc = fmaf(bf_lo(w.z), b.x, acc);
+  acc = fmaf(bf_hi(w.z), b.y, acc);
+  acc = fmaf(bf_lo(w.w), b.z, acc);
+  acc = fmaf(bf_hi(w.w), b.w, acc);
+  return acc;
+}
+
+// Four OCP e4m3 codes (one dword, byte 0 first) to fp32, exactly.
+__device__ __forceinline__ void fp8x4(uint32_t w, float (&o)[4]) {
+  v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+
+// Sixteen fp8 weights (one 16-byte load) dotted with sixteen activations.
+__device__ __forceinline__ float dot16_fp8(v4i w, const float *x) {
+  float acc = 0.f, f[4];
+  const float4 *x4 = reinterpret_cast<const float4 *>(x);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    fp8x4((uint32_t)w[q], f);
+    const float4 a = x4[q];
+    acc = fmaf(f[0], a.x, acc);
+    acc = fmaf(f[1], a.y, acc);
+    acc = fmaf(f[2], a.z, acc);
+    acc = fmaf(f[3], a.w, acc);
+  }
+  return acc;
+}
+
+// Wavefront index inside the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
+}  // namespace pre

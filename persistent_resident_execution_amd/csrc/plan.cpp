@@ -1,0 +1,379 @@
+// Host-side construction and validation of the decode step's task table.
+//
+// Built once per engine: it fixes which workgroup computes which rows /
+// chunks of every stage of every layer, which ready-flag slots each task
+// waits on, and where every activation lives in the workspace.  The
+// validator re-derives the producer/consumer relation from the shapes and
+// checks the table against it, so a mistake in the builder is caught on the
+// host before anything is launched.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/pre.h"
+#include "plan.h"
+
+namespace pre {
+
+static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+static int32_t pad_to(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+static int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+int derive_dims(const pre_config *c, int n_cus, Dims *D) {
+  if (!c || !D) return PRE_ERR_ARG;
+  std::memset(D, 0, sizeof(*D));
+  if (c->n_layers < 1 || c->hidden < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->vocab < 1 || c->max_ctx < 2 || c->batch < 1)
+    return PRE_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return PRE_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return PRE_ERR_SHAPE;
+  if (c->hidden % 8 || (c->n_q_heads * c->head_dim) % 8) return PRE_ERR_SHAPE;
+  if (c->batch > 8) return PRE_ERR_SHAPE;
+  if (c->batch != 1) return PRE_ERR_UNSUPPORTED;
+  const bool moe = c->n_experts > 0;
+  if (moe) {
+    if (c->expert_dtype != 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 16 ||
+        c->n_shared < 0 || c->n_shared > 4 || c->expert_ffn < 16 || c->expert_ffn % 16 ||
+        c->hidden % 16 || c->n_experts > 1024)
+      return PRE_ERR_SHAPE;
+  } else {
+    if (c->ffn_dim < 8 || c->ffn_dim % 8) return PRE_ERR_SHAPE;
+  }
+  D->L = c->n_layers; D->h = c->hidden; D->Hq = c->n_q_heads; D->Hkv = c->n_kv_heads;
+  D->d = c->head_dim; D->ffn = c->ffn_dim; D->V = c->vocab; D->B = c->batch;
+  D->max_ctx = c->max_ctx;
+  D->E = moe ? c->n_experts : 0; D->top_k = moe ? c->top_k : 0;
+  D->n_shared = moe ? c->n_shared : 0; D->effn = moe ? c->expert_ffn : 0; D->moe = moe;
+  D->G = c->n_q_heads / c->n_kv_heads;
+  if (D->G > 8) return PRE_ERR_SHAPE;
+  D->qkv_pairs = D->Hkv * (D->G + 2) * D->d / 2;
+  D->F = moe ? (D->top_k + D->n_shared) * D->effn : D->ffn;
+  D->W = c->grid_wgs > 0 ? c->grid_wgs : n_cus;
+  if (D->W < 1 || D->W > 4096) return PRE_ERR_SHAPE;
+  D->X = 8;
+  const int bg = D->B * D->Hkv;
+  D->NC = c->attn_splits > 0 ? c->attn_splits : std::max(1, D->W / bg);
+  if (bg * D->NC > D->W) return PRE_ERR_SHAPE;
+  D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
+  if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
+  D->stages_per_layer = moe ? 6 : 5;
+  D->n_si = D->L * D->stages_per_layer + 1;
+  D->kmax = pad_to(std::max({D->h, D->Hq * D->d, D->F, moe ? D->E : 0}), 1024);
+  D->cmax = cdiv(D->max_ctx, D->NC);
+  const int waves = D->threads / 64;
+  // GEMV phase: staged input + reduction scratch.  Attention phase: q, scores,
+  // per-wave output partials, softmax stats.
+  int64_t gemv = (int64_t)D->kmax + 256;
+  int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
+                 (int64_t)waves * D->G * D->d + 4 * D->G + 256;
+  D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);
+  if (D->lds_bytes > 160 * 1024) return PRE_ERR_SHAPE;
+  D->eps = c->rms_eps;
+  D->theta = c->rope_theta;
+  return PRE_OK;
+}
+
+void build_layout(const Dims &D, Layout *Lo) {
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
+  const int64_t f = 4;
+  Lo->status = take(sizeof(DevStatus));
+  Lo->flags = take((int64_t)D.n_si * D.W * 4);
+  Lo->counters = take((int64_t)D.L * D.B * D.Hkv * 4);
+  Lo->layers = take((int64_t)D.L * sizeof(DevLayer));
+  Lo->tasks = take((int64_t)D.n_si * D.W * sizeof(Task));
+  Lo->rope = take((int64_t)D.max_ctx * D.d * f);          // cos then sin, [pos][d/2] each
+  Lo->xcc = take((int64_t)D.W * 4);
+  Lo->x_out = take((int64_t)D.L * D.B * D.h * f);
+  Lo->xm = take((int64_t)D.L * D.B * D.h * f);
+  Lo->q = take((int64_t)D.L * D.B * D.Hq * D.d * f);
+  Lo->o = take((int64_t)D.L * D.B * D.Hq * D.d * f);
+  Lo->u = take((int64_t)D.L * D.B * D.F * f);
+  Lo->rl = take((int64_t)D.L * D.B * std::max(D.E, 1) * f);
+  Lo->part = take((int64_t)D.L * D.B * D.Hkv * D.NC * D.G * (D.d + 2) * f);
+  Lo->lmp = take((int64_t)D.W * D.B * 8);
+  Lo->x_emb = take((int64_t)D.B * D.h * f);
+  Lo->a_norm = take((int64_t)D.B * D.kmax * f);
+  Lo->tok = take((int64_t)D.B * 4 * 4);
+  Lo->total = off;
+}
+
+// Balanced split of n items over W tasks.
+static inline void split(int64_t n, int W, int t, int32_t *lo, int32_t *hi) {
+  *lo = (int32_t)(n * t / W);
+  *hi = (int32_t)(n * (t + 1) / W);
+}
+
+static inline int32_t slot(const Dims &D, int si, int i) { return si * D.W + i; }
+
+void build_tasks(const Dims &D, std::vector<Task> &T) {
+  const int W = D.W, spl = D.stages_per_layer;
+  T.assign((size_t)D.n_si * W, Task{});
+  auto at = [&](int si, int lam) -> Task & { return T[(size_t)si * W + lam]; };
+  const int P = D.qkv_pairs, PG = P / D.Hkv;  // pairs per KV group
+  for (int l = 0; l < D.L; ++l) {
+    const int s_qkv = l * spl, s_attn = s_qkv + 1, s_o = s_qkv + 2;
+    const int s_prev = l > 0 ? l * spl - 1 : -1;  // previous layer's last FFN stage
+    for (int lam = 0; lam < W; ++lam) {
+      Task &t = at(s_qkv, lam);
+      t.op = OP_QKV; t.layer = l;
+      split(P, W, lam, &t.r0, &t.r1);
+      t.wait_lo = s_prev >= 0 ? slot(D, s_prev, 0) : 0;
+      t.wait_hi = s_prev >= 0 ? slot(D, s_prev, W) : 0;
+      t.signal = slot(D, s_qkv, lam);
+    }
+    const int nattn = D.B * D.Hkv * D.NC;
+    for (int lam = 0; lam < W; ++lam) {
+      Task &t = at(s_attn, lam);
+      if (lam >= nattn) { t.op = OP_NONE; t.signal = -1; continue; }
+      const int bg = lam / D.NC, c = lam % D.NC, g = bg % D.Hkv;
+      t.op = OP_ATTN; t.layer = l; t.r0 = c; t.r1 = D.NC; t.aux = bg;
+      // producers: QKV tasks whose pair range meets group g's pairs
+      int lo = -1, hi = -1;
+      for (int q = 0; q < W; ++q) {
+        int32_t a, b;
+        split(P, W, q, &a, &b);
+        if (a < b && a < (g + 1) * PG && b > g * PG) {
+          if (lo < 0) lo = q;
+          hi = q + 1;
+        }
+      }
+      t.wait_lo = slot(D, s_qkv, lo);
+      t.wait_hi = slot(D, s_qkv, hi);
+      t.signal = slot(D, s_attn, bg);
+    }
+    for (int lam = 0; lam < W; ++lam) {
+      Task &t = at(s_o, lam);
+      t.op = OP_OPROJ; t.layer = l;
+      split(D.h, W, lam, &t.r0, &t.r1);
+      t.wait_lo = slot(D, s_attn, 0);
+      t.wait_hi = slot(D, s_attn, D.B * D.Hkv);
+      t.signal = slot(D, s_o, lam);
+    }
+    if (!D.moe) {
+      const int s_gu = s_qkv + 3, s_dn = s_qkv + 4;
+      for (int lam = 0; lam < W; ++lam) {
+        Task &g = at(s_gu, lam);
+        g.op = OP_GU; g.layer = l;
+        split(D.ffn, W, lam, &g.r0, &g.r1);
+        g.wait_lo = slot(D, s_o, 0); g.wait_hi = slot(D, s_o, W);
+        g.signal = slot(D, s_gu, lam);
+        Task &dn = at(s_dn, lam);
+        dn.op = OP_DOWN; dn.layer = l;
+        split(D.h, W, lam, &dn.r0, &dn.r1);
+        dn.wait_lo = slot(D, s_gu, 0); dn.wait_hi = slot(D, s_gu, W);
+        dn.signal = slot(D, s_dn, lam);
+      }
+    } else {
+      const int s_r = s_qkv + 3, s_egu = s_qkv + 4, s_ed = s_qkv + 5;
+      for (int lam = 0; lam < W; ++lam) {
+        Task &r = at(s_r, lam);
+        r.op = OP_ROUTER; r.layer = l;
+        split(D.E, W, lam, &r.r0, &r.r1);
+        r.wait_lo = slot(D, s_o, 0); r.wait_hi = slot(D, s_o, W);
+        r.signal = slot(D, s_r, lam);
+        Task &g = at(s_egu, lam);
+        g.op = OP_EGU; g.layer = l;
+        split(D.F, W, lam, &g.r0, &g.r1);
+        g.wait_lo = slot(D, s_r, 0); g.wait_hi = slot(D, s_r, W);
+        g.signal = slot(D, s_egu, lam);
+        Task &dn = at(s_ed, lam);
+        dn.op = OP_EDOWN; dn.layer = l;
+        split(D.h, W, lam, &dn.r0, &dn.r1);
+        dn.wait_lo = slot(D, s_egu, 0); dn.wait_hi = slot(D, s_egu, W);
+        dn.signal = slot(D, s_ed, lam);
+      }
+    }
+  }
+  const int s_lm = D.L * spl, s_last = s_lm - 1;
+  for (int lam = 0; lam < W; ++lam) {
+    Task &t = at(s_lm, lam);
+    t.op = OP_LM; t.layer = D.L;
+    split(D.V, W, lam, &t.r0, &t.r1);
+    t.wait_lo = slot(D, s_last, 0); t.wait_hi = slot(D, s_last, W);
+    t.signal = slot(D, s_lm, lam);
+  }
+}
+
+// Expected op of a stage instance.
+static int32_t op_of_stage(const Dims &D, int si) {
+  if (si == D.L * D.stages_per_layer) return OP_LM;
+  const int k = si % D.stages_per_layer;
+  static const int32_t dense[5] = {OP_QKV, OP_ATTN, OP_OPROJ, OP_GU, OP_DOWN};
+  static const int32_t moe[6] = {OP_QKV, OP_ATTN, OP_OPROJ, OP_ROUTER, OP_EGU, OP_EDOWN};
+  return D.moe ? moe[k] : dense[k];
+}
+
+// Rows (or pairs, or chunks) a GEMV stage must cover.
+static int64_t coverage_target(const Dims &D, int32_t op) {
+  switch (op) {
+    case OP_QKV: return D.qkv_pairs;
+    case OP_OPROJ: case OP_DOWN: case OP_EDOWN: return D.h;
+    case OP_GU: return D.ffn;
+    case OP_ROUTER: return D.E;
+    case OP_EGU: return D.F;
+    case OP_LM: return D.V;
+    default: return -1;
+  }
+}
+
+// Returns 0 if every check passes, else the number of the first failed one:
+//  1 table size; 2 op of each task matches its stage; 3 wait ranges point
+//  only at slots of earlier stage instances that some task sets; 4 no two
+//  stage instances' tasks set the same slot and each GEMV task sets its own;
+//  5 row/pair coverage exactly once per GEMV stage; 6 every attention
+//  (sequence, KV head) has each chunk exactly once; 7 every consumer waits on
+//  all producers of its input; 8 every workgroup takes part in every GEMV
+//  stage (this orders slot reuse across steps); 9 layer numbers.
+int validate(const Dims &D, const std::vector<Task> &T) {
+  const int W = D.W, n_slots = D.n_si * W;
+  if ((int64_t)T.size() != (int64_t)D.n_si * W) return 1;
+  std::vector<int> setter_si(n_slots, -1);
+  for (int si = 0; si < D.n_si; ++si) {
+    const int32_t want = op_of_stage(D, si);
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      if (t.op != want && !(want == OP_ATTN && t.op == OP_NONE)) return 2;
+      if (t.op == OP_NONE) continue;
+      if (t.signal < 0 || t.signal >= n_slots || t.signal / W != si) return 4;
+      if (setter_si[t.signal] >= 0 && setter_si[t.signal] != si) return 4;
+      setter_si[t.signal] = si;
+      if (t.op != OP_ATTN && t.signal != si * W + lam) return 4;
+    }
+  }
+  for (int si = 0; si < D.n_si; ++si)
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      if (t.op == OP_NONE) continue;
+      if (t.wait_lo < 0 || t.wait_hi < t.wait_lo || t.wait_hi > n_slots) return 3;
+      for (int s = t.wait_lo; s < t.wait_hi; ++s)
+        if (setter_si[s] < 0 || setter_si[s] >= si) return 3;
+      const int want_layer = (t.op == OP_LM) ? D.L : si / D.stages_per_layer;
+      if (t.layer != want_layer) return 9;
+    }
+  // coverage
+  for (int si = 0; si < D.n_si; ++si) {
+    const int32_t op = op_of_stage(D, si);
+    if (op == OP_ATTN) {
+      std::vector<int> seen((size_t)D.B * D.Hkv * D.NC, 0);
+      for (int lam = 0; lam < W; ++lam) {
+        const Task &t = T[(size_t)si * W + lam];
+        if (t.op != OP_ATTN) continue;
+        if (t.aux < 0 || t.aux >= D.B * D.Hkv || t.r0 < 0 || t.r0 >= D.NC || t.r1 != D.NC) return 6;
+        if (t.signal != si * W + t.aux) return 6;
+        seen[(size_t)t.aux * D.NC + t.r0]++;
+      }
+      for (int v : seen) if (v != 1) return 6;
+      continue;
+    }
+    const int64_t n = coverage_target(D, op);
+    std::vector<int> cnt(n, 0);
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      if (t.r0 < 0 || t.r1 < t.r0 || t.r1 > n) return 5;
+      for (int r = t.r0; r < t.r1; ++r) cnt[r]++;
+    }
+    for (int v : cnt) if (v != 1) return 5;
+  }
+  // dependencies: the exact producer set each consumer needs
+  auto covers = [&](const Task &t, int si_prod, int lo, int hi) {
+    // every slot si_prod*W + [lo, hi) inside the wait range
+    return t.wait_lo <= si_prod * W + lo && t.wait_hi >= si_prod * W + hi;
+  };
+  const int spl = D.stages_per_layer;
+  const int PG = D.qkv_pairs / D.Hkv;
+  for (int si = 0; si < D.n_si; ++si) {
+    const int32_t op = op_of_stage(D, si);
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      if (t.op == OP_NONE) continue;
+      bool ok = true;
+      switch (op) {
+        case OP_QKV: if (si > 0) ok = covers(t, si - 1, 0, W); break;
+        case OP_ATTN: {
+          const int g = t.aux % D.Hkv;
+          for (int q = 0; q < W && ok; ++q) {
+            const Task &p = T[(size_t)(si - 1) * W + q];
+            if (p.r0 < p.r1 && p.r0 < (g + 1) * PG && p.r1 > g * PG) ok = covers(t, si - 1, q, q + 1);
+          }
+          break;
+        }
+        case OP_OPROJ: ok = covers(t, si - 1, 0, D.B * D.Hkv); break;
+        case OP_LM: ok = covers(t, si - 1, 0, W); break;
+        default: ok = covers(t, si - 1, 0, W); break;  // GU, DOWN, ROUTER, EGU, EDOWN
+      }
+      if (!ok) return 7;
+    }
+    if (op != OP_ATTN)
+      for (int lam = 0; lam < W; ++lam)
+        if (T[(size_t)si * W + lam].op == OP_NONE) return 8;
+  }
+  (void)spl;
+  return 0;
+}
+
+int64_t step_bytes(const pre_config *c, const int32_t *pos) {
+  if (c->n_layers < 1 || c->hidden < 1 || c->batch < 1 || c->batch > 8) return -1;
+  const int64_t h = c->hidden, d = c->head_dim, L = c->n_layers;
+  int64_t w = 0;
+  w += (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * d * h * 2;  // qkv
+  w += h * c->n_q_heads * d * 2;                                   // o
+  w += 2 * h * 2;                                                  // norms
+  if (c->n_experts > 0) {
+    const int64_t f = c->expert_ffn;
+    const int64_t blk_up = ((f + 127) / 128) * ((h + 127) / 128) * 2;
+    const int64_t per = 3 * f * h + 3 * blk_up;
+    w += (int64_t)c->n_experts * h * 2;                          // router
+    w += (int64_t)(c->top_k + c->n_shared) * per;                // active experts
+  } else {
+    w += 3 * (int64_t)c->ffn_dim * h * 2;
+  }
+  int64_t total = w * L + (int64_t)c->vocab * h * 2 + h * 2;     // LM head + final norm
+  for (int b = 0; b < c->batch; ++b) {
+    total += h * 2;                                              // embedding row
+    const int64_t kv_row = (int64_t)c->n_kv_heads * d * 2;       // one position, K or V
+    total += L * 2 * kv_row * ((int64_t)pos[b] + 1);             // attend 0..pos
+    total += L * 2 * kv_row;                                     // append at pos
+  }
+  return total;
+}
+
+}  // namespace pre
+
+extern "C" int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int32_t *h_tasks,
+                                 int32_t max_tasks) {
+  if (!cfg || !out) return PRE_ERR_ARG;
+  pre::Dims D;
+  int rc = pre::derive_dims(cfg, 256, &D);
+  if (rc != PRE_OK) return rc;
+  std::vector<pre::Task> T;
+  pre::build_tasks(D, T);
+  pre::Layout Lo;
+  pre::build_layout(D, &Lo);
+  out->n_stage_inst = D.n_si;
+  out->n_wgs = D.W;
+  out->n_slots = D.n_si * D.W;
+  out->n_tasks = (int32_t)T.size();
+  out->attn_splits = D.NC;
+  out->validator = pre::validate(D, T);
+  out->workspace_bytes = Lo.total;
+  if (h_tasks)
+    for (int32_t i = 0; i < max_tasks && i < (int32_t)T.size(); ++i)
+      std::memcpy(h_tasks + 8 * (int64_t)i, &T[i], sizeof(pre::Task));
+  return PRE_OK;
+}
+
+extern "C" int pre_plan_validate(const pre_config *cfg, const int32_t *h_tasks, int32_t n_tasks) {
+  if (!cfg || !h_tasks) return PRE_ERR_ARG;
+  pre::Dims D;
+  int rc = pre::derive_dims(cfg, 256, &D);
+  if (rc != PRE_OK) return rc;
+  std::vector<pre::Task> T((size_t)std::max(n_tasks, 0));
+  if (n_tasks > 0) std::memcpy(T.data(), h_tasks, sizeof(pre::Task) * (size_t)n_tasks);
+  return pre::validate(D, T);
+}
+
+extern "C" int64_t pre_step_bytes(const pre_config *cfg, const int32_t *h_pos) {
+  if (!cfg || !h_pos) return -1;
+  return pre::step_bytes(cfg, h_pos);
+}

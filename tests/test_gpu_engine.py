@@ -1,0 +1,176 @@
+"""GPU parity of the HIP decode path against the CPU oracle (through the C ABI).
+
+Both paths -- the persistent resident kernel and the one-kernel-per-operator
+baseline -- fill the cache from the same seeded prompt (teacher-forced) and
+then decode greedily; the oracle does the same on its own.  The rules are in
+tests/parity.py.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import parity  # noqa: E402
+
+from persistent_resident_execution_amd import engine as E  # noqa: E402
+from persistent_resident_execution_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny(oracle_lib):
+    _say("[setup] tiny dense weights + oracle run (prompt 128, 64 steps)")
+    S = parity.DenseSetup(oracle_lib, synth.TINY, seed=0)
+    prompt = synth.gen_tokens(synth.TINY.vocab, 128, seed=0).numpy()
+    ref = parity.oracle_run(S.om, prompt, 64)
+    return S, prompt, ref
+
+
+def _check_run(S, prompt, ref, baseline, **kw):
+    eng = S.engine(**kw)
+    g0, toks, lgs, hds = parity.gpu_run(eng, S.m, prompt, len(ref[2]), baseline=baseline)
+    recs = parity.check_streams(g0, ref[0], ref[1], (toks, lgs, hds), (ref[2], ref[3], ref[4]))
+    worst = max((r.get("max_dlogit", 0) for r in recs), default=0)
+    _say(f"  {'baseline' if baseline else 'persistent'} {kw}: {len(recs)} steps compared, "
+         f"max dlogit {worst:.2e}, max hidden rel "
+         f"{max((r.get('hidden_rel', 0) for r in recs), default=0):.2e}")
+    return eng, toks, lgs
+
+
+def test_fp8_unpacking_matches_oracle_decoder(oracle_lib):
+    _say("[test] fp8 e4m3 unpacking, all 256 codes")
+    got = E.fp8_decode_table().double().numpy()
+    ref = oracle_lib.fp8_to_f64(np.arange(256, dtype=np.uint8))
+    finite = ~np.isnan(ref)
+    assert np.array_equal(got[finite], ref[finite])
+
+
+def test_tiny_persistent_matches_oracle(tiny):
+    S, prompt, ref = tiny
+    _say("[test] tiny persistent, 256 workgroups")
+    _check_run(S, prompt, ref, baseline=False)
+
+
+def test_tiny_persistent_cache_matches_oracle_prefill(tiny):
+    S, prompt, ref = tiny
+    _say("[test] tiny persistent prefill cache vs oracle cache")
+    eng = S.engine()
+    P = len(prompt)
+    eng.set_positions([0])
+    eng.decode(P, forced=torch.as_tensor(prompt.astype(np.int32), device="cuda").view(P, 1))
+    torch.cuda.synchronize()
+    eng.status()
+    kc_ref, vc_ref = ref[5]
+    for name, dev, host in (("K", S.kc, kc_ref), ("V", S.vc, vc_ref)):
+        got = dev[:, 0, :, :P].float().cpu().numpy()
+        want = host[:, :, :P].view(np.uint16).astype(np.uint32) << 16
+        want = want.view(np.float32)
+        diff = np.abs(got - want)
+        rel = diff.max() / np.abs(want).max()
+        frac = float(np.mean(diff > 0))
+        _say(f"  {name}: max rel diff {rel:.2e}, fraction of differing bf16 values {frac:.2e}")
+        assert rel < 1e-2 and frac < 1e-2
+
+
+def test_tiny_baseline_matches_oracle(tiny):
+    S, prompt, ref = tiny
+    _say("[test] tiny one-kernel-per-op baseline")
+    _check_run(S, prompt, ref, baseline=True)
+
+
+@pytest.mark.parametrize("grid", [16, 64])
+def test_tiny_persistent_fewer_workgroups(tiny, grid):
+    S, prompt, ref = tiny
+    _say(f"[test] tiny persistent, {grid} workgroups")
+    _check_run(S, prompt, ref, baseline=False, grid_wgs=grid)
+
+
+def test_persistent_deterministic_and_resumable(tiny):
+    S, prompt, ref = tiny
+    _say("[test] determinism and decode(n)+decode(m) == decode(n+m)")
+    eng = S.engine()
+    P = len(prompt)
+    forced = torch.as_tensor(prompt.astype(np.int32), device="cuda").view(P, 1)
+    runs = []
+    for split in (None, 7):
+        eng.set_positions([0])
+        g0 = int(eng.decode(P, forced=forced)[-1, 0])
+        lg = torch.zeros((20, 1, S.m.vocab), device="cuda")
+        inp = torch.tensor([g0], dtype=torch.int32, device="cuda")
+        if split is None:
+            out = eng.decode(20, in_tokens=inp, logits=lg)
+        else:
+            a = eng.decode(split, in_tokens=inp, logits=lg[:split])
+            b = eng.decode(20 - split, in_tokens=a[-1].contiguous(), logits=lg[split:])
+            out = torch.cat([a, b])
+        torch.cuda.synchronize()
+        eng.status()
+        runs.append((out.cpu().numpy(), lg.cpu().numpy()))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1], runs[1][1])
+
+
+def test_persistent_equals_baseline_tokens(tiny):
+    S, prompt, ref = tiny
+    _say("[test] persistent vs baseline")
+    _, t1, l1 = _check_run(S, prompt, ref, baseline=False)
+    _, t2, l2 = _check_run(S, prompt, ref, baseline=True)
+    assert np.array_equal(t1, t2)
+    assert np.max(np.abs(l1 - l2)) < 1e-3
+
+
+def test_bad_token_is_latched_and_reset_clears_it(tiny):
+    S, _, _ = tiny
+    _say("[test] out-of-range token -> device error, reset")
+    eng = S.engine()
+    eng.set_positions([0])
+    eng.decode(1, in_tokens=torch.tensor([S.m.vocab + 5], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    st = eng.status(raise_on_error=False)
+    assert st["error"] == 2 and st["observed"] == S.m.vocab + 5
+    with pytest.raises(E.PreError):
+        eng.decode(1, in_tokens=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    eng.reset()
+    eng.set_positions([0])
+    eng.decode(1, in_tokens=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert eng.status()["error"] == 0
+
+
+def test_context_limit_is_checked_on_host(tiny):
+    S, _, _ = tiny
+    eng = S.engine()
+    eng.set_positions([S.m.max_ctx - 2])
+    with pytest.raises(E.PreError) as ei:
+        eng.decode(3, in_tokens=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    assert ei.value.code == -9
+
+
+@pytest.fixture(scope="module")
+def small(oracle_lib):
+    _say("[setup] small dense (ragged shapes) + oracle run (prompt 40, 24 steps)")
+    S = parity.DenseSetup(oracle_lib, synth.SMALL_DENSE, seed=3)
+    prompt = synth.gen_tokens(synth.SMALL_DENSE.vocab, 40, seed=3).numpy()
+    ref = parity.oracle_run(S.om, prompt, 24)
+    return S, prompt, ref
+
+
+@pytest.mark.parametrize("grid,threads", [(0, 0), (16, 256), (37, 512)])
+def test_small_dense_ragged_persistent(small, grid, threads):
+    S, prompt, ref = small
+    _say(f"[test] small dense persistent grid={grid} threads={threads}")
+    _check_run(S, prompt, ref, baseline=False, grid_wgs=grid, wg_threads=threads)
+
+
+def test_small_dense_ragged_baseline(small):
+    S, prompt, ref = small
+    _say("[test] small dense baseline")
+    _check_run(S, prompt, ref, baseline=True)

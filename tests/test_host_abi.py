@@ -1,0 +1,136 @@
+"""Host-side checks that need no GPU: the C-ABI library loads and exports
+every function include/pre.h declares; the task-table builder produces
+tables its validator accepts for every workload; the validator rejects
+tables with planted faults; and the per-step byte count agrees with an
+independent count from the shapes."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from persistent_resident_execution_amd import engine as E
+from persistent_resident_execution_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(E.LIB_PATH):
+        from persistent_resident_execution_amd import build
+        build.build()
+    return E.lib()
+
+
+def test_library_exports_every_declared_function(lib):
+    hdr = open(os.path.join(ROOT, "include", "pre.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"\b(pre_[a-z_0-9]+)\s*\(", hdr))
+    assert len(names) >= 15
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in pre.h but not exported"
+    assert names >= set(E.EXPORTS)
+
+
+def test_strerror_and_argument_errors(lib):
+    import ctypes as C
+    assert lib.pre_strerror(0) == b"ok"
+    for code in range(-1, -10, -1):
+        assert lib.pre_strerror(code) != b"unknown error"
+    chk = E.Check(None, None)
+    assert lib.pre_engine_decode(None, 1, None, None, None, C.byref(chk), None) == -1
+    assert lib.pre_baseline_decode(None, 1, None, None, None, C.byref(chk), None) == -1
+    assert lib.pre_engine_destroy(None) == -1
+    st = E.Status()
+    assert lib.pre_engine_status(None, C.byref(st)) == -1
+
+
+ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
+    synth.TINY, synth.SMALL_DENSE, synth.SMALL_MOE]
+
+
+@pytest.mark.parametrize("m", ALL, ids=lambda m: f"{m.name}-{m.max_ctx}")
+@pytest.mark.parametrize("grid", [0, 1, 7, 16, 37, 256])
+def test_plans_validate(lib, m, grid):
+    if grid and grid < m.n_kv_heads:
+        with pytest.raises(E.PreError):
+            E.plan_describe(m, grid_wgs=grid)
+        return
+    info, _ = E.plan_describe(m, grid_wgs=grid)
+    assert info.validator == 0
+    assert info.n_stage_inst == m.n_layers * (6 if m.is_moe else 5) + 1
+    assert info.workspace_bytes > 0
+
+
+def test_microbatch_reported_unsupported(lib):
+    with pytest.raises(E.PreError) as ei:
+        E.plan_describe(synth.WORKLOADS["dense8b_mb8"].model)
+    assert ei.value.code == -6
+
+
+def test_attention_is_xcd_local_on_the_8b_shape(lib):
+    """Each KV head's attention chunks sit on one XCD and wait only on QKV
+    tasks of that XCD (the head-to-XCD routing)."""
+    m = synth.DENSE8B
+    info, T = E.plan_describe(m, with_tasks=True)
+    W = info.n_wgs
+    per = W // 8
+    attn = T[1 * W:2 * W]
+    for lam in range(W):
+        op, layer, r0, r1, aux, lo, hi, sig = attn[lam]
+        g = aux % m.n_kv_heads
+        assert op == 2 and lam // per == g
+        assert lo == W + 0 * W - W + g * per and hi == g * per + per  # slots of QKV stage 0
+
+
+def _planted(m, mutate):
+    info, T = E.plan_describe(m, with_tasks=True)
+    T = T.copy()
+    mutate(T, info.n_wgs)
+    return E.plan_validate(m, T)
+
+
+def test_validator_rejects_planted_faults(lib):
+    m = synth.SMALL_DENSE
+    W = E.plan_describe(m)[0].n_wgs
+    info, T = E.plan_describe(m, with_tasks=True)
+    assert E.plan_validate(m, T) == 0
+    # a consumer that no longer waits for one producer
+    assert _planted(m, lambda T, W: T.__setitem__((2 * W + 5, 6), T[2 * W + 5, 6] - 1)) == 7
+    # two tasks computing the same rows (duplicate), one row range lost
+    def dup(T, W):
+        T[3 * W + 4, 2:4] = T[3 * W + 3, 2:4]
+    assert _planted(m, dup) == 5
+    # a wait on a slot of a later stage (would deadlock)
+    assert _planted(m, lambda T, W: T.__setitem__((3 * W, 6), 9 * W)) == 3
+    # a workgroup skipping a GEMV stage (breaks slot-reuse ordering)
+    def skip(T, W):
+        T[4 * W + 2] = [0, 0, 0, 0, 0, 0, 0, -1]
+    assert _planted(m, skip) in (2, 8)
+    # an attention chunk dropped
+    def drop(T, W):
+        T[1 * W + 3, 2] = T[1 * W + 2, 2]
+    assert _planted(m, drop) == 6
+    # a signal slot shared by two tasks
+    assert _planted(m, lambda T, W: T.__setitem__((4 * W + 1, 7), 4 * W + 0)) == 4
+
+
+def _independent_step_bytes(m, pos):
+    wb = synth.weight_bytes(m)
+    total = sum(v for k, v in wb.items())
+    kv_row = m.n_kv_heads * m.head_dim * 2
+    total += m.n_layers * 2 * kv_row * (pos + 1) + m.n_layers * 2 * kv_row
+    return total
+
+
+@pytest.mark.parametrize("m", [synth.TINY, synth.DENSE8B, synth.MOE], ids=lambda m: m.name)
+def test_step_bytes_matches_shape_count(lib, m):
+    for pos in (0, 1023, 4000):
+        assert E.step_bytes(m, [pos]) == _independent_step_bytes(m, pos)
+
+
+def test_step_bytes_8b_order_of_magnitude(lib):
+    # 8B-shape: 32 x 436 MB of layer weights + 1.05 GB LM head ~ 15.0 GB of weights
+    b = E.step_bytes(synth.DENSE8B, [1024])
+    assert 15.0e9 < b < 15.3e9
