@@ -1,0 +1,205 @@
+"""Decode benchmark: µs/token and achieved HBM bandwidth of the persistent
+decode kernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 32] [--workload dense8b_ctx1024]
+
+One "step" is one decode step (one token) through the whole hot path.  The
+default workload is the 8B-shape dense decoder at batch 1: 32 layers, hidden
+4096, 32 query / 8 KV heads of 128, SwiGLU 14336, vocabulary 128256, bf16
+weights ~N(0, 0.02) from seed 0, the KV cache prefilled on the GPU from 1024
+random tokens, then greedy decode.  The timed region is ONE engine call of
+--steps steps (one persistent kernel launch), bracketed by device
+synchronisation; it is repeated --repeats times from the same prefilled
+position and the median is reported.  Inputs are resident in HBM.
+
+Also reported: the roofline of the persistent kernel (algorithmic bytes per
+launch over the launch time measured with HIP events on the launch stream,
+against 8 TB/s), the one-kernel-per-operator baseline on the same workload,
+the tiny-decoder persistent vs baseline latency, and the CPU oracle timed on
+a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup(workload, device="cuda", seed=0, **eng_kw):
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    from persistent_resident_execution_amd import synth
+    w = synth.WORKLOADS[workload]
+    m = w.model
+    t0 = time.time()
+    W = synth.gen_weights(m, seed=seed, device=device)
+    shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    eng = E.Engine(m, W, kc, vc, **eng_kw)
+    P = w.contexts[0]
+    prompt = synth.gen_tokens(m.vocab, P, seed=seed, device=device)
+    eng.set_positions([0])
+    out = eng.decode(P, forced=prompt.view(P, 1))  # cache filled by the engine itself
+    torch.cuda.synchronize()
+    eng.status()
+    g0 = out[-1].contiguous()
+    log(f"[bench] {workload}: weights + prefill of {P} tokens in {time.time() - t0:.1f}s")
+    return w, m, W, kc, vc, eng, g0
+
+
+def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
+    """Median/min seconds of one call of n_steps from position P; also returns
+    the per-call event times."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = torch.empty((max(n_steps, warmup_steps, 1), 1), dtype=torch.int32, device="cuda")
+    if warmup_steps:
+        eng.set_positions([P])
+        fn(warmup_steps, in_tokens=g0, out_tokens=out[:warmup_steps])
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        eng.set_positions([P])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn(n_steps, in_tokens=g0, out_tokens=out[:n_steps])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    eng.status()
+    return times, out[:n_steps, 0].cpu()
+
+
+def cpu_baseline(m, W, P, budget_s=15.0, max_steps=64):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    decode steps at context P of the same model (weights copied to the host;
+    the cache is a seeded synthetic one -- its values do not change the work)."""
+    import numpy as np
+    import oracle
+    from persistent_resident_execution_amd import synth
+    t0 = time.time()
+    om = oracle.OracleModel(m, synth.weights_to_numpy(W))
+    kc_t, vc_t = synth.gen_kv_cache(m, P, seed=1, device="cpu")
+    kc = synth.to_bits(kc_t)[:, 0]
+    vc = synth.to_bits(vc_t)[:, 0]
+    log(f"[bench] oracle set-up {time.time() - t0:.1f}s ({oracle.num_threads()} threads)")
+    tok, steps, t_start = 1, 0, time.time()
+    while steps < max_steps:
+        tok, _, _ = om.decode_step(kc, vc, int(tok), P + steps, want_logits=False, want_hidden=False)
+        steps += 1
+        if time.time() - t_start >= budget_s:
+            break
+    el = time.time() - t_start
+    return {"value": round(el / steps * 1e6, 1), "unit": "us/token", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} decode step(s) of the same {m.name} decoder at context {P}, batch 1, "
+                      f"fp64 C oracle, {el:.1f}s wall"}
+
+
+def tiny_comparison(repeats=5):
+    """Persistent vs one-kernel-per-op on the tiny decoder (latency bound)."""
+    import torch
+    _, m, _, _, _, eng, g0 = setup("tiny")
+    P, n = 128, 64
+    tp, _ = time_calls(eng, eng.decode, n, g0, P, repeats, 8)
+    tb, _ = time_calls(eng, eng.baseline_decode, n, g0, P, repeats, 8)
+    res = {}
+    for grid in (8, 16, 32, 64):
+        e2 = __import__("persistent_resident_execution_amd.engine", fromlist=["Engine"]).Engine(
+            m, eng._keep[0], eng._keep[1], eng._keep[2], grid_wgs=grid)
+        t, _ = time_calls(e2, e2.decode, n, g0, P, repeats, 8)
+        res[grid] = statistics.median(t) / n * 1e6
+        e2.close()
+    up = statistics.median(tp) / n * 1e6
+    ub = statistics.median(tb) / n * 1e6
+    best_grid = min(res, key=res.get)
+    eng.close()
+    torch.cuda.synchronize()
+    return {"persistent_us_per_token": round(up, 2), "per_op_us_per_token": round(ub, 2),
+            "speedup": round(ub / up, 2),
+            "persistent_us_per_token_by_grid": {str(k): round(v, 2) for k, v in res.items()},
+            "best_grid": best_grid, "best_speedup": round(ub / min(up, res[best_grid]), 2),
+            "launches_per_token_per_op": 8 * m.n_layers + 4, "launches_per_token_persistent": 1 / n}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--repeats", type=int, default=5)
+    ap.add_argument("--workload", default="dense8b_ctx1024")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle sample")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timing")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-decoder comparison")
+    ap.add_argument("--grid", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    torch.cuda.set_device(0)
+
+    w, m, W, kc, vc, eng, g0 = setup(args.workload, grid_wgs=args.grid)
+    P, K = w.contexts[0], args.steps
+    log(f"[bench] timing {args.repeats} x {K} persistent steps from position {P}")
+    tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
+    t_med = statistics.median(tp)
+    bytes_call = sum(E.step_bytes(m, [P + s]) for s in range(K))
+    us_tok = t_med / K * 1e6
+    gbps = bytes_call / t_med / 1e9
+    result = {
+        "metric": "decode us/token (batch 1) + achieved HBM GB/s as % of MI355X peak",
+        "value": round(us_tok, 2), "unit": "us/token", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us_tok / 1e3, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 weights/KV, fp32 compute",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, random prompt tokens)",
+        "config": {"workload": w.note, "layers": m.n_layers, "hidden": m.hidden,
+                   "heads": f"{m.n_q_heads}q/{m.n_kv_heads}kv x {m.head_dim}",
+                   "ffn": m.ffn_dim, "vocab": m.vocab, "context": P, "batch": m.batch,
+                   "parallelism": "single GPU, one workgroup per CU"},
+        "tokens_per_s": round(K / t_med, 1),
+        "hbm_gbps_algorithmic": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "repeats_us_per_token": [round(t / K * 1e6, 2) for t in tp],
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "pre_persistent", "bytes_per_launch": bytes_call,
+                     "launch_ms": round(t_med * 1e3, 3)},
+    }
+    if not args.no_baseline:
+        log("[bench] timing the one-kernel-per-op baseline")
+        tb, btoks = time_calls(eng, eng.baseline_decode, K, g0, P, max(1, args.repeats // 2), 0)
+        ub = statistics.median(tb) / K * 1e6
+        result["per_op_baseline"] = {"us_per_token": round(ub, 2),
+                                     "launches_per_token": 8 * m.n_layers + 4,
+                                     "persistent_speedup": round(ub / us_tok, 3),
+                                     "same_tokens": bool((btoks == toks).all())}
+    eng.close()
+    if not args.no_tiny:
+        log("[bench] tiny decoder persistent vs per-op")
+        result["tiny"] = tiny_comparison()
+    if not args.no_cpu:
+        log("[bench] CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(m, W, P)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

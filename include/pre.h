@@ -191,9 +191,10 @@ int pre_engine_reset(pre_engine *e, void *stream);
 int pre_engine_set_watchdog(pre_engine *e, uint32_t ms);
 
 /* Optional per-task timestamps.  d_buf receives, per (step, stage instance,
- * workgroup) executed, 4 uint32: {stage | wg << 16, t_wait_begin, t_start,
- * t_end} in 100 MHz realtime ticks (low 32 bits); records beyond `bytes` are
- * dropped.  NULL disables. */
+ * workgroup) executed, 8 uint32: {stage | wg << 16, t_begin, t_wait_end,
+ * t_end, m0, m1, m2, m3} in 100 MHz realtime ticks (low 32 bits), where m*
+ * are task phase marks (input staged, rows streamed, ...; stale where a task
+ * kind sets fewer); records beyond `bytes` are dropped.  NULL disables. */
 int pre_engine_set_trace(pre_engine *e, void *d_buf, size_t bytes);
 
 /* Free the host-side state (no device memory is owned). */

@@ -22,6 +22,7 @@ namespace pre {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Cache-policy operand of the buffer intrinsics on gfx94x/gfx950:
 // bit 0 = sc0, bit 1 = nt, bit 4 = sc1.
@@ -41,6 +42,10 @@ __device__ __forceinline__ Rsrc mkbuf(const void *p, uint32_t bytes) {
 template <int CP>
 __device__ __forceinline__ v4i ld128(Rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ v2i ld64(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP);
 }
 template <int CP>
 __device__ __forceinline__ float ldf(Rsrc r, uint32_t off) {
@@ -102,10 +107,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0x143, 0xc>(v);  // row_bcast:31
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// DPP move where lanes the row mask excludes keep their own value.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp_keep(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, ROWMASK, 0xf, false));
+}
+// Maximum over the 64 lanes, wave-uniform result.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_keep<0xb1>(v));
+  v = fmaxf(v, dpp_keep<0x4e>(v));
+  v = fmaxf(v, dpp_keep<0x141>(v));
+  v = fmaxf(v, dpp_keep<0x140>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Sum of the four 16-lane rows, lane by lane (lane i gets x[i%16] + x[i%16+16]
+// + x[i%16+32] + x[i%16+48]), with the gfx950 row-swap permutes.  Both
+// registers of a swap are results (v_permlane16_swap exchanges the odd rows of
+// the first with the even rows of the second; v_permlane32_swap the upper half
+// of the first with the lower half of the second), so they are written as
+// in/out asm operands; the builtins' second result is not usable with this
+// compiler.  The s_nop pads cover the VALU-write / permlane-read hazard.
+__device__ __forceinline__ float xrow_sum(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  v = a + b;  // rows (0+1), (0+1), (2+3), (2+3)
+  float c = v, e = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(c), "+v"(e));
+  return c + e;
 }
 
 // ---- unpacking -----------------------------------------------------------
@@ -157,8 +188,11 @@ __device__ __forceinline__ float dot16_fp8(v4i w, const float *x) {
   return acc;
 }
 
-// Wavefront index inside the workgroup, as a wave-uniform (scalar) value.
+// Wavefront index inside the workgroup and the number of wavefronts, as
+// wave-uniform (scalar) values: read through readfirstlane so that the
+// compiler keeps everything derived from them in scalar registers.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int nwaves() { return __builtin_amdgcn_readfirstlane(blockDim.x >> 6); }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 

@@ -32,8 +32,9 @@ int validate(const Dims &D, const std::vector<Task> &T);
 // Everything a kernel needs, passed by value (kernel argument segment).
 struct KP {
   // shapes
-  int32_t L, h, Hq, Hkv, d, ffn, V, B, max_ctx, E, top_k, n_shared, effn, moe, G, F, W, X, NC;
-  int32_t n_si, spl, kmax, cmax;
+  int32_t L, h, Hq, Hkv, d, ffn, V, B, max_ctx, E, top_k, n_shared, effn, moe, G, F, W, X, NC, Tg;
+  int32_t n_si, spl, kmax, ymax, cmax, lds_floats;
+  int32_t nthr, nw;  // threads and wavefronts per workgroup (scalar: never re-read from the dispatch packet)
   float eps, attn_scale;
   // model
   const DevLayer *layers;
@@ -41,10 +42,10 @@ struct KP {
   uint16_t *kc, *vc;
   // workspace
   const Task *tasks;
-  uint32_t *flags, *counters, *xcc;
+  uint32_t *flags, *xcc;
   DevStatus *status;
   const float *rope;
-  float *x_out, *xm, *q, *o, *u, *rl, *part, *lmp, *x_emb, *a_norm;
+  float *x_out, *pbuf, *q, *u, *rl, *part, *lmp, *x_emb, *a_norm;
   int32_t *tok_slot;
   // this call
   int32_t n_steps, pos0;
@@ -58,10 +59,11 @@ struct KP {
 };
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
 // error latch / abort
 
-__device__ __forceinline__ void latch_error(const KP &P, int kind, int step, int stage, int slot, uint32_t obs,
-                            uint32_t expd) {
+__device__ __forceinline__ void latch_error(const KP &P, int kind, int step, int stage, int slot,
+                                            uint32_t obs, uint32_t expd) {
   int32_t zero = 0;
   if (__hip_atomic_compare_exchange_strong(&P.status->error, &zero, kind, __ATOMIC_RELAXED,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -79,8 +81,8 @@ __device__ __forceinline__ void latch_error(const KP &P, int kind, int step, int
 // Spin (wave 0) until flags[lo..hi) >= ep; all threads return the same
 // verdict.  Bounded by the watchdog; leaves early if another workgroup
 // aborted.
-__device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t ep, int step, int stage,
-                           int *sh) {
+__device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t ep, int step,
+                                           int stage, int *sh) {
   if (lo >= hi) return true;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -98,7 +100,6 @@ __device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t
       if ((++iter & 15) == 0) {
         if (ld_flag(&P.status->abort)) { verdict = 0; break; }
         if (now_ticks() - t0 > P.watchdog_ticks) {
-          // the lowest lane still waiting reports its slot
           uint64_t m = __ballot(!ok);
           int first = __ffsll((unsigned long long)m) - 1;
           if (lane == first) latch_error(P, PRE_DEV_TIMEOUT, step, stage, bad, seen, ep);
@@ -116,6 +117,23 @@ __device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t
   return r;
 }
 
+// The dependency wait of one task (a no-op in the per-operator baseline).
+struct Waiter {
+  int active, lo, hi, step, stage;
+  uint32_t ep;
+  int *sh;
+  __device__ __forceinline__ bool operator()(const KP &P) const {
+    if (!active) return true;
+    const bool ok = wait_slots(P, lo, hi, ep, step, stage, sh);
+    if (threadIdx.x == 0) sh[3] = (int)(uint32_t)now_ticks();  // trace: end of the wait
+    return ok;
+  }
+  // trace: time of phase k (0..3) of the task, taken by thread 0
+  __device__ __forceinline__ void mark(int k) const {
+    if (active && threadIdx.x == 0) sh[4 + k] = (int)(uint32_t)now_ticks();
+  }
+};
+
 // Publish: every thread's stores are complete, then one sc1 flag store.
 __device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep) {
   drain();
@@ -126,25 +144,37 @@ __device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep) 
 // ---------------------------------------------------------------------------
 // staging a GEMV input vector into LDS (fp32), optionally RMS-normalised
 
+// x = base (+ the nparts partial vectors of the split output projection),
+// then RMSNorm with `gain` when it is given.
 struct Src {
-  const float *f32;      // fp32 slot (device-scope loads), or
-  const uint16_t *bf16;  // bf16 row (embedding)
+  const float *f32;      // fp32 base vector (device-scope loads), or
+  const uint16_t *bf16;  // bf16 base row (embedding)
+  const float *parts;    // nparts fp32 vectors at stride pstride, added in order
+  int nparts, pstride;
   const uint16_t *gain;  // non-NULL: fold RMSNorm with these gains
 };
+constexpr int MAXPARTS = 8;  // KV heads per sequence (partials of the split O projection)
 
 // xs[0..K) = src (normalised if gain), xs[K..Kpad) = 0.  Ends with a barrier.
-__device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, const Src &s, int K, int Kpad) {
-  const int tid = threadIdx.x, T = blockDim.x;
+// The gains are fetched together with the data, so staging costs one device
+// round trip (two when K exceeds GK * 4 * threads and gains are refetched).
+constexpr int GK = 4;
+__device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, const Src &s, int K,
+                                          int Kpad) {
+  const int tid = threadIdx.x, T = P.nthr, n4 = K >> 2;
   float ss = 0.f;
-  if (s.f32) {
+  const Rsrc rg = mkbuf(s.gain, s.gain ? (uint32_t)K * 2 : 0u);
+  v2i gr[GK];
+#pragma unroll
+  for (int k = 0; k < GK; ++k) gr[k] = s.gain ? ld64<CP_DEF>(rg, (uint32_t)(tid + k * T) * 8) : v2i{0, 0};
+  if (s.f32 && s.nparts == 0) {
     const Rsrc r = mkbuf(s.f32, (uint32_t)K * 4);
-    const int n4 = K >> 2;
-    for (int i = tid; i < n4; i += 4 * T) {
-      v4i a[4];
+    for (int i = tid; i < n4; i += 8 * T) {
+      v4i a[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
+      for (int j = 0; j < 8; ++j) a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
         if (i + j * T < n4) {
           float4 f = __builtin_bit_cast(float4, a[j]);
           reinterpret_cast<float4 *>(xs)[i + j * T] = f;
@@ -153,113 +183,226 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
         }
     }
   } else {
-    const Rsrc r = mkbuf(s.bf16, (uint32_t)K * 2);
-    const int n8 = K >> 3;
-    for (int i = tid; i < n8; i += T) {
-      v4i w = ld128<CP_DEF>(r, (uint32_t)i * 16);
-      float f[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
-                    bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+    // base (fp32 or bf16) plus partial vectors, two float4 per thread per round
+    const Rsrc rb = mkbuf(s.f32 ? (const void *)s.f32 : (const void *)s.bf16, (uint32_t)K * (s.f32 ? 4 : 2));
+    const Rsrc rp = mkbuf(s.parts, s.parts ? (uint32_t)((s.nparts - 1) * s.pstride + K) * 4 : 0u);
+    for (int i0 = tid; i0 < n4; i0 += 2 * T) {
+      v4i pv[2][MAXPARTS], bv[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { xs[i * 8 + j] = f[j]; ss = fmaf(f[j], f[j], ss); }
+      for (int k = 0; k < 2; ++k) {
+        const int i = i0 + k * T;  // past n4 the buffers return 0
+#pragma unroll
+        for (int p = 0; p < MAXPARTS; ++p)
+          if (p < s.nparts) pv[k][p] = ld128<CP_SC1>(rp, (uint32_t)(p * s.pstride + 4 * i) * 4);
+        if (s.f32) {
+          bv[k] = ld128<CP_SC1>(rb, (uint32_t)i * 16);
+        } else {
+          const v2i w = ld64<CP_DEF>(rb, (uint32_t)i * 8);
+          bv[k] = __builtin_bit_cast(v4i, float4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)});
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = i0 + k * T;
+        if (i >= n4) break;
+        float4 f = __builtin_bit_cast(float4, bv[k]);
+#pragma unroll
+        for (int p = 0; p < MAXPARTS; ++p)
+          if (p < s.nparts) {
+            const float4 q = __builtin_bit_cast(float4, pv[k][p]);
+            f.x += q.x; f.y += q.y; f.z += q.z; f.w += q.w;
+          }
+        reinterpret_cast<float4 *>(xs)[i] = f;
+        ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
+        ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
+      }
     }
   }
   for (int i = K + tid; i < Kpad; i += T) xs[i] = 0.f;
   if (s.gain) {
-    const int wave = wave_id(), nw = T >> 6;
+    const int wave = wave_id(), nw = P.nw;
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[wave] = ss;
     __syncthreads();
     float tot = 0.f;
     for (int w = 0; w < nw; ++w) tot += red[w];
     const float rinv = 1.0f / sqrtf(tot / (float)K + P.eps);
-    const Rsrc g = mkbuf(s.gain, (uint32_t)K * 2);
-    for (int i = tid; i < (K >> 3); i += T) {
-      v4i w = ld128<CP_DEF>(g, (uint32_t)i * 16);
-      float gf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
-                     bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xs[i * 8 + j] = xs[i * 8 + j] * rinv * gf[j];
+    for (int k = 0; k < GK; ++k) {
+      const int i = tid + k * T;
+      if (i < n4) {
+        const float4 f = reinterpret_cast<float4 *>(xs)[i];
+        reinterpret_cast<float4 *>(xs)[i] = float4{f.x * rinv * bf_lo(gr[k].x), f.y * rinv * bf_hi(gr[k].x),
+                                                   f.z * rinv * bf_lo(gr[k].y), f.w * rinv * bf_hi(gr[k].y)};
+      }
+    }
+    for (int i = tid + GK * T; i < n4; i += T) {  // beyond the gains held in registers
+      const v2i g = ld64<CP_DEF>(rg, (uint32_t)i * 8);
+      const float4 f = reinterpret_cast<float4 *>(xs)[i];
+      reinterpret_cast<float4 *>(xs)[i] = float4{f.x * rinv * bf_lo(g.x), f.y * rinv * bf_hi(g.x),
+                                                 f.z * rinv * bf_lo(g.y), f.w * rinv * bf_hi(g.y)};
     }
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// GEMV cores: RF rows at a time per wavefront, K split across the 64 lanes
-// (8 bf16 or 16 fp8 per lane per 16-byte load), U loads per row in flight.
+// Streamed GEMV core.
+//
+// A task computes groups [0, ng) of R weight rows that share the same K-long
+// input (a RoPE pair, a gate/up pair, or single rows).  Each row is cut into
+// chunks of one 16-byte load per lane (8 bf16 or 16 fp8 values; 512 or 1024
+// columns per chunk), so every load instruction of a wavefront reads 1 KB of
+// consecutive weight bytes.  The task's (group, chunk) units, group-major,
+// are split into one contiguous span per wavefront (split-K across
+// wavefronts where a span ends inside a group), so every wavefront streams
+// the same amount.  A ring of D units (D * R loads) is kept in flight per
+// wavefront: unit u is consumed while unit u + D is being fetched, across row
+// boundaries, with no barrier.  The first D units are issued before the task
+// waits for its producers (weights never wait on activations).  Loads past a
+// row's end, or past the span's end, address a zero-length buffer and return
+// 0 without touching memory, so every ring slot issues exactly R loads and
+// the wait counts stay static.  A wavefront writes one partial sum per
+// (group it touched, row) into LDS; the task's epilogue adds the wavefronts'
+// partials in wavefront order (deterministic).
 
-constexpr int U = 8;
+constexpr int CP_W = CP_NT;  // weight loads: streaming (read once per step)
 
-// out[r] = sum_k W_r[k] * xs_r[k] over K (bf16 rows; NULL row -> 0).
-template <int RF>
-__device__ __forceinline__ void dot_bf16(const uint16_t *const (&row)[RF], const float *const (&xs)[RF],
-                                         int K, float (&out)[RF]) {
+template <int R, int D, bool FP8, int CP = CP_W>
+struct Stream {
+  v4i buf[D][R];
+  float sc[D][R];
+  const void *rp[R];      // rows of the group being issued
+  uint32_t rb[R];
+  const uint16_t *sp[R];  // fp8: block-scale row of each row
+  uint32_t sb[R];
+  int ig, ic, cg, cc, nch, left;  // issue / compute cursors, units left to issue
+  int wave, nw;                   // this wavefront, wavefronts per workgroup
+  float acc[R];
+};
+
+// Issue the next unit of the span into ring slot j (the caller knows one is
+// left).
+template <int R, int D, bool FP8, int CP, class RowFn>
+__device__ __forceinline__ void st_issue(Stream<R, D, FP8, CP> &S, int j, RowFn &rowfn) {
   const int lane = threadIdx.x & 63;
-  float acc[RF];
-  Rsrc rs[RF];
+  const int col = FP8 ? S.ic * 1024 + lane * 16 : S.ic * 512 + lane * 8;
+  const uint32_t off = FP8 ? (uint32_t)col : (uint32_t)col * 2;
 #pragma unroll
-  for (int r = 0; r < RF; ++r) {
-    acc[r] = 0.f;
-    rs[r] = mkbuf(row[r], row[r] ? (uint32_t)K * 2 : 0u);
+  for (int r = 0; r < R; ++r) {
+    S.buf[j][r] = ld128<CP>(mkbuf(S.rp[r], S.rb[r]), off);
+    if (FP8) {
+      // two bf16 scales per dword; this lane's 16 columns share one 128-wide block
+      const int blk = col >> 7;
+      const uint32_t w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(mkbuf(S.sp[r], S.sb[r]),
+                                                                         (uint32_t)(blk >> 1) * 4, 0, CP_DEF);
+      S.sc[j][r] = bf16f((uint16_t)((blk & 1) ? (w >> 16) : (w & 0xffffu)));
+    }
   }
-  const int nch = (K + 511) >> 9;
-  for (int c0 = 0; c0 < nch; c0 += U) {
-    v4i w[RF][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < RF; ++r)
-        w[r][u] = (c0 + u < nch) ? ld128<CP_DEF>(rs[r], (uint32_t)((c0 + u) * 512 + lane * 8) * 2)
-                                 : v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (c0 + u < nch) {
-#pragma unroll
-        for (int r = 0; r < RF; ++r) {
-          const float4 *x4 = reinterpret_cast<const float4 *>(xs[r] + (c0 + u) * 512 + lane * 8);
-          acc[r] = dot8_bf16(w[r][u], x4[0], x4[1], acc[r]);
-        }
-      }
+  --S.left;
+  if (++S.ic == S.nch) {
+    S.ic = 0;
+    ++S.ig;
+    if (S.left > 0) rowfn(S.ig, S);
   }
-#pragma unroll
-  for (int r = 0; r < RF; ++r) out[r] = wave_sum(acc[r]);
 }
 
-// fp8 rows with one bf16 scale per 128-column block (scale row pointer srow).
-template <int RF>
-__device__ __forceinline__ void dot_fp8(const uint8_t *const (&row)[RF], const uint16_t *const (&srow)[RF],
-                                        const float *const (&xs)[RF], int K, float (&out)[RF]) {
+// This wavefront's span of the task's ng * nch units; issues its first D
+// units (all of them when the span is shorter).  Returns the span length.
+// When the span covers a whole ring the D issues are unconditional, so the
+// ring's wait counts stay static through the main loop.
+template <int R, int D, bool FP8, int CP, class RowFn>
+__device__ __forceinline__ int st_begin(Stream<R, D, FP8, CP> &S, RowFn &rowfn, int ng, int K, int nw) {
+  const int wave = wave_id();
+  S.wave = wave;
+  S.nw = nw;
+  S.nch = FP8 ? (K + 1023) >> 10 : (K + 511) >> 9;
+  const int N = ng * S.nch, u0 = (int)((int64_t)N * wave / nw), u1 = (int)((int64_t)N * (wave + 1) / nw);
+  const int n = u1 - u0;
+  S.ig = S.cg = u0 / S.nch;
+  S.ic = S.cc = u0 % S.nch;
+  S.left = n;
+#pragma unroll
+  for (int r = 0; r < R; ++r) { S.acc[r] = 0.f; S.rp[r] = nullptr; S.rb[r] = 0; S.sp[r] = nullptr; S.sb[r] = 0; }
+  if (n > 0) rowfn(S.ig, S);
+  if (n >= D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) st_issue(S, j, rowfn);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < n) st_issue(S, j, rowfn);
+  }
+  return n;
+}
+
+// Unit in ring slot j: accumulate; at the end of a group (or of the span)
+// write the wavefront's partial of that group to ys[(g * nw + wave) * R + r].
+template <int R, int D, bool FP8, int CP, class XFn>
+__device__ __forceinline__ void st_compute(Stream<R, D, FP8, CP> &S, int j, bool span_end, XFn &xfn,
+                                           float *ys) {
   const int lane = threadIdx.x & 63;
-  float acc[RF];
-  Rsrc rs[RF];
 #pragma unroll
-  for (int r = 0; r < RF; ++r) {
-    acc[r] = 0.f;
-    rs[r] = mkbuf(row[r], row[r] ? (uint32_t)K : 0u);
+  for (int r = 0; r < R; ++r) {
+    const float *xb = xfn(S.cg, r) + (FP8 ? S.cc * 1024 + lane * 16 : S.cc * 512 + lane * 8);
+    if (FP8) {
+      S.acc[r] = fmaf(S.sc[j][r], dot16_fp8(S.buf[j][r], xb), S.acc[r]);
+    } else {
+      const float4 *x4 = reinterpret_cast<const float4 *>(xb);
+      S.acc[r] = dot8_bf16(S.buf[j][r], x4[0], x4[1], S.acc[r]);
+    }
   }
-  const int nch = (K + 1023) >> 10;
-  for (int c0 = 0; c0 < nch; c0 += U) {
-    v4i w[RF][U];
-    float sc[RF][U];
+  const bool row_end = ++S.cc == S.nch;
+  if (row_end || span_end) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < RF; ++r) {
-        const int k = (c0 + u) * 1024 + lane * 16;
-        const bool in = (c0 + u < nch) && row[r] && k < K;
-        w[r][u] = in ? ld128<CP_DEF>(rs[r], (uint32_t)k) : v4i{0, 0, 0, 0};
-        sc[r][u] = in ? bf16f(srow[r][k >> 7]) : 0.f;
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (c0 + u < nch) {
-#pragma unroll
-        for (int r = 0; r < RF; ++r)
-          acc[r] = fmaf(sc[r][u], dot16_fp8(w[r][u], xs[r] + (c0 + u) * 1024 + lane * 16), acc[r]);
-      }
+    for (int r = 0; r < R; ++r) {
+      const float y = wave_sum(S.acc[r]);
+      S.acc[r] = 0.f;
+      if (lane == 0) ys[(S.cg * S.nw + S.wave) * R + r] = y;
+    }
+    if (row_end) { S.cc = 0; ++S.cg; }
   }
+}
+
+// Consume the span of n units: xfn(g, r) is the LDS input of row r of group g.
+// Full rounds of the ring first (one unconditional issue per consumed unit),
+// then the last one or two rounds without further issues past the span.
+template <int R, int D, bool FP8, int CP, class RowFn, class XFn>
+__device__ __forceinline__ void st_run(Stream<R, D, FP8, CP> &S, int n, RowFn &rowfn, XFn xfn, float *ys) {
+  if (n >= D) {
+    const int m = (n - D) / D;  // rounds whose every issue lies inside the span
+    for (int q = 0; q < m; ++q) {
 #pragma unroll
-  for (int r = 0; r < RF; ++r) out[r] = wave_sum(acc[r]);
+      for (int j = 0; j < D; ++j) {
+        st_compute(S, j, false, xfn, ys);
+        st_issue(S, j, rowfn);
+      }
+    }
+    const int rem = n - m * D;  // D <= rem < 2D
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      st_compute(S, j, j == rem - 1, xfn, ys);
+      if (j + D < rem) st_issue(S, j, rowfn);
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j + D < rem) st_compute(S, j, j + D == rem - 1, xfn, ys);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < n) st_compute(S, j, j == n - 1, xfn, ys);
+  }
+}
+
+// Zero the partial-sum buffer of ng groups (before the task's staging barrier).
+__device__ __forceinline__ void ys_clear(float *ys, int ng, int R, int nw, int nthr) {
+  const int n = ng * nw * R;
+  for (int i = threadIdx.x; i < n; i += nthr) ys[i] = 0.f;
+}
+// Result r of group g: the wavefronts' partials added in wavefront order.
+__device__ __forceinline__ float ys_get(const float *ys, int g, int r, int R, int nw) {
+  float y = 0.f;
+  for (int w = 0; w < nw; ++w) y += ys[(g * nw + w) * R + r];
+  return y;
 }
 
 // ---------------------------------------------------------------------------
@@ -268,156 +411,308 @@ __device__ __forceinline__ void dot_fp8(const uint8_t *const (&row)[RF], const u
 __device__ __forceinline__ int64_t vec_off(const KP &P, int l, int b, int width) {
   return ((int64_t)l * P.B + b) * width;
 }
-// x entering layer l: the embedding row (l == 0) or the previous layer's output.
+// The residual stream entering layer l: the embedding row of the token (the
+// baseline keeps it in x_emb) or the previous layer's output.
 __device__ __forceinline__ Src layer_input(const KP &P, int l, int tok, const uint16_t *gain) {
-  Src s{nullptr, nullptr, gain};
-  if (l == 0) s.bf16 = P.embed + (int64_t)tok * P.h;
-  else s.f32 = P.x_out + vec_off(P, l - 1, 0, P.h);
+  Src s{nullptr, nullptr, nullptr, 0, 0, gain};
+  if (l > 0) s.f32 = P.x_out + vec_off(P, l - 1, 0, P.h);
+  else if (P.persistent) s.bf16 = P.embed + (int64_t)tok * P.h;
+  else s.f32 = P.x_emb;
   return s;
 }
-__device__ __forceinline__ float residual_in(const KP &P, int l, int tok, int i) {
-  if (l == 0) return P.persistent ? bf16f(P.embed[(int64_t)tok * P.h + i]) : ld_sc1(P.x_emb + i);
-  return ld_sc1(P.x_out + vec_off(P, l - 1, 0, P.h) + i);
+// The residual stream after attention of layer l: layer input plus the KV
+// heads' output-projection partials.
+__device__ __forceinline__ Src mid_input(const KP &P, int l, int tok, const uint16_t *gain) {
+  Src s = layer_input(P, l, tok, gain);
+  s.parts = P.pbuf + vec_off(P, l, 0, P.Hkv * P.h);
+  s.nparts = P.Hkv;
+  s.pstride = P.h;
+  return s;
+}
+// Element i of the layer-l post-attention residual (same addition order as
+// stage_vec).
+__device__ __forceinline__ float mid_elem(const KP &P, int l, int tok, int i) {
+  float x;
+  if (l > 0) x = ld_sc1(P.x_out + vec_off(P, l - 1, 0, P.h) + i);
+  else if (P.persistent) x = bf16f(P.embed[(int64_t)tok * P.h + i]);
+  else x = ld_sc1(P.x_emb + i);
+  const float *pb = P.pbuf + vec_off(P, l, 0, P.Hkv * P.h) + i;
+  float pv[MAXPARTS];
+#pragma unroll
+  for (int p = 0; p < MAXPARTS; ++p) pv[p] = p < P.Hkv ? ld_sc1(pb + (int64_t)p * P.h) : 0.f;
+#pragma unroll
+  for (int p = 0; p < MAXPARTS; ++p)
+    if (p < P.Hkv) x += pv[p];
+  return x;
 }
 
-// ---------------------------------------------------------------------------
-// tasks
-
-// QKV: pairs [r0, r1) in group-major order (per KV head g: its G query
-// heads, then k head g, then v head g; d/2 RoPE pairs (j, j + d/2) each).
-__device__ __forceinline__ void task_qkv(const KP &P, const Task &t, int pos, int tok, float *lds) {
-  const int l = t.layer;
-  const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  if (P.persistent) stage_vec(P, xs, red, layer_input(P, l, tok, (const uint16_t *)Lw.attn_norm), P.h, P.kmax);
-  else stage_vec(P, xs, red, Src{P.a_norm, nullptr, nullptr}, P.h, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const int half = P.d >> 1, per_group = (P.G + 2) * half;
-  const float *cosT = P.rope + (int64_t)pos * half;
-  const float *sinT = P.rope + (int64_t)P.max_ctx * half + (int64_t)pos * half;
-  for (int p = t.r0 + wave; p < t.r1; p += nw) {
-    const int g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
-    const uint16_t *W;
-    int head;
-    if (hh < P.G) { W = (const uint16_t *)Lw.wq; head = g * P.G + hh; }
-    else if (hh == P.G) { W = (const uint16_t *)Lw.wk; head = g; }
-    else { W = (const uint16_t *)Lw.wv; head = g; }
-    const uint16_t *rows[2] = {W + ((int64_t)head * P.d + j) * P.h,
-                               W + ((int64_t)head * P.d + j + half) * P.h};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, P.h, y);
-    if (lane == 0) {
-      float a = y[0], b = y[1];
-      if (hh <= P.G) {  // RoPE on q and k
-        const float c = cosT[j], s = sinT[j];
-        const float a2 = a * c - b * s, b2 = b * c + a * s;
-        a = a2; b = b2;
-      }
-      if (hh < P.G) {
-        float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)head * P.d;
-        st_sc1(qd + j, a);
-        st_sc1(qd + j + half, b);
-      } else {
-        uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
-        const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
-        const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
-        st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j) * 2, f2bf(a));
-        st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j + half) * 2, f2bf(b));
-      }
-    }
-  }
-}
-
-// O projection rows [r0, r1) + residual: xm = x_in + Wo o.
-__device__ __forceinline__ void task_oproj(const KP &P, const Task &t, int tok, float *lds) {
-  const int l = t.layer;
-  const DevLayer &Lw = P.layers[l];
-  const int K = P.Hq * P.d;
-  float *xs = lds, *red = lds + P.kmax;
-  stage_vec(P, xs, red, Src{P.o + vec_off(P, l, 0, K), nullptr, nullptr}, K, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const uint16_t *W = (const uint16_t *)Lw.wo;
-  float *xm = P.xm + vec_off(P, l, 0, P.h);
-  for (int i = t.r0 + 2 * wave; i < t.r1; i += 2 * nw) {
-    const bool two = i + 1 < t.r1;
-    const uint16_t *rows[2] = {W + (int64_t)i * K, two ? W + (int64_t)(i + 1) * K : nullptr};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, K, y);
-    if (lane == 0) st_sc1(xm + i, residual_in(P, l, tok, i) + y[0]);
-    if (lane == 1 && two) st_sc1(xm + i + 1, residual_in(P, l, tok, i + 1) + y[1]);
-  }
+// Field f of a layer's pointer table (the order of DevLayer): selecting a
+// matrix by index keeps the choice in scalar registers.
+enum LField { F_WQ = 1, F_WK = 2, F_WV = 3, F_EWG = 10, F_EWU = 11, F_EWD = 12, F_ESG = 13,
+              F_ESU = 14, F_ESD = 15, F_SWG = 16, F_SWU = 17, F_SWD = 18, F_SSG = 19,
+              F_SSU = 20, F_SSD = 21 };
+__device__ __forceinline__ const void *lptr(const DevLayer *L, int f) {
+  return reinterpret_cast<const void *const *>(L)[f];
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Dense gate/up row pairs [r0, r1): u_j = silu(Wg_j b) * (Wu_j b).
-__device__ __forceinline__ void task_gu(const KP &P, const Task &t, float *lds) {
-  const int l = t.layer;
-  const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  if (P.persistent)
-    stage_vec(P, xs, red, Src{P.xm + vec_off(P, l, 0, P.h), nullptr, (const uint16_t *)Lw.ffn_norm}, P.h, P.kmax);
-  else stage_vec(P, xs, red, Src{P.a_norm, nullptr, nullptr}, P.h, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  float *u = P.u + vec_off(P, l, 0, P.F);
-  for (int j = t.r0 + wave; j < t.r1; j += nw) {
-    const uint16_t *rows[2] = {(const uint16_t *)Lw.wg + (int64_t)j * P.h,
-                               (const uint16_t *)Lw.wu + (int64_t)j * P.h};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, P.h, y);
-    if (lane == 0) st_sc1(u + j, silu(y[0]) * y[1]);
+// LDS layout of the GEMV tasks: xs[kmax] | ys[ymax * waves] | red[256]
+struct GemvLds {
+  float *xs, *ys, *red;
+};
+__device__ __forceinline__ GemvLds gemv_lds(const KP &P, float *lds) {
+  float *ys = lds + P.kmax;
+  return GemvLds{lds, ys, ys + P.ymax * P.nw};
+}
+
+// Row-wise GEMV over one bf16 matrix W [rows][K] starting at row r0.
+struct RowsBf16 {
+  const uint16_t *W;
+  int K, r0;
+  __device__ __forceinline__ void operator()(int g, Stream<1, 8, false> &S) const {
+    S.rp[0] = W + (int64_t)(r0 + g) * K;
+    S.rb[0] = (uint32_t)K * 2;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// tasks.  Each: prefetch the first weight units, wait for producers, stage
+// the input, stream the rows, run the epilogue with all threads.  Returns
+// false if the wait was aborted.
+
+// QKV: pairs [r0, r1) in group-major order (per KV head g: its G query
+// heads, then k head g, then v head g; d/2 RoPE pairs (j, j + d/2) each).
+__device__ __forceinline__ bool task_qkv(const KP &P, const Task &t, int pos, int tok, float *lds,
+                                         const Waiter &wait) {
+  const int l = t.layer, ng = t.r1 - t.r0;
+  const GemvLds M = gemv_lds(P, lds);
+  const int half = P.d >> 1, per_group = (P.G + 2) * half, h = P.h;
+  const DevLayer *Lp = P.layers + l;
+  const int G = P.G, dd = P.d, r0 = t.r0;
+  auto rowfn = [=](int gi, Stream<2, 8, false> &S) {
+    const int p = r0 + gi, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
+    const uint16_t *W = (const uint16_t *)lptr(Lp, hh < G ? F_WQ : (hh == G ? F_WK : F_WV));
+    const int head = hh < G ? g * G + hh : g;
+    S.rp[0] = W + ((int64_t)head * dd + j) * h;
+    S.rp[1] = W + ((int64_t)head * dd + j + half) * h;
+    S.rb[0] = S.rb[1] = (uint32_t)h * 2;
+  };
+  Stream<2, 8, false> S;
+  const int n = st_begin(S, rowfn, ng, h, P.nw);
+  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
+  if (!wait(P)) return false;
+  if (P.persistent) stage_vec(P, M.xs, M.red, layer_input(P, l, tok, (const uint16_t *)Lp->attn_norm), h, P.kmax);
+  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
+  wait.mark(0);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
+  wait.mark(1);
+  const float *cosT = P.rope + (int64_t)pos * half;
+  const float *sinT = P.rope + (int64_t)P.max_ctx * half + (int64_t)pos * half;
+  for (int i = threadIdx.x; i < ng; i += P.nthr) {
+    const int p = t.r0 + i, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
+    float a = ys_get(M.ys, i, 0, 2, P.nw), b = ys_get(M.ys, i, 1, 2, P.nw);
+    if (hh <= P.G) {  // RoPE on q and k
+      const float c = cosT[j], s = sinT[j];
+      const float a2 = a * c - b * s, b2 = b * c + a * s;
+      a = a2; b = b2;
+    }
+    if (hh < P.G) {
+      float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
+      st_sc1(qd + j, a);
+      st_sc1(qd + j + half, b);
+    } else {
+      uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
+      const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
+      const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
+      st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j) * 2, f2bf(a));
+      st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j + half) * 2, f2bf(b));
+    }
+  }
+  return true;
+}
+
+// Combine the NC chunk partials of (sequence b, KV head g) into
+// xs[0 .. G*d): o_h = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c with
+// M = max_c m_c.  The partial block [NC][G][d + 2] is contiguous; it is read
+// with wide loads into the LDS behind xs (in slices of chunks when it does
+// not fit), so the combine costs one device round trip (two with slices).
+__device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, float *lds, int lds_n, float *xs) {
+  const int b = bg / P.Hkv, g = bg % P.Hkv, G = P.G, d = P.d, NC = P.NC, rec = d + 2;
+  const int tid = threadIdx.x, T = P.nthr;
+  const float *src = P.part + (((int64_t)l * P.B + b) * P.Hkv + g) * NC * G * rec;
+  const int go = (G * d + 3) & ~3;
+  float *wt = lds + go;          // [NC][G] e^{m - M}
+  float *den = wt + NC * G;      // [G] sum, [G] max
+  float *blk = lds + ((go + NC * G + 2 * G + 3) & ~3);
+  const int room = (lds_n - (int)(blk - lds)) / (G * rec);
+  const int per = max(1, min(NC, room));
+  const Rsrc r = mkbuf(src, (uint32_t)NC * G * rec * 4);
+  float num[4] = {0.f, 0.f, 0.f, 0.f}, dsum = 0.f;
+  for (int c0 = 0; c0 < NC; c0 += per) {
+    const int c1 = min(NC, c0 + per), nf = (c1 - c0) * G * rec;  // nf is even
+    const uint32_t base = (uint32_t)c0 * G * rec * 4;
+    for (int i = tid * 2; i < nf; i += 16 * T) {
+      v2i a[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = i + k * 2 * T;
+        a[k] = e < nf ? ld64<CP_SC1>(r, base + (uint32_t)e * 4) : v2i{0, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = i + k * 2 * T;
+        if (e < nf) *reinterpret_cast<float2 *>(blk + e) = __builtin_bit_cast(float2, a[k]);
+      }
+    }
+    __syncthreads();
+    if (c0 == 0) {  // the maxima; every slice after the first must reload them
+      if (tid < G) {
+        float Mx = -INFINITY;
+        if (per == NC)
+          for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, blk[(cc * G + tid) * rec]);
+        else
+          for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, ldf<CP_SC1>(r, (uint32_t)(cc * G + tid) * rec * 4));
+        den[G + tid] = Mx;
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < (c1 - c0) * G; i += T) wt[c0 * G + i] = expf(blk[i * rec] - den[G + i % G]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * T;
+      if (i < G * d) {
+        const int hh = i / d, j = i % d;
+        for (int cc = c0; cc < c1; ++cc)
+          num[q] = fmaf(wt[cc * G + hh], blk[((cc - c0) * G + hh) * rec + 2 + j], num[q]);
+      }
+    }
+    if (tid < G)
+      for (int cc = c0; cc < c1; ++cc) dsum = fmaf(wt[cc * G + tid], blk[((cc - c0) * G + tid) * rec + 1], dsum);
+    __syncthreads();
+  }
+  if (tid < G) den[tid] = dsum;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = tid + q * T;
+    if (i < G * d) xs[i] = num[q] / den[i / d];
   }
 }
 
-// Dense down rows [r0, r1) + residual: x_out = xm + Wd u.
-__device__ __forceinline__ void task_down(const KP &P, const Task &t, int step, float *lds) {
-  const int l = t.layer;
+// Output projection of one KV head: rows [r0, r1) of Wo restricted to the
+// head group's G*d columns, times that group's attention output (combined
+// here from its chunk partials).  Writes the split-K partial
+// pbuf[l][b][g][rows]; the residual add happens where the partials are read.
+__device__ __forceinline__ bool task_oproj(const KP &P, const Task &t, float *lds, const Waiter &wait) {
+  const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, ng = t.r1 - t.r0;
+  const int K = P.G * P.d, ld = P.Hq * P.d;
+  const GemvLds M = gemv_lds(P, lds);
+  RowsBf16 rowfn{(const uint16_t *)P.layers[l].wo + (int64_t)g * K, ld, t.r0};
+  // row g of the slice: W + row * ld; K columns
+  auto rows = [=](int gi, Stream<1, 16, false> &S) {
+    S.rp[0] = rowfn.W + (int64_t)(rowfn.r0 + gi) * ld;
+    S.rb[0] = (uint32_t)K * 2;
+  };
+  Stream<1, 16, false> S;
+  const int n = st_begin(S, rows, ng, K, P.nw);
+  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  if (!wait(P)) return false;
+  // combine into xs[0..K); its scratch lies behind the padded input and
+  // overlaps ys, which is cleared again once the combine is done
+  const int Kp = (K + 511) & ~511;
+  attn_combine_lds(P, l, bg, lds + Kp, P.lds_floats - Kp, M.xs);
+  __syncthreads();
+  wait.mark(0);
+  for (int i = K + threadIdx.x; i < Kp; i += P.nthr) M.xs[i] = 0.f;
+  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  __syncthreads();
+  st_run(S, n, rows, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
+  wait.mark(1);
+  float *dst = P.pbuf + ((int64_t)(l * P.B + b) * P.Hkv + g) * P.h + t.r0;
+  for (int i = threadIdx.x; i < ng; i += P.nthr) st_sc1(dst + i, ys_get(M.ys, i, 0, 1, P.nw));
+  return true;
+}
+
+// Dense gate/up row pairs [r0, r1): u_j = silu(Wg_j b) * (Wu_j b).
+__device__ __forceinline__ bool task_gu(const KP &P, const Task &t, int tok, float *lds, const Waiter &wait) {
+  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
   const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  stage_vec(P, xs, red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr}, P.ffn, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const uint16_t *W = (const uint16_t *)Lw.wd;
-  const float *xm = P.xm + vec_off(P, l, 0, P.h);
+  const GemvLds M = gemv_lds(P, lds);
+  const uint16_t *wg = (const uint16_t *)Lw.wg, *wu = (const uint16_t *)Lw.wu;
+  const int r0 = t.r0;
+  auto rowfn = [=](int gi, Stream<2, 4, false> &S) {
+    S.rp[0] = wg + (int64_t)(r0 + gi) * h;
+    S.rp[1] = wu + (int64_t)(r0 + gi) * h;
+    S.rb[0] = S.rb[1] = (uint32_t)h * 2;
+  };
+  Stream<2, 4, false> S;
+  const int n = st_begin(S, rowfn, ng, h, P.nw);
+  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
+  if (!wait(P)) return false;
+  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
+  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
+  wait.mark(0);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
+  wait.mark(1);
+  float *u = P.u + vec_off(P, l, 0, P.F);
+  for (int i = threadIdx.x; i < ng; i += P.nthr)
+    st_sc1(u + t.r0 + i, silu(ys_get(M.ys, i, 0, 2, P.nw)) * ys_get(M.ys, i, 1, 2, P.nw));
+  return true;
+}
+
+// Dense down rows [r0, r1) + residual: x_out = x_mid + Wd u.
+__device__ __forceinline__ bool task_down(const KP &P, const Task &t, int step, int tok, float *lds,
+                                          const Waiter &wait) {
+  const int l = t.layer, ng = t.r1 - t.r0;
+  const GemvLds M = gemv_lds(P, lds);
+  RowsBf16 rowfn{(const uint16_t *)P.layers[l].wd, P.ffn, t.r0};
+  Stream<1, 8, false> S;
+  const int n = st_begin(S, rowfn, ng, P.ffn, P.nw);
+  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  // the post-attention residual was final before the gate/up stage this
+  // workgroup passed: fetch it now
+  const int tid = threadIdx.x;
+  const float res0 = tid < ng ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
+  if (!wait(P)) return false;
+  stage_vec(P, M.xs, M.red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr, 0, 0, nullptr}, P.ffn, P.kmax);
+  wait.mark(0);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
+  wait.mark(1);
   float *xo = P.x_out + vec_off(P, l, 0, P.h);
   float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h : nullptr;
-  for (int i = t.r0 + 2 * wave; i < t.r1; i += 2 * nw) {
-    const bool two = i + 1 < t.r1;
-    const uint16_t *rows[2] = {W + (int64_t)i * P.ffn, two ? W + (int64_t)(i + 1) * P.ffn : nullptr};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, P.ffn, y);
-    if (lane < 2 && (lane == 0 || two)) {
-      const int ii = i + lane;
-      const float v = ld_sc1(xm + ii) + (lane == 0 ? y[0] : y[1]);
-      st_sc1(xo + ii, v);
-      if (hid) hid[ii] = v;
-    }
+  for (int i = tid; i < ng; i += P.nthr) {
+    const int row = t.r0 + i;
+    const float v = (i == tid ? res0 : mid_elem(P, l, tok, row)) + ys_get(M.ys, i, 0, 1, P.nw);
+    st_sc1(xo + row, v);
+    if (hid) hid[row] = v;
   }
+  return true;
 }
 
 // Router rows [r0, r1): rl = Wr b (MoE).
-__device__ __forceinline__ void task_router(const KP &P, const Task &t, float *lds) {
-  const int l = t.layer;
+__device__ __forceinline__ bool task_router(const KP &P, const Task &t, int tok, float *lds,
+                                            const Waiter &wait) {
+  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
   const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  if (P.persistent)
-    stage_vec(P, xs, red, Src{P.xm + vec_off(P, l, 0, P.h), nullptr, (const uint16_t *)Lw.ffn_norm}, P.h, P.kmax);
-  else stage_vec(P, xs, red, Src{P.a_norm, nullptr, nullptr}, P.h, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const uint16_t *W = (const uint16_t *)Lw.router;
+  const GemvLds M = gemv_lds(P, lds);
+  RowsBf16 rowfn{(const uint16_t *)Lw.router, h, t.r0};
+  Stream<1, 8, false> S;
+  const int n = st_begin(S, rowfn, ng, h, P.nw);
+  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  if (!wait(P)) return false;
+  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
+  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
   float *rl = P.rl + vec_off(P, l, 0, P.E);
-  for (int i = t.r0 + 2 * wave; i < t.r1; i += 2 * nw) {
-    const bool two = i + 1 < t.r1;
-    const uint16_t *rows[2] = {W + (int64_t)i * P.h, two ? W + (int64_t)(i + 1) * P.h : nullptr};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, P.h, y);
-    if (lane == 0) st_sc1(rl + i, y[0]);
-    if (lane == 1 && two) st_sc1(rl + i + 1, y[1]);
-  }
+  for (int i = threadIdx.x; i < ng; i += P.nthr) st_sc1(rl + t.r0 + i, ys_get(M.ys, i, 0, 1, P.nw));
+  return true;
 }
 
 // Softmax over the router logits and top-k selection (ties -> lower expert
@@ -425,7 +720,7 @@ __device__ __forceinline__ void task_router(const KP &P, const Task &t, float *l
 // that needs the choice computes it; the inputs and the order of operations
 // are the same everywhere, so all of them agree.  sel/selw in LDS.
 __device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw, float *scratch) {
-  const int tid = threadIdx.x, T = blockDim.x;
+  const int tid = threadIdx.x, T = P.nthr;
   const float *rl = P.rl + vec_off(P, l, 0, P.E);
   for (int i = tid; i < P.E; i += T) scratch[i] = ld_sc1(rl + i);
   __syncthreads();
@@ -437,20 +732,19 @@ __device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw,
     float s = 0.f;
     for (int i = lane; i < P.E; i += 64) s += expf(scratch[i] - m);
     s = wave_sum(s);
-    uint64_t taken_lo = 0;  // per-lane bitmask of taken local indices (E <= 1024 -> 16 per lane)
+    uint32_t taken = 0;  // bit li: local index lane + 64 * li already chosen (E <= 1024)
     for (int k = 0; k < P.top_k; ++k) {
       float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      int li = 0;
+      int bi = 0x7fffffff, li = 0;
       for (int i = lane; i < P.E; i += 64, ++li)
-        if (!((taken_lo >> li) & 1) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
+        if (!((taken >> li) & 1u) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const float ov = __shfl_xor(bv, o);
         const int oi = __shfl_xor(bi, o);
         if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
-      if ((bi & 63) == lane) taken_lo |= 1ull << (bi >> 6);
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
       if (lane == 0) { sel[k] = bi; selw[k] = expf(bv - m) / s; }
     }
     if (lane == 0)
@@ -459,128 +753,139 @@ __device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw,
   __syncthreads();
 }
 
-// Expert gate/up pairs [r0, r1) over (slot k, row j): u[k][j].
-__device__ __forceinline__ void task_egu(const KP &P, const Task &t, float *lds) {
-  const int l = t.layer;
+// Expert gate/up pairs [r0, r1) over (slot k, row j): u[k][j].  The rows
+// depend on the routing, so the stream starts after it.
+__device__ __forceinline__ bool task_egu(const KP &P, const Task &t, int tok, float *lds, const Waiter &wait) {
+  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
   const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  int *sel = reinterpret_cast<int *>(red + 64);
-  float *selw = red + 96;
-  route(P, l, sel, selw, xs);  // uses xs as scratch before the input is staged
-  if (P.persistent)
-    stage_vec(P, xs, red, Src{P.xm + vec_off(P, l, 0, P.h), nullptr, (const uint16_t *)Lw.ffn_norm}, P.h, P.kmax);
-  else stage_vec(P, xs, red, Src{P.a_norm, nullptr, nullptr}, P.h, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const int f = P.effn, hb = (P.h + 127) / 128, fb = (f + 127) / 128;
+  const GemvLds M = gemv_lds(P, lds);
+  int *sel = reinterpret_cast<int *>(M.red + 64);
+  float *selw = M.red + 96;
+  if (!wait(P)) return false;
+  route(P, l, sel, selw, M.xs);
+  const int f = P.effn, hb = (h + 127) / 128, fb = (f + 127) / 128;
+  const int top_k = P.top_k, r0 = t.r0;
+  const DevLayer *Lp = P.layers + l;
+  auto rowfn = [=](int gi, Stream<2, 4, true> &S) {
+    const int p = r0 + gi, k = p / f, j = p % f, e = sel[k];
+    const int sh = k >= top_k ? F_SWG - F_EWG : 0;
+    const uint8_t *wg = (const uint8_t *)lptr(Lp, F_EWG + sh);
+    const uint8_t *wu = (const uint8_t *)lptr(Lp, F_EWU + sh);
+    const uint16_t *sg = (const uint16_t *)lptr(Lp, F_ESG + sh);
+    const uint16_t *su = (const uint16_t *)lptr(Lp, F_ESU + sh);
+    const int64_t wofs = ((int64_t)e * f + j) * h, sofs = ((int64_t)e * fb + j / 128) * hb;
+    S.rp[0] = wg + wofs; S.rp[1] = wu + wofs;
+    S.rb[0] = S.rb[1] = (uint32_t)h;
+    S.sp[0] = sg + sofs; S.sp[1] = su + sofs;
+    S.sb[0] = S.sb[1] = (uint32_t)hb * 2;
+  };
+  Stream<2, 4, true> S;
+  const int n = st_begin(S, rowfn, ng, h, P.nw);
+  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
+  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
+  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
   float *u = P.u + vec_off(P, l, 0, P.F);
-  for (int p = t.r0 + wave; p < t.r1; p += nw) {
-    const int k = p / f, j = p % f;
-    const int e = sel[k];
-    const bool shared = k >= P.top_k;
-    const uint8_t *wg = (const uint8_t *)(shared ? Lw.s_wg : Lw.e_wg);
-    const uint8_t *wu = (const uint8_t *)(shared ? Lw.s_wu : Lw.e_wu);
-    const uint16_t *sg = (const uint16_t *)(shared ? Lw.s_sg : Lw.e_sg);
-    const uint16_t *su = (const uint16_t *)(shared ? Lw.s_su : Lw.e_su);
-    const int64_t wofs = ((int64_t)e * f + j) * P.h;
-    const int64_t sofs = ((int64_t)e * fb + j / 128) * hb;
-    const uint8_t *rows[2] = {wg + wofs, wu + wofs};
-    const uint16_t *srows[2] = {sg + sofs, su + sofs};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_fp8<2>(rows, srows, xsr, P.h, y);
-    if (lane == 0) st_sc1(u + p, silu(y[0]) * y[1]);
-  }
+  for (int i = threadIdx.x; i < ng; i += P.nthr)
+    st_sc1(u + t.r0 + i, silu(ys_get(M.ys, i, 0, 2, P.nw)) * ys_get(M.ys, i, 1, 2, P.nw));
+  return true;
 }
 
-// Expert down rows [r0, r1): x_out = xm + sum_k w_k Wd_{e_k} u_k.
-__device__ __forceinline__ void task_edown(const KP &P, const Task &t, int step, float *lds) {
-  const int l = t.layer;
-  const DevLayer &Lw = P.layers[l];
-  float *xs = lds, *red = lds + P.kmax;
-  int *sel = reinterpret_cast<int *>(red + 64);
-  float *selw = red + 96;
-  route(P, l, sel, selw, xs);
-  stage_vec(P, xs, red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr}, P.F, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+// Expert down rows [r0, r1): x_out = x_mid + sum_k w_k Wd_{e_k} u_k.  The
+// stream runs over (row, slot) pairs; the epilogue sums the slots of a row
+// in slot order.
+__device__ __forceinline__ bool task_edown(const KP &P, const Task &t, int step, int tok, float *lds,
+                                           const Waiter &wait) {
+  const int l = t.layer, rows = t.r1 - t.r0;
+  const GemvLds M = gemv_lds(P, lds);
+  int *sel = reinterpret_cast<int *>(M.red + 64);
+  float *selw = M.red + 96;
+  const int tid = threadIdx.x;
+  const float res0 = tid < rows ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
+  if (!wait(P)) return false;
+  route(P, l, sel, selw, M.xs);
   const int f = P.effn, hb = (P.h + 127) / 128, fb = (f + 127) / 128;
   const int nk = P.top_k + P.n_shared;
-  const float *xm = P.xm + vec_off(P, l, 0, P.h);
+  const int top_k = P.top_k, hh = P.h, r0 = t.r0;
+  const DevLayer *Lp = P.layers + l;
+  auto rowfn = [=](int q, Stream<1, 8, true> &S) {
+    const int i = r0 + q / nk, k = q % nk, e = sel[k];
+    const int sh = k >= top_k ? F_SWG - F_EWG : 0;
+    S.rp[0] = (const uint8_t *)lptr(Lp, F_EWD + sh) + ((int64_t)e * hh + i) * f;
+    S.rb[0] = (uint32_t)f;
+    S.sp[0] = (const uint16_t *)lptr(Lp, F_ESD + sh) + ((int64_t)e * hb + i / 128) * fb;
+    S.sb[0] = (uint32_t)fb * 2;
+  };
+  Stream<1, 8, true> S;
+  const int n = st_begin(S, rowfn, rows * nk, f, P.nw);
+  ys_clear(M.ys, rows * nk, 1, P.nw, P.nthr);
+  stage_vec(P, M.xs, M.red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr, 0, 0, nullptr}, P.F, P.kmax);
+  st_run(S, n, rowfn, [=](int q, int) { return (const float *)(M.xs + (q % nk) * f); }, M.ys);
+  __syncthreads();
   float *xo = P.x_out + vec_off(P, l, 0, P.h);
   float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h : nullptr;
-  for (int i = t.r0 + wave; i < t.r1; i += nw) {
+  for (int i = tid; i < rows; i += P.nthr) {
     float acc = 0.f;
-    for (int k0 = 0; k0 < nk; k0 += 2) {
-      const uint8_t *rows[2];
-      const uint16_t *srows[2];
-      const float *xsr[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int k = k0 + q;
-        if (k < nk) {
-          const bool shared = k >= P.top_k;
-          const int e = sel[k];
-          rows[q] = (const uint8_t *)(shared ? Lw.s_wd : Lw.e_wd) + ((int64_t)e * P.h + i) * f;
-          srows[q] = (const uint16_t *)(shared ? Lw.s_sd : Lw.e_sd) + ((int64_t)e * hb + i / 128) * fb;
-          xsr[q] = xs + (int64_t)k * f;
-        } else {
-          rows[q] = nullptr; srows[q] = nullptr; xsr[q] = xs;
-        }
-      }
-      float y[2];
-      dot_fp8<2>(rows, srows, xsr, f, y);
-      acc += selw[k0] * y[0];
-      if (k0 + 1 < nk) acc += selw[k0 + 1] * y[1];
-    }
-    if (lane == 0) {
-      const float v = ld_sc1(xm + i) + acc;
-      st_sc1(xo + i, v);
-      if (hid) hid[i] = v;
-    }
+    for (int k = 0; k < nk; ++k) acc = fmaf(selw[k], ys_get(M.ys, i * nk + k, 0, 1, P.nw), acc);
+    const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + acc;
+    st_sc1(xo + t.r0 + i, v);
+    if (hid) hid[t.r0 + i] = v;
   }
+  return true;
+}
+
+// Best (value, lowest index) of two candidates.
+__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
 }
 
 // LM head rows [r0, r1): logits (check mode) and this task's (max, lowest
 // index) partial.  A NaN logit makes the partial NaN.
-__device__ __forceinline__ void task_lm(const KP &P, const Task &t, int lam, int step, float *lds) {
-  float *xs = lds, *red = lds + P.kmax;
+__device__ __forceinline__ bool task_lm(const KP &P, const Task &t, int lam, int step, float *lds,
+                                        const Waiter &wait) {
+  const GemvLds M = gemv_lds(P, lds);
+  const int wave = wave_id(), nw = P.nw, lane = threadIdx.x & 63, ng = t.r1 - t.r0;
+  RowsBf16 rowfn{P.lm_head, P.h, t.r0};
+  Stream<1, 8, false> S;
+  const int n = st_begin(S, rowfn, ng, P.h, P.nw);
+  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  if (!wait(P)) return false;
   if (P.persistent)
-    stage_vec(P, xs, red, Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, P.final_norm}, P.h, P.kmax);
-  else stage_vec(P, xs, red, Src{P.a_norm, nullptr, nullptr}, P.h, P.kmax);
-  const int wave = wave_id(), nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  float best = -INFINITY;
-  int bidx = 0x7fffffff;
-  bool nan = false;
+    stage_vec(P, M.xs, M.red, Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm},
+              P.h, P.kmax);
+  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, P.h, P.kmax);
+  wait.mark(0);
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  __syncthreads();
+  wait.mark(1);
   float *lg = P.chk_logits ? P.chk_logits + (int64_t)step * P.B * P.V : nullptr;
-  for (int i = t.r0 + 2 * wave; i < t.r1; i += 2 * nw) {
-    const bool two = i + 1 < t.r1;
-    const uint16_t *rows[2] = {P.lm_head + (int64_t)i * P.h, two ? P.lm_head + (int64_t)(i + 1) * P.h : nullptr};
-    const float *xsr[2] = {xs, xs};
-    float y[2];
-    dot_bf16<2>(rows, xsr, P.h, y);
-    if (y[0] != y[0] || (two && y[1] != y[1])) nan = true;
-    if (y[0] > best) { best = y[0]; bidx = i; }
-    if (two && y[1] > best) { best = y[1]; bidx = i + 1; }
-    if (lg) {
-      if (lane == 0) lg[i] = y[0];
-      if (lane == 1 && two) lg[i + 1] = y[1];
-    }
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  bool nan = false;
+  for (int i = threadIdx.x; i < ng; i += P.nthr) {
+    const float y = ys_get(M.ys, i, 0, 1, P.nw);
+    if (y != y) nan = true;
+    else argmax_merge(bv, bi, y, t.r0 + i);
+    if (lg) lg[t.r0 + i] = y;
   }
-  float *wv = red + 128;
-  int *wi = reinterpret_cast<int *>(red + 160);
-  int *wn = reinterpret_cast<int *>(red + 192);
-  if (lane == 0) { wv[wave] = best; wi[wave] = bidx; wn[wave] = nan; }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+  const bool wnan = __any(nan);
+  float *wv = M.red + 128;
+  int *wi = reinterpret_cast<int *>(M.red + 160);
+  int *wn = reinterpret_cast<int *>(M.red + 192);
+  if (lane == 0) { wv[wave] = bv; wi[wave] = bi; wn[wave] = wnan; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff, anynan = 0;
-    for (int w = 0; w < nw; ++w) {
-      anynan |= wn[w];
-      if (wv[w] > bv || (wv[w] == bv && wi[w] < bi)) { bv = wv[w]; bi = wi[w]; }
-    }
-    if (anynan) bv = __builtin_nanf("");
-    st_sc1(P.lmp + 2 * lam, bv);
-    st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * lam + 1, (uint32_t)bi);
+    float v = -INFINITY;
+    int ix = 0x7fffffff, anynan = 0;
+    for (int w = 0; w < nw; ++w) { anynan |= wn[w]; argmax_merge(v, ix, wv[w], wi[w]); }
+    if (anynan) v = __builtin_nanf("");
+    st_sc1(P.lmp + 2 * lam, v);
+    st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * lam + 1, (uint32_t)ix);
   }
+  return true;
 }
 
 // Global greedy token from the W partials (all threads get it); -1 on NaN.
@@ -594,14 +899,10 @@ __device__ __forceinline__ int reduce_lm(const KP &P, int *sh) {
       const float v = ld_sc1(P.lmp + 2 * i);
       const int ix = (int)ld_flag(reinterpret_cast<const uint32_t *>(P.lmp) + 2 * i + 1);
       if (v != v) nan = true;
-      else if (v > bv || (v == bv && ix < bi)) { bv = v; bi = ix; }
+      else argmax_merge(bv, bi, v, ix);
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
     const bool anynan = __any(nan);
     if (lane == 0) sh[1] = anynan ? -1 : bi;
   }
@@ -611,34 +912,74 @@ __device__ __forceinline__ int reduce_lm(const KP &P, int *sh) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
 // Split-KV attention: chunk c of (sequence b, KV head g), all G query heads
-// of the group at once so K/V are read once (query-head folding).  Writes the
-// chunk's (max, sum, unnormalised output) per head.
-__device__ __forceinline__ void attn_chunk(const KP &P, const Task &t, int pos, float *lds) {
+// of the group at once so K/V are read once (query-head folding).  The chunk's
+// cached rows were written in earlier steps, so their loads are issued before
+// the dependency wait; only the newest position (written by this step's QKV
+// tasks) and q are read after it.  Writes the chunk's (max, sum,
+// unnormalised output) per head; the output projection combines the chunks.
+
+constexpr int APB = 4;  // attention passes whose K/V rows are held in registers
+
+__device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
+                                           const Waiter &wait) {
   const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, c = t.r0, NC = t.r1;
-  const int G = P.G, d = P.d, tid = threadIdx.x, T = blockDim.x;
-  const int wave = wave_id(), nw = T >> 6, lane = tid & 63;
+  const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr;
+  const int wave = wave_id(), nw = P.nw, lane = tid & 63;
   const int n = pos + 1, C = (n + NC - 1) / NC, t0 = c * C;
   const int cnt = max(0, min(n, t0 + C) - t0);
   const int cpad = ((P.cmax + 63) / 64) * 64;
   float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
-  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
-  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
-  __syncthreads();
   const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * d;
   const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * d * 2);
   const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * d * 2);
   const int LPP = d / 8, PPW = 64 / LPP, sub = lane % LPP, grp = lane / LPP;
+  const int PASS = nw * PPW;
+  auto koff = [=](int tt) { return (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2; };
+  // cached rows of the first batch, before the wait
+  v4i kb[APB], vb[APB];
+#pragma unroll
+  for (int p = 0; p < APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    const bool old = tt < cnt && t0 + tt != pos;
+    kb[p] = old ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
+    vb[p] = old ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
+  }
+  if (!wait(P)) return false;
+  // q of the group and the newest row
+  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
+  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
+#pragma unroll
+  for (int p = 0; p < APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    if (tt < cnt && t0 + tt == pos) {
+      kb[p] = ld128<CP_SC1>(kr, koff(tt));
+      vb[p] = ld128<CP_SC1>(vr, koff(tt));
+    }
+  }
+  __syncthreads();
+  wait.mark(0);
   // scores
-  for (int base = wave * PPW; base < cnt; base += nw * PPW) {
-    const int tt = base + grp;
-    const bool live = tt < cnt;
-    v4i kw = live ? ld128<CP_SC1>(kr, (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2) : v4i{0, 0, 0, 0};
-    for (int hh = 0; hh < G; ++hh) {
-      const float4 *q4 = reinterpret_cast<const float4 *>(qs + hh * d + sub * 8);
-      float s = dot8_bf16(kw, q4[0], q4[1], 0.f);
-      s = (LPP == 16) ? sum16(s) : sum8(s);
-      if (live && sub == 0) sc[hh * cpad + tt] = s;
+  for (int base = 0; base < cnt; base += APB * PASS) {
+    if (base > 0) {
+#pragma unroll
+      for (int p = 0; p < APB; ++p) {
+        const int tt = base + p * PASS + wave * PPW + grp;
+        kb[p] = tt < cnt ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < APB; ++p) {
+      const int tt = base + p * PASS + wave * PPW + grp;
+      if (base + p * PASS < cnt) {
+        for (int hh = 0; hh < G; ++hh) {
+          const float4 *q4 = reinterpret_cast<const float4 *>(qs + hh * d + sub * 8);
+          float s = dot8_bf16(kb[p], q4[0], q4[1], 0.f);
+          s = (LPP == 16) ? sum16(s) : sum8(s);
+          if (tt < cnt && sub == 0) sc[hh * cpad + tt] = s;
+        }
+      }
     }
   }
   __syncthreads();
@@ -657,35 +998,48 @@ __device__ __forceinline__ void attn_chunk(const KP &P, const Task &t, int pos, 
     if (lane == 0) { st[2 * hh] = cnt > 0 ? m : -1e30f; st[2 * hh + 1] = s; }
   }
   __syncthreads();
-  // o = sum_t p_t V_t: lane owns 8 dims of one position per pass
+  wait.mark(1);
+  // o = sum_t p_t V_t: a lane owns 8 dims of one position per pass
   float acc[8][8];
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  for (int base = wave * PPW; base < cnt; base += nw * PPW) {
-    const int tt = base + grp;
-    if (tt >= cnt) continue;
-    const v4i vw = ld128<CP_SC1>(vr, (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2);
-    const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
-                        bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+  for (int base = 0; base < cnt; base += APB * PASS) {
+    if (base > 0) {
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
-      if (hh < G) {
-        const float p = sc[hh * cpad + tt];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
+      for (int p = 0; p < APB; ++p) {
+        const int tt = base + p * PASS + wave * PPW + grp;
+        vb[p] = tt < cnt ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
       }
+    }
+#pragma unroll
+    for (int p = 0; p < APB; ++p) {
+      const int tt = base + p * PASS + wave * PPW + grp;
+      if (tt < cnt) {
+        const v4i vw = vb[p];
+        const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
+                            bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh)
+          if (hh < G) {
+            const float pr = sc[hh * cpad + tt];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, v[e], acc[hh][e]);
+          }
+      }
+    }
   }
-  // reduce the PPW position groups of the wave (lanes sub, sub+LPP, ...)
+  // reduce the PPW position groups of the wave (lanes sub, sub + LPP, ...):
+  // the two 8-lane halves of a row first when LPP = 8, then across rows
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh)
     if (hh < G) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v = acc[hh][e];
-        for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o);
-        acc[hh][e] = v;
+        if (LPP == 8) v += dpp<0x128>(v);  // row_ror:8
+        acc[hh][e] = xrow_sum(v);
       }
     }
   if (grp == 0) {
@@ -696,6 +1050,7 @@ __device__ __forceinline__ void attn_chunk(const KP &P, const Task &t, int pos, 
         for (int e = 0; e < 8; ++e) ored[(wave * G + hh) * d + sub * 8 + e] = acc[hh][e];
   }
   __syncthreads();
+  wait.mark(2);
   float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * (d + 2);
   for (int i = tid; i < G * d; i += T) {
     const int hh = i / d, j = i % d;
@@ -707,69 +1062,41 @@ __device__ __forceinline__ void attn_chunk(const KP &P, const Task &t, int pos, 
     st_sc1(pdst + hh * (d + 2), st[2 * hh]);
     st_sc1(pdst + hh * (d + 2) + 1, st[2 * hh + 1]);
   }
-}
-
-// Combine the NC chunk partials of (sequence b, KV head g) into o.
-__device__ __forceinline__ void attn_combine(const KP &P, int l, int bg, float *lds) {
-  const int b = bg / P.Hkv, g = bg % P.Hkv, G = P.G, d = P.d, NC = P.NC;
-  const int tid = threadIdx.x, T = blockDim.x;
-  const float *src = P.part + (((int64_t)l * P.B + b) * P.Hkv + g) * NC * G * (d + 2);
-  float *ml = lds;  // [NC][G][2]
-  for (int i = tid; i < NC * G; i += T) {
-    const int cc = i / G, hh = i % G;
-    ml[2 * i] = ld_sc1(src + ((int64_t)cc * G + hh) * (d + 2));
-    ml[2 * i + 1] = ld_sc1(src + ((int64_t)cc * G + hh) * (d + 2) + 1);
-  }
-  __syncthreads();
-  float *dst = P.o + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
-  for (int i = tid; i < G * d; i += T) {
-    const int hh = i / d, j = i % d;
-    float M = -INFINITY;
-    for (int cc = 0; cc < NC; ++cc) M = fmaxf(M, ml[2 * (cc * G + hh)]);
-    float num = 0.f, den = 0.f;
-    for (int cc = 0; cc < NC; ++cc) {
-      const float wgt = expf(ml[2 * (cc * G + hh)] - M);
-      den = fmaf(wgt, ml[2 * (cc * G + hh) + 1], den);
-      num = fmaf(wgt, ld_sc1(src + ((int64_t)cc * G + hh) * (d + 2) + 2 + j), num);
-    }
-    st_sc1(dst + i, num / den);
-  }
-}
-
-// Persistent attention task: chunk, then the last of the NC chunk tasks of
-// this (sequence, KV head) to arrive combines and publishes the group.
-__device__ __forceinline__ void task_attn(const KP &P, const Task &t, int pos, uint32_t ep, float *lds, int *sh) {
-  attn_chunk(P, t, pos, lds);
-  drain();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t *cnt = P.counters + (int64_t)t.layer * P.B * P.Hkv + t.aux;
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh[2] = (old == (uint32_t)t.r1 * ep - 1u);
-  }
-  __syncthreads();
-  const bool last = sh[2] != 0;
-  __syncthreads();
-  if (last) {
-    attn_combine(P, t.layer, t.aux, lds);
-    signal_slot(P, t.signal, ep);
-  }
+  return true;
 }
 
 __device__ __forceinline__ void trace_rec(const KP &P, int step, int si, int lam, uint32_t a, uint32_t b,
-                                          uint32_t c) {
+                                          uint32_t c, const int *sh) {
   if (!P.trace || threadIdx.x != 0) return;
   const uint64_t idx = ((uint64_t)step * P.n_si + si) * P.W + lam;
   if (idx >= P.trace_cap) return;
-  uint32_t *r = P.trace + 4 * idx;
+  uint32_t *r = P.trace + 8 * idx;
   r[0] = (uint32_t)si | ((uint32_t)lam << 16);
   r[1] = a; r[2] = b; r[3] = c;
+  for (int k = 0; k < 4; ++k) r[4 + k] = (uint32_t)sh[4 + k];
 }
 
 __device__ __forceinline__ bool token_ok(const KP &P, int tok, int step) {
   if (tok >= 0 && tok < P.V) return true;
   if (threadIdx.x == 0) latch_error(P, PRE_DEV_BAD_TOKEN, step, -1, -1, (uint32_t)tok, 0);
   return false;
+}
+
+// Run one task of the table (both paths).
+__device__ __forceinline__ bool run_task(const KP &P, const Task &t, int lam, int step, int pos, int tok,
+                                         float *lds, const Waiter &wait) {
+  switch (t.op) {
+    case OP_QKV: return task_qkv(P, t, pos, tok, lds, wait);
+    case OP_ATTN: return attn_chunk(P, t, pos, lds, wait);
+    case OP_OPROJ: return task_oproj(P, t, lds, wait);
+    case OP_GU: return task_gu(P, t, tok, lds, wait);
+    case OP_DOWN: return task_down(P, t, step, tok, lds, wait);
+    case OP_ROUTER: return task_router(P, t, tok, lds, wait);
+    case OP_EGU: return task_egu(P, t, tok, lds, wait);
+    case OP_EDOWN: return task_edown(P, t, step, tok, lds, wait);
+    case OP_LM: return task_lm(P, t, lam, step, lds, wait);
+    default: return true;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -795,22 +1122,10 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
       const Task t = P.tasks[(int64_t)si * P.W + lam];
       if (t.op == OP_NONE) continue;
       const uint32_t tw = (uint32_t)now_ticks();
-      if (!wait_slots(P, t.wait_lo, t.wait_hi, ep, s, si, sh)) return;
-      const uint32_t ts = (uint32_t)now_ticks();
-      switch (t.op) {
-        case OP_QKV: task_qkv(P, t, pos, tok, lds); break;
-        case OP_ATTN: task_attn(P, t, pos, ep, lds, sh); break;
-        case OP_OPROJ: task_oproj(P, t, tok, lds); break;
-        case OP_GU: task_gu(P, t, lds); break;
-        case OP_DOWN: task_down(P, t, s, lds); break;
-        case OP_ROUTER: task_router(P, t, lds); break;
-        case OP_EGU: task_egu(P, t, lds); break;
-        case OP_EDOWN: task_edown(P, t, s, lds); break;
-        case OP_LM: task_lm(P, t, lam, s, lds); break;
-        default: break;
-      }
-      if (t.op != OP_ATTN) signal_slot(P, t.signal, ep);
-      trace_rec(P, s, si, lam, tw, ts, (uint32_t)now_ticks());
+      const Waiter wait{1, t.wait_lo, t.wait_hi, s, si, ep, sh};
+      if (!run_task(P, t, lam, s, pos, tok, lds, wait)) return;
+      signal_slot(P, t.signal, ep);
+      trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
     }
     // greedy token of step s: every workgroup when it feeds the next step,
     // workgroup 0 always (it writes the output)
@@ -839,40 +1154,27 @@ extern "C" __global__ void __launch_bounds__(512) pre_k_embed(KP P, int step) {
     tok = 0;
   }
   if (threadIdx.x == 0 && blockIdx.x == 0) P.tok_slot[1] = tok;  // token of this step
-  for (int i = threadIdx.x; i < P.h; i += blockDim.x) P.x_emb[i] = bf16f(P.embed[(int64_t)tok * P.h + i]);
+  for (int i = threadIdx.x; i < P.h; i += P.nthr) P.x_emb[i] = bf16f(P.embed[(int64_t)tok * P.h + i]);
 }
 
-// a_norm = RMSNorm(src, gain)
-extern "C" __global__ void __launch_bounds__(512) pre_k_norm(KP P, const float *src, const uint16_t *gain) {
+// a_norm = RMSNorm(x, gain) with x the layer input (mid = 0), the
+// post-attention residual (mid = 1) or the last layer's output (mid = 2).
+extern "C" __global__ void __launch_bounds__(512) pre_k_norm(KP P, int l, int mid, const uint16_t *gain) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   float *xs = lds, *red = lds + P.kmax;
-  stage_vec(P, xs, red, Src{src, nullptr, gain}, P.h, P.kmax);
-  for (int i = threadIdx.x; i < P.kmax; i += blockDim.x) P.a_norm[i] = xs[i];
+  Src s = mid == 2 ? Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, gain}
+                   : (mid ? mid_input(P, l, 0, gain) : layer_input(P, l, 0, gain));
+  stage_vec(P, xs, red, s, P.h, P.kmax);
+  for (int i = threadIdx.x; i < P.kmax; i += P.nthr) P.a_norm[i] = xs[i];
 }
 
 extern "C" __global__ void __launch_bounds__(512) pre_k_task(KP P, int si, int step) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ int sh[8];
   const int lam = blockIdx.x;
   const Task t = P.tasks[(int64_t)si * P.W + lam];
-  const int pos = P.pos0 + step;
-  const int tok = P.tok_slot[1];
-  switch (t.op) {
-    case OP_QKV: task_qkv(P, t, pos, tok, lds); break;
-    case OP_ATTN: attn_chunk(P, t, pos, lds); break;
-    case OP_OPROJ: task_oproj(P, t, tok, lds); break;
-    case OP_GU: task_gu(P, t, lds); break;
-    case OP_DOWN: task_down(P, t, step, lds); break;
-    case OP_ROUTER: task_router(P, t, lds); break;
-    case OP_EGU: task_egu(P, t, lds); break;
-    case OP_EDOWN: task_edown(P, t, step, lds); break;
-    case OP_LM: task_lm(P, t, lam, step, lds); break;
-    default: break;
-  }
-}
-
-extern "C" __global__ void __launch_bounds__(512) pre_k_combine(KP P, int l) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  attn_combine(P, l, blockIdx.x, lds);
+  const Waiter none{0, 0, 0, 0, 0, 0u, sh};
+  run_task(P, t, lam, step, P.pos0 + step, P.tok_slot[1], lds, none);
 }
 
 extern "C" __global__ void __launch_bounds__(512) pre_k_argmax(KP P, int step) {
@@ -885,6 +1187,20 @@ extern "C" __global__ void __launch_bounds__(512) pre_k_argmax(KP P, int step) {
   }
 }
 
+// Debug: the wavefront primitives on one wave of input (64 floats):
+// out[0..64) sum8, [64..128) sum16, [128] wave_sum, [129] wave_max,
+// [192..256) row_ror:8 pair sums, [256..320) xrow_sum.
+extern "C" __global__ void pre_k_lane_ops(const float *in, float *out) {
+  const int lane = threadIdx.x & 63;
+  const float v = in[lane];
+  out[lane] = sum8(v);
+  out[64 + lane] = sum16(v);
+  const float ws = wave_sum(v), wm = wave_max(v);
+  if (lane == 0) { out[128] = ws; out[129] = wm; }
+  out[192 + lane] = v + dpp<0x128>(v);
+  out[256 + lane] = xrow_sum(v);
+}
+
 // Debug: decode n fp8 codes with the GEMV's unpacking (checks the format).
 extern "C" __global__ void pre_k_fp8_decode(const uint8_t *in, float *out, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -893,6 +1209,35 @@ extern "C" __global__ void pre_k_fp8_decode(const uint8_t *in, float *out, int n
     fp8x4(*reinterpret_cast<const uint32_t *>(in + 4 * i), f);
     for (int k = 0; k < 4; ++k) out[4 * i + k] = f[k];
   }
+}
+
+// Debug / tuning: the streamed GEMV alone, y = W x over rows split evenly
+// across the grid, for a given ring depth and weight cache policy.
+template <int D, int CP>
+__global__ void __launch_bounds__(1024) pre_k_gemv_bench(const uint16_t *W, int rows, int K, const float *x,
+                                                         float *y) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int nthr = __builtin_amdgcn_readfirstlane(blockDim.x), nw = nthr >> 6;
+  const int Kp = (K + 511) / 512 * 512;
+  for (int i = threadIdx.x; i < Kp; i += nthr) lds[i] = i < K ? x[i] : 0.f;
+  float *ys = lds + Kp;
+  const int r0 = (int)((int64_t)rows * blockIdx.x / gridDim.x);
+  const int r1 = (int)((int64_t)rows * (blockIdx.x + 1) / gridDim.x);
+  struct Rows {
+    const uint16_t *W;
+    int K, r0;
+    __device__ void operator()(int g, Stream<1, D, false, CP> &S) const {
+      S.rp[0] = W + (int64_t)(r0 + g) * K;
+      S.rb[0] = (uint32_t)K * 2;
+    }
+  } rowfn{W, K, r0};
+  Stream<1, D, false, CP> S;
+  const int n = st_begin(S, rowfn, r1 - r0, K, nw);
+  ys_clear(ys, r1 - r0, 1, nw, nthr);
+  __syncthreads();
+  st_run(S, n, rowfn, [=](int, int) { return (const float *)lds; }, ys);
+  __syncthreads();
+  for (int i = threadIdx.x; i < r1 - r0; i += nthr) y[r0 + i] = ys_get(ys, i, 0, 1, nw);
 }
 
 }  // namespace pre
@@ -997,8 +1342,6 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
       hipFuncSetAttribute((const void *)pre_k_task, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
-          hipSuccess ||
-      hipFuncSetAttribute((const void *)pre_k_combine, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
     return PRE_ERR_HIP;
   int per_cu = 0;
@@ -1073,8 +1416,11 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   std::memset(&P, 0, sizeof(P));
   P.L = D.L; P.h = D.h; P.Hq = D.Hq; P.Hkv = D.Hkv; P.d = D.d; P.ffn = D.ffn; P.V = D.V; P.B = D.B;
   P.max_ctx = D.max_ctx; P.E = D.E; P.top_k = D.top_k; P.n_shared = D.n_shared; P.effn = D.effn;
-  P.moe = D.moe; P.G = D.G; P.F = D.F; P.W = D.W; P.X = D.X; P.NC = D.NC; P.n_si = D.n_si;
-  P.spl = D.stages_per_layer; P.kmax = D.kmax; P.cmax = D.cmax;
+  P.moe = D.moe; P.G = D.G; P.F = D.F; P.W = D.W; P.X = D.X; P.NC = D.NC; P.Tg = D.Tg; P.n_si = D.n_si;
+  P.spl = D.stages_per_layer; P.kmax = D.kmax; P.ymax = D.ymax; P.cmax = D.cmax;
+  P.lds_floats = e->lds_dyn / 4;
+  P.nthr = D.threads;
+  P.nw = D.threads / 64;
   P.eps = D.eps;
   P.attn_scale = (float)(1.0 / std::sqrt((double)D.d));
   char *ws = e->ws;
@@ -1087,14 +1433,12 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.vc = (uint16_t *)e->kv.v;
   P.tasks = (const Task *)(ws + Lo.tasks);
   P.flags = (uint32_t *)(ws + Lo.flags);
-  P.counters = (uint32_t *)(ws + Lo.counters);
   P.xcc = (uint32_t *)(ws + Lo.xcc);
   P.status = (DevStatus *)(ws + Lo.status);
   P.rope = (const float *)(ws + Lo.rope);
   P.x_out = (float *)(ws + Lo.x_out);
-  P.xm = (float *)(ws + Lo.xm);
+  P.pbuf = (float *)(ws + Lo.pbuf);
   P.q = (float *)(ws + Lo.q);
-  P.o = (float *)(ws + Lo.o);
   P.u = (float *)(ws + Lo.u);
   P.rl = (float *)(ws + Lo.rl);
   P.part = (float *)(ws + Lo.part);
@@ -1131,7 +1475,7 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   P.chk_logits = chk ? chk->logits : nullptr;
   P.chk_hidden = chk ? chk->hidden : nullptr;
   P.trace = e->trace;
-  P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 16, 0xffffffffu);
+  P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 32, 0xffffffffu);
   void *args[] = {&P};
   hipError_t err = hipLaunchCooperativeKernel((const void *)pre_persistent, dim3(e->D.W),
                                               dim3(e->D.threads), args, (unsigned)e->lds_dyn,
@@ -1159,28 +1503,19 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
   const Dims &D = e->D;
   const dim3 blk(D.threads);
   const unsigned lds = (unsigned)e->lds_dyn;
-  const char *ws = e->ws;
-  const float *x_out = (const float *)(ws + e->Lo.x_out), *xm = (const float *)(ws + e->Lo.xm);
-  const float *x_emb = (const float *)(ws + e->Lo.x_emb);
   const std::vector<pre_layer_w> &lw = e->lw;
-  static_assert(sizeof(pre_layer_w) == sizeof(DevLayer), "layer table layout");
   for (int s = 0; s < n_steps; ++s) {
     hipLaunchKernelGGL(pre_k_embed, dim3(1), blk, 0, st, P, s);
     for (int l = 0; l < D.L; ++l) {
       const int si0 = l * D.stages_per_layer;
-      const float *xin = l == 0 ? x_emb : x_out + (int64_t)(l - 1) * D.B * D.h;
-      hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, xin, (const uint16_t *)lw[l].attn_norm);
-      hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + 0, s);
-      hipLaunchKernelGGL(pre_k_task, dim3(D.B * D.Hkv * D.NC), blk, lds, st, P, si0 + 1, s);
-      hipLaunchKernelGGL(pre_k_combine, dim3(D.B * D.Hkv), blk, lds, st, P, l);
-      hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + 2, s);
-      hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, xm + (int64_t)l * D.B * D.h,
-                         (const uint16_t *)lw[l].ffn_norm);
+      hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, l, 0, (const uint16_t *)lw[l].attn_norm);
+      for (int k = 0; k < 3; ++k)  // QKV, attention chunks, O projection
+        hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + k, s);
+      hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, l, 1, (const uint16_t *)lw[l].ffn_norm);
       for (int k = 3; k < D.stages_per_layer; ++k)
         hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + k, s);
     }
-    hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, x_out + (int64_t)(D.L - 1) * D.B * D.h,
-                       (const uint16_t *)e->final_norm);
+    hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, D.L - 1, 2, (const uint16_t *)e->final_norm);
     hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, D.n_si - 1, s);
     hipLaunchKernelGGL(pre_k_argmax, dim3(1), dim3(64), 0, st, P, s);
   }
@@ -1215,8 +1550,7 @@ extern "C" int pre_engine_reset(pre_engine *e, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   const Layout &Lo = e->Lo;
   if (hipMemsetAsync(e->ws + Lo.status, 0, sizeof(DevStatus), st) != hipSuccess ||
-      hipMemsetAsync(e->ws + Lo.flags, 0, (size_t)(Lo.counters - Lo.flags) + (size_t)(Lo.layers - Lo.counters),
-                     st) != hipSuccess)
+      hipMemsetAsync(e->ws + Lo.flags, 0, (size_t)(Lo.layers - Lo.flags), st) != hipSuccess)
     return PRE_ERR_HIP;
   e->epoch_base = 0;
   e->broken = 0;
@@ -1265,5 +1599,50 @@ extern "C" int pre_debug_fp8_decode(const void *d_codes, float *d_out, int n, vo
   const int th = 64, nb = (n / 4 + th - 1) / th;
   hipLaunchKernelGGL(pre_k_fp8_decode, dim3(nb), dim3(th), 0, (hipStream_t)stream, (const uint8_t *)d_codes,
                      d_out, n);
+  return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
+}
+
+// Debug / tuning entry: time the streamed GEMV variants.  variant = 2 * i + c
+// with ring depth {8, 16, 24, 32}[i] and weight cache policy {default,
+// streaming}[c]; rows are split over `grid` workgroups of `threads` threads,
+// each given at least lds_min bytes of LDS (96 KB keeps one per CU).
+extern "C" int pre_debug_gemv(int variant, const void *d_w, int rows, int K, const float *d_x, float *d_y,
+                              int grid, int threads, int lds_min, void *stream) {
+  if (!d_w || !d_x || !d_y || rows < 1 || K < 8 || K % 8 || grid < 1 || threads < 64 || threads > 1024)
+    return PRE_ERR_ARG;
+  const int Kp = (K + 511) / 512 * 512;
+  const size_t lds = std::max<size_t>((size_t)(Kp + (rows + grid - 1) / grid + 64) * 4, (size_t)lds_min);
+  if (lds > 160 * 1024) return PRE_ERR_SHAPE;
+  const void *fns[8] = {(const void *)pre_k_gemv_bench<8, CP_DEF>, (const void *)pre_k_gemv_bench<8, CP_NT>,
+                        (const void *)pre_k_gemv_bench<16, CP_DEF>, (const void *)pre_k_gemv_bench<16, CP_NT>,
+                        (const void *)pre_k_gemv_bench<24, CP_DEF>, (const void *)pre_k_gemv_bench<24, CP_NT>,
+                        (const void *)pre_k_gemv_bench<32, CP_DEF>, (const void *)pre_k_gemv_bench<32, CP_NT>};
+  if (variant < 0 || variant >= 8) return PRE_ERR_ARG;
+  if (hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return PRE_ERR_HIP;
+  const uint16_t *w = (const uint16_t *)d_w;
+  void *args[] = {&w, &rows, &K, &d_x, &d_y};
+  if (hipLaunchKernel(fns[variant], dim3(grid), dim3(threads), args, lds, (hipStream_t)stream) != hipSuccess)
+    return PRE_ERR_HIP;
+  return PRE_OK;
+}
+
+// Debug: byte offsets of the workspace regions (status, flags, layers, tasks,
+// rope, xcc, x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, total) --
+// 17 int64 values.
+extern "C" int pre_debug_layout(const pre_engine *e, int64_t *out) {
+  if (!e || !out) return PRE_ERR_ARG;
+  const Layout &L = e->Lo;
+  const int64_t v[17] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u,
+                         L.rl, L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.total};
+  for (int i = 0; i < 17; ++i) out[i] = v[i];
+  return PRE_OK;
+}
+
+// Debug entry: run pre_k_lane_ops on 64 inputs (see the kernel for the layout
+// of the 320 outputs).
+extern "C" int pre_debug_lane_ops(const float *d_in, float *d_out, void *stream) {
+  if (!d_in || !d_out) return PRE_ERR_ARG;
+  hipLaunchKernelGGL(pre_k_lane_ops, dim3(1), dim3(64), 0, (hipStream_t)stream, d_in, d_out);
   return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
 }

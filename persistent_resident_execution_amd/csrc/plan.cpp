@@ -52,8 +52,12 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (D->W < 1 || D->W > 4096) return PRE_ERR_SHAPE;
   D->X = 8;
   const int bg = D->B * D->Hkv;
-  D->NC = c->attn_splits > 0 ? c->attn_splits : std::max(1, D->W / bg);
-  if (bg * D->NC > D->W) return PRE_ERR_SHAPE;
+  if (D->Hkv > 8 || D->W < bg) return PRE_ERR_SHAPE;
+  D->Tg = D->W / bg;
+  // about 256 positions per attention chunk, at most one chunk per workgroup
+  // of the (sequence, KV head)'s share
+  D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 256)));
+  if (D->NC > D->Tg) return PRE_ERR_SHAPE;
   D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
   if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
   D->stages_per_layer = moe ? 6 : 5;
@@ -61,9 +65,16 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   D->kmax = pad_to(std::max({D->h, D->Hq * D->d, D->F, moe ? D->E : 0}), 1024);
   D->cmax = cdiv(D->max_ctx, D->NC);
   const int waves = D->threads / 64;
-  // GEMV phase: staged input + reduction scratch.  Attention phase: q, scores,
-  // per-wave output partials, softmax stats.
-  int64_t gemv = (int64_t)D->kmax + 256;
+  {
+    const int W = D->W, nk = D->top_k + D->n_shared;
+    int y = std::max({2 * cdiv(D->qkv_pairs, W), cdiv(D->h, W), cdiv(D->V, W), cdiv(D->h, D->Tg)});
+    if (moe) y = std::max({y, cdiv(D->E, W), 2 * cdiv(D->F, W), cdiv(D->h, W) * nk});
+    else y = std::max(y, 2 * cdiv(D->ffn, W));
+    D->ymax = pad_to(y, 64);
+  }
+  // GEMV phase: staged input, per-row results, reduction scratch.  Attention
+  // phase: q, scores, per-wave output partials, softmax stats.
+  int64_t gemv = (int64_t)D->kmax + (int64_t)D->ymax * waves + 256;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
   D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);
@@ -79,15 +90,13 @@ void build_layout(const Dims &D, Layout *Lo) {
   const int64_t f = 4;
   Lo->status = take(sizeof(DevStatus));
   Lo->flags = take((int64_t)D.n_si * D.W * 4);
-  Lo->counters = take((int64_t)D.L * D.B * D.Hkv * 4);
   Lo->layers = take((int64_t)D.L * sizeof(DevLayer));
   Lo->tasks = take((int64_t)D.n_si * D.W * sizeof(Task));
   Lo->rope = take((int64_t)D.max_ctx * D.d * f);          // cos then sin, [pos][d/2] each
   Lo->xcc = take((int64_t)D.W * 4);
   Lo->x_out = take((int64_t)D.L * D.B * D.h * f);
-  Lo->xm = take((int64_t)D.L * D.B * D.h * f);
+  Lo->pbuf = take((int64_t)D.L * D.B * D.Hkv * D.h * f);  // O-projection partial per KV head
   Lo->q = take((int64_t)D.L * D.B * D.Hq * D.d * f);
-  Lo->o = take((int64_t)D.L * D.B * D.Hq * D.d * f);
   Lo->u = take((int64_t)D.L * D.B * D.F * f);
   Lo->rl = take((int64_t)D.L * D.B * std::max(D.E, 1) * f);
   Lo->part = take((int64_t)D.L * D.B * D.Hkv * D.NC * D.G * (D.d + 2) * f);
@@ -122,11 +131,13 @@ void build_tasks(const Dims &D, std::vector<Task> &T) {
       t.wait_hi = s_prev >= 0 ? slot(D, s_prev, W) : 0;
       t.signal = slot(D, s_qkv, lam);
     }
-    const int nattn = D.B * D.Hkv * D.NC;
+    // attention chunk c of (sequence, KV head) bg on workgroup bg * Tg + c:
+    // the XCD that computed that head's QKV rows (lambda is XCD-major)
     for (int lam = 0; lam < W; ++lam) {
       Task &t = at(s_attn, lam);
-      if (lam >= nattn) { t.op = OP_NONE; t.signal = -1; continue; }
-      const int bg = lam / D.NC, c = lam % D.NC, g = bg % D.Hkv;
+      const int bg = lam / D.Tg, c = lam % D.Tg;
+      if (bg >= D.B * D.Hkv || c >= D.NC) { t.op = OP_NONE; t.signal = -1; continue; }
+      const int g = bg % D.Hkv;
       t.op = OP_ATTN; t.layer = l; t.r0 = c; t.r1 = D.NC; t.aux = bg;
       // producers: QKV tasks whose pair range meets group g's pairs
       int lo = -1, hi = -1;
@@ -138,16 +149,24 @@ void build_tasks(const Dims &D, std::vector<Task> &T) {
           hi = q + 1;
         }
       }
-      t.wait_lo = slot(D, s_qkv, lo);
-      t.wait_hi = slot(D, s_qkv, hi);
-      t.signal = slot(D, s_attn, bg);
+      t.wait_lo = slot(D, s_attn - 1, lo);
+      t.wait_hi = slot(D, s_attn - 1, hi);
+      t.signal = slot(D, s_attn, lam);
     }
+    // output projection, split over KV heads: workgroup bg * Tg + i combines
+    // head bg's chunks and multiplies rows i of Wo's column slice for bg
     for (int lam = 0; lam < W; ++lam) {
       Task &t = at(s_o, lam);
+      const int bg = lam / D.Tg, i = lam % D.Tg;
       t.op = OP_OPROJ; t.layer = l;
-      split(D.h, W, lam, &t.r0, &t.r1);
-      t.wait_lo = slot(D, s_attn, 0);
-      t.wait_hi = slot(D, s_attn, D.B * D.Hkv);
+      if (bg < D.B * D.Hkv) {
+        t.aux = bg;
+        split(D.h, D.Tg, i, &t.r0, &t.r1);
+      } else {  // left-over workgroup: no rows, still takes part in the stage
+        t.aux = 0; t.r0 = t.r1 = 0;
+      }
+      t.wait_lo = slot(D, s_attn, t.aux * D.Tg);
+      t.wait_hi = slot(D, s_attn, t.aux * D.Tg + D.NC);
       t.signal = slot(D, s_o, lam);
     }
     if (!D.moe) {
@@ -238,7 +257,7 @@ int validate(const Dims &D, const std::vector<Task> &T) {
       if (t.signal < 0 || t.signal >= n_slots || t.signal / W != si) return 4;
       if (setter_si[t.signal] >= 0 && setter_si[t.signal] != si) return 4;
       setter_si[t.signal] = si;
-      if (t.op != OP_ATTN && t.signal != si * W + lam) return 4;
+      if (t.signal != si * W + lam) return 4;
     }
   }
   for (int si = 0; si < D.n_si; ++si)
@@ -260,18 +279,20 @@ int validate(const Dims &D, const std::vector<Task> &T) {
         const Task &t = T[(size_t)si * W + lam];
         if (t.op != OP_ATTN) continue;
         if (t.aux < 0 || t.aux >= D.B * D.Hkv || t.r0 < 0 || t.r0 >= D.NC || t.r1 != D.NC) return 6;
-        if (t.signal != si * W + t.aux) return 6;
         seen[(size_t)t.aux * D.NC + t.r0]++;
       }
       for (int v : seen) if (v != 1) return 6;
       continue;
     }
     const int64_t n = coverage_target(D, op);
-    std::vector<int> cnt(n, 0);
+    const int copies = op == OP_OPROJ ? D.B * D.Hkv : 1;  // O-projection: every row once per head
+    std::vector<int> cnt((size_t)n * copies, 0);
     for (int lam = 0; lam < W; ++lam) {
       const Task &t = T[(size_t)si * W + lam];
       if (t.r0 < 0 || t.r1 < t.r0 || t.r1 > n) return 5;
-      for (int r = t.r0; r < t.r1; ++r) cnt[r]++;
+      const int k = op == OP_OPROJ ? t.aux : 0;
+      if (k < 0 || k >= copies) return 5;
+      for (int r = t.r0; r < t.r1; ++r) cnt[(size_t)k * n + r]++;
     }
     for (int v : cnt) if (v != 1) return 5;
   }
@@ -298,7 +319,12 @@ int validate(const Dims &D, const std::vector<Task> &T) {
           }
           break;
         }
-        case OP_OPROJ: ok = covers(t, si - 1, 0, D.B * D.Hkv); break;
+        case OP_OPROJ:  // every chunk task of its (sequence, KV head)
+          for (int q = 0; q < W && ok; ++q) {
+            const Task &p = T[(size_t)(si - 1) * W + q];
+            if (p.op == OP_ATTN && p.aux == t.aux) ok = covers(t, si - 1, q, q + 1);
+          }
+          break;
         case OP_LM: ok = covers(t, si - 1, 0, W); break;
         default: ok = covers(t, si - 1, 0, W); break;  // GU, DOWN, ROUTER, EGU, EDOWN
       }

@@ -25,7 +25,7 @@ enum Op : int32_t {
   OP_NONE = 0,
   OP_QKV = 1,    // RMSNorm-folded QKV rows (RoPE pairs), K/V append
   OP_ATTN = 2,   // one KV chunk of one (sequence, KV head); last arriver combines
-  OP_OPROJ = 3,  // output projection rows + residual
+  OP_OPROJ = 3,  // one KV head's slice of the output projection (split-K partial)
   OP_GU = 4,     // gate/up row pairs + SwiGLU
   OP_DOWN = 5,   // down projection rows + residual
   OP_ROUTER = 6, // router rows (MoE)
@@ -38,7 +38,7 @@ enum Op : int32_t {
 struct Task {
   int32_t op, layer;
   int32_t r0, r1;     // row / pair range [r0, r1); ATTN: r0 = chunk, r1 = chunks
-  int32_t aux;        // ATTN: sequence * n_kv_heads + kv head
+  int32_t aux;        // ATTN, OPROJ: sequence * n_kv_heads + kv head
   int32_t wait_lo, wait_hi;  // ready slots [lo, hi) that must reach this step's epoch
   int32_t signal;     // slot set to the epoch when done (ATTN: set by the combiner)
 };
@@ -63,8 +63,8 @@ struct DevStatus {
 
 // Byte offsets of everything inside the caller's workspace.
 struct Layout {
-  int64_t status, flags, counters, layers, tasks, rope, xcc;
-  int64_t x_out, xm, q, o, u, rl, part, lmp, x_emb, a_norm, tok;
+  int64_t status, flags, layers, tasks, rope, xcc;
+  int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok;
   int64_t total;
 };
 
@@ -76,8 +76,10 @@ struct Dims {
   int32_t qkv_pairs;  // RoPE pairs of all QKV rows: Hkv * (G + 2) * d / 2
   int32_t F;          // width of the FFN activation slot (ffn or (top_k+n_shared)*effn)
   int32_t W, X, NC;   // workgroups, XCDs, attention chunks per (sequence, KV head)
+  int32_t Tg;         // workgroups per (sequence, KV head): W / (batch * n_kv_heads)
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded
+  int32_t ymax;       // most GEMV results one task produces (x waves: LDS partials)
   int32_t cmax;       // longest attention chunk (positions)
   int32_t lds_bytes;  // dynamic LDS per workgroup
   float eps, theta;

@@ -105,6 +105,9 @@ def lib():
         L.pre_step_bytes.restype = C.c_int64
         L.pre_step_bytes.argtypes = [C.POINTER(Config), C.POINTER(i32)]
         L.pre_debug_fp8_decode.argtypes = [vp, vp, C.c_int, vp]
+        L.pre_debug_layout.argtypes = [vp, vp]
+        L.pre_debug_lane_ops.argtypes = [vp, vp, vp]
+        L.pre_debug_gemv.argtypes = [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp]
         _lib = L
     return _lib
 
@@ -247,6 +250,18 @@ class Engine:
         _check(lib().pre_engine_set_trace(self.h, _ptr(buf), 0 if buf is None else buf.numel() *
                                           buf.element_size()), "set_trace")
 
+    LAYOUT = ["status", "flags", "layers", "tasks", "rope", "xcc", "x_out", "pbuf", "q", "u", "rl",
+              "part", "lmp", "x_emb", "a_norm", "tok", "total"]
+
+    def debug_slot(self, name, count, dtype=torch.float32, offset=0):
+        """A view of a workspace region (debugging)."""
+        import numpy as np
+        off = np.zeros(17, np.int64)
+        _check(lib().pre_debug_layout(self.h, C.c_void_p(off.ctypes.data)), "debug_layout")
+        start = int(off[self.LAYOUT.index(name)]) + offset
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return self.workspace[start:start + count * esz].view(dtype)
+
     def close(self):
         if getattr(self, "h", None):
             lib().pre_engine_destroy(self.h)
@@ -264,5 +279,21 @@ def fp8_decode_table(device="cuda"):
     codes = torch.arange(256, dtype=torch.uint8, device=device)
     out = torch.empty(256, dtype=torch.float32, device=device)
     _check(lib().pre_debug_fp8_decode(_ptr(codes), _ptr(out), 256, _stream()), "fp8_decode")
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def debug_gemv(variant, W, x, y, grid=256, threads=512, lds_min=96 * 1024):
+    """Tuning entry: y = W x with the streamed GEMV variant (see pre_debug_gemv)."""
+    rows, K = W.shape
+    _check(lib().pre_debug_gemv(int(variant), _ptr(W), rows, K, _ptr(x), _ptr(y), int(grid),
+                                int(threads), int(lds_min), _stream()), "debug_gemv")
+
+
+def debug_lane_ops(x):
+    """Wavefront primitives applied to 64 floats (debug entry pre_debug_lane_ops)."""
+    inp = x.to(device="cuda", dtype=torch.float32).contiguous()
+    out = torch.zeros(320, dtype=torch.float32, device="cuda")
+    _check(lib().pre_debug_lane_ops(_ptr(inp), _ptr(out), _stream()), "debug_lane_ops")
     torch.cuda.synchronize()
     return out.cpu()

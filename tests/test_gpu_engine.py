@@ -53,6 +53,23 @@ def test_fp8_unpacking_matches_oracle_decoder(oracle_lib):
     assert np.array_equal(got[finite], ref[finite])
 
 
+def test_wavefront_lane_primitives():
+    """The DPP / permlane reductions the tiles use, on known data."""
+    _say("[test] wavefront lane primitives")
+    x = torch.arange(64, dtype=torch.float32) * 1.5 - 17.0
+    x[37] = 1000.0
+    out = E.debug_lane_ops(x).numpy()
+    xv = x.numpy()
+    groups8 = xv.reshape(8, 8).sum(axis=1)
+    rows16 = xv.reshape(4, 16).sum(axis=1)
+    assert np.allclose(out[0:64], np.repeat(groups8, 8))
+    assert np.allclose(out[64:128], np.repeat(rows16, 16))
+    assert np.isclose(out[128], xv.sum()) and out[129] == xv.max()
+    r = xv.reshape(4, 2, 8)
+    assert np.allclose(out[192:256], np.repeat((r[:, 0] + r[:, 1])[:, None, :], 2, axis=1).ravel())
+    assert np.allclose(out[256:320], np.tile(xv.reshape(4, 16).sum(axis=0), 4))
+
+
 def test_tiny_persistent_matches_oracle(tiny):
     S, prompt, ref = tiny
     _say("[test] tiny persistent, 256 workgroups")
@@ -174,3 +191,49 @@ def test_small_dense_ragged_baseline(small):
     S, prompt, ref = small
     _say("[test] small dense baseline")
     _check_run(S, prompt, ref, baseline=True)
+
+
+@pytest.mark.parametrize("persistent", [True, False])
+def test_layer0_intermediates_match_oracle_primitives(oracle_lib, persistent):
+    """One decode step at position 0: each intermediate activation of layer 0
+    (q, the per-KV-head output-projection partials, residual after attention,
+    SwiGLU output, layer output) against the
+    oracle's primitives applied step by step -- localises a faulty tile."""
+    _say(f"[test] layer-0 intermediates, {'persistent' if persistent else 'baseline'}")
+    m = synth.TINY
+    S = parity.DenseSetup(oracle_lib, m, seed=0)
+    W, L0, tok, d = S.Wnp, S.Wnp["layers"][0], 5, m.head_dim
+    f = lambda b: oracle_lib.bf16_to_f64(b).reshape(b.shape)  # noqa: E731
+    x = f(W["embed"][tok])
+    a = oracle_lib.rmsnorm(x, L0["attn_norm"], m.rms_eps)
+    q, v = oracle_lib.gemv_bf16(L0["wq"], a), oracle_lib.gemv_bf16(L0["wv"], a)
+    vb = f(oracle_lib.f32_to_bf16(v.astype(np.float32)))  # single key: attention returns V
+    grp = lambda h: h * m.n_kv_heads // m.n_q_heads  # noqa: E731
+    o = np.concatenate([vb[grp(h) * d:(grp(h) + 1) * d] for h in range(m.n_q_heads)])
+    xm = x + oracle_lib.gemv_bf16(L0["wo"], o)
+    b = oracle_lib.rmsnorm(xm, L0["ffn_norm"], m.rms_eps)
+    g, up = oracle_lib.gemv_bf16(L0["wg"], b), oracle_lib.gemv_bf16(L0["wu"], b)
+    u = np.array([oracle_lib.silu(z) for z in g]) * up
+    xo = xm + oracle_lib.gemv_bf16(L0["wd"], u)
+    eng = S.engine(grid_wgs=16)
+    eng.set_positions([0])
+    run = eng.decode if persistent else eng.baseline_decode
+    run(1, in_tokens=torch.tensor([tok], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    eng.status()
+    sl = lambda n, c: eng.debug_slot(n, c).cpu().numpy().astype(np.float64)  # noqa: E731
+    # the O projection is split by KV head: its partials plus the layer input
+    # make the post-attention residual
+    pb = sl("pbuf", m.n_kv_heads * m.hidden).reshape(m.n_kv_heads, m.hidden)
+    got_xm = x + pb.sum(axis=0)
+    o_proj_by_head = [oracle_lib.gemv_bf16(np.ascontiguousarray(
+        L0["wo"][:, g * (m.n_q_heads // m.n_kv_heads) * d:(g + 1) * (m.n_q_heads // m.n_kv_heads) * d]),
+        o[g * (m.n_q_heads // m.n_kv_heads) * d:(g + 1) * (m.n_q_heads // m.n_kv_heads) * d])
+        for g in range(m.n_kv_heads)]
+    for name, got, ref in (("q", sl("q", q.size), q), ("o-proj by head", pb, np.array(o_proj_by_head)),
+                           ("xm", got_xm, xm), ("u", sl("u", m.ffn_dim), u),
+                           ("x_out", sl("x_out", m.hidden), xo)):
+        rel = np.abs(got - ref).max() / np.abs(ref).max()
+        _say(f"  {name}: rel err {rel:.1e}")
+        assert rel < 1e-5, name
+    eng.close()

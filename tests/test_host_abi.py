@@ -53,9 +53,14 @@ ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
 @pytest.mark.parametrize("m", ALL, ids=lambda m: f"{m.name}-{m.max_ctx}")
 @pytest.mark.parametrize("grid", [0, 1, 7, 16, 37, 256])
 def test_plans_validate(lib, m, grid):
-    if grid and grid < m.n_kv_heads:
-        with pytest.raises(E.PreError):
+    W = grid or 256
+    kmax = -(-max(m.hidden, m.n_q_heads * m.head_dim, m.ffn_dim,
+                  (m.top_k + m.n_shared) * m.expert_ffn, m.n_experts) // 1024) * 1024
+    lds = (kmax + 8 * -(-m.vocab // W) + 256) * 4  # LM-head rows dominate the result buffer
+    if grid and (grid < m.n_kv_heads or lds > 160 * 1024):
+        with pytest.raises(E.PreError) as ei:
             E.plan_describe(m, grid_wgs=grid)
+        assert ei.value.code == -2
         return
     info, _ = E.plan_describe(m, grid_wgs=grid)
     assert info.validator == 0
@@ -69,19 +74,29 @@ def test_microbatch_reported_unsupported(lib):
     assert ei.value.code == -6
 
 
-def test_attention_is_xcd_local_on_the_8b_shape(lib):
-    """Each KV head's attention chunks sit on one XCD and wait only on QKV
-    tasks of that XCD (the head-to-XCD routing)."""
+def test_attention_and_o_projection_are_xcd_local_on_the_8b_shape(lib):
+    """Each KV head's attention chunks and its slice of the output projection
+    sit on the XCD that computed the head's QKV rows, and wait only on tasks
+    of that XCD (the head-to-XCD routing)."""
     m = synth.DENSE8B
     info, T = E.plan_describe(m, with_tasks=True)
     W = info.n_wgs
-    per = W // 8
-    attn = T[1 * W:2 * W]
+    per = W // 8  # workgroups per XCD (lambda is XCD-major)
+    attn, oproj = T[1 * W:2 * W], T[2 * W:3 * W]
+    n_attn = 0
     for lam in range(W):
         op, layer, r0, r1, aux, lo, hi, sig = attn[lam]
-        g = aux % m.n_kv_heads
-        assert op == 2 and lam // per == g
-        assert lo == W + 0 * W - W + g * per and hi == g * per + per  # slots of QKV stage 0
+        if op == 0:
+            continue
+        n_attn += 1
+        assert op == 2 and lam // per == aux % m.n_kv_heads
+        assert lo == (aux % m.n_kv_heads) * per and hi == lo + per  # QKV slots of that XCD
+        op, layer, r0, r1, aux, lo, hi, sig = oproj[lam]
+    assert n_attn == m.n_kv_heads * info.attn_splits
+    for lam in range(W):
+        op, layer, r0, r1, aux, lo, hi, sig = oproj[lam]
+        assert op == 3 and aux == lam // per
+        assert lo == W + aux * per and hi == lo + info.attn_splits  # that head's chunk tasks
 
 
 def _planted(m, mutate):
@@ -108,9 +123,9 @@ def test_validator_rejects_planted_faults(lib):
     def skip(T, W):
         T[4 * W + 2] = [0, 0, 0, 0, 0, 0, 0, -1]
     assert _planted(m, skip) in (2, 8)
-    # an attention chunk dropped
+    # an attention chunk dropped (two tasks on the same chunk)
     def drop(T, W):
-        T[1 * W + 3, 2] = T[1 * W + 2, 2]
+        T[1 * W + 1, 2] = T[1 * W + 0, 2]
     assert _planted(m, drop) == 6
     # a signal slot shared by two tasks
     assert _planted(m, lambda T, W: T.__setitem__((4 * W + 1, 7), 4 * W + 0)) == 4
