@@ -107,6 +107,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0x143, 0xc>(v);  // row_bcast:31
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// Two sums over the 64 lanes at once (same order as wave_sum); the totals
+// are valid in lane 63 only, which saves the final readlane.
+__device__ __forceinline__ float2 wave_sum2_l63(float a, float b) {
+  a += dpp<0xb1>(a); b += dpp<0xb1>(b);
+  a += dpp<0x4e>(a); b += dpp<0x4e>(b);
+  a += dpp<0x141>(a); b += dpp<0x141>(b);
+  a += dpp<0x140>(a); b += dpp<0x140>(b);
+  a += dpp<0x142, 0xa>(a); b += dpp<0x142, 0xa>(b);
+  a += dpp<0x143, 0xc>(a); b += dpp<0x143, 0xc>(b);
+  return float2{a, b};
+}
 // DPP move where lanes the row mask excludes keep their own value.
 template <int CTRL, int ROWMASK = 0xf>
 __device__ __forceinline__ float dpp_keep(float v) {

@@ -56,6 +56,7 @@ struct KP {
   uint32_t *trace;
   uint32_t trace_cap;
   int32_t persistent;
+  int32_t b_si, b_step;  // baseline launches: the stage and step to run
 };
 
 // ---------------------------------------------------------------------------
@@ -248,162 +249,245 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
 // ---------------------------------------------------------------------------
 // Streamed GEMV core.
 //
-// A task computes groups [0, ng) of R weight rows that share the same K-long
-// input (a RoPE pair, a gate/up pair, or single rows).  Each row is cut into
-// chunks of one 16-byte load per lane (8 bf16 or 16 fp8 values; 512 or 1024
-// columns per chunk), so every load instruction of a wavefront reads 1 KB of
-// consecutive weight bytes.  The task's (group, chunk) units, group-major,
-// are split into one contiguous span per wavefront (split-K across
-// wavefronts where a span ends inside a group), so every wavefront streams
-// the same amount.  A ring of D units (D * R loads) is kept in flight per
-// wavefront: unit u is consumed while unit u + D is being fetched, across row
-// boundaries, with no barrier.  The first D units are issued before the task
-// waits for its producers (weights never wait on activations).  Loads past a
-// row's end, or past the span's end, address a zero-length buffer and return
-// 0 without touching memory, so every ring slot issues exactly R loads and
-// the wait counts stay static.  A wavefront writes one partial sum per
-// (group it touched, row) into LDS; the task's epilogue adds the wavefronts'
-// partials in wavefront order (deterministic).
+// Every projection of the step runs as a stream of row *pairs* that share
+// one input vector: a RoPE pair (j, j + d/2) of one q/k/v head, a gate/up
+// pair, or two consecutive rows (the second one absent at a ragged end).  A
+// task's pairs form a few segments -- runs of pairs inside one matrix (a
+// head, an expert slot, a row range) -- listed in LDS.  Each row is cut into
+// chunks of one 16-byte load per lane (512 bf16 or 1024 fp8 columns), so
+// every load instruction of a wavefront reads 1 KB of consecutive weight
+// bytes.  The task's (pair, chunk) units are split into one contiguous span
+// per wavefront (split-K across wavefronts where a span ends inside a pair),
+// so every wavefront streams the same amount.  A ring of D units (2D loads)
+// is kept in flight per wavefront: unit u is consumed while unit u + D is
+// being fetched, across row and segment boundaries, with no barrier.  The
+// first D units are issued before the task waits for its producers (weights
+// never wait on activations).  Loads past a row's end, or past the span's
+// end, address a zero-length buffer and return 0 without touching memory.
+// A wavefront writes one partial sum per (pair it touched, row) into LDS;
+// the epilogue adds the wavefronts' partials in wavefront order
+// (deterministic).
+//
+// Every projection shares this one loop -- one copy for bf16 weights, one
+// for fp8 experts -- so the code the resident kernel runs stays small enough
+// to stay in the instruction cache across task switches.
 
 constexpr int CP_W = CP_NT;  // weight loads: streaming (read once per step)
+constexpr int RING = 4;      // units (pairs of 16-byte loads per lane) in flight
 
-template <int R, int D, bool FP8, int CP = CP_W>
-struct Stream {
-  v4i buf[D][R];
-  float sc[D][R];
-  const void *rp[R];      // rows of the group being issued
-  uint32_t rb[R];
-  const uint16_t *sp[R];  // fp8: block-scale row of each row
-  uint32_t sb[R];
-  int ig, ic, cg, cc, nch, left;  // issue / compute cursors, units left to issue
-  int wave, nw;                   // this wavefront, wavefronts per workgroup
-  float acc[R];
+// A run of n pairs inside one matrix.  Pair i of the run has its A row at
+// a + i * pstride and its B row at b + i * pstride (pairs i >= nB have no B
+// row); its row index, for the fp8 block scales, is j0 + i * gstep.
+struct Seg {
+  uint64_t a, b;    // byte addresses of the first pair's A and B rows (b = 0: none)
+  uint64_t sa, sb;  // fp8: block-scale matrices of A and B (row block 0)
+  int32_t j0, n, nB, xo;  // first row index, pairs, pairs with a B row, input offset (floats)
+};
+constexpr int SEGMAX = 80;  // most segments of one task (every q/k/v head of a layer)
+constexpr int SEG_FLOATS = SEGMAX * (int)(sizeof(Seg) / 4);
+
+// Geometry shared by all pairs of a task (wave-uniform).
+struct Geo {
+  int K;             // columns of every row
+  uint32_t rowbytes; // bytes of one row's K columns
+  uint32_t pstride;  // bytes from one pair's A row to the next pair's
+  int gstep, jb;     // rows from one pair's A row to the next's; B row index - A row index
+  uint32_t srow;     // fp8: bytes per row block of a block-scale matrix
+  int nseg, NG;      // segments, pairs in all
 };
 
-// Issue the next unit of the span into ring slot j (the caller knows one is
-// left).
-template <int R, int D, bool FP8, int CP, class RowFn>
-__device__ __forceinline__ void st_issue(Stream<R, D, FP8, CP> &S, int j, RowFn &rowfn) {
-  const int lane = threadIdx.x & 63;
-  const int col = FP8 ? S.ic * 1024 + lane * 16 : S.ic * 512 + lane * 8;
-  const uint32_t off = FP8 ? (uint32_t)col : (uint32_t)col * 2;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    S.buf[j][r] = ld128<CP>(mkbuf(S.rp[r], S.rb[r]), off);
-    if (FP8) {
-      // two bf16 scales per dword; this lane's 16 columns share one 128-wide block
-      const int blk = col >> 7;
-      const uint32_t w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(mkbuf(S.sp[r], S.sb[r]),
-                                                                         (uint32_t)(blk >> 1) * 4, 0, CP_DEF);
-      S.sc[j][r] = bf16f((uint16_t)((blk & 1) ? (w >> 16) : (w & 0xffffu)));
-    }
-  }
-  --S.left;
-  if (++S.ic == S.nch) {
-    S.ic = 0;
-    ++S.ig;
-    if (S.left > 0) rowfn(S.ig, S);
+// The geometry as scalar values.  Builders compute it next to a branch taken
+// by one thread (the one writing the table); the compiler may then merge the
+// two copies into a value it must treat as per-lane, which would turn every
+// weight load into a loop over lanes.  Reading each field through
+// readfirstlane keeps it scalar.
+__device__ __forceinline__ int rfl(int v);
+__device__ __forceinline__ Geo geo_uniform(const Geo &g) {
+  return Geo{rfl(g.K), (uint32_t)rfl((int)g.rowbytes), (uint32_t)rfl((int)g.pstride), rfl(g.gstep), rfl(g.jb),
+             (uint32_t)rfl((int)g.srow), rfl(g.nseg), rfl(g.NG)};
+}
+
+template <bool FP8, int D = RING, int CP = CP_W>
+struct PStream {
+  v4i buf[D][2];
+  float sc[D][2];  // fp8: the block scale of each lane's 16 weights
+  int xo[D];       // fp8: input offset of the unit in each slot
+  // issue cursor (wave-uniform)
+  uint64_t pa, pb, sa, sb;
+  int j, ig, is, ic, segn, segnB, segxo;
+  uint32_t rbA;
+  // compute cursor
+  int cg, cc;
+  int nch, left, wave, nw;
+  float acc[2];
+};
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t rfl64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ Rsrc mkbuf64(uint64_t p, uint32_t bytes) {
+  return mkbuf(reinterpret_cast<const void *>(p), bytes);
+}
+
+// Point the issue cursor at the first pair of segment s (past the last
+// segment every row has length 0).
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void seg_enter(PStream<FP8, D, CP> &S, const Seg *tab, const Geo &G, int s) {
+  S.ig = 0;
+  if (s < G.nseg) {
+    const Seg &e = tab[s];
+    S.pa = rfl64(e.a);
+    S.pb = rfl64(e.b);
+    if (FP8) { S.sa = rfl64(e.sa); S.sb = rfl64(e.sb); }
+    S.j = rfl(e.j0);
+    S.segn = rfl(e.n);
+    S.segnB = rfl(e.nB);
+    S.segxo = rfl(e.xo);
+    S.rbA = G.rowbytes;
+  } else {
+    S.pa = S.pb = S.sa = S.sb = 0;
+    S.j = 0;
+    S.segn = 0x7fffffff;
+    S.segnB = 0;
+    S.segxo = 0;
+    S.rbA = 0;
   }
 }
 
-// This wavefront's span of the task's ng * nch units; issues its first D
-// units (all of them when the span is shorter).  Returns the span length.
-// When the span covers a whole ring the D issues are unconditional, so the
-// ring's wait counts stay static through the main loop.
-template <int R, int D, bool FP8, int CP, class RowFn>
-__device__ __forceinline__ int st_begin(Stream<R, D, FP8, CP> &S, RowFn &rowfn, int ng, int K, int nw) {
+// Issue the unit under the cursor into ring slot jj and advance the cursor.
+// Once the span is used up every further issue reads nothing.
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_issue(PStream<FP8, D, CP> &S, int jj, const Seg *tab, const Geo &G) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t col = FP8 ? (uint32_t)S.ic * 1024 + lane * 16 : (uint32_t)S.ic * 512 + lane * 8;
+  const uint32_t off = FP8 ? col : col * 2;
+  const uint32_t rbB = S.ig < S.segnB ? S.rbA : 0u;
+  S.buf[jj][0] = ld128<CP>(mkbuf64(S.pa, S.rbA), off);
+  S.buf[jj][1] = ld128<CP>(mkbuf64(S.pb, rbB), off);
+  if (FP8) {
+    // this lane's 16 columns share one 128-wide block: one bf16 scale each
+    const uint32_t so = (col >> 7) * 2;
+    S.sc[jj][0] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(
+        mkbuf64(S.sa + (uint64_t)(S.j >> 7) * G.srow, S.rbA ? G.srow : 0u), so, 0, CP_DEF));
+    S.sc[jj][1] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(
+        mkbuf64(S.sb + (uint64_t)((S.j + G.jb) >> 7) * G.srow, rbB ? G.srow : 0u), so, 0, CP_DEF));
+    S.xo[jj] = S.segxo;
+  }
+  if (--S.left <= 0) {
+    S.rbA = 0;
+  } else if (++S.ic == S.nch) {
+    S.ic = 0;
+    if (++S.ig == S.segn) {
+      seg_enter(S, tab, G, ++S.is);
+    } else {
+      S.pa += G.pstride;
+      S.pb += G.pstride;
+      S.j += G.gstep;
+    }
+  }
+}
+
+// This wavefront's span of the task's NG * nch units; issues its first D
+// units (reading nothing past the span).  Returns the span length.
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ int st_begin(PStream<FP8, D, CP> &S, const Seg *tab, const Geo &G, int nw) {
   const int wave = wave_id();
   S.wave = wave;
   S.nw = nw;
-  S.nch = FP8 ? (K + 1023) >> 10 : (K + 511) >> 9;
-  const int N = ng * S.nch, u0 = (int)((int64_t)N * wave / nw), u1 = (int)((int64_t)N * (wave + 1) / nw);
+  S.nch = FP8 ? (G.K + 1023) >> 10 : (G.K + 511) >> 9;
+  const uint32_t N = (uint32_t)(G.NG * S.nch);  // < 2^26 for every supported shape
+  const int u0 = (int)(N * (uint32_t)wave / (uint32_t)nw), u1 = (int)(N * (uint32_t)(wave + 1) / (uint32_t)nw);
   const int n = u1 - u0;
-  S.ig = S.cg = u0 / S.nch;
-  S.ic = S.cc = u0 % S.nch;
+  int g = u0 / S.nch;
+  S.cg = g;
+  S.cc = S.ic = u0 - g * S.nch;
   S.left = n;
-#pragma unroll
-  for (int r = 0; r < R; ++r) { S.acc[r] = 0.f; S.rp[r] = nullptr; S.rb[r] = 0; S.sp[r] = nullptr; S.sb[r] = 0; }
-  if (n > 0) rowfn(S.ig, S);
-  if (n >= D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) st_issue(S, j, rowfn);
-  } else {
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < n) st_issue(S, j, rowfn);
+  S.acc[0] = S.acc[1] = 0.f;
+  int s = 0;
+  while (s < G.nseg) {  // the segment holding the span's first pair
+    const int ns = rfl(tab[s].n);
+    if (g < ns) break;
+    g -= ns;
+    ++s;
   }
+  S.is = s;
+  seg_enter(S, tab, G, s);
+  S.ig = g;
+  S.pa += (uint64_t)g * G.pstride;
+  S.pb += (uint64_t)g * G.pstride;
+  S.j += g * G.gstep;
+  if (n <= 0) S.rbA = 0;
+#pragma unroll
+  for (int jj = 0; jj < D; ++jj) st_issue(S, jj, tab, G);
   return n;
 }
 
-// Unit in ring slot j: accumulate; at the end of a group (or of the span)
-// write the wavefront's partial of that group to ys[(g * nw + wave) * R + r].
-template <int R, int D, bool FP8, int CP, class XFn>
-__device__ __forceinline__ void st_compute(Stream<R, D, FP8, CP> &S, int j, bool span_end, XFn &xfn,
+// Unit in ring slot jj: accumulate; at the end of a pair (or of the span)
+// lane 63 writes the wavefront's partials of that pair to
+// ys[(pair * nw + wave) * 2 + {0, 1}].
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_compute(PStream<FP8, D, CP> &S, int jj, bool span_end, const float *xs,
                                            float *ys) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float *xb = xfn(S.cg, r) + (FP8 ? S.cc * 1024 + lane * 16 : S.cc * 512 + lane * 8);
-    if (FP8) {
-      S.acc[r] = fmaf(S.sc[j][r], dot16_fp8(S.buf[j][r], xb), S.acc[r]);
-    } else {
-      const float4 *x4 = reinterpret_cast<const float4 *>(xb);
-      S.acc[r] = dot8_bf16(S.buf[j][r], x4[0], x4[1], S.acc[r]);
-    }
+  const float *xb = xs + (FP8 ? S.xo[jj] + S.cc * 1024 + lane * 16 : S.cc * 512 + lane * 8);
+  if (FP8) {
+    S.acc[0] = fmaf(S.sc[jj][0], dot16_fp8(S.buf[jj][0], xb), S.acc[0]);
+    S.acc[1] = fmaf(S.sc[jj][1], dot16_fp8(S.buf[jj][1], xb), S.acc[1]);
+  } else {
+    const float4 *x4 = reinterpret_cast<const float4 *>(xb);
+    const float4 x0 = x4[0], x1 = x4[1];
+    S.acc[0] = dot8_bf16(S.buf[jj][0], x0, x1, S.acc[0]);
+    S.acc[1] = dot8_bf16(S.buf[jj][1], x0, x1, S.acc[1]);
   }
   const bool row_end = ++S.cc == S.nch;
   if (row_end || span_end) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float y = wave_sum(S.acc[r]);
-      S.acc[r] = 0.f;
-      if (lane == 0) ys[(S.cg * S.nw + S.wave) * R + r] = y;
-    }
+    const float2 y = wave_sum2_l63(S.acc[0], S.acc[1]);
+    S.acc[0] = S.acc[1] = 0.f;
+    if (lane == 63) *reinterpret_cast<float2 *>(ys + (S.cg * S.nw + S.wave) * 2) = y;
     if (row_end) { S.cc = 0; ++S.cg; }
   }
 }
 
-// Consume the span of n units: xfn(g, r) is the LDS input of row r of group g.
-// Full rounds of the ring first (one unconditional issue per consumed unit),
-// then the last one or two rounds without further issues past the span.
-template <int R, int D, bool FP8, int CP, class RowFn, class XFn>
-__device__ __forceinline__ void st_run(Stream<R, D, FP8, CP> &S, int n, RowFn &rowfn, XFn xfn, float *ys) {
-  if (n >= D) {
-    const int m = (n - D) / D;  // rounds whose every issue lies inside the span
-    for (int q = 0; q < m; ++q) {
+// Consume the span of n units.  Full rounds of the ring first (one issue per
+// consumed unit, all inside the span), then the last one or two rounds.
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_run(PStream<FP8, D, CP> &S, int n, const Seg *tab, const Geo &G,
+                                       const float *xs, float *ys) {
+  const int m = n >= D ? (n - D) / D : 0;  // rounds whose every issue lies inside the span
+  for (int q = 0; q < m; ++q) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
-        st_compute(S, j, false, xfn, ys);
-        st_issue(S, j, rowfn);
-      }
+    for (int jj = 0; jj < D; ++jj) {
+      st_compute(S, jj, false, xs, ys);
+      st_issue(S, jj, tab, G);
     }
-    const int rem = n - m * D;  // D <= rem < 2D
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      st_compute(S, j, j == rem - 1, xfn, ys);
-      if (j + D < rem) st_issue(S, j, rowfn);
-    }
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j + D < rem) st_compute(S, j, j + D == rem - 1, xfn, ys);
-  } else {
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < n) st_compute(S, j, j == n - 1, xfn, ys);
   }
+  const int rem = n - m * D;  // 0 <= rem < 2D
+#pragma unroll
+  for (int jj = 0; jj < D; ++jj) {
+    if (jj < rem) st_compute(S, jj, jj == rem - 1, xs, ys);
+    if (jj + D < rem) st_issue(S, jj, tab, G);
+  }
+#pragma unroll
+  for (int jj = 0; jj < D; ++jj)
+    if (jj + D < rem) st_compute(S, jj, jj + D == rem - 1, xs, ys);
 }
 
-// Zero the partial-sum buffer of ng groups (before the task's staging barrier).
-__device__ __forceinline__ void ys_clear(float *ys, int ng, int R, int nw, int nthr) {
-  const int n = ng * nw * R;
+// Zero the partials of ng pairs (before the task's staging barrier).
+__device__ __forceinline__ void ys_clear(float *ys, int ng, int nw, int nthr) {
+  const int n = ng * nw * 2;
   for (int i = threadIdx.x; i < n; i += nthr) ys[i] = 0.f;
 }
-// Result r of group g: the wavefronts' partials added in wavefront order.
-__device__ __forceinline__ float ys_get(const float *ys, int g, int r, int R, int nw) {
+// Row r (0: A, 1: B) of pair g: the wavefronts' partials in wavefront order.
+__device__ __forceinline__ float ys_get(const float *ys, int g, int r, int nw) {
   float y = 0.f;
-  for (int w = 0; w < nw; ++w) y += ys[(g * nw + w) * R + r];
+  for (int w = 0; w < nw; ++w) y += ys[(g * nw + w) * 2 + r];
   return y;
 }
+// Row e of a task made of consecutive-row pairs.
+__device__ __forceinline__ float ys_row(const float *ys, int e, int nw) { return ys_get(ys, e >> 1, e & 1, nw); }
 
 // ---------------------------------------------------------------------------
 // per-layer addressing helpers
@@ -446,91 +530,169 @@ __device__ __forceinline__ float mid_elem(const KP &P, int l, int tok, int i) {
   return x;
 }
 
-// Field f of a layer's pointer table (the order of DevLayer): selecting a
-// matrix by index keeps the choice in scalar registers.
-enum LField { F_WQ = 1, F_WK = 2, F_WV = 3, F_EWG = 10, F_EWU = 11, F_EWD = 12, F_ESG = 13,
-              F_ESU = 14, F_ESD = 15, F_SWG = 16, F_SWU = 17, F_SWD = 18, F_SSG = 19,
-              F_SSU = 20, F_SSD = 21 };
-__device__ __forceinline__ const void *lptr(const DevLayer *L, int f) {
-  return reinterpret_cast<const void *const *>(L)[f];
-}
-
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// LDS layout of the GEMV tasks: xs[kmax] | ys[ymax * waves] | red[256]
+// LDS layout of the GEMV tasks: xs[kmax] | ys[ymax * waves] | red[256] | seg table
 struct GemvLds {
   float *xs, *ys, *red;
+  Seg *seg;
 };
 __device__ __forceinline__ GemvLds gemv_lds(const KP &P, float *lds) {
-  float *ys = lds + P.kmax;
-  return GemvLds{lds, ys, ys + P.ymax * P.nw};
+  float *ys = lds + P.kmax, *red = ys + P.ymax * P.nw;
+  return GemvLds{lds, ys, red, reinterpret_cast<Seg *>(red + 256)};
 }
 
-// Row-wise GEMV over one bf16 matrix W [rows][K] starting at row r0.
-struct RowsBf16 {
-  const uint16_t *W;
-  int K, r0;
-  __device__ __forceinline__ void operator()(int g, Stream<1, 8, false> &S) const {
-    S.rp[0] = W + (int64_t)(r0 + g) * K;
-    S.rb[0] = (uint32_t)K * 2;
-  }
-};
-
-// ---------------------------------------------------------------------------
-// tasks.  Each: prefetch the first weight units, wait for producers, stage
-// the input, stream the rows, run the epilogue with all threads.  Returns
-// false if the wait was aborted.
-
-// QKV: pairs [r0, r1) in group-major order (per KV head g: its G query
-// heads, then k head g, then v head g; d/2 RoPE pairs (j, j + d/2) each).
-__device__ __forceinline__ bool task_qkv(const KP &P, const Task &t, int pos, int tok, float *lds,
-                                         const Waiter &wait) {
-  const int l = t.layer, ng = t.r1 - t.r0;
-  const GemvLds M = gemv_lds(P, lds);
-  const int half = P.d >> 1, per_group = (P.G + 2) * half, h = P.h;
-  const DevLayer *Lp = P.layers + l;
-  const int G = P.G, dd = P.d, r0 = t.r0;
-  auto rowfn = [=](int gi, Stream<2, 8, false> &S) {
-    const int p = r0 + gi, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
-    const uint16_t *W = (const uint16_t *)lptr(Lp, hh < G ? F_WQ : (hh == G ? F_WK : F_WV));
-    const int head = hh < G ? g * G + hh : g;
-    S.rp[0] = W + ((int64_t)head * dd + j) * h;
-    S.rp[1] = W + ((int64_t)head * dd + j + half) * h;
-    S.rb[0] = S.rb[1] = (uint32_t)h * 2;
-  };
-  Stream<2, 8, false> S;
-  const int n = st_begin(S, rowfn, ng, h, P.nw);
-  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
-  if (!wait(P)) return false;
-  if (P.persistent) stage_vec(P, M.xs, M.red, layer_input(P, l, tok, (const uint16_t *)Lp->attn_norm), h, P.kmax);
-  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
-  wait.mark(0);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+// Softmax over the router logits and top-k selection (ties -> lower expert
+// id), then the n_shared shared experts with weight 1.  Every workgroup
+// that needs the choice computes it; the inputs and the order of operations
+// are the same everywhere, so all of them agree.  sel/selw in LDS.
+__device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw, float *scratch) {
+  const int tid = threadIdx.x, T = P.nthr;
+  const float *rl = P.rl + vec_off(P, l, 0, P.E);
+  for (int i = tid; i < P.E; i += T) scratch[i] = ld_sc1(rl + i);
   __syncthreads();
-  wait.mark(1);
-  const float *cosT = P.rope + (int64_t)pos * half;
-  const float *sinT = P.rope + (int64_t)P.max_ctx * half + (int64_t)pos * half;
-  for (int i = threadIdx.x; i < ng; i += P.nthr) {
-    const int p = t.r0 + i, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
-    float a = ys_get(M.ys, i, 0, 2, P.nw), b = ys_get(M.ys, i, 1, 2, P.nw);
-    if (hh <= P.G) {  // RoPE on q and k
-      const float c = cosT[j], s = sinT[j];
-      const float a2 = a * c - b * s, b2 = b * c + a * s;
-      a = a2; b = b2;
+  if (tid < 64) {
+    const int lane = tid;
+    float m = -INFINITY;
+    for (int i = lane; i < P.E; i += 64) m = fmaxf(m, scratch[i]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int i = lane; i < P.E; i += 64) s += expf(scratch[i] - m);
+    s = wave_sum(s);
+    uint32_t taken = 0;  // bit li: local index lane + 64 * li already chosen (E <= 1024)
+    for (int k = 0; k < P.top_k; ++k) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff, li = 0;
+      for (int i = lane; i < P.E; i += 64, ++li)
+        if (!((taken >> li) & 1u) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) { sel[k] = bi; selw[k] = expf(bv - m) / s; }
     }
-    if (hh < P.G) {
-      float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
-      st_sc1(qd + j, a);
-      st_sc1(qd + j + half, b);
-    } else {
-      uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
-      const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
-      const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
-      st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j) * 2, f2bf(a));
-      st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j + half) * 2, f2bf(b));
-    }
+    if (lane == 0)
+      for (int k = 0; k < P.n_shared; ++k) { sel[P.top_k + k] = k; selw[P.top_k + k] = 1.0f; }
   }
-  return true;
+  __syncthreads();
+}
+
+// Field f of a layer's pointer table (the order of DevLayer).
+enum LField { F_WQ = 1, F_WK = 2, F_WV = 3, F_EWG = 10, F_EWU = 11, F_EWD = 12, F_ESG = 13,
+              F_ESU = 14, F_ESD = 15, F_SWG = 16 };
+__device__ __forceinline__ uint64_t lptr(const DevLayer *L, int f) {
+  return (uint64_t)reinterpret_cast<const void *const *>(L)[f];
+}
+
+// One run of consecutive-row pairs: rows [r0, r0 + rows) of a matrix whose
+// rows are `stride` bytes apart.
+__device__ __forceinline__ void seg_rows(Seg *tab, uint64_t a, int r0, int rows, uint32_t stride, int xo) {
+  tab->a = a + (uint64_t)r0 * stride;
+  tab->b = tab->a + stride;
+  tab->sa = tab->sb = 0;
+  tab->j0 = r0;
+  tab->n = (rows + 1) >> 1;
+  tab->nB = rows >> 1;
+  tab->xo = xo;
+}
+__device__ __forceinline__ Geo geo_rows(int K, uint32_t elt, uint32_t stride, int rows) {
+  return Geo{K, (uint32_t)K * elt, 2 * stride, 2, 1, 0u, rows > 0 ? 1 : 0, (rows + 1) >> 1};
+}
+
+// Segments of the bf16 tasks (QKV, OPROJ, GU, DOWN, ROUTER, LM); thread 0
+// writes single-segment tables, the QKV heads are written in parallel.
+__device__ __forceinline__ Geo segs_bf16(const KP &P, const Task &t, Seg *tab) {
+  const int l = t.layer, r0 = t.r0, rows = t.r1 - t.r0, tid = threadIdx.x, h = P.h;
+  const DevLayer *Lp = P.layers + l;
+  Geo G;
+  switch (t.op) {
+    case OP_QKV: {
+      // pairs [r0, r1) in group-major order: per KV head g its G query heads,
+      // then k head g, then v head g; d/2 RoPE pairs (j, j + d/2) per head
+      const int half = P.d >> 1;
+      const int H0 = r0 / half, nseg = rows > 0 ? (t.r1 - 1) / half - H0 + 1 : 0;
+      G = Geo{h, (uint32_t)h * 2, (uint32_t)h * 2, 1, 0, 0u, nseg, rows};
+      for (int s = tid; s < nseg; s += P.nthr) {
+        const int hr = H0 + s, g = hr / (P.G + 2), hh = hr - g * (P.G + 2);
+        const int jlo = max(r0, hr * half) - hr * half, jhi = min(t.r1, (hr + 1) * half) - hr * half;
+        const uint64_t W = lptr(Lp, hh < P.G ? F_WQ : (hh == P.G ? F_WK : F_WV));
+        const int head = hh < P.G ? g * P.G + hh : g;
+        Seg &e = tab[s];
+        e.a = W + ((uint64_t)head * P.d + jlo) * h * 2;
+        e.b = e.a + (uint64_t)half * h * 2;
+        e.sa = e.sb = 0;
+        e.j0 = jlo;
+        e.n = e.nB = jhi - jlo;
+        e.xo = 0;
+      }
+      return G;
+    }
+    case OP_OPROJ: {
+      // rows [r0, r1) of Wo restricted to KV head g's G*d columns
+      const int K = P.G * P.d, ld = P.Hq * P.d, g = t.aux % P.Hkv;
+      if (tid == 0) seg_rows(tab, (uint64_t)Lp->wo + (uint64_t)g * K * 2, r0, rows, (uint32_t)ld * 2, 0);
+      return geo_rows(K, 2, (uint32_t)ld * 2, rows);
+    }
+    case OP_GU:
+      if (tid == 0) {
+        tab->a = (uint64_t)Lp->wg + (uint64_t)r0 * h * 2;
+        tab->b = (uint64_t)Lp->wu + (uint64_t)r0 * h * 2;
+        tab->sa = tab->sb = 0;
+        tab->j0 = r0;
+        tab->n = tab->nB = rows;
+        tab->xo = 0;
+      }
+      return Geo{h, (uint32_t)h * 2, (uint32_t)h * 2, 1, 0, 0u, rows > 0 ? 1 : 0, rows};
+    case OP_DOWN:
+      if (tid == 0) seg_rows(tab, (uint64_t)Lp->wd, r0, rows, (uint32_t)P.ffn * 2, 0);
+      return geo_rows(P.ffn, 2, (uint32_t)P.ffn * 2, rows);
+    case OP_ROUTER:
+      if (tid == 0) seg_rows(tab, (uint64_t)Lp->router, r0, rows, (uint32_t)h * 2, 0);
+      return geo_rows(h, 2, (uint32_t)h * 2, rows);
+    default:  // OP_LM
+      if (tid == 0) seg_rows(tab, (uint64_t)P.lm_head, r0, rows, (uint32_t)h * 2, 0);
+      return geo_rows(h, 2, (uint32_t)h * 2, rows);
+  }
+}
+
+// Segments of the routed-expert tasks (after routing: sel in LDS).
+__device__ __forceinline__ Geo segs_fp8(const KP &P, const Task &t, const int *sel, Seg *tab) {
+  const int l = t.layer, r0 = t.r0, rows = t.r1 - t.r0, tid = threadIdx.x;
+  const int f = P.effn, h = P.h, hb = (h + 127) / 128, fb = (f + 127) / 128, nk = P.top_k + P.n_shared;
+  const DevLayer *Lp = P.layers + l;
+  if (t.op == OP_EGU) {
+    // flat rows [r0, r1) over (slot k, row j of expert sel[k]): gate/up pairs
+    const int K0 = r0 / f, nseg = rows > 0 ? (t.r1 - 1) / f - K0 + 1 : 0;
+    for (int s = tid; s < nseg; s += P.nthr) {
+      const int k = K0 + s, e = sel[k], sh = k >= P.top_k ? F_SWG - F_EWG : 0;
+      const int jlo = max(r0, k * f) - k * f, jhi = min(t.r1, (k + 1) * f) - k * f;
+      Seg &g = tab[s];
+      g.a = lptr(Lp, F_EWG + sh) + ((uint64_t)e * f + jlo) * h;
+      g.b = lptr(Lp, F_EWU + sh) + ((uint64_t)e * f + jlo) * h;
+      g.sa = lptr(Lp, F_ESG + sh) + (uint64_t)e * fb * hb * 2;
+      g.sb = lptr(Lp, F_ESU + sh) + (uint64_t)e * fb * hb * 2;
+      g.j0 = jlo;
+      g.n = g.nB = jhi - jlo;
+      g.xo = 0;
+    }
+    return Geo{h, (uint32_t)h, (uint32_t)h, 1, 0, (uint32_t)hb * 2, nseg, rows};
+  }
+  // OP_EDOWN: rows [r0, r1) of every chosen expert's down matrix, slot-major;
+  // slot k reads its own part u[k] of the activation
+  for (int k = tid; k < nk; k += P.nthr) {
+    const int e = sel[k], sh = k >= P.top_k ? F_SWG - F_EWG : 0;
+    seg_rows(tab + k, lptr(Lp, F_EWD + sh) + (uint64_t)e * h * f, r0, rows, (uint32_t)f, k * f);
+    tab[k].sa = tab[k].sb = lptr(Lp, F_ESD + sh) + (uint64_t)e * hb * fb * 2;
+  }
+  return Geo{f, (uint32_t)f, 2u * f, 2, 1, (uint32_t)fb * 2, rows > 0 ? nk : 0, rows > 0 ? nk * ((rows + 1) >> 1) : 0};
+}
+
+// Best (value, lowest index) of two candidates.
+__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
 }
 
 // Combine the NC chunk partials of (sequence b, KV head g) into
@@ -602,290 +764,181 @@ __device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, flo
   }
 }
 
-// Output projection of one KV head: rows [r0, r1) of Wo restricted to the
-// head group's G*d columns, times that group's attention output (combined
-// here from its chunk partials).  Writes the split-K partial
-// pbuf[l][b][g][rows]; the residual add happens where the partials are read.
-__device__ __forceinline__ bool task_oproj(const KP &P, const Task &t, float *lds, const Waiter &wait) {
-  const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, ng = t.r1 - t.r0;
-  const int K = P.G * P.d, ld = P.Hq * P.d;
-  const GemvLds M = gemv_lds(P, lds);
-  RowsBf16 rowfn{(const uint16_t *)P.layers[l].wo + (int64_t)g * K, ld, t.r0};
-  // row g of the slice: W + row * ld; K columns
-  auto rows = [=](int gi, Stream<1, 16, false> &S) {
-    S.rp[0] = rowfn.W + (int64_t)(rowfn.r0 + gi) * ld;
-    S.rb[0] = (uint32_t)K * 2;
-  };
-  Stream<1, 16, false> S;
-  const int n = st_begin(S, rows, ng, K, P.nw);
-  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
-  if (!wait(P)) return false;
-  // combine into xs[0..K); its scratch lies behind the padded input and
-  // overlaps ys, which is cleared again once the combine is done
-  const int Kp = (K + 511) & ~511;
-  attn_combine_lds(P, l, bg, lds + Kp, P.lds_floats - Kp, M.xs);
-  __syncthreads();
-  wait.mark(0);
-  for (int i = K + threadIdx.x; i < Kp; i += P.nthr) M.xs[i] = 0.f;
-  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
-  __syncthreads();
-  st_run(S, n, rows, [=](int, int) { return (const float *)M.xs; }, M.ys);
-  __syncthreads();
-  wait.mark(1);
-  float *dst = P.pbuf + ((int64_t)(l * P.B + b) * P.Hkv + g) * P.h + t.r0;
-  for (int i = threadIdx.x; i < ng; i += P.nthr) st_sc1(dst + i, ys_get(M.ys, i, 0, 1, P.nw));
-  return true;
-}
+// ---------------------------------------------------------------------------
+// The GEMV tasks.  Each: list its segments, prefetch the first weight units,
+// wait for producers, stage the input (RMSNorm folded in where the input is
+// a residual stream; the attention combine for the O projection), stream,
+// then the task's epilogue with all threads.  Returns false if the wait was
+// aborted.  FP8 selects the routed-expert tasks (EGU, EDOWN), whose rows
+// depend on the routing and so are listed after the wait.
+//
+//   QKV    RoPE pairs of q/k/v rows; epilogue: RoPE, q to the workspace,
+//          k/v appended to the bf16 cache
+//   OPROJ  one KV head's slice of Wo times that head group's attention
+//          output; epilogue: the split-K partial pbuf[l][b][g]
+//   GU     gate/up pairs; epilogue: SwiGLU u = silu(g) * up
+//   DOWN   Wd rows; epilogue: residual x_out = x_mid + Wd u
+//   ROUTER router rows; epilogue: router logits
+//   EGU    expert gate/up pairs over (slot, row); epilogue: SwiGLU
+//   EDOWN  expert down rows, slot-major; epilogue: x_mid + sum_k w_k Wd_k u_k
+//   LM     LM-head rows; epilogue: logits (check mode) and the task's
+//          (max, lowest index) partial, NaN if any logit is NaN
 
-// Dense gate/up row pairs [r0, r1): u_j = silu(Wg_j b) * (Wu_j b).
-__device__ __forceinline__ bool task_gu(const KP &P, const Task &t, int tok, float *lds, const Waiter &wait) {
-  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
-  const DevLayer &Lw = P.layers[l];
+template <bool FP8>
+__device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, int step, int pos, int tok,
+                                          float *lds, const Waiter &wait) {
+  const int l = t.layer, rows = t.r1 - t.r0, tid = threadIdx.x, nw = P.nw, op = t.op;
   const GemvLds M = gemv_lds(P, lds);
-  const uint16_t *wg = (const uint16_t *)Lw.wg, *wu = (const uint16_t *)Lw.wu;
-  const int r0 = t.r0;
-  auto rowfn = [=](int gi, Stream<2, 4, false> &S) {
-    S.rp[0] = wg + (int64_t)(r0 + gi) * h;
-    S.rp[1] = wu + (int64_t)(r0 + gi) * h;
-    S.rb[0] = S.rb[1] = (uint32_t)h * 2;
-  };
-  Stream<2, 4, false> S;
-  const int n = st_begin(S, rowfn, ng, h, P.nw);
-  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
-  if (!wait(P)) return false;
-  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
-  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
-  wait.mark(0);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  int *sel = reinterpret_cast<int *>(M.red + 64);
+  float *selw = M.red + 96;
+  Geo G;
+  if (FP8) {
+    if (!wait(P)) return false;
+    route(P, l, sel, selw, M.xs);
+    G = segs_fp8(P, t, sel, M.seg);
+  } else {
+    G = segs_bf16(P, t, M.seg);
+  }
+  G = geo_uniform(G);
   __syncthreads();
-  wait.mark(1);
-  float *u = P.u + vec_off(P, l, 0, P.F);
-  for (int i = threadIdx.x; i < ng; i += P.nthr)
-    st_sc1(u + t.r0 + i, silu(ys_get(M.ys, i, 0, 2, P.nw)) * ys_get(M.ys, i, 1, 2, P.nw));
-  return true;
-}
-
-// Dense down rows [r0, r1) + residual: x_out = x_mid + Wd u.
-__device__ __forceinline__ bool task_down(const KP &P, const Task &t, int step, int tok, float *lds,
-                                          const Waiter &wait) {
-  const int l = t.layer, ng = t.r1 - t.r0;
-  const GemvLds M = gemv_lds(P, lds);
-  RowsBf16 rowfn{(const uint16_t *)P.layers[l].wd, P.ffn, t.r0};
-  Stream<1, 8, false> S;
-  const int n = st_begin(S, rowfn, ng, P.ffn, P.nw);
-  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
+  PStream<FP8> S;
+  const int n = st_begin(S, M.seg, G, nw);
+  ys_clear(M.ys, G.NG, nw, P.nthr);
   // the post-attention residual was final before the gate/up stage this
   // workgroup passed: fetch it now
-  const int tid = threadIdx.x;
-  const float res0 = tid < ng ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
-  if (!wait(P)) return false;
-  stage_vec(P, M.xs, M.red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr, 0, 0, nullptr}, P.ffn, P.kmax);
-  wait.mark(0);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
-  __syncthreads();
-  wait.mark(1);
-  float *xo = P.x_out + vec_off(P, l, 0, P.h);
-  float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h : nullptr;
-  for (int i = tid; i < ng; i += P.nthr) {
-    const int row = t.r0 + i;
-    const float v = (i == tid ? res0 : mid_elem(P, l, tok, row)) + ys_get(M.ys, i, 0, 1, P.nw);
-    st_sc1(xo + row, v);
-    if (hid) hid[row] = v;
-  }
-  return true;
-}
-
-// Router rows [r0, r1): rl = Wr b (MoE).
-__device__ __forceinline__ bool task_router(const KP &P, const Task &t, int tok, float *lds,
-                                            const Waiter &wait) {
-  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
-  const DevLayer &Lw = P.layers[l];
-  const GemvLds M = gemv_lds(P, lds);
-  RowsBf16 rowfn{(const uint16_t *)Lw.router, h, t.r0};
-  Stream<1, 8, false> S;
-  const int n = st_begin(S, rowfn, ng, h, P.nw);
-  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
-  if (!wait(P)) return false;
-  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
-  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
-  __syncthreads();
-  float *rl = P.rl + vec_off(P, l, 0, P.E);
-  for (int i = threadIdx.x; i < ng; i += P.nthr) st_sc1(rl + t.r0 + i, ys_get(M.ys, i, 0, 1, P.nw));
-  return true;
-}
-
-// Softmax over the router logits and top-k selection (ties -> lower expert
-// id), then the n_shared shared experts with weight 1.  Every workgroup
-// that needs the choice computes it; the inputs and the order of operations
-// are the same everywhere, so all of them agree.  sel/selw in LDS.
-__device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw, float *scratch) {
-  const int tid = threadIdx.x, T = P.nthr;
-  const float *rl = P.rl + vec_off(P, l, 0, P.E);
-  for (int i = tid; i < P.E; i += T) scratch[i] = ld_sc1(rl + i);
-  __syncthreads();
-  if (tid < 64) {
-    const int lane = tid;
-    float m = -INFINITY;
-    for (int i = lane; i < P.E; i += 64) m = fmaxf(m, scratch[i]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int i = lane; i < P.E; i += 64) s += expf(scratch[i] - m);
-    s = wave_sum(s);
-    uint32_t taken = 0;  // bit li: local index lane + 64 * li already chosen (E <= 1024)
-    for (int k = 0; k < P.top_k; ++k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff, li = 0;
-      for (int i = lane; i < P.E; i += 64, ++li)
-        if (!((taken >> li) & 1u) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { sel[k] = bi; selw[k] = expf(bv - m) / s; }
+  const bool down = op == OP_DOWN || op == OP_EDOWN;
+  const float res0 = down && tid < rows ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
+  if (!FP8 && !wait(P)) return false;
+  if (op == OP_OPROJ) {
+    // combine into xs[0..K); its scratch lies behind the padded input, up to
+    // the segment table, and overlaps ys, which is cleared again afterwards
+    const int Kp = (G.K + 511) & ~511;
+    attn_combine_lds(P, l, t.aux, lds + Kp, (int)(reinterpret_cast<float *>(M.seg) - lds) - Kp, M.xs);
+    __syncthreads();
+    for (int i = G.K + tid; i < Kp; i += P.nthr) M.xs[i] = 0.f;
+    ys_clear(M.ys, G.NG, nw, P.nthr);
+    __syncthreads();
+  } else {
+    Src src{P.a_norm, nullptr, nullptr, 0, 0, nullptr};  // the baseline's normalised input
+    int K = P.h;
+    if (down) {
+      src.f32 = P.u + vec_off(P, l, 0, P.F);
+      K = P.F;
+    } else if (P.persistent) {
+      const DevLayer &Lw = P.layers[l];
+      if (op == OP_QKV) src = layer_input(P, l, tok, (const uint16_t *)Lw.attn_norm);
+      else if (op == OP_LM) src = Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm};
+      else src = mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm);
     }
-    if (lane == 0)
-      for (int k = 0; k < P.n_shared; ++k) { sel[P.top_k + k] = k; selw[P.top_k + k] = 1.0f; }
+    stage_vec(P, M.xs, M.red, src, K, P.kmax);
   }
-  __syncthreads();
-}
-
-// Expert gate/up pairs [r0, r1) over (slot k, row j): u[k][j].  The rows
-// depend on the routing, so the stream starts after it.
-__device__ __forceinline__ bool task_egu(const KP &P, const Task &t, int tok, float *lds, const Waiter &wait) {
-  const int l = t.layer, h = P.h, ng = t.r1 - t.r0;
-  const DevLayer &Lw = P.layers[l];
-  const GemvLds M = gemv_lds(P, lds);
-  int *sel = reinterpret_cast<int *>(M.red + 64);
-  float *selw = M.red + 96;
-  if (!wait(P)) return false;
-  route(P, l, sel, selw, M.xs);
-  const int f = P.effn, hb = (h + 127) / 128, fb = (f + 127) / 128;
-  const int top_k = P.top_k, r0 = t.r0;
-  const DevLayer *Lp = P.layers + l;
-  auto rowfn = [=](int gi, Stream<2, 4, true> &S) {
-    const int p = r0 + gi, k = p / f, j = p % f, e = sel[k];
-    const int sh = k >= top_k ? F_SWG - F_EWG : 0;
-    const uint8_t *wg = (const uint8_t *)lptr(Lp, F_EWG + sh);
-    const uint8_t *wu = (const uint8_t *)lptr(Lp, F_EWU + sh);
-    const uint16_t *sg = (const uint16_t *)lptr(Lp, F_ESG + sh);
-    const uint16_t *su = (const uint16_t *)lptr(Lp, F_ESU + sh);
-    const int64_t wofs = ((int64_t)e * f + j) * h, sofs = ((int64_t)e * fb + j / 128) * hb;
-    S.rp[0] = wg + wofs; S.rp[1] = wu + wofs;
-    S.rb[0] = S.rb[1] = (uint32_t)h;
-    S.sp[0] = sg + sofs; S.sp[1] = su + sofs;
-    S.sb[0] = S.sb[1] = (uint32_t)hb * 2;
-  };
-  Stream<2, 4, true> S;
-  const int n = st_begin(S, rowfn, ng, h, P.nw);
-  ys_clear(M.ys, ng, 2, P.nw, P.nthr);
-  if (P.persistent) stage_vec(P, M.xs, M.red, mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm), h, P.kmax);
-  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, h, P.kmax);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
-  __syncthreads();
-  float *u = P.u + vec_off(P, l, 0, P.F);
-  for (int i = threadIdx.x; i < ng; i += P.nthr)
-    st_sc1(u + t.r0 + i, silu(ys_get(M.ys, i, 0, 2, P.nw)) * ys_get(M.ys, i, 1, 2, P.nw));
-  return true;
-}
-
-// Expert down rows [r0, r1): x_out = x_mid + sum_k w_k Wd_{e_k} u_k.  The
-// stream runs over (row, slot) pairs; the epilogue sums the slots of a row
-// in slot order.
-__device__ __forceinline__ bool task_edown(const KP &P, const Task &t, int step, int tok, float *lds,
-                                           const Waiter &wait) {
-  const int l = t.layer, rows = t.r1 - t.r0;
-  const GemvLds M = gemv_lds(P, lds);
-  int *sel = reinterpret_cast<int *>(M.red + 64);
-  float *selw = M.red + 96;
-  const int tid = threadIdx.x;
-  const float res0 = tid < rows ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
-  if (!wait(P)) return false;
-  route(P, l, sel, selw, M.xs);
-  const int f = P.effn, hb = (P.h + 127) / 128, fb = (f + 127) / 128;
-  const int nk = P.top_k + P.n_shared;
-  const int top_k = P.top_k, hh = P.h, r0 = t.r0;
-  const DevLayer *Lp = P.layers + l;
-  auto rowfn = [=](int q, Stream<1, 8, true> &S) {
-    const int i = r0 + q / nk, k = q % nk, e = sel[k];
-    const int sh = k >= top_k ? F_SWG - F_EWG : 0;
-    S.rp[0] = (const uint8_t *)lptr(Lp, F_EWD + sh) + ((int64_t)e * hh + i) * f;
-    S.rb[0] = (uint32_t)f;
-    S.sp[0] = (const uint16_t *)lptr(Lp, F_ESD + sh) + ((int64_t)e * hb + i / 128) * fb;
-    S.sb[0] = (uint32_t)fb * 2;
-  };
-  Stream<1, 8, true> S;
-  const int n = st_begin(S, rowfn, rows * nk, f, P.nw);
-  ys_clear(M.ys, rows * nk, 1, P.nw, P.nthr);
-  stage_vec(P, M.xs, M.red, Src{P.u + vec_off(P, l, 0, P.F), nullptr, nullptr, 0, 0, nullptr}, P.F, P.kmax);
-  st_run(S, n, rowfn, [=](int q, int) { return (const float *)(M.xs + (q % nk) * f); }, M.ys);
-  __syncthreads();
-  float *xo = P.x_out + vec_off(P, l, 0, P.h);
-  float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h : nullptr;
-  for (int i = tid; i < rows; i += P.nthr) {
-    float acc = 0.f;
-    for (int k = 0; k < nk; ++k) acc = fmaf(selw[k], ys_get(M.ys, i * nk + k, 0, 1, P.nw), acc);
-    const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + acc;
-    st_sc1(xo + t.r0 + i, v);
-    if (hid) hid[t.r0 + i] = v;
-  }
-  return true;
-}
-
-// Best (value, lowest index) of two candidates.
-__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-}
-
-// LM head rows [r0, r1): logits (check mode) and this task's (max, lowest
-// index) partial.  A NaN logit makes the partial NaN.
-__device__ __forceinline__ bool task_lm(const KP &P, const Task &t, int lam, int step, float *lds,
-                                        const Waiter &wait) {
-  const GemvLds M = gemv_lds(P, lds);
-  const int wave = wave_id(), nw = P.nw, lane = threadIdx.x & 63, ng = t.r1 - t.r0;
-  RowsBf16 rowfn{P.lm_head, P.h, t.r0};
-  Stream<1, 8, false> S;
-  const int n = st_begin(S, rowfn, ng, P.h, P.nw);
-  ys_clear(M.ys, ng, 1, P.nw, P.nthr);
-  if (!wait(P)) return false;
-  if (P.persistent)
-    stage_vec(P, M.xs, M.red, Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm},
-              P.h, P.kmax);
-  else stage_vec(P, M.xs, M.red, Src{P.a_norm, nullptr, nullptr, 0, 0, nullptr}, P.h, P.kmax);
   wait.mark(0);
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)M.xs; }, M.ys);
+  st_run(S, n, M.seg, G, M.xs, M.ys);
   __syncthreads();
   wait.mark(1);
-  float *lg = P.chk_logits ? P.chk_logits + (int64_t)step * P.B * P.V : nullptr;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  bool nan = false;
-  for (int i = threadIdx.x; i < ng; i += P.nthr) {
-    const float y = ys_get(M.ys, i, 0, 1, P.nw);
-    if (y != y) nan = true;
-    else argmax_merge(bv, bi, y, t.r0 + i);
-    if (lg) lg[t.r0 + i] = y;
+  const float *ys = M.ys;
+  if (FP8) {
+    if (op == OP_EGU) {
+      float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
+      for (int i = tid; i < rows; i += P.nthr) st_sc1(u + i, silu(ys_get(ys, i, 0, nw)) * ys_get(ys, i, 1, nw));
+    } else {
+      const int nk = P.top_k + P.n_shared, np = (rows + 1) >> 1;
+      float *xo = P.x_out + vec_off(P, l, 0, P.h) + t.r0;
+      float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h + t.r0 : nullptr;
+      for (int i = tid; i < rows; i += P.nthr) {
+        float acc = 0.f;
+        for (int k = 0; k < nk; ++k) acc = fmaf(selw[k], ys_get(ys, k * np + (i >> 1), i & 1, nw), acc);
+        const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + acc;
+        st_sc1(xo + i, v);
+        if (hid) hid[i] = v;
+      }
+    }
+    return true;
   }
+  switch (op) {
+    case OP_QKV: {
+      const int half = P.d >> 1, per_group = (P.G + 2) * half;
+      const float *cosT = P.rope + (int64_t)pos * half;
+      const float *sinT = P.rope + (int64_t)P.max_ctx * half + (int64_t)pos * half;
+      for (int i = tid; i < rows; i += P.nthr) {
+        const int p = t.r0 + i, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
+        float a = ys_get(ys, i, 0, nw), b = ys_get(ys, i, 1, nw);
+        if (hh <= P.G) {  // RoPE on q and k
+          const float c = cosT[j], s = sinT[j];
+          const float a2 = a * c - b * s, b2 = b * c + a * s;
+          a = a2; b = b2;
+        }
+        if (hh < P.G) {
+          float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
+          st_sc1(qd + j, a);
+          st_sc1(qd + j + half, b);
+        } else {
+          uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
+          const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
+          const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
+          st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j) * 2, f2bf(a));
+          st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j + half) * 2, f2bf(b));
+        }
+      }
+      return true;
+    }
+    case OP_OPROJ: {
+      const int b = t.aux / P.Hkv, g = t.aux % P.Hkv;
+      float *dst = P.pbuf + ((int64_t)(l * P.B + b) * P.Hkv + g) * P.h + t.r0;
+      for (int i = tid; i < rows; i += P.nthr) st_sc1(dst + i, ys_row(ys, i, nw));
+      return true;
+    }
+    case OP_GU: {
+      float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
+      for (int i = tid; i < rows; i += P.nthr) st_sc1(u + i, silu(ys_get(ys, i, 0, nw)) * ys_get(ys, i, 1, nw));
+      return true;
+    }
+    case OP_DOWN: {
+      float *xo = P.x_out + vec_off(P, l, 0, P.h) + t.r0;
+      float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h + t.r0 : nullptr;
+      for (int i = tid; i < rows; i += P.nthr) {
+        const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + ys_row(ys, i, nw);
+        st_sc1(xo + i, v);
+        if (hid) hid[i] = v;
+      }
+      return true;
+    }
+    case OP_ROUTER: {
+      float *rl = P.rl + vec_off(P, l, 0, P.E) + t.r0;
+      for (int i = tid; i < rows; i += P.nthr) st_sc1(rl + i, ys_row(ys, i, nw));
+      return true;
+    }
+    default: {  // OP_LM
+      float *lg = P.chk_logits ? P.chk_logits + (int64_t)step * P.B * P.V + t.r0 : nullptr;
+      const int wave = wave_id(), lane = tid & 63;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      bool nan = false;
+      for (int i = tid; i < rows; i += P.nthr) {
+        const float y = ys_row(ys, i, nw);
+        if (y != y) nan = true;
+        else argmax_merge(bv, bi, y, t.r0 + i);
+        if (lg) lg[i] = y;
+      }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
-  const bool wnan = __any(nan);
-  float *wv = M.red + 128;
-  int *wi = reinterpret_cast<int *>(M.red + 160);
-  int *wn = reinterpret_cast<int *>(M.red + 192);
-  if (lane == 0) { wv[wave] = bv; wi[wave] = bi; wn[wave] = wnan; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = -INFINITY;
-    int ix = 0x7fffffff, anynan = 0;
-    for (int w = 0; w < nw; ++w) { anynan |= wn[w]; argmax_merge(v, ix, wv[w], wi[w]); }
-    if (anynan) v = __builtin_nanf("");
-    st_sc1(P.lmp + 2 * lam, v);
-    st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * lam + 1, (uint32_t)ix);
+      for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+      const bool wnan = __any(nan);
+      float *wv = M.red + 128;
+      int *wi = reinterpret_cast<int *>(M.red + 160);
+      int *wn = reinterpret_cast<int *>(M.red + 192);
+      if (lane == 0) { wv[wave] = bv; wi[wave] = bi; wn[wave] = wnan; }
+      __syncthreads();
+      if (tid == 0) {
+        float v = -INFINITY;
+        int ix = 0x7fffffff, anynan = 0;
+        for (int w = 0; w < nw; ++w) { anynan |= wn[w]; argmax_merge(v, ix, wv[w], wi[w]); }
+        if (anynan) v = __builtin_nanf("");
+        st_sc1(P.lmp + 2 * lam, v);
+        st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * lam + 1, (uint32_t)ix);
+      }
+      return true;
+    }
   }
-  return true;
 }
 
 // Global greedy token from the W partials (all threads get it); -1 on NaN.
@@ -1082,51 +1135,72 @@ __device__ __forceinline__ bool token_ok(const KP &P, int tok, int step) {
   return false;
 }
 
+// The kernel arguments, re-read from the argument segment by the caller.
+// The compiler treats argument loads as invariant and would hoist every
+// field a task ever reads to the start of the kernel, where they do not fit
+// in scalar registers and get spilled; reading them through a pointer it
+// cannot look through confines each field to the task that uses it.
+__device__ __forceinline__ const KP &kp_fresh() {
+  const __attribute__((address_space(4))) KP *p =
+      (const __attribute__((address_space(4))) KP *)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const KP *)p;
+}
+
 // Run one task of the table (both paths).
-__device__ __forceinline__ bool run_task(const KP &P, const Task &t, int lam, int step, int pos, int tok,
-                                         float *lds, const Waiter &wait) {
+__device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int pos, int tok, float *lds,
+                                         const Waiter &wait) {
+  const KP &P = kp_fresh();
   switch (t.op) {
-    case OP_QKV: return task_qkv(P, t, pos, tok, lds, wait);
+    case OP_NONE: return true;
     case OP_ATTN: return attn_chunk(P, t, pos, lds, wait);
-    case OP_OPROJ: return task_oproj(P, t, lds, wait);
-    case OP_GU: return task_gu(P, t, tok, lds, wait);
-    case OP_DOWN: return task_down(P, t, step, tok, lds, wait);
-    case OP_ROUTER: return task_router(P, t, tok, lds, wait);
-    case OP_EGU: return task_egu(P, t, tok, lds, wait);
-    case OP_EDOWN: return task_edown(P, t, step, tok, lds, wait);
-    case OP_LM: return task_lm(P, t, lam, step, lds, wait);
-    default: return true;
+    case OP_EGU:
+    case OP_EDOWN: return task_gemv<true>(P, t, lam, step, pos, tok, lds, wait);
+    default: return task_gemv<false>(P, t, lam, step, pos, tok, lds, wait);
   }
 }
 
 // ---------------------------------------------------------------------------
 // the resident kernel
 
+// The resident kernel.  With P.persistent = 0 it is the per-operator
+// baseline's task kernel instead: every workgroup runs its task of stage
+// P.b_si for step P.b_step once, without waits or flags (stream order is the
+// only synchronisation).  Both modes go through the one call of run_task, so
+// the task code exists once in the binary.
 extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
-  const int lam = lambda_of_block(blockIdx.x, P.W, P.X);
-  if (threadIdx.x == 0) {
+  const bool res = P.persistent != 0;
+  const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
+  if (res && threadIdx.x == 0) {
     const uint32_t x = xcc_id();
     P.xcc[lam] = x;
     if (P.W % P.X == 0 && (int)x != (int)(blockIdx.x % P.X))
       __hip_atomic_fetch_add(&P.status->xcc_mismatch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  int tok = P.forced ? P.forced[0] : P.in_tok[0];
-  for (int s = 0; s < P.n_steps; ++s) {
+  const int s_end = res ? P.n_steps : P.b_step + 1;
+  const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
+  int tok = res ? (P.forced ? P.forced[0] : P.in_tok[0]) : P.tok_slot[1];
+  for (int s = res ? 0 : P.b_step; s < s_end; ++s) {
     const uint32_t ep = P.epoch_base + (uint32_t)s + 1u;
     const int pos = P.pos0 + s;
-    if (P.forced) tok = P.forced[(int64_t)s * P.B];
-    if (!token_ok(P, tok, s)) return;
-    for (int si = 0; si < P.n_si; ++si) {
+    if (res) {
+      if (P.forced) tok = P.forced[(int64_t)s * P.B];
+      if (!token_ok(P, tok, s)) return;
+    }
+    for (int si = si0; si < si1; ++si) {
       const Task t = P.tasks[(int64_t)si * P.W + lam];
       if (t.op == OP_NONE) continue;
       const uint32_t tw = (uint32_t)now_ticks();
-      const Waiter wait{1, t.wait_lo, t.wait_hi, s, si, ep, sh};
-      if (!run_task(P, t, lam, s, pos, tok, lds, wait)) return;
-      signal_slot(P, t.signal, ep);
-      trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
+      const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh};
+      if (!run_task(t, lam, s, pos, tok, lds, wait)) return;
+      if (res) {
+        signal_slot(P, t.signal, ep);
+        trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
+      }
     }
+    if (!res) return;
     // greedy token of step s: every workgroup when it feeds the next step,
     // workgroup 0 always (it writes the output)
     const bool need = (!P.forced && s + 1 < P.n_steps) || lam == 0;
@@ -1168,15 +1242,6 @@ extern "C" __global__ void __launch_bounds__(512) pre_k_norm(KP P, int l, int mi
   for (int i = threadIdx.x; i < P.kmax; i += P.nthr) P.a_norm[i] = xs[i];
 }
 
-extern "C" __global__ void __launch_bounds__(512) pre_k_task(KP P, int si, int step) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  __shared__ int sh[8];
-  const int lam = blockIdx.x;
-  const Task t = P.tasks[(int64_t)si * P.W + lam];
-  const Waiter none{0, 0, 0, 0, 0, 0u, sh};
-  run_task(P, t, lam, step, P.pos0 + step, P.tok_slot[1], lds, none);
-}
-
 extern "C" __global__ void __launch_bounds__(512) pre_k_argmax(KP P, int step) {
   __shared__ int sh[8];
   const int nt = reduce_lm(P, sh);
@@ -1212,7 +1277,8 @@ extern "C" __global__ void pre_k_fp8_decode(const uint8_t *in, float *out, int n
 }
 
 // Debug / tuning: the streamed GEMV alone, y = W x over rows split evenly
-// across the grid, for a given ring depth and weight cache policy.
+// across the grid (consecutive-row pairs), for a given ring depth and weight
+// cache policy.
 template <int D, int CP>
 __global__ void __launch_bounds__(1024) pre_k_gemv_bench(const uint16_t *W, int rows, int K, const float *x,
                                                          float *y) {
@@ -1220,24 +1286,20 @@ __global__ void __launch_bounds__(1024) pre_k_gemv_bench(const uint16_t *W, int 
   const int nthr = __builtin_amdgcn_readfirstlane(blockDim.x), nw = nthr >> 6;
   const int Kp = (K + 511) / 512 * 512;
   for (int i = threadIdx.x; i < Kp; i += nthr) lds[i] = i < K ? x[i] : 0.f;
-  float *ys = lds + Kp;
   const int r0 = (int)((int64_t)rows * blockIdx.x / gridDim.x);
   const int r1 = (int)((int64_t)rows * (blockIdx.x + 1) / gridDim.x);
-  struct Rows {
-    const uint16_t *W;
-    int K, r0;
-    __device__ void operator()(int g, Stream<1, D, false, CP> &S) const {
-      S.rp[0] = W + (int64_t)(r0 + g) * K;
-      S.rb[0] = (uint32_t)K * 2;
-    }
-  } rowfn{W, K, r0};
-  Stream<1, D, false, CP> S;
-  const int n = st_begin(S, rowfn, r1 - r0, K, nw);
-  ys_clear(ys, r1 - r0, 1, nw, nthr);
+  Seg *tab = reinterpret_cast<Seg *>(lds + Kp);
+  float *ys = lds + Kp + 64;
+  if (threadIdx.x == 0) seg_rows(tab, (uint64_t)W, r0, r1 - r0, (uint32_t)K * 2, 0);
+  const Geo G = geo_uniform(geo_rows(K, 2, (uint32_t)K * 2, r1 - r0));
   __syncthreads();
-  st_run(S, n, rowfn, [=](int, int) { return (const float *)lds; }, ys);
+  PStream<false, D, CP> S;
+  const int n = st_begin(S, tab, G, nw);
+  ys_clear(ys, G.NG, nw, nthr);
   __syncthreads();
-  for (int i = threadIdx.x; i < r1 - r0; i += nthr) y[r0 + i] = ys_get(ys, i, 0, 1, nw);
+  st_run(S, n, tab, G, lds, ys);
+  __syncthreads();
+  for (int i = threadIdx.x; i < r1 - r0; i += nthr) y[r0 + i] = ys_row(ys, i, nw);
 }
 
 }  // namespace pre
@@ -1338,8 +1400,6 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
   if (hipFuncSetAttribute((const void *)pre_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
-          hipSuccess ||
-      hipFuncSetAttribute((const void *)pre_k_task, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
@@ -1504,19 +1564,23 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
   const dim3 blk(D.threads);
   const unsigned lds = (unsigned)e->lds_dyn;
   const std::vector<pre_layer_w> &lw = e->lw;
+  // one stage of one step per launch of the task kernel
+  auto stage = [&](int si, int s) {
+    P.b_si = si;
+    P.b_step = s;
+    hipLaunchKernelGGL(pre_persistent, dim3(D.W), blk, lds, st, P);
+  };
   for (int s = 0; s < n_steps; ++s) {
     hipLaunchKernelGGL(pre_k_embed, dim3(1), blk, 0, st, P, s);
     for (int l = 0; l < D.L; ++l) {
       const int si0 = l * D.stages_per_layer;
       hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, l, 0, (const uint16_t *)lw[l].attn_norm);
-      for (int k = 0; k < 3; ++k)  // QKV, attention chunks, O projection
-        hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + k, s);
+      for (int k = 0; k < 3; ++k) stage(si0 + k, s);  // QKV, attention chunks, O projection
       hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, l, 1, (const uint16_t *)lw[l].ffn_norm);
-      for (int k = 3; k < D.stages_per_layer; ++k)
-        hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, si0 + k, s);
+      for (int k = 3; k < D.stages_per_layer; ++k) stage(si0 + k, s);
     }
     hipLaunchKernelGGL(pre_k_norm, dim3(D.B), blk, lds, st, P, D.L - 1, 2, (const uint16_t *)e->final_norm);
-    hipLaunchKernelGGL(pre_k_task, dim3(D.W), blk, lds, st, P, D.n_si - 1, s);
+    stage(D.n_si - 1, s);
     hipLaunchKernelGGL(pre_k_argmax, dim3(1), dim3(64), 0, st, P, s);
   }
   if (hipGetLastError() != hipSuccess) return PRE_ERR_HIP;
@@ -1603,7 +1667,7 @@ extern "C" int pre_debug_fp8_decode(const void *d_codes, float *d_out, int n, vo
 }
 
 // Debug / tuning entry: time the streamed GEMV variants.  variant = 2 * i + c
-// with ring depth {8, 16, 24, 32}[i] and weight cache policy {default,
+// with ring depth {2, 4, 8, 12}[i] row pairs and weight cache policy {default,
 // streaming}[c]; rows are split over `grid` workgroups of `threads` threads,
 // each given at least lds_min bytes of LDS (96 KB keeps one per CU).
 extern "C" int pre_debug_gemv(int variant, const void *d_w, int rows, int K, const float *d_x, float *d_y,
@@ -1611,12 +1675,13 @@ extern "C" int pre_debug_gemv(int variant, const void *d_w, int rows, int K, con
   if (!d_w || !d_x || !d_y || rows < 1 || K < 8 || K % 8 || grid < 1 || threads < 64 || threads > 1024)
     return PRE_ERR_ARG;
   const int Kp = (K + 511) / 512 * 512;
-  const size_t lds = std::max<size_t>((size_t)(Kp + (rows + grid - 1) / grid + 64) * 4, (size_t)lds_min);
+  const size_t lds = std::max<size_t>((size_t)(Kp + 64 + ((rows + grid - 1) / grid + 1) * (threads / 64)) * 4,
+                                      (size_t)lds_min);
   if (lds > 160 * 1024) return PRE_ERR_SHAPE;
-  const void *fns[8] = {(const void *)pre_k_gemv_bench<8, CP_DEF>, (const void *)pre_k_gemv_bench<8, CP_NT>,
-                        (const void *)pre_k_gemv_bench<16, CP_DEF>, (const void *)pre_k_gemv_bench<16, CP_NT>,
-                        (const void *)pre_k_gemv_bench<24, CP_DEF>, (const void *)pre_k_gemv_bench<24, CP_NT>,
-                        (const void *)pre_k_gemv_bench<32, CP_DEF>, (const void *)pre_k_gemv_bench<32, CP_NT>};
+  const void *fns[8] = {(const void *)pre_k_gemv_bench<2, CP_DEF>, (const void *)pre_k_gemv_bench<2, CP_NT>,
+                        (const void *)pre_k_gemv_bench<4, CP_DEF>, (const void *)pre_k_gemv_bench<4, CP_NT>,
+                        (const void *)pre_k_gemv_bench<8, CP_DEF>, (const void *)pre_k_gemv_bench<8, CP_NT>,
+                        (const void *)pre_k_gemv_bench<12, CP_DEF>, (const void *)pre_k_gemv_bench<12, CP_NT>};
   if (variant < 0 || variant >= 8) return PRE_ERR_ARG;
   if (hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return PRE_ERR_HIP;

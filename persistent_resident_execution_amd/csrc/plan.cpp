@@ -62,19 +62,27 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
   D->stages_per_layer = moe ? 6 : 5;
   D->n_si = D->L * D->stages_per_layer + 1;
-  D->kmax = pad_to(std::max({D->h, D->Hq * D->d, D->F, moe ? D->E : 0}), 1024);
+  // longest staged GEMV input; the fp8 expert-down chunks of the last slot
+  // read up to (slots - 1) * effn + effn rounded up to whole 1024-column chunks
+  const int nk = D->top_k + D->n_shared;
+  D->kmax = pad_to(std::max({D->h, D->Hq * D->d, D->F, moe ? D->E : 0,
+                             moe ? (nk - 1) * D->effn + pad_to(D->effn, 1024) : 0}), 1024);
   D->cmax = cdiv(D->max_ctx, D->NC);
   const int waves = D->threads / 64;
   {
-    const int W = D->W, nk = D->top_k + D->n_shared;
-    int y = std::max({2 * cdiv(D->qkv_pairs, W), cdiv(D->h, W), cdiv(D->V, W), cdiv(D->h, D->Tg)});
-    if (moe) y = std::max({y, cdiv(D->E, W), 2 * cdiv(D->F, W), cdiv(D->h, W) * nk});
+    // results (2 per row pair) of the largest task of any GEMV stage
+    const int W = D->W;
+    auto rows2 = [](int r) { return r + (r & 1); };  // consecutive-row pairs
+    int y = std::max({2 * cdiv(D->qkv_pairs, W), rows2(cdiv(D->h, W)), rows2(cdiv(D->V, W)),
+                      rows2(cdiv(D->h, D->Tg))});
+    if (moe) y = std::max({y, rows2(cdiv(D->E, W)), 2 * cdiv(D->F, W), rows2(cdiv(D->h, W)) * nk});
     else y = std::max(y, 2 * cdiv(D->ffn, W));
     D->ymax = pad_to(y, 64);
   }
-  // GEMV phase: staged input, per-row results, reduction scratch.  Attention
-  // phase: q, scores, per-wave output partials, softmax stats.
-  int64_t gemv = (int64_t)D->kmax + (int64_t)D->ymax * waves + 256;
+  // GEMV phase: staged input, per-row results, reduction scratch, segment
+  // table (80 entries of 12 words).  Attention phase: q, scores, per-wave
+  // output partials, softmax stats.
+  int64_t gemv = (int64_t)D->kmax + (int64_t)D->ymax * waves + 256 + 80 * 12;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
   D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);

@@ -237,3 +237,25 @@ def test_layer0_intermediates_match_oracle_primitives(oracle_lib, persistent):
         _say(f"  {name}: rel err {rel:.1e}")
         assert rel < 1e-5, name
     eng.close()
+
+
+@pytest.fixture(scope="module")
+def small_moe(oracle_lib):
+    _say("[setup] small MoE (fp8 experts, odd scale-block count) + oracle run (prompt 24, 16 steps)")
+    S = parity.DenseSetup(oracle_lib, synth.SMALL_MOE, seed=5)
+    prompt = synth.gen_tokens(synth.SMALL_MOE.vocab, 24, seed=5).numpy()
+    ref = parity.oracle_run(S.om, prompt, 16)
+    return S, prompt, ref
+
+
+@pytest.mark.parametrize("grid,threads", [(0, 0), (37, 256)])
+def test_small_moe_persistent(small_moe, grid, threads):
+    S, prompt, ref = small_moe
+    _say(f"[test] small MoE persistent grid={grid} threads={threads}")
+    _check_run(S, prompt, ref, baseline=False, grid_wgs=grid, wg_threads=threads)
+
+
+def test_small_moe_baseline(small_moe):
+    S, prompt, ref = small_moe
+    _say("[test] small MoE baseline")
+    _check_run(S, prompt, ref, baseline=True)

@@ -46,6 +46,31 @@ def test_strerror_and_argument_errors(lib):
     assert lib.pre_engine_status(None, C.byref(st)) == -1
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _gemv_lds_bytes(m, W, threads=512):
+    """LDS of the GEMV tasks: the staged input (padded to 1024 columns), two
+    results per row pair per wavefront for the largest task of any stage,
+    256 reduction words and the 80-entry segment table (12 words each)."""
+    nk = m.top_k + m.n_shared
+    F = nk * m.expert_ffn if m.is_moe else m.ffn_dim
+    kmax = _cdiv(max(m.hidden, m.n_q_heads * m.head_dim, F, m.n_experts,
+                     ((nk - 1) * m.expert_ffn + _cdiv(m.expert_ffn, 1024) * 1024) if m.is_moe else 0),
+                 1024) * 1024
+    rows2 = lambda r: r + (r & 1)  # noqa: E731  (consecutive-row pairs)
+    Tg = W // m.n_kv_heads
+    pairs = m.n_kv_heads * (m.n_q_heads // m.n_kv_heads + 2) * m.head_dim // 2
+    y = [2 * _cdiv(pairs, W), rows2(_cdiv(m.hidden, W)), rows2(_cdiv(m.vocab, W)), rows2(_cdiv(m.hidden, Tg))]
+    if m.is_moe:
+        y += [rows2(_cdiv(m.n_experts, W)), 2 * _cdiv(F, W), rows2(_cdiv(m.hidden, W)) * nk]
+    else:
+        y += [2 * _cdiv(m.ffn_dim, W)]
+    ymax = _cdiv(max(y), 64) * 64
+    return (kmax + ymax * (threads // 64) + 256 + 80 * 12) * 4
+
+
 ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
     synth.TINY, synth.SMALL_DENSE, synth.SMALL_MOE]
 
@@ -54,10 +79,11 @@ ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
 @pytest.mark.parametrize("grid", [0, 1, 7, 16, 37, 256])
 def test_plans_validate(lib, m, grid):
     W = grid or 256
-    kmax = -(-max(m.hidden, m.n_q_heads * m.head_dim, m.ffn_dim,
-                  (m.top_k + m.n_shared) * m.expert_ffn, m.n_experts) // 1024) * 1024
-    lds = (kmax + 8 * -(-m.vocab // W) + 256) * 4  # LM-head rows dominate the result buffer
-    if grid and (grid < m.n_kv_heads or lds > 160 * 1024):
+    if grid and grid < m.n_kv_heads:
+        lds = None
+    else:
+        lds = _gemv_lds_bytes(m, W)
+    if grid and (lds is None or lds > 160 * 1024):
         with pytest.raises(E.PreError) as ei:
             E.plan_describe(m, grid_wgs=grid)
         assert ei.value.code == -2
