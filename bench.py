@@ -37,7 +37,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(workload, device="cuda", seed=0, **eng_kw):
+def setup(workload, device="cuda", seed=0, prefill="engine", **eng_kw):
+    """Weights, cache and engine of a workload.  prefill="engine" fills the
+    cache by teacher-forced decode of the workload's random prompt (the
+    workload as specified); "synthetic" writes seeded N(0,1) K/V rows instead
+    and decodes from token 1 -- the same bytes and flops per step, without a
+    prefill launch (used for profiler runs that must see only timed launches)."""
     import torch
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import synth
@@ -45,19 +50,32 @@ def setup(workload, device="cuda", seed=0, **eng_kw):
     m = w.model
     t0 = time.time()
     W = synth.gen_weights(m, seed=seed, device=device)
-    shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
-    kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-    vc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-    eng = E.Engine(m, W, kc, vc, **eng_kw)
     P = w.contexts[0]
-    prompt = synth.gen_tokens(m.vocab, P, seed=seed, device=device)
-    eng.set_positions([0])
-    out = eng.decode(P, forced=prompt.view(P, 1))  # cache filled by the engine itself
-    torch.cuda.synchronize()
-    eng.status()
-    g0 = out[-1].contiguous()
-    log(f"[bench] {workload}: weights + prefill of {P} tokens in {time.time() - t0:.1f}s")
+    if prefill == "synthetic":
+        kc, vc = synth.gen_kv_cache(m, P, seed=seed + 1, device=device)
+    else:
+        shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
+        kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        vc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    eng = E.Engine(m, W, kc, vc, **eng_kw)
+    if prefill == "synthetic":
+        g0 = torch.ones(1, dtype=torch.int32, device=device)
+    else:
+        prompt = synth.gen_tokens(m.vocab, P, seed=seed, device=device)
+        eng.set_positions([0])
+        out = eng.decode(P, forced=prompt.view(P, 1))  # cache filled by the engine itself
+        torch.cuda.synchronize()
+        eng.status()
+        g0 = out[-1].contiguous()
+    log(f"[bench] {workload}: weights + {prefill} prefill of {P} tokens in {time.time() - t0:.1f}s")
     return w, m, W, kc, vc, eng, g0
+
+
+def launches_per_token_per_op(m):
+    """Kernels the one-kernel-per-operator path launches per token: embedding;
+    per layer two norms and one launch per task stage (5 dense, 6 MoE); final
+    norm, LM head, argmax."""
+    return (8 if m.is_moe else 7) * m.n_layers + 4
 
 
 def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
@@ -133,7 +151,7 @@ def tiny_comparison(repeats=5):
             "speedup": round(ub / up, 2),
             "persistent_us_per_token_by_grid": {str(k): round(v, 2) for k, v in res.items()},
             "best_grid": best_grid, "best_speedup": round(ub / min(up, res[best_grid]), 2),
-            "launches_per_token_per_op": 8 * m.n_layers + 4, "launches_per_token_persistent": 1 / n}
+            "launches_per_token_per_op": launches_per_token_per_op(m), "launches_per_token_persistent": 1 / n}
 
 
 def main():
@@ -147,6 +165,9 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timing")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-decoder comparison")
     ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first copy this many MiB with the library's copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -154,9 +175,17 @@ def main():
         sys.exit(2)
     import torch
     from persistent_resident_execution_amd import engine as E
+    from persistent_resident_execution_amd import profiling
     torch.cuda.set_device(0)
 
-    w, m, W, kc, vc, eng, g0 = setup(args.workload, grid_wgs=args.grid)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        E.debug_copy(a, b)
+        torch.cuda.synchronize()
+        del a, b
+    w, m, W, kc, vc, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill)
     P, K = w.contexts[0], args.steps
     log(f"[bench] timing {args.repeats} x {K} persistent steps from position {P}")
     tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
@@ -179,7 +208,8 @@ def main():
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "repeats_us_per_token": [round(t / K * 1e6, 2) for t in tp],
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": profiling.traffic_for(args.workload, K),
                      "kernel": "pre_persistent", "bytes_per_launch": bytes_call,
                      "launch_ms": round(t_med * 1e3, 3)},
     }
@@ -188,7 +218,7 @@ def main():
         tb, btoks = time_calls(eng, eng.baseline_decode, K, g0, P, max(1, args.repeats // 2), 0)
         ub = statistics.median(tb) / K * 1e6
         result["per_op_baseline"] = {"us_per_token": round(ub, 2),
-                                     "launches_per_token": 8 * m.n_layers + 4,
+                                     "launches_per_token": launches_per_token_per_op(m),
                                      "persistent_speedup": round(ub / us_tok, 3),
                                      "same_tokens": bool((btoks == toks).all())}
     eng.close()

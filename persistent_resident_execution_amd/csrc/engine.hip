@@ -1276,6 +1276,13 @@ extern "C" __global__ void pre_k_fp8_decode(const uint8_t *in, float *out, int n
   }
 }
 
+// Plain copy of n16 16-byte words (reference kernel for the memory-traffic
+// counters: it reads and writes exactly 16 * n16 bytes).
+extern "C" __global__ void __launch_bounds__(256) pre_k_copy(const v4i *src, v4i *dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 // Debug / tuning: the streamed GEMV alone, y = W x over rows split evenly
 // across the grid (consecutive-row pairs), for a given ring depth and weight
 // cache policy.
@@ -1690,6 +1697,16 @@ extern "C" int pre_debug_gemv(int variant, const void *d_w, int rows, int K, con
   if (hipLaunchKernel(fns[variant], dim3(grid), dim3(threads), args, lds, (hipStream_t)stream) != hipSuccess)
     return PRE_ERR_HIP;
   return PRE_OK;
+}
+
+// Debug entry: copy `bytes` (a multiple of 16, 16-byte aligned buffers) with
+// pre_k_copy -- the calibration kernel for memory-traffic counters.
+extern "C" int pre_debug_copy(const void *d_src, void *d_dst, size_t bytes, void *stream) {
+  if (!d_src || !d_dst || bytes == 0 || (bytes & 15) || !al16(d_src) || !al16(d_dst)) return PRE_ERR_ARG;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(pre_k_copy, dim3(2048), dim3(256), 0, (hipStream_t)stream, (const v4i *)d_src, (v4i *)d_dst,
+                     n16);
+  return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
 }
 
 // Debug: byte offsets of the workspace regions (status, flags, layers, tasks,

@@ -108,6 +108,7 @@ def lib():
         L.pre_debug_layout.argtypes = [vp, vp]
         L.pre_debug_lane_ops.argtypes = [vp, vp, vp]
         L.pre_debug_gemv.argtypes = [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp]
+        L.pre_debug_copy.argtypes = [vp, vp, C.c_size_t, vp]
         _lib = L
     return _lib
 
@@ -297,3 +298,11 @@ def debug_lane_ops(x):
     _check(lib().pre_debug_lane_ops(_ptr(inp), _ptr(out), _stream()), "debug_lane_ops")
     torch.cuda.synchronize()
     return out.cpu()
+
+
+def debug_copy(src, dst):
+    """dst[:] = src[:] with the library's plain copy kernel (byte counts must
+    match and be a multiple of 16); the reference for traffic counters."""
+    n = src.numel() * src.element_size()
+    assert n == dst.numel() * dst.element_size() and n % 16 == 0
+    _check(lib().pre_debug_copy(_ptr(src), _ptr(dst), n, _stream()), "debug_copy")

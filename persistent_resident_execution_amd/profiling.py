@@ -1,0 +1,193 @@
+"""Condense rocprofv3 output into the short text summaries kept under
+profiles/, and read them back for the benchmark.
+
+    python -m persistent_resident_execution_amd.profiling stats DIR --out FILE --command "..."
+    python -m persistent_resident_execution_amd.profiling traffic FETCH_DIR WRITE_DIR --out FILE \\
+        --command "..." --copy-bytes N --workload W --steps K
+    python -m persistent_resident_execution_amd.profiling counters DIR --out FILE --command "..."
+
+`stats` condenses a `rocprofv3 --kernel-trace --stats` run: calls and
+durations per kernel, plus every pre_persistent dispatch from the trace.
+
+`traffic` takes two `--pmc` runs of the same command, one collecting
+FETCH_SIZE and one WRITE_SIZE (both KiB per dispatch).  The command runs
+the library's plain copy kernel (pre_k_copy) on a known number of bytes
+before the decode launch; each counter of the decode launch (the last
+pre_persistent dispatch) is scaled by copy bytes / the copy's reading of
+that counter.  The summary records a hash of the kernel sources it was
+measured with: the benchmark reports the traffic only while the sources
+still hash the same.
+
+`counters` lists any other counters of the last pre_persistent dispatch
+(L2 hits and misses, GPU-active cycles).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL = "pre_persistent"
+COPY_KERNEL = "pre_k_copy"
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources, the C ABI header and the build recipe."""
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [
+        os.path.join(ROOT, "include", "pre.h"), os.path.join(PKG, "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        if os.path.isfile(f):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _csv(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(hits[0], newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name, n=60):
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def summarize_stats(d, out, command):
+    rows = _csv(d, "kernel_stats.csv")
+    trace = _csv(d, "kernel_trace.csv")
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+            if r["Kernel_Name"] == KERNEL]
+    lines = [f"# rocprofv3 kernel trace + stats", f"command: {command}", f"source_sha256: {source_hash()}", "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>12s} {'min_us':>12s} {'max_us':>12s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name']):60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} "
+                     f"{float(r['MinNs']) / 1e3:12.1f} {float(r['MaxNs']) / 1e3:12.1f} "
+                     f"{float(r['Percentage']):6.2f}")
+    lines += ["", f"{KERNEL} dispatches (us): " + ", ".join(f"{x:.1f}" for x in durs)]
+    if durs:
+        lines.append(f"{KERNEL} mean_us: {statistics.mean(durs):.1f}")
+    _write(out, lines)
+
+
+def _last_dispatch_value(rows, kernel, counter):
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and r["Kernel_Name"] == kernel:
+            did = int(r["Dispatch_Id"])
+            vals[did] = vals.get(did, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise ValueError(f"no {counter} rows for {kernel}")
+    return vals[max(vals)], len(vals)
+
+
+def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, steps):
+    fr, wr = _csv(fetch_dir, "counter_collection.csv"), _csv(write_dir, "counter_collection.csv")
+    f_k, nf = _last_dispatch_value(fr, KERNEL, "FETCH_SIZE")
+    w_k, nw = _last_dispatch_value(wr, KERNEL, "WRITE_SIZE")
+    f_c, _ = _last_dispatch_value(fr, COPY_KERNEL, "FETCH_SIZE")
+    w_c, _ = _last_dispatch_value(wr, COPY_KERNEL, "WRITE_SIZE")
+    ff, fw = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
+    fetch_b, write_b = f_k * 1024.0 * ff, w_k * 1024.0 * fw
+    lines = ["# HBM traffic of one decode launch from rocprofv3 --pmc (two runs)",
+             f"command: {command}",
+             f"workload: {workload}", f"steps: {steps}", f"source_sha256: {source_hash()}",
+             f"copy_bytes: {copy_bytes}",
+             f"copy_FETCH_SIZE_KiB: {f_c:.1f}", f"copy_WRITE_SIZE_KiB: {w_c:.1f}",
+             f"fetch_scale: {ff:.4f}", f"write_scale: {fw:.4f}",
+             f"kernel_FETCH_SIZE_KiB: {f_k:.1f}  (last of {nf} {KERNEL} dispatches)",
+             f"kernel_WRITE_SIZE_KiB: {w_k:.1f}  (last of {nw} {KERNEL} dispatches)",
+             f"fetch_bytes_per_launch: {fetch_b:.0f}", f"write_bytes_per_launch: {write_b:.0f}",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+             f"traffic_bytes_per_step: {(fetch_b + write_b) / steps:.0f}"]
+    _write(out, lines)
+
+
+def summarize_counters(d, out, command):
+    rows = _csv(d, "counter_collection.csv")
+    names = sorted({r["Counter_Name"] for r in rows if r["Kernel_Name"] == KERNEL})
+    lines = ["# rocprofv3 --pmc counters of the last decode launch", f"command: {command}",
+             f"source_sha256: {source_hash()}"]
+    vals = {}
+    for n in names:
+        v, cnt = _last_dispatch_value(rows, KERNEL, n)
+        vals[n] = v
+        lines.append(f"{n}: {v:.0f}  (last of {cnt} dispatches)")
+    if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
+        tot = vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"]
+        lines.append(f"L2_hit_rate: {vals['TCC_HIT_sum'] / tot:.4f}" if tot else "L2_hit_rate: n/a")
+    if "GRBM_GUI_ACTIVE" in vals and vals.get("GRBM_COUNT"):
+        lines.append(f"gpu_active_frac: {vals['GRBM_GUI_ACTIVE'] / vals['GRBM_COUNT']:.4f}")
+    _write(out, lines)
+
+
+def _write(out, lines):
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_summary(path) -> dict:
+    """key: value lines of a summary file (values as strings)."""
+    res = {}
+    if not os.path.exists(path):
+        return res
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                res[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    return res
+
+
+def traffic_for(workload, steps):
+    """Measured HBM bytes of one launch of `steps` steps, or None when no
+    summary matches this workload, step count and the current sources."""
+    s = read_summary(os.path.join(ROOT, "profiles", f"{KERNEL}_{workload}_traffic.txt"))
+    if not s or s.get("workload") != workload or s.get("steps") != str(steps):
+        return None
+    if s.get("source_sha256") != source_hash():
+        return None
+    return int(float(s["traffic_bytes_per_launch"]))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("--out", required=True)
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_dir")
+    b.add_argument("write_dir")
+    b.add_argument("--out", required=True)
+    b.add_argument("--command", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--steps", type=int, required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", required=True)
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        summarize_stats(args.dir, args.out, args.command)
+    elif args.cmd == "traffic":
+        summarize_traffic(args.fetch_dir, args.write_dir, args.out, args.command, args.copy_bytes,
+                          args.workload, args.steps)
+    else:
+        summarize_counters(args.dir, args.out, args.command)
+
+
+if __name__ == "__main__":
+    main()
