@@ -70,6 +70,8 @@ extern "C" {
 #define PRE_DEV_TIMEOUT 1   /* a dependency wait exceeded the watchdog      */
 #define PRE_DEV_BAD_TOKEN 2 /* an input or forced token outside [0, vocab)  */
 #define PRE_DEV_NAN 3       /* a NaN logit reached the argmax               */
+#define PRE_DEV_PLACEMENT 4 /* a workgroup ran on another XCD than the
+                               XCD-local hand-offs assume (see xcd_local)   */
 
 /* ---- model configuration ---------------------------------------------- */
 /* Plain data, read once at create.  n_experts == 0 means a dense SwiGLU FFN
@@ -80,13 +82,20 @@ extern "C" {
  * RoPE pairs element i with i + head_dim/2 (rotate-half).
  * grid_wgs: workgroups that take part (0 = one per CU); wg_threads: threads
  * per workgroup (0 = 512).  attn_splits: KV chunks per KV head and sequence
- * (0 = derive from grid_wgs). */
+ * (0 = derive from grid_wgs).  xcd_local: 0 = hand the q/K/V rows and the
+ * attention partials from producer to consumer through the XCD's own L2
+ * when every consumer sits on the producer's XCD (8 KV heads, a grid that is
+ * a multiple of 8: KV head g's QKV rows, attention chunks and output
+ * projection slice all run on XCD g); -1 = always hand off at device scope.
+ * The persistent kernel checks the placement it assumes and latches
+ * PRE_DEV_PLACEMENT if the hardware put a workgroup elsewhere. */
 typedef struct pre_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t batch, max_ctx;
   float rope_theta, rms_eps;
   int32_t n_experts, top_k, n_shared, expert_ffn, expert_dtype;
   int32_t grid_wgs, wg_threads, attn_splits;
+  int32_t xcd_local;
 } pre_config;
 
 /* Per-layer weights (device pointers).  Dense: wg, wu [ffn][hidden], wd
@@ -211,6 +220,7 @@ const char *pre_strerror(int code);
  * aux, wait_lo, wait_hi, signal) in table order when h_tasks is non-NULL. */
 typedef struct pre_plan_info {
   int32_t n_stage_inst, n_wgs, n_slots, n_tasks, attn_splits, validator;
+  int32_t xcd_local;  /* 1 if the XCD-local hand-offs are in use */
   int64_t workspace_bytes;
 } pre_plan_info;
 int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int32_t *h_tasks,

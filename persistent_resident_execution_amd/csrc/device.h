@@ -27,6 +27,7 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 // Cache-policy operand of the buffer intrinsics on gfx94x/gfx950:
 // bit 0 = sc0, bit 1 = nt, bit 4 = sc1.
 constexpr int CP_DEF = 0;
+constexpr int CP_SC0 = 1;
 constexpr int CP_NT = 2;
 constexpr int CP_SC1 = 16;
 

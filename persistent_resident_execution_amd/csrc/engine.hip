@@ -57,7 +57,10 @@ struct KP {
   uint32_t trace_cap;
   int32_t persistent;
   int32_t b_si, b_step;  // baseline launches: the stage and step to run
+  int32_t local;         // XCD-local hand-offs (QKV -> attention -> O projection)
 };
+
+
 
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
@@ -119,27 +122,40 @@ __device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t
 }
 
 // The dependency wait of one task (a no-op in the per-operator baseline).
+// Timestamps are taken only when a trace buffer is set: reading the clock is
+// a scalar-memory round trip that the barrier after it would make every
+// wavefront wait for.
 struct Waiter {
   int active, lo, hi, step, stage;
   uint32_t ep;
   int *sh;
+  int tr;  // tracing on
   __device__ __forceinline__ bool operator()(const KP &P) const {
     if (!active) return true;
     const bool ok = wait_slots(P, lo, hi, ep, step, stage, sh);
-    if (threadIdx.x == 0) sh[3] = (int)(uint32_t)now_ticks();  // trace: end of the wait
+    if (tr && threadIdx.x == 0) sh[3] = (int)(uint32_t)now_ticks();  // trace: end of the wait
     return ok;
   }
   // trace: time of phase k (0..3) of the task, taken by thread 0
   __device__ __forceinline__ void mark(int k) const {
-    if (active && threadIdx.x == 0) sh[4 + k] = (int)(uint32_t)now_ticks();
+    if (tr && threadIdx.x == 0) sh[4 + k] = (int)(uint32_t)now_ticks();
   }
 };
 
-// Publish: every thread's stores are complete, then one sc1 flag store.
-__device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep) {
+// Publish: every thread's stores are complete, then one flag store.  When
+// all of the flag's readers are on this XCD (the QKV and attention stages
+// with XCD-local placement) the flag goes into the XCD's L2 (sc0), where the
+// readers' device-scope polls find it without a round trip to memory; the
+// data itself is always written through at device scope: under the weight
+// stream, L2-scope stores of partly written lines drain several times
+// slower.
+__device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep, bool local) {
   drain();
   __syncthreads();
-  if (threadIdx.x == 0 && slot >= 0) st_flag(P.flags + slot, ep);
+  if (threadIdx.x == 0 && slot >= 0) {
+    if (local) __builtin_amdgcn_raw_buffer_store_b32(ep, mkbuf(P.flags + slot, 4), 0, 0, CP_SC0);
+    else st_flag(P.flags + slot, ep);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -155,6 +171,7 @@ struct Src {
   const uint16_t *gain;  // non-NULL: fold RMSNorm with these gains
 };
 constexpr int MAXPARTS = 8;  // KV heads per sequence (partials of the split O projection)
+constexpr int MAXW = 8;      // wavefronts per workgroup (at most 512 threads)
 
 // xs[0..K) = src (normalised if gain), xs[K..Kpad) = 0.  Ends with a barrier.
 // The gains are fetched together with the data, so staging costs one device
@@ -225,8 +242,12 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[wave] = ss;
     __syncthreads();
+    float rw[MAXW];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) rw[w] = w < nw ? red[w] : 0.f;
     float tot = 0.f;
-    for (int w = 0; w < nw; ++w) tot += red[w];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) tot += rw[w];
     const float rinv = 1.0f / sqrtf(tot / (float)K + P.eps);
     for (int k = 0; k < GK; ++k) {
       const int i = tid + k * T;
@@ -481,9 +502,15 @@ __device__ __forceinline__ void ys_clear(float *ys, int ng, int nw, int nthr) {
   for (int i = threadIdx.x; i < n; i += nthr) ys[i] = 0.f;
 }
 // Row r (0: A, 1: B) of pair g: the wavefronts' partials in wavefront order.
+// All loads are issued before the first add (one LDS round trip).
 __device__ __forceinline__ float ys_get(const float *ys, int g, int r, int nw) {
+  const float *p = ys + g * nw * 2 + r;
+  float v[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) v[w] = w < nw ? p[2 * w] : 0.f;
   float y = 0.f;
-  for (int w = 0; w < nw; ++w) y += ys[(g * nw + w) * 2 + r];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) y += v[w];
   return y;
 }
 // Row e of a task made of consecutive-row pairs.
@@ -694,6 +721,22 @@ __device__ __forceinline__ Geo segs_fp8(const KP &P, const Task &t, const int *s
 __device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
   if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
 }
+template <int CTRL, int RM = 0xf>
+__device__ __forceinline__ void argmax_dpp(float &bv, int &bi) {
+  const float ov = dpp_keep<CTRL, RM>(bv);
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, RM, 0xf, false);
+  argmax_merge(bv, bi, ov, oi);
+}
+// (max, lowest index) over the 64 lanes with DPP moves (the merge is
+// commutative and associative); the result is valid in lane 63.
+__device__ __forceinline__ void wave_argmax_l63(float &bv, int &bi) {
+  argmax_dpp<0xb1>(bv, bi);
+  argmax_dpp<0x4e>(bv, bi);
+  argmax_dpp<0x141>(bv, bi);
+  argmax_dpp<0x140>(bv, bi);
+  argmax_dpp<0x142, 0xa>(bv, bi);
+  argmax_dpp<0x143, 0xc>(bv, bi);
+}
 
 // Combine the NC chunk partials of (sequence b, KV head g) into
 // xs[0 .. G*d): o_h = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c with
@@ -708,9 +751,50 @@ __device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, flo
   float *wt = lds + go;          // [NC][G] e^{m - M}
   float *den = wt + NC * G;      // [G] sum, [G] max
   float *blk = lds + ((go + NC * G + 2 * G + 3) & ~3);
-  const int room = (lds_n - (int)(blk - lds)) / (G * rec);
-  const int per = max(1, min(NC, room));
+  const int per = NC * G * rec <= lds_n ? NC : max(1, min(NC, (lds_n - (int)(blk - lds)) / (G * rec)));
   const Rsrc r = mkbuf(src, (uint32_t)NC * G * rec * 4);
+  if (per == NC) {
+    // the whole block fits: one bulk load, then every output element forms
+    // its head's maximum and weighted sums itself (no further barrier)
+    float *bk = lds;
+    const int nf = NC * G * rec;
+    for (int i = tid * 2; i < nf; i += 16 * T) {
+      v2i a[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = i + k * 2 * T;
+        a[k] = e < nf ? ld64<CP_SC1>(r, (uint32_t)e * 4) : v2i{0, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = i + k * 2 * T;
+        if (e < nf) *reinterpret_cast<float2 *>(bk + e) = __builtin_bit_cast(float2, a[k]);
+      }
+    }
+    __syncthreads();
+    const int cs = G * rec;  // stride between chunks
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * T;
+      if (i < G * d) {
+        const int hh = i / d, j = i - hh * d;
+        const float *bh = bk + hh * rec;
+        float Mx = -INFINITY;
+#pragma unroll 4
+        for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, bh[cc * cs]);
+        float num = 0.f, den = 0.f;
+#pragma unroll 4
+        for (int cc = 0; cc < NC; ++cc) {
+          const float w = expf(bh[cc * cs] - Mx);
+          num = fmaf(w, bh[cc * cs + 2 + j], num);
+          den = fmaf(w, bh[cc * cs + 1], den);
+        }
+        xs[i] = num / den;
+      }
+    }
+    return;
+  }
+  // sliced: the chunk partials are staged a few chunks at a time
   float num[4] = {0.f, 0.f, 0.f, 0.f}, dsum = 0.f;
   for (int c0 = 0; c0 < NC; c0 += per) {
     const int c1 = min(NC, c0 + per), nf = (c1 - c0) * G * rec;  // nf is even
@@ -808,6 +892,14 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   // workgroup passed: fetch it now
   const bool down = op == OP_DOWN || op == OP_EDOWN;
   const float res0 = down && tid < rows ? mid_elem(P, l, tok, t.r0 + tid) : 0.f;
+  // QKV: this thread's first pair's RoPE factors (a table lookup; fetched
+  // now so the epilogue does not wait for memory)
+  float cos0 = 1.f, sin0 = 0.f;
+  if (!FP8 && op == OP_QKV && tid < rows) {
+    const int half = P.d >> 1, j = (t.r0 + tid) % ((P.G + 2) * half) % half;
+    cos0 = P.rope[(int64_t)pos * half + j];
+    sin0 = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + j];
+  }
   if (!FP8 && !wait(P)) return false;
   if (op == OP_OPROJ) {
     // combine into xs[0..K); its scratch lies behind the padded input, up to
@@ -864,7 +956,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         const int p = t.r0 + i, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
         float a = ys_get(ys, i, 0, nw), b = ys_get(ys, i, 1, nw);
         if (hh <= P.G) {  // RoPE on q and k
-          const float c = cosT[j], s = sinT[j];
+          const float c = i == tid ? cos0 : cosT[j], s = i == tid ? sin0 : sinT[j];
           const float a2 = a * c - b * s, b2 = b * c + a * s;
           a = a2; b = b2;
         }
@@ -876,8 +968,9 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
           uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
           const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
           const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
-          st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j) * 2, f2bf(a));
-          st16<CP_SC1>(r, (uint32_t)((int64_t)pos * P.d + j + half) * 2, f2bf(b));
+          const uint32_t o0 = (uint32_t)((int64_t)pos * P.d + j) * 2, o1 = o0 + (uint32_t)half * 2;
+          st16<CP_SC1>(r, o0, f2bf(a));
+          st16<CP_SC1>(r, o1, f2bf(b));
         }
       }
       return true;
@@ -920,13 +1013,12 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         else argmax_merge(bv, bi, y, t.r0 + i);
         if (lg) lg[i] = y;
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+      wave_argmax_l63(bv, bi);
       const bool wnan = __any(nan);
       float *wv = M.red + 128;
       int *wi = reinterpret_cast<int *>(M.red + 160);
       int *wn = reinterpret_cast<int *>(M.red + 192);
-      if (lane == 0) { wv[wave] = bv; wi[wave] = bi; wn[wave] = wnan; }
+      if (lane == 63) { wv[wave] = bv; wi[wave] = bi; wn[wave] = wnan; }
       __syncthreads();
       if (tid == 0) {
         float v = -INFINITY;
@@ -954,10 +1046,9 @@ __device__ __forceinline__ int reduce_lm(const KP &P, int *sh) {
       if (v != v) nan = true;
       else argmax_merge(bv, bi, v, ix);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+    wave_argmax_l63(bv, bi);
     const bool anynan = __any(nan);
-    if (lane == 0) sh[1] = anynan ? -1 : bi;
+    if (lane == 63) sh[1] = anynan ? -1 : bi;
   }
   __syncthreads();
   const int r = sh[1];
@@ -1108,7 +1199,11 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
   for (int i = tid; i < G * d; i += T) {
     const int hh = i / d, j = i % d;
     float s = 0.f;
-    for (int w = 0; w < nw; ++w) s += ored[(w * G + hh) * d + j];
+    float ov[MAXW];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) s += ov[w];
     st_sc1(pdst + hh * (d + 2) + 2 + j, s);
   }
   for (int hh = tid; hh < G; hh += T) {
@@ -1173,11 +1268,19 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   __shared__ int sh[8];
   const bool res = P.persistent != 0;
   const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
-  if (res && threadIdx.x == 0) {
-    const uint32_t x = xcc_id();
-    P.xcc[lam] = x;
-    if (P.W % P.X == 0 && (int)x != (int)(blockIdx.x % P.X))
-      __hip_atomic_fetch_add(&P.status->xcc_mismatch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (res) {
+    // the XCD this workgroup runs on; the task placement assumes block b on
+    // XCD b % 8, and the XCD-local hand-offs need it
+    if (threadIdx.x == 0) {
+      const uint32_t x = xcc_id();
+      P.xcc[lam] = x;
+      const int bad = P.W % P.X == 0 && (int)x != (int)(blockIdx.x % P.X);
+      if (bad) __hip_atomic_fetch_add(&P.status->xcc_mismatch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (bad && P.local) latch_error(P, PRE_DEV_PLACEMENT, 0, -1, lam, x, blockIdx.x % P.X);
+      sh[2] = bad;
+    }
+    __syncthreads();
+    if (P.local && sh[2]) return;
   }
   const int s_end = res ? P.n_steps : P.b_step + 1;
   const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
@@ -1192,12 +1295,13 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
     for (int si = si0; si < si1; ++si) {
       const Task t = P.tasks[(int64_t)si * P.W + lam];
       if (t.op == OP_NONE) continue;
-      const uint32_t tw = (uint32_t)now_ticks();
-      const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh};
+      const int tr = res && P.trace != nullptr;
+      const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
+      const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
       if (!run_task(t, lam, s, pos, tok, lds, wait)) return;
       if (res) {
-        signal_slot(P, t.signal, ep);
-        trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
+        signal_slot(P, t.signal, ep, P.local && (t.op == OP_QKV || t.op == OP_ATTN));
+        if (tr) trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
       }
     }
     if (!res) return;
@@ -1515,6 +1619,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;
+  P.local = D.local;
 }
 
 static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in, const int32_t *d_forced,

@@ -54,6 +54,10 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   const int bg = D->B * D->Hkv;
   if (D->Hkv > 8 || D->W < bg) return PRE_ERR_SHAPE;
   D->Tg = D->W / bg;
+  // KV head g's QKV pairs, attention chunks and O-projection slice occupy
+  // lambdas [g * W/8, (g + 1) * W/8): one XCD, when there are 8 KV heads and
+  // the grid splits evenly over the 8 XCDs
+  D->local = c->xcd_local >= 0 && D->Hkv == D->X && D->B == 1 && D->W % D->X == 0;
   // about 256 positions per attention chunk, at most one chunk per workgroup
   // of the (sequence, KV head)'s share
   D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 256)));
@@ -390,6 +394,7 @@ extern "C" int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int3
   out->n_tasks = (int32_t)T.size();
   out->attn_splits = D.NC;
   out->validator = pre::validate(D, T);
+  out->xcd_local = D.local;
   out->workspace_bytes = Lo.total;
   if (h_tasks)
     for (int32_t i = 0; i < max_tasks && i < (int32_t)T.size(); ++i)

@@ -76,6 +76,7 @@ struct Dims {
   int32_t qkv_pairs;  // RoPE pairs of all QKV rows: Hkv * (G + 2) * d / 2
   int32_t F;          // width of the FFN activation slot (ffn or (top_k+n_shared)*effn)
   int32_t W, X, NC;   // workgroups, XCDs, attention chunks per (sequence, KV head)
+  int32_t local;      // QKV->attention->O-projection hand-offs stay inside one XCD's L2
   int32_t Tg;         // workgroups per (sequence, KV head): W / (batch * n_kv_heads)
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded

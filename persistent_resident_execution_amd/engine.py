@@ -35,7 +35,7 @@ class Config(C.Structure):
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "batch", "max_ctx")] + [("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [
         (n, C.c_int32) for n in ("n_experts", "top_k", "n_shared", "expert_ffn", "expert_dtype",
-                                 "grid_wgs", "wg_threads", "attn_splits")]
+                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local")]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "router",
@@ -67,7 +67,7 @@ class Status(C.Structure):
 
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_stage_inst", "n_wgs", "n_slots", "n_tasks",
-                                         "attn_splits", "validator")] + [
+                                         "attn_splits", "validator", "xcd_local")] + [
         ("workspace_bytes", C.c_int64)]
 
 
@@ -113,7 +113,7 @@ def lib():
     return _lib
 
 
-def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0) -> Config:
+def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, xcd_local=0) -> Config:
     c = Config()
     for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
               "batch", "max_ctx", "n_experts", "top_k", "n_shared", "expert_ffn"):
@@ -122,6 +122,7 @@ def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0) -
     c.rms_eps = float(m.rms_eps)
     c.expert_dtype = 1 if m.is_moe else 0
     c.grid_wgs, c.wg_threads, c.attn_splits = int(grid_wgs), int(wg_threads), int(attn_splits)
+    c.xcd_local = int(xcd_local)
     return c
 
 
@@ -173,9 +174,9 @@ class Engine:
     """
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
-                 wg_threads=0, attn_splits=0, stream=None):
+                 wg_threads=0, attn_splits=0, stream=None, xcd_local=0):
         self.m = m
-        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits)
+        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local)
         L = lib()
         nbytes = C.c_size_t()
         _check(L.pre_workspace_size(C.byref(self.cfg), C.byref(nbytes)), "workspace_size")

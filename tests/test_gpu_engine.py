@@ -259,3 +259,29 @@ def test_small_moe_baseline(small_moe):
     S, prompt, ref = small_moe
     _say("[test] small MoE baseline")
     _check_run(S, prompt, ref, baseline=True)
+
+
+@pytest.fixture(scope="module")
+def gqa8(oracle_lib):
+    _say("[setup] small 8-KV-head decoder (XCD-local hand-offs) + oracle run (prompt 48, 24 steps)")
+    S = parity.DenseSetup(oracle_lib, synth.SMALL_GQA8, seed=7)
+    prompt = synth.gen_tokens(synth.SMALL_GQA8.vocab, 48, seed=7).numpy()
+    ref = parity.oracle_run(S.om, prompt, 24)
+    return S, prompt, ref
+
+
+@pytest.mark.parametrize("grid", [0, 40])
+def test_gqa8_xcd_local_matches_oracle(gqa8, grid):
+    S, prompt, ref = gqa8
+    _say(f"[test] 8-KV-head persistent, XCD-local hand-offs, grid={grid}")
+    assert E.plan_describe(S.m, grid_wgs=grid)[0].xcd_local == 1
+    _check_run(S, prompt, ref, baseline=False, grid_wgs=grid)
+
+
+def test_gqa8_xcd_local_equals_device_scope(gqa8):
+    """Only the cache scope of the hand-offs differs: identical results."""
+    S, prompt, ref = gqa8
+    _say("[test] 8-KV-head persistent, XCD-local vs device-scope hand-offs")
+    _, t1, l1 = _check_run(S, prompt, ref, baseline=False)
+    _, t2, l2 = _check_run(S, prompt, ref, baseline=False, xcd_local=-1)
+    assert np.array_equal(t1, t2) and np.array_equal(l1, l2)

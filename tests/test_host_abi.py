@@ -72,7 +72,7 @@ def _gemv_lds_bytes(m, W, threads=512):
 
 
 ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
-    synth.TINY, synth.SMALL_DENSE, synth.SMALL_MOE]
+    synth.TINY, synth.SMALL_DENSE, synth.SMALL_MOE, synth.SMALL_GQA8]
 
 
 @pytest.mark.parametrize("m", ALL, ids=lambda m: f"{m.name}-{m.max_ctx}")
@@ -175,3 +175,27 @@ def test_step_bytes_8b_order_of_magnitude(lib):
     # 8B-shape: 32 x 436 MB of layer weights + 1.05 GB LM head ~ 15.0 GB of weights
     b = E.step_bytes(synth.DENSE8B, [1024])
     assert 15.0e9 < b < 15.3e9
+
+
+@pytest.mark.parametrize("m,grid,flag,want", [
+    (synth.DENSE8B, 0, 0, 1), (synth.DENSE8B, 64, 0, 1), (synth.DENSE8B, 0, -1, 0),
+    (synth.DENSE8B, 100, 0, 0), (synth.MOE, 0, 0, 1), (synth.TINY, 0, 0, 0),
+    (synth.SMALL_GQA8, 0, 0, 1), (synth.SMALL_GQA8, 40, 0, 1), (synth.SMALL_GQA8, 36, 0, 0)],
+    ids=lambda v: str(getattr(v, "name", v)))
+def test_xcd_local_mode_only_where_each_head_fits_one_xcd(lib, m, grid, flag, want):
+    """The L2-local hand-offs are used only with 8 KV heads on a grid that
+    splits evenly over the 8 XCDs; there every QKV, attention and O-projection
+    task of head g, and every slot it waits on, lies in XCD g's lambda range."""
+    info, T = E.plan_describe(m, with_tasks=True, grid_wgs=grid, xcd_local=flag)
+    assert info.xcd_local == want
+    if not want:
+        return
+    W, per = info.n_wgs, info.n_wgs // 8
+    spl = 6 if m.is_moe else 5
+    for layer in range(m.n_layers):
+        for k in range(3):  # QKV, ATTN, OPROJ
+            for lam in range(W):
+                op, _, r0, r1, aux, lo, hi, sig = T[(layer * spl + k) * W + lam]
+                if op == 0 or lo >= hi or k == 0:
+                    continue
+                assert all((s % W) // per == lam // per for s in range(lo, hi)), (layer, k, lam)
