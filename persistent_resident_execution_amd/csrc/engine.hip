@@ -173,29 +173,35 @@ struct Src {
 constexpr int MAXPARTS = 8;  // KV heads per sequence (partials of the split O projection)
 constexpr int MAXW = 8;      // wavefronts per workgroup (at most 512 threads)
 
-// xs[0..K) = src (normalised if gain), xs[K..Kpad) = 0.  Ends with a barrier.
-// The gains are fetched together with the data, so staging costs one device
-// round trip (two when K exceeds GK * 4 * threads and gains are refetched).
-constexpr int GK = 4;
+// xs[0..K) = src (times the gains if given), xs[K..Kpad) = 0.  Ends with a
+// barrier.  RMSNorm is folded: with gains, each wavefront's sum of squares
+// of the unscaled input goes to red[wave], and the consumer multiplies its
+// results by norm_scale() -- W (x * g) / rms(x) equals W (x * g / rms(x)) --
+// so staging needs neither a second pass nor a barrier before it.  The gains
+// are fetched together with the data: staging costs one device round trip.
 __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, const Src &s, int K,
                                           int Kpad) {
   const int tid = threadIdx.x, T = P.nthr, n4 = K >> 2;
   float ss = 0.f;
   const Rsrc rg = mkbuf(s.gain, s.gain ? (uint32_t)K * 2 : 0u);
-  v2i gr[GK];
-#pragma unroll
-  for (int k = 0; k < GK; ++k) gr[k] = s.gain ? ld64<CP_DEF>(rg, (uint32_t)(tid + k * T) * 8) : v2i{0, 0};
+  auto scaled = [](float4 f, v2i g) {
+    return float4{f.x * bf_lo(g.x), f.y * bf_hi(g.x), f.z * bf_lo(g.y), f.w * bf_hi(g.y)};
+  };
   if (s.f32 && s.nparts == 0) {
     const Rsrc r = mkbuf(s.f32, (uint32_t)K * 4);
     for (int i = tid; i < n4; i += 8 * T) {
       v4i a[8];
+      v2i g[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
+      for (int j = 0; j < 8; ++j) {
+        a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
+        g[j] = s.gain ? ld64<CP_DEF>(rg, (uint32_t)(i + j * T) * 8) : v2i{0, 0};
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (i + j * T < n4) {
-          float4 f = __builtin_bit_cast(float4, a[j]);
-          reinterpret_cast<float4 *>(xs)[i + j * T] = f;
+          const float4 f = __builtin_bit_cast(float4, a[j]);
+          reinterpret_cast<float4 *>(xs)[i + j * T] = s.gain ? scaled(f, g[j]) : f;
           ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
           ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
         }
@@ -206,6 +212,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
     const Rsrc rp = mkbuf(s.parts, s.parts ? (uint32_t)((s.nparts - 1) * s.pstride + K) * 4 : 0u);
     for (int i0 = tid; i0 < n4; i0 += 2 * T) {
       v4i pv[2][MAXPARTS], bv[2];
+      v2i g[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int i = i0 + k * T;  // past n4 the buffers return 0
@@ -218,6 +225,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
           const v2i w = ld64<CP_DEF>(rb, (uint32_t)i * 8);
           bv[k] = __builtin_bit_cast(v4i, float4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)});
         }
+        g[k] = s.gain ? ld64<CP_DEF>(rg, (uint32_t)i * 8) : v2i{0, 0};
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -230,7 +238,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
             const float4 q = __builtin_bit_cast(float4, pv[k][p]);
             f.x += q.x; f.y += q.y; f.z += q.z; f.w += q.w;
           }
-        reinterpret_cast<float4 *>(xs)[i] = f;
+        reinterpret_cast<float4 *>(xs)[i] = s.gain ? scaled(f, g[k]) : f;
         ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
         ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
       }
@@ -238,33 +246,22 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
   }
   for (int i = K + tid; i < Kpad; i += T) xs[i] = 0.f;
   if (s.gain) {
-    const int wave = wave_id(), nw = P.nw;
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[wave] = ss;
-    __syncthreads();
-    float rw[MAXW];
-#pragma unroll
-    for (int w = 0; w < MAXW; ++w) rw[w] = w < nw ? red[w] : 0.f;
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < MAXW; ++w) tot += rw[w];
-    const float rinv = 1.0f / sqrtf(tot / (float)K + P.eps);
-    for (int k = 0; k < GK; ++k) {
-      const int i = tid + k * T;
-      if (i < n4) {
-        const float4 f = reinterpret_cast<float4 *>(xs)[i];
-        reinterpret_cast<float4 *>(xs)[i] = float4{f.x * rinv * bf_lo(gr[k].x), f.y * rinv * bf_hi(gr[k].x),
-                                                   f.z * rinv * bf_lo(gr[k].y), f.w * rinv * bf_hi(gr[k].y)};
-      }
-    }
-    for (int i = tid + GK * T; i < n4; i += T) {  // beyond the gains held in registers
-      const v2i g = ld64<CP_DEF>(rg, (uint32_t)i * 8);
-      const float4 f = reinterpret_cast<float4 *>(xs)[i];
-      reinterpret_cast<float4 *>(xs)[i] = float4{f.x * rinv * bf_lo(g.x), f.y * rinv * bf_hi(g.x),
-                                                 f.z * rinv * bf_lo(g.y), f.w * rinv * bf_hi(g.y)};
-    }
+    const float w = wave_sum2_l63(ss, 0.f).x;
+    if ((tid & 63) == 63) red[wave_id()] = w;
   }
   __syncthreads();
+}
+
+// 1 / rms of the input staged with gains: from the per-wavefront sums of
+// squares that stage_vec left in red (read after a later barrier).
+__device__ __forceinline__ float norm_scale(const KP &P, const float *red, int K) {
+  float rw[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) rw[w] = w < P.nw ? red[w] : 0.f;
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) tot += rw[w];
+  return 1.0f / sqrtf(tot / (float)K + P.eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -901,6 +898,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     sin0 = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + j];
   }
   if (!FP8 && !wait(P)) return false;
+  bool normed = false;  // RMSNorm folded into the staging: results scale by norm_scale
+  int Kst = 0;
   if (op == OP_OPROJ) {
     // combine into xs[0..K); its scratch lies behind the padded input, up to
     // the segment table, and overlaps ys, which is cleared again afterwards
@@ -913,6 +912,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   } else {
     Src src{P.a_norm, nullptr, nullptr, 0, 0, nullptr};  // the baseline's normalised input
     int K = P.h;
+    Kst = K;
     if (down) {
       src.f32 = P.u + vec_off(P, l, 0, P.F);
       K = P.F;
@@ -923,16 +923,20 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       else src = mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm);
     }
     stage_vec(P, M.xs, M.red, src, K, P.kmax);
+    normed = src.gain != nullptr;
+    Kst = K;
   }
   wait.mark(0);
   st_run(S, n, M.seg, G, M.xs, M.ys);
   __syncthreads();
   wait.mark(1);
   const float *ys = M.ys;
+  const float rs = normed ? norm_scale(P, M.red, Kst) : 1.f;
   if (FP8) {
     if (op == OP_EGU) {
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
-      for (int i = tid; i < rows; i += P.nthr) st_sc1(u + i, silu(ys_get(ys, i, 0, nw)) * ys_get(ys, i, 1, nw));
+      for (int i = tid; i < rows; i += P.nthr)
+        st_sc1(u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
     } else {
       const int nk = P.top_k + P.n_shared, np = (rows + 1) >> 1;
       float *xo = P.x_out + vec_off(P, l, 0, P.h) + t.r0;
@@ -954,7 +958,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       const float *sinT = P.rope + (int64_t)P.max_ctx * half + (int64_t)pos * half;
       for (int i = tid; i < rows; i += P.nthr) {
         const int p = t.r0 + i, g = p / per_group, rem = p % per_group, hh = rem / half, j = rem % half;
-        float a = ys_get(ys, i, 0, nw), b = ys_get(ys, i, 1, nw);
+        float a = rs * ys_get(ys, i, 0, nw), b = rs * ys_get(ys, i, 1, nw);
         if (hh <= P.G) {  // RoPE on q and k
           const float c = i == tid ? cos0 : cosT[j], s = i == tid ? sin0 : sinT[j];
           const float a2 = a * c - b * s, b2 = b * c + a * s;
@@ -983,7 +987,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     }
     case OP_GU: {
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
-      for (int i = tid; i < rows; i += P.nthr) st_sc1(u + i, silu(ys_get(ys, i, 0, nw)) * ys_get(ys, i, 1, nw));
+      for (int i = tid; i < rows; i += P.nthr)
+        st_sc1(u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
       return true;
     }
     case OP_DOWN: {
@@ -998,7 +1003,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     }
     case OP_ROUTER: {
       float *rl = P.rl + vec_off(P, l, 0, P.E) + t.r0;
-      for (int i = tid; i < rows; i += P.nthr) st_sc1(rl + i, ys_row(ys, i, nw));
+      for (int i = tid; i < rows; i += P.nthr) st_sc1(rl + i, rs * ys_row(ys, i, nw));
       return true;
     }
     default: {  // OP_LM
@@ -1008,7 +1013,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       int bi = 0x7fffffff;
       bool nan = false;
       for (int i = tid; i < rows; i += P.nthr) {
-        const float y = ys_row(ys, i, nw);
+        const float y = rs * ys_row(ys, i, nw);
         if (y != y) nan = true;
         else argmax_merge(bv, bi, y, t.r0 + i);
         if (lg) lg[i] = y;
@@ -1343,7 +1348,8 @@ extern "C" __global__ void __launch_bounds__(512) pre_k_norm(KP P, int l, int mi
   Src s = mid == 2 ? Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, gain}
                    : (mid ? mid_input(P, l, 0, gain) : layer_input(P, l, 0, gain));
   stage_vec(P, xs, red, s, P.h, P.kmax);
-  for (int i = threadIdx.x; i < P.kmax; i += P.nthr) P.a_norm[i] = xs[i];
+  const float r = norm_scale(P, red, P.h);
+  for (int i = threadIdx.x; i < P.kmax; i += P.nthr) P.a_norm[i] = xs[i] * r;
 }
 
 extern "C" __global__ void __launch_bounds__(512) pre_k_argmax(KP P, int step) {
