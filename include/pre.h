@@ -80,9 +80,11 @@ extern "C" {
  * expert_ffn) with expert_dtype 1 = fp8 e4m3 (OCP) codes and one bf16 scale
  * per 128x128 block.  Query head h reads KV head h * n_kv_heads / n_q_heads.
  * RoPE pairs element i with i + head_dim/2 (rotate-half).
- * grid_wgs: workgroups that take part (0 = one per CU); wg_threads: threads
- * per workgroup (0 = 512).  attn_splits: KV chunks per KV head and sequence
- * (0 = derive from grid_wgs).  xcd_local: 0 = hand the q/K/V rows and the
+ * grid_wgs: workgroups that take part (0 = one per CU, or fewer -- one per
+ * 32 KB of a layer's weights, a multiple of 8 -- for small models);
+ * wg_threads: threads per workgroup (0 = 512).  attn_splits: KV chunks per KV
+ * head and sequence (0 = about one per 128 positions of max_ctx, at most the
+ * workgroups per KV head).  xcd_local: 0 = hand the q/K/V rows and the
  * attention partials from producer to consumer through the XCD's own L2
  * when every consumer sits on the producer's XCD (8 KV heads, a grid that is
  * a multiple of 8: KV head g's QKV rows, attention chunks and output

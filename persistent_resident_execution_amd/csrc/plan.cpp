@@ -48,7 +48,21 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (D->G > 8) return PRE_ERR_SHAPE;
   D->qkv_pairs = D->Hkv * (D->G + 2) * D->d / 2;
   D->F = moe ? (D->top_k + D->n_shared) * D->effn : D->ffn;
-  D->W = c->grid_wgs > 0 ? c->grid_wgs : n_cus;
+  // default grid: one workgroup per CU, unless a layer's weights are too
+  // few to keep that many busy: then about one workgroup per 32 KB of a
+  // layer's weights (a multiple of 8, so the XCDs get equal shares)
+  if (c->grid_wgs > 0) {
+    D->W = c->grid_wgs;
+  } else {
+    const int64_t h = c->hidden, qkv = (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    int64_t lb = 2 * h * qkv + 2 * (int64_t)c->n_q_heads * c->head_dim * h;
+    if (moe)
+      lb += 2 * (int64_t)c->n_experts * h + (int64_t)(c->top_k + c->n_shared) * 3 * c->expert_ffn * h;
+    else
+      lb += 6 * (int64_t)c->ffn_dim * h;
+    const int64_t by_size = std::max<int64_t>(8, lb / (32 * 1024) / 8 * 8);
+    D->W = (int32_t)std::min<int64_t>(n_cus, by_size);
+  }
   if (D->W < 1 || D->W > 4096) return PRE_ERR_SHAPE;
   D->X = 8;
   const int bg = D->B * D->Hkv;
@@ -58,9 +72,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // lambdas [g * W/8, (g + 1) * W/8): one XCD, when there are 8 KV heads and
   // the grid splits evenly over the 8 XCDs
   D->local = c->xcd_local >= 0 && D->Hkv == D->X && D->B == 1 && D->W % D->X == 0;
-  // about 256 positions per attention chunk, at most one chunk per workgroup
-  // of the (sequence, KV head)'s share
-  D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 256)));
+  // about 128 positions per attention chunk at the longest context, at most
+  // one chunk per workgroup of the (sequence, KV head)'s share
+  D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 128)));
   if (D->NC > D->Tg) return PRE_ERR_SHAPE;
   D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
   if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
