@@ -174,16 +174,18 @@ int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos);
  * token after that, unless d_forced is non-NULL, in which case it is
  * d_forced[s * batch + b] (teacher forcing; used to fill a cache from a
  * prompt).  d_out_tokens[s * batch + b] receives the greedy token of step s.
- * Advances the host positions by n_steps.  Returns PRE_ERR_CONTEXT if a
- * position would reach max_ctx, PRE_ERR_BROKEN after a latched device error
- * until pre_engine_reset. */
+ * Advances the host positions by n_steps.  n_steps == 0 returns PRE_OK at
+ * once without reading any buffer.  Returns PRE_ERR_CONTEXT if a position
+ * would pass max_ctx, PRE_ERR_BROKEN after a latched device error until
+ * pre_engine_reset. */
 int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
                       const int32_t *d_forced, int32_t *d_out_tokens, const pre_check *chk,
                       void *stream);
 
 /* The same decode as a conventional one-kernel-per-operator launch sequence
- * (about ten launches per layer per step), using the same tile code and the
- * same workspace, so that both paths can be timed through identical calls. */
+ * (seven launches per dense layer, eight per MoE layer, four per step),
+ * using the same tile code and the same workspace, so that both paths can be
+ * timed through identical calls. */
 int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
                         const int32_t *d_forced, int32_t *d_out_tokens, const pre_check *chk,
                         void *stream);

@@ -1630,7 +1630,9 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
 
 static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in, const int32_t *d_forced,
                       const int32_t *d_out) {
-  if (!e || n_steps < 0 || !d_out || (!d_in && !d_forced)) return PRE_ERR_ARG;
+  if (!e || n_steps < 0) return PRE_ERR_ARG;
+  if (n_steps == 0) return PRE_OK;  // nothing to do; the buffers are not read
+  if (!d_out || (!d_in && !d_forced)) return PRE_ERR_ARG;
   if (e->broken) return PRE_ERR_BROKEN;
   for (int b = 0; b < e->D.B; ++b)
     if ((int64_t)e->pos[b] + n_steps > e->D.max_ctx) return PRE_ERR_CONTEXT;

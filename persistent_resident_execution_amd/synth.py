@@ -87,6 +87,9 @@ SMALL_DENSE = ModelConfig("small_dense", n_layers=3, hidden=384, n_q_heads=6, n_
 SMALL_MOE = ModelConfig("small_moe", n_layers=2, hidden=384, n_q_heads=6, n_kv_heads=2,
                         head_dim=64, ffn_dim=0, vocab=1500, max_ctx=192, n_experts=16, top_k=4,
                         n_shared=1, expert_ffn=256)
+# One query head per KV head (plain multi-head attention, G = 1).
+SMALL_MHA = ModelConfig("small_mha", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=4,
+                        head_dim=64, ffn_dim=512, vocab=1024, max_ctx=160)
 # Eight KV heads (one per XCD, as in the 8B and MoE shapes), so the XCD-local
 # hand-offs are in use; ragged hidden and ffn.
 SMALL_GQA8 = ModelConfig("small_gqa8", n_layers=2, hidden=640, n_q_heads=16, n_kv_heads=8,

@@ -285,3 +285,58 @@ def test_gqa8_xcd_local_equals_device_scope(gqa8):
     _, t1, l1 = _check_run(S, prompt, ref, baseline=False)
     _, t2, l2 = _check_run(S, prompt, ref, baseline=False, xcd_local=-1)
     assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+
+
+def test_zero_steps_launch_nothing(tiny):
+    S, _, _ = tiny
+    eng = S.engine()
+    eng.set_positions([5])
+    out = eng.decode(0, in_tokens=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0 and eng.positions() == [5]
+    assert eng.status()["error"] == 0
+
+
+@pytest.mark.parametrize("persistent", [True, False])
+def test_last_position_matches_oracle(oracle_lib, persistent):
+    """One step at position max_ctx - 1 (the cache's last row) over a seeded
+    synthetic cache handed to both sides."""
+    m = synth.TINY
+    _say(f"[test] last position, {'persistent' if persistent else 'baseline'}")
+    S = parity.DenseSetup(oracle_lib, m, seed=11)
+    P = m.max_ctx - 1
+    kc, vc = synth.gen_kv_cache(m, P, seed=12, device="cuda")
+    S.kc.copy_(kc)
+    S.vc.copy_(vc)
+    kc_h = np.ascontiguousarray(synth.to_bits(kc)[:, 0])
+    vc_h = np.ascontiguousarray(synth.to_bits(vc)[:, 0])
+    eng = S.engine()
+    eng.set_positions([P])
+    lg = torch.zeros((1, 1, m.vocab), device="cuda")
+    hd = torch.zeros((1, 1, m.hidden), device="cuda")
+    run = eng.decode if persistent else eng.baseline_decode
+    out = run(1, in_tokens=torch.tensor([3], dtype=torch.int32, device="cuda"), logits=lg, hidden=hd)
+    torch.cuda.synchronize()
+    eng.status()
+    nxt, ref_lg, ref_hd = S.om.decode_step(kc_h, vc_h, 3, P)
+    parity.compare_step(0, int(out[0, 0]), lg[0, 0].cpu().numpy(), hd[0, 0].cpu().numpy(), nxt, ref_lg, ref_hd)
+    with pytest.raises(E.PreError) as ei:  # the cache is full now
+        run(1, in_tokens=torch.tensor([3], dtype=torch.int32, device="cuda"))
+    assert ei.value.code == -9
+    eng.close()
+
+
+@pytest.fixture(scope="module")
+def mha(oracle_lib):
+    _say("[setup] small multi-head decoder (one query head per KV head) + oracle run")
+    S = parity.DenseSetup(oracle_lib, synth.SMALL_MHA, seed=9)
+    prompt = synth.gen_tokens(synth.SMALL_MHA.vocab, 32, seed=9).numpy()
+    ref = parity.oracle_run(S.om, prompt, 16)
+    return S, prompt, ref
+
+
+@pytest.mark.parametrize("baseline", [False, True])
+def test_mha_matches_oracle(mha, baseline):
+    S, prompt, ref = mha
+    _say(f"[test] MHA (G = 1) {'baseline' if baseline else 'persistent'}")
+    _check_run(S, prompt, ref, baseline=baseline)
