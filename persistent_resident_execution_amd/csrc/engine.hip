@@ -45,7 +45,7 @@ struct KP {
   uint32_t *flags, *xcc;
   DevStatus *status;
   const float *rope;
-  float *x_out, *pbuf, *q, *u, *rl, *part, *lmp, *x_emb, *a_norm;
+  float *x_out, *pbuf, *q, *u, *rl, *part, *lmp, *x_emb, *a_norm, *xmid;
   int32_t *tok_slot;
   // this call
   int32_t n_steps, pos0;
@@ -169,9 +169,12 @@ struct Src {
   const float *parts;    // nparts fp32 vectors at stride pstride, added in order
   int nparts, pstride;
   const uint16_t *gain;  // non-NULL: fold RMSNorm with these gains
+  float *dump;           // non-NULL: write float4s [d0, d1) of the summed vector here
+  int d0, d1;
 };
 constexpr int MAXPARTS = 8;  // KV heads per sequence (partials of the split O projection)
 constexpr int MAXW = 8;      // wavefronts per workgroup (at most 512 threads)
+constexpr int PREC_O = 4;    // attention chunk record: m, l, two unused words, then o[d]
 
 // xs[0..K) = src (times the gains if given), xs[K..Kpad) = 0.  Ends with a
 // barrier.  RMSNorm is folded: with gains, each wavefront's sum of squares
@@ -239,6 +242,8 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
             f.x += q.x; f.y += q.y; f.z += q.z; f.w += q.w;
           }
         reinterpret_cast<float4 *>(xs)[i] = s.gain ? scaled(f, g[k]) : f;
+        if (s.dump && i >= s.d0 && i < s.d1)
+          st128<CP_SC1>(mkbuf(s.dump, (uint32_t)K * 4), (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
         ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
         ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
       }
@@ -538,8 +543,10 @@ __device__ __forceinline__ Src mid_input(const KP &P, int l, int tok, const uint
   return s;
 }
 // Element i of the layer-l post-attention residual (same addition order as
-// stage_vec).
+// stage_vec).  MoE layers in the resident kernel have it materialised by the
+// router stage.
 __device__ __forceinline__ float mid_elem(const KP &P, int l, int tok, int i) {
+  if (P.persistent && P.moe) return ld_sc1(P.xmid + vec_off(P, l, 0, P.h) + i);
   float x;
   if (l > 0) x = ld_sc1(P.x_out + vec_off(P, l - 1, 0, P.h) + i);
   else if (P.persistent) x = bf16f(P.embed[(int64_t)tok * P.h + i]);
@@ -566,6 +573,27 @@ __device__ __forceinline__ GemvLds gemv_lds(const KP &P, float *lds) {
   return GemvLds{lds, ys, red, reinterpret_cast<Seg *>(red + 256)};
 }
 
+// Best (value, lowest index) of two candidates.
+__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL, int RM = 0xf>
+__device__ __forceinline__ void argmax_dpp(float &bv, int &bi) {
+  const float ov = dpp_keep<CTRL, RM>(bv);
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, RM, 0xf, false);
+  argmax_merge(bv, bi, ov, oi);
+}
+// (max, lowest index) over the 64 lanes with DPP moves (the merge is
+// commutative and associative); the result is valid in lane 63.
+__device__ __forceinline__ void wave_argmax_l63(float &bv, int &bi) {
+  argmax_dpp<0xb1>(bv, bi);
+  argmax_dpp<0x4e>(bv, bi);
+  argmax_dpp<0x141>(bv, bi);
+  argmax_dpp<0x140>(bv, bi);
+  argmax_dpp<0x142, 0xa>(bv, bi);
+  argmax_dpp<0x143, 0xc>(bv, bi);
+}
+
 // Softmax over the router logits and top-k selection (ties -> lower expert
 // id), then the n_shared shared experts with weight 1.  Every workgroup
 // that needs the choice computes it; the inputs and the order of operations
@@ -589,14 +617,13 @@ __device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw,
       int bi = 0x7fffffff, li = 0;
       for (int i = lane; i < P.E; i += 64, ++li)
         if (!((taken >> li) & 1u) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { sel[k] = bi; selw[k] = expf(bv - m) / s; }
+      wave_argmax_l63(bv, bi);
+      // a NaN logit leaves no winner: expert E-1 keeps the addresses valid and
+      // the NaN weight reaches the LM head's NaN check
+      const int win = min(__builtin_amdgcn_readlane(bi, 63), P.E - 1);
+      const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 63));
+      if ((win & 63) == lane) taken |= 1u << (win >> 6);
+      if (lane == 0) { sel[k] = win; selw[k] = expf(wv - m) / s; }
     }
     if (lane == 0)
       for (int k = 0; k < P.n_shared; ++k) { sel[P.top_k + k] = k; selw[P.top_k + k] = 1.0f; }
@@ -714,76 +741,59 @@ __device__ __forceinline__ Geo segs_fp8(const KP &P, const Task &t, const int *s
   return Geo{f, (uint32_t)f, 2u * f, 2, 1, (uint32_t)fb * 2, rows > 0 ? nk : 0, rows > 0 ? nk * ((rows + 1) >> 1) : 0};
 }
 
-// Best (value, lowest index) of two candidates.
-__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-}
-template <int CTRL, int RM = 0xf>
-__device__ __forceinline__ void argmax_dpp(float &bv, int &bi) {
-  const float ov = dpp_keep<CTRL, RM>(bv);
-  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, RM, 0xf, false);
-  argmax_merge(bv, bi, ov, oi);
-}
-// (max, lowest index) over the 64 lanes with DPP moves (the merge is
-// commutative and associative); the result is valid in lane 63.
-__device__ __forceinline__ void wave_argmax_l63(float &bv, int &bi) {
-  argmax_dpp<0xb1>(bv, bi);
-  argmax_dpp<0x4e>(bv, bi);
-  argmax_dpp<0x141>(bv, bi);
-  argmax_dpp<0x140>(bv, bi);
-  argmax_dpp<0x142, 0xa>(bv, bi);
-  argmax_dpp<0x143, 0xc>(bv, bi);
-}
-
 // Combine the NC chunk partials of (sequence b, KV head g) into
 // xs[0 .. G*d): o_h = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c with
-// M = max_c m_c.  The partial block [NC][G][d + 2] is contiguous; it is read
-// with wide loads into the LDS behind xs (in slices of chunks when it does
-// not fit), so the combine costs one device round trip (two with slices).
+// M = max_c m_c.  The partial block [NC][G][rec] is contiguous (a record is
+// m, l, two unused words, o[d]: 16-byte aligned); it is read with 16-byte
+// loads into the LDS behind xs, all in flight at once (in slices of chunks
+// when it does not fit), so the combine costs one device round trip.
 __device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, float *lds, int lds_n, float *xs) {
-  const int b = bg / P.Hkv, g = bg % P.Hkv, G = P.G, d = P.d, NC = P.NC, rec = d + 2;
+  const int b = bg / P.Hkv, g = bg % P.Hkv, G = P.G, d = P.d, NC = P.NC, rec = d + PREC_O;
   const int tid = threadIdx.x, T = P.nthr;
   const float *src = P.part + (((int64_t)l * P.B + b) * P.Hkv + g) * NC * G * rec;
   const int go = (G * d + 3) & ~3;
   float *wt = lds + go;          // [NC][G] e^{m - M}
   float *den = wt + NC * G;      // [G] sum, [G] max
   float *blk = lds + ((go + NC * G + 2 * G + 3) & ~3);
-  const int per = NC * G * rec <= lds_n ? NC : max(1, min(NC, (lds_n - (int)(blk - lds)) / (G * rec)));
+  const int per = NC * G * (rec + 1) <= lds_n ? NC : max(1, min(NC, (lds_n - (int)(blk - lds)) / (G * rec)));
   const Rsrc r = mkbuf(src, (uint32_t)NC * G * rec * 4);
   if (per == NC) {
     // the whole block fits: one bulk load, then every output element forms
     // its head's maximum and weighted sums itself (no further barrier)
     float *bk = lds;
-    const int nf = NC * G * rec;
-    for (int i = tid * 2; i < nf; i += 16 * T) {
-      v2i a[8];
+    const int nf = NC * G * rec, n16 = nf / 4;
+    for (int i = tid; i < n16; i += 16 * T) {
+      v4i a[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = i + k * 2 * T;
-        a[k] = e < nf ? ld64<CP_SC1>(r, (uint32_t)e * 4) : v2i{0, 0};
-      }
+      for (int k = 0; k < 16; ++k) a[k] = ld128<CP_SC1>(r, (uint32_t)(i + k * T) * 16);  // past the end: 0
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = i + k * 2 * T;
-        if (e < nf) *reinterpret_cast<float2 *>(bk + e) = __builtin_bit_cast(float2, a[k]);
-      }
+      for (int k = 0; k < 16; ++k)
+        if (i + k * T < n16) reinterpret_cast<v4i *>(bk)[i + k * T] = a[k];
     }
     __syncthreads();
     const int cs = G * rec;  // stride between chunks
+    // e^{m_c - M} of every (chunk, head), once
+    float *wt = bk + nf;
+    for (int i = tid; i < NC * G; i += T) {
+      const int hh = i % G;
+      const float *bh = bk + hh * rec;
+      float Mx = -INFINITY;
+#pragma unroll 4
+      for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, bh[cc * cs]);
+      wt[i] = expf(bk[(i / G) * cs + hh * rec] - Mx);
+    }
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = tid + q * T;
       if (i < G * d) {
         const int hh = i / d, j = i - hh * d;
         const float *bh = bk + hh * rec;
-        float Mx = -INFINITY;
-#pragma unroll 4
-        for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, bh[cc * cs]);
         float num = 0.f, den = 0.f;
 #pragma unroll 4
         for (int cc = 0; cc < NC; ++cc) {
-          const float w = expf(bh[cc * cs] - Mx);
-          num = fmaf(w, bh[cc * cs + 2 + j], num);
+          const float w = wt[cc * G + hh];
+          num = fmaf(w, bh[cc * cs + PREC_O + j], num);
           den = fmaf(w, bh[cc * cs + 1], den);
         }
         xs[i] = num / den;
@@ -829,7 +839,7 @@ __device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, flo
       if (i < G * d) {
         const int hh = i / d, j = i % d;
         for (int cc = c0; cc < c1; ++cc)
-          num[q] = fmaf(wt[cc * G + hh], blk[((cc - c0) * G + hh) * rec + 2 + j], num[q]);
+          num[q] = fmaf(wt[cc * G + hh], blk[((cc - c0) * G + hh) * rec + PREC_O + j], num[q]);
       }
     }
     if (tid < G)
@@ -873,9 +883,16 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   int *sel = reinterpret_cast<int *>(M.red + 64);
   float *selw = M.red + 96;
   Geo G;
+  // The rows are known before the wait except for the routed experts' gate/up
+  // task (and every expert task on the per-operator path): in the resident
+  // kernel the down task of a layer runs on the workgroup that just routed
+  // the same layer for its gate/up task, and the choice is still in LDS.
+  const bool known = !FP8 || (P.persistent && op == OP_EDOWN);
   if (FP8) {
-    if (!wait(P)) return false;
-    route(P, l, sel, selw, M.xs);
+    if (!known) {
+      if (!wait(P)) return false;
+      route(P, l, sel, selw, M.xs);
+    }
     G = segs_fp8(P, t, sel, M.seg);
   } else {
     G = segs_bf16(P, t, M.seg);
@@ -897,7 +914,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     cos0 = P.rope[(int64_t)pos * half + j];
     sin0 = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + j];
   }
-  if (!FP8 && !wait(P)) return false;
+  if (known && !wait(P)) return false;
   bool normed = false;  // RMSNorm folded into the staging: results scale by norm_scale
   int Kst = 0;
   if (op == OP_OPROJ) {
@@ -918,9 +935,22 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       K = P.F;
     } else if (P.persistent) {
       const DevLayer &Lw = P.layers[l];
-      if (op == OP_QKV) src = layer_input(P, l, tok, (const uint16_t *)Lw.attn_norm);
-      else if (op == OP_LM) src = Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm};
-      else src = mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm);
+      if (op == OP_QKV) {
+        src = layer_input(P, l, tok, (const uint16_t *)Lw.attn_norm);
+      } else if (op == OP_LM) {
+        src = Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm};
+      } else if (op == OP_EGU) {
+        // the post-attention residual, summed once by the router stage
+        src = Src{P.xmid + vec_off(P, l, 0, P.h), nullptr, nullptr, 0, 0, (const uint16_t *)Lw.ffn_norm};
+      } else {
+        src = mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm);
+        if (op == OP_ROUTER) {  // sum the residual once for the expert stages: this task's share
+          const int n4 = P.h >> 2;
+          src.dump = P.xmid + vec_off(P, l, 0, P.h);
+          src.d0 = (int)((int64_t)n4 * lam / P.W);
+          src.d1 = (int)((int64_t)n4 * (lam + 1) / P.W);
+        }
+      }
     }
     stage_vec(P, M.xs, M.red, src, K, P.kmax);
     normed = src.gain != nullptr;
@@ -1200,7 +1230,8 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
   }
   __syncthreads();
   wait.mark(2);
-  float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * (d + 2);
+  const int rec = d + PREC_O;
+  float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * rec;
   for (int i = tid; i < G * d; i += T) {
     const int hh = i / d, j = i % d;
     float s = 0.f;
@@ -1209,11 +1240,11 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
     for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) s += ov[w];
-    st_sc1(pdst + hh * (d + 2) + 2 + j, s);
+    st_sc1(pdst + hh * rec + PREC_O + j, s);
   }
   for (int hh = tid; hh < G; hh += T) {
-    st_sc1(pdst + hh * (d + 2), st[2 * hh]);
-    st_sc1(pdst + hh * (d + 2) + 1, st[2 * hh + 1]);
+    st_sc1(pdst + hh * rec, st[2 * hh]);
+    st_sc1(pdst + hh * rec + 1, st[2 * hh + 1]);
   }
   return true;
 }
@@ -1622,6 +1653,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.lmp = (float *)(ws + Lo.lmp);
   P.x_emb = (float *)(ws + Lo.x_emb);
   P.a_norm = (float *)(ws + Lo.a_norm);
+  P.xmid = (float *)(ws + Lo.xmid);
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;

@@ -125,11 +125,12 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->q = take((int64_t)D.L * D.B * D.Hq * D.d * f);
   Lo->u = take((int64_t)D.L * D.B * D.F * f);
   Lo->rl = take((int64_t)D.L * D.B * std::max(D.E, 1) * f);
-  Lo->part = take((int64_t)D.L * D.B * D.Hkv * D.NC * D.G * (D.d + 2) * f);
+  Lo->part = take((int64_t)D.L * D.B * D.Hkv * D.NC * D.G * (D.d + 4) * f);  // records m, l, -, -, o[d]
   Lo->lmp = take((int64_t)D.W * D.B * 8);
   Lo->x_emb = take((int64_t)D.B * D.h * f);
   Lo->a_norm = take((int64_t)D.B * D.kmax * f);
   Lo->tok = take((int64_t)D.B * 4 * 4);
+  Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers)
   Lo->total = off;
 }
 

@@ -64,7 +64,7 @@ struct DevStatus {
 // Byte offsets of everything inside the caller's workspace.
 struct Layout {
   int64_t status, flags, layers, tasks, rope, xcc;
-  int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok;
+  int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid;
   int64_t total;
 };
 
