@@ -33,7 +33,7 @@ int validate(const Dims &D, const std::vector<Task> &T);
 struct KP {
   // shapes
   int32_t L, h, Hq, Hkv, d, ffn, V, B, max_ctx, E, top_k, n_shared, effn, moe, G, F, W, X, NC, Tg;
-  int32_t n_si, spl, kmax, ymax, cmax, lds_floats;
+  int32_t n_si, spl, kmax, ymax, segoff, cmax, lds_floats;
   int32_t nthr, nw;  // threads and wavefronts per workgroup (scalar: never re-read from the dispatch packet)
   float eps, attn_scale;
   // model
@@ -563,14 +563,15 @@ __device__ __forceinline__ float mid_elem(const KP &P, int l, int tok, int i) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// LDS layout of the GEMV tasks: xs[kmax] | ys[ymax * waves] | red[256] | seg table
+// LDS layout of the GEMV tasks: xs[kmax] | ys[ymax * waves] | red[256] | ... |
+// seg table at segoff (the gap, if any, is for the attention chunk combine)
 struct GemvLds {
   float *xs, *ys, *red;
   Seg *seg;
 };
 __device__ __forceinline__ GemvLds gemv_lds(const KP &P, float *lds) {
   float *ys = lds + P.kmax, *red = ys + P.ymax * P.nw;
-  return GemvLds{lds, ys, red, reinterpret_cast<Seg *>(red + 256)};
+  return GemvLds{lds, ys, red, reinterpret_cast<Seg *>(lds + P.segoff)};
 }
 
 // Best (value, lowest index) of two candidates.
@@ -765,7 +766,8 @@ __device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, flo
     for (int i = tid; i < n16; i += 16 * T) {
       v4i a[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) a[k] = ld128<CP_SC1>(r, (uint32_t)(i + k * T) * 16);  // past the end: 0
+      for (int k = 0; k < 16; ++k)
+        a[k] = i + k * T < n16 ? ld128<CP_SC1>(r, (uint32_t)(i + k * T) * 16) : v4i{0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < 16; ++k)
         if (i + k * T < n16) reinterpret_cast<v4i *>(bk)[i + k * T] = a[k];
@@ -1099,7 +1101,7 @@ __device__ __forceinline__ int reduce_lm(const KP &P, int *sh) {
 // tasks) and q are read after it.  Writes the chunk's (max, sum,
 // unnormalised output) per head; the output projection combines the chunks.
 
-constexpr int APB = 4;  // attention passes whose K/V rows are held in registers
+constexpr int APB = 5;  // attention passes whose K/V rows are held in registers
 
 __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
                                            const Waiter &wait) {
@@ -1625,7 +1627,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.L = D.L; P.h = D.h; P.Hq = D.Hq; P.Hkv = D.Hkv; P.d = D.d; P.ffn = D.ffn; P.V = D.V; P.B = D.B;
   P.max_ctx = D.max_ctx; P.E = D.E; P.top_k = D.top_k; P.n_shared = D.n_shared; P.effn = D.effn;
   P.moe = D.moe; P.G = D.G; P.F = D.F; P.W = D.W; P.X = D.X; P.NC = D.NC; P.Tg = D.Tg; P.n_si = D.n_si;
-  P.spl = D.stages_per_layer; P.kmax = D.kmax; P.ymax = D.ymax; P.cmax = D.cmax;
+  P.spl = D.stages_per_layer; P.kmax = D.kmax; P.ymax = D.ymax; P.segoff = D.segoff; P.cmax = D.cmax;
   P.lds_floats = e->lds_dyn / 4;
   P.nthr = D.threads;
   P.nw = D.threads / 64;

@@ -53,7 +53,10 @@ def _cdiv(a, b):
 def _gemv_lds_bytes(m, W, threads=512):
     """LDS of the GEMV tasks: the staged input (padded to 1024 columns), two
     results per row pair per wavefront for the largest task of any stage,
-    256 reduction words and the 80-entry segment table (12 words each)."""
+    256 reduction words -- or, if larger, the output projection's padded
+    input plus its KV head's attention chunk records (m, l, two unused
+    words, o) and one weight each -- then the 80-entry segment table (12
+    words each)."""
     nk = m.top_k + m.n_shared
     F = nk * m.expert_ffn if m.is_moe else m.ffn_dim
     kmax = _cdiv(max(m.hidden, m.n_q_heads * m.head_dim, F, m.n_experts,
@@ -68,7 +71,10 @@ def _gemv_lds_bytes(m, W, threads=512):
     else:
         y += [2 * _cdiv(m.ffn_dim, W)]
     ymax = _cdiv(max(y), 64) * 64
-    return (kmax + ymax * (threads // 64) + 256 + 80 * 12) * 4
+    G = m.n_q_heads // m.n_kv_heads
+    nc = min(Tg, max(1, _cdiv(m.max_ctx, 128)))
+    comb = _cdiv(G * m.head_dim, 512) * 512 + nc * G * (m.head_dim + 5)  # input + chunk records + weights
+    return (_cdiv(max(kmax + ymax * (threads // 64) + 256, comb), 4) * 4 + 80 * 12) * 4
 
 
 ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
