@@ -33,6 +33,18 @@ constexpr int CP_SC1 = 16;
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
+// A pointer every lane holds the same value of, as a scalar.  Buffer
+// descriptors must live in scalar registers; when the compiler cannot prove
+// a base pointer uniform (values merged across branches, pointers read from
+// memory) it would otherwise loop over the lanes' copies at every access.
+template <class T>
+__device__ __forceinline__ T *uni_ptr(T *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T *)(((uint64_t)hi << 32) | lo);
+}
+
 // Raw buffer over [p, p + bytes): loads past the end return 0, stores past
 // the end are dropped.  Word 3 is the gfx9 data-format default.
 __device__ __forceinline__ Rsrc mkbuf(const void *p, uint32_t bytes) {

@@ -58,6 +58,10 @@ struct KP {
   int32_t persistent;
   int32_t b_si, b_step;  // baseline launches: the stage and step to run
   int32_t local;         // XCD-local hand-offs (QKV -> attention -> O projection)
+  // micro-batch
+  int32_t pos0v[8];      // each sequence's position at the call's first step
+  uint8_t *pk;           // packed GEMM inputs
+  float *ssq;            // per-workgroup sums of squares of the normalised inputs
 };
 
 
@@ -186,12 +190,12 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
                                           int Kpad) {
   const int tid = threadIdx.x, T = P.nthr, n4 = K >> 2;
   float ss = 0.f;
-  const Rsrc rg = mkbuf(s.gain, s.gain ? (uint32_t)K * 2 : 0u);
+  const Rsrc rg = mkbuf(uni_ptr(s.gain), s.gain ? (uint32_t)K * 2 : 0u);
   auto scaled = [](float4 f, v2i g) {
     return float4{f.x * bf_lo(g.x), f.y * bf_hi(g.x), f.z * bf_lo(g.y), f.w * bf_hi(g.y)};
   };
   if (s.f32 && s.nparts == 0) {
-    const Rsrc r = mkbuf(s.f32, (uint32_t)K * 4);
+    const Rsrc r = mkbuf(uni_ptr(s.f32), (uint32_t)K * 4);
     for (int i = tid; i < n4; i += 8 * T) {
       v4i a[8];
       v2i g[8];
@@ -211,8 +215,9 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
     }
   } else {
     // base (fp32 or bf16) plus partial vectors, two float4 per thread per round
-    const Rsrc rb = mkbuf(s.f32 ? (const void *)s.f32 : (const void *)s.bf16, (uint32_t)K * (s.f32 ? 4 : 2));
-    const Rsrc rp = mkbuf(s.parts, s.parts ? (uint32_t)((s.nparts - 1) * s.pstride + K) * 4 : 0u);
+    const Rsrc rb = mkbuf(uni_ptr(s.f32 ? (const void *)s.f32 : (const void *)s.bf16), (uint32_t)K * (s.f32 ? 4 : 2));
+    const Rsrc rp = mkbuf(uni_ptr(s.parts), s.parts ? (uint32_t)((s.nparts - 1) * s.pstride + K) * 4 : 0u);
+    const Rsrc rd = mkbuf(uni_ptr(s.dump), s.dump ? (uint32_t)K * 4 : 0u);
     for (int i0 = tid; i0 < n4; i0 += 2 * T) {
       v4i pv[2][MAXPARTS], bv[2];
       v2i g[2];
@@ -243,7 +248,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
           }
         reinterpret_cast<float4 *>(xs)[i] = s.gain ? scaled(f, g[k]) : f;
         if (s.dump && i >= s.d0 && i < s.d1)
-          st128<CP_SC1>(mkbuf(s.dump, (uint32_t)K * 4), (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
+          st128<CP_SC1>(rd, (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
         ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
         ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
       }
@@ -306,8 +311,7 @@ struct Seg {
   uint64_t sa, sb;  // fp8: block-scale matrices of A and B (row block 0)
   int32_t j0, n, nB, xo;  // first row index, pairs, pairs with a B row, input offset (floats)
 };
-constexpr int SEGMAX = 80;  // most segments of one task (every q/k/v head of a layer)
-constexpr int SEG_FLOATS = SEGMAX * (int)(sizeof(Seg) / 4);
+[[maybe_unused]] constexpr int SEGMAX = 80;  // most segments of one task (every q/k/v head of a layer)
 
 // Geometry shared by all pairs of a task (wave-uniform).
 struct Geo {
@@ -1000,13 +1004,19 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
           float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
           st_sc1(qd + j, a);
           st_sc1(qd + j + half, b);
-        } else {
-          uint16_t *cache = (hh == P.G) ? P.kc : P.vc;
-          const int64_t base = (((int64_t)l * P.B + 0) * P.Hkv + g) * P.max_ctx * P.d;
-          const Rsrc r = mkbuf(cache + base, (uint32_t)P.max_ctx * P.d * 2);
-          const uint32_t o0 = (uint32_t)((int64_t)pos * P.d + j) * 2, o1 = o0 + (uint32_t)half * 2;
-          st16<CP_SC1>(r, o0, f2bf(a));
-          st16<CP_SC1>(r, o1, f2bf(b));
+        } else {  // the layer's K or V cache of every KV head under one descriptor each
+          const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
+          const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
+          const uint32_t o0 = (uint32_t)(((int64_t)g * P.max_ctx + pos) * P.d + j) * 2, o1 = o0 + (uint32_t)half * 2;
+          if (hh == P.G) {
+            const Rsrc r = mkbuf(P.kc + lbase, bytes);
+            st16<CP_SC1>(r, o0, f2bf(a));
+            st16<CP_SC1>(r, o1, f2bf(b));
+          } else {
+            const Rsrc r = mkbuf(P.vc + lbase, bytes);
+            st16<CP_SC1>(r, o0, f2bf(a));
+            st16<CP_SC1>(r, o1, f2bf(b));
+          }
         }
       }
       return true;
@@ -1360,6 +1370,9 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   }
 }
 
+// the micro-batch task set and kernel
+#include "mb.h"
+
 // ---------------------------------------------------------------------------
 // baseline: one kernel per operator, stream order as the only sync
 
@@ -1549,14 +1562,13 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   const int want = std::min(ldsm, 96 * 1024);
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
-  if (hipFuncSetAttribute((const void *)pre_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
-          hipSuccess ||
+  const void *kern = D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
     return PRE_ERR_HIP;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)pre_persistent, D.threads, dyn) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, D.threads, dyn) != hipSuccess)
     return PRE_ERR_HIP;
   if (per_cu < 1 || (int64_t)per_cu * cus < D.W) return PRE_ERR_SHAPE;
 
@@ -1656,6 +1668,9 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.x_emb = (float *)(ws + Lo.x_emb);
   P.a_norm = (float *)(ws + Lo.a_norm);
   P.xmid = (float *)(ws + Lo.xmid);
+  P.pk = D.mb ? (uint8_t *)(ws + Lo.pk) : nullptr;
+  P.ssq = D.mb ? (float *)(ws + Lo.ssq) : nullptr;
+  for (int b = 0; b < D.B; ++b) P.pos0v[b] = e->pos[b];
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;
@@ -1691,8 +1706,8 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   P.trace = e->trace;
   P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 32, 0xffffffffu);
   void *args[] = {&P};
-  hipError_t err = hipLaunchCooperativeKernel((const void *)pre_persistent, dim3(e->D.W),
-                                              dim3(e->D.threads), args, (unsigned)e->lds_dyn,
+  const void *kern = e->D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
+  hipError_t err = hipLaunchCooperativeKernel(kern, dim3(e->D.W), dim3(e->D.threads), args, (unsigned)e->lds_dyn,
                                               (hipStream_t)stream);
   if (err != hipSuccess) return PRE_ERR_HIP;
   e->epoch_base += (uint32_t)n_steps;
@@ -1722,9 +1737,14 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
   auto stage = [&](int si, int s) {
     P.b_si = si;
     P.b_step = s;
-    hipLaunchKernelGGL(pre_persistent, dim3(D.W), blk, lds, st, P);
+    if (D.mb) hipLaunchKernelGGL(pre_persistent_mb, dim3(D.W), blk, lds, st, P);
+    else hipLaunchKernelGGL(pre_persistent, dim3(D.W), blk, lds, st, P);
   };
-  for (int s = 0; s < n_steps; ++s) {
+  for (int s = 0; s < n_steps && D.mb; ++s) {  // micro-batch: every stage is a task kernel
+    for (int si = 0; si < D.n_si; ++si) stage(si, s);
+    hipLaunchKernelGGL(pre_k_argmax_mb, dim3(1), blk, 0, st, P, s);
+  }
+  for (int s = 0; s < n_steps && !D.mb; ++s) {
     hipLaunchKernelGGL(pre_k_embed, dim3(1), blk, 0, st, P, s);
     for (int l = 0; l < D.L; ++l) {
       const int si0 = l * D.stages_per_layer;
@@ -1856,15 +1876,24 @@ extern "C" int pre_debug_copy(const void *d_src, void *d_dst, size_t bytes, void
   return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
 }
 
+// Debug: the MFMA lane-layout probe (A 16x32, B 32x16 bf16 row-major; D
+// 16x16 fp32).
+extern "C" int pre_debug_mfma(const void *d_a, const void *d_b, float *d_d, void *stream) {
+  if (!d_a || !d_b || !d_d) return PRE_ERR_ARG;
+  hipLaunchKernelGGL(pre_k_mfma_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint16_t *)d_a,
+                     (const uint16_t *)d_b, d_d);
+  return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
+}
+
 // Debug: byte offsets of the workspace regions (status, flags, layers, tasks,
-// rope, xcc, x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, total) --
-// 17 int64 values.
+// rope, xcc, x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid, pk,
+// ssq, total) -- 20 int64 values.
 extern "C" int pre_debug_layout(const pre_engine *e, int64_t *out) {
   if (!e || !out) return PRE_ERR_ARG;
   const Layout &L = e->Lo;
-  const int64_t v[17] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u,
-                         L.rl, L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.total};
-  for (int i = 0; i < 17; ++i) out[i] = v[i];
+  const int64_t v[20] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u,
+                         L.rl, L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.xmid, L.pk, L.ssq, L.total};
+  for (int i = 0; i < 20; ++i) out[i] = v[i];
   return PRE_OK;
 }
 

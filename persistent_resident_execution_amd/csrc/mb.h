@@ -1,0 +1,887 @@
+// Micro-batch decode (2..8 sequences in lockstep, each at its own context
+// length): the resident kernel's second task set.  Included by engine.hip
+// after the batch-1 tiles, whose helpers it shares (waits, flags, scalar
+// reductions, the attention tile's inner loops).
+//
+// What changes with a batch (TileRT notes, "tile pipeline" and the skinny
+// GEMM discussion; persistent-execution survey, section 6.2):
+//
+//  * Projections become skinny GEMMs.  Each weight is still read once per
+//    step, but now multiplies up to 8 activation columns, so the work runs on
+//    the matrix cores: v_mfma_f32_16x16x32_bf16 on 16 weight rows x 32
+//    columns per instruction.  The activations enter as two bf16 columns per
+//    sequence, hi = bf16(x) and lo = bf16(x - hi): their products with the
+//    bf16 weights are exact in the fp32 accumulator, so the result carries
+//    about 16 bits of the activation (better than one fp32 rounding of a
+//    long dot product needs).  16 columns = 8 sequences x (hi, lo).
+//  * The producers write their outputs straight into that packed layout:
+//    32 GEMM columns per 1 KB block, [block][k8 of 4][column of 16][8 bf16],
+//    so lane l of an MFMA reads its 16 bytes at block * 1024 + l * 16.  The
+//    RMSNorm that precedes a projection is folded as in the batch-1 tiles:
+//    the producer packs x * g and leaves its share of sum(x^2) per sequence;
+//    the consumer scales its outputs by 1 / rms.
+//  * Attention is balanced over the workgroups of each KV head: the head's
+//    (sequence, position) pairs of this step are cut into equal contiguous
+//    shares, so long and short contexts cost the same per workgroup.  A
+//    share that crosses a sequence boundary leaves one record per sequence;
+//    a combine stage merges each sequence's records and packs the heads'
+//    outputs for the O projection, which then runs like every other GEMM.
+
+// ---------------------------------------------------------------------------
+// MFMA operands and the packed layout
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16 rows x 32) * B(32 x 16 columns).  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each as the 8 consecutive k of
+// group l / 16; it receives D rows 4 * (l / 16) .. + 3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+template <int CP>
+__device__ __forceinline__ v4i ld128s(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
+}
+
+// Byte offset of the 16 bytes that hold columns k8 * 8 .. + 7 of GEMM input
+// column `col` (sequence b: col b = hi, col 8 + b = lo).
+__device__ __forceinline__ uint32_t pk_off(int k8, int col) {
+  return (((uint32_t)k8 >> 2) * 64u + ((uint32_t)k8 & 3u) * 16u + (uint32_t)col) * 16u;
+}
+__device__ __forceinline__ int64_t pk_bytes(int K) { return (int64_t)(K >> 5) * 1024; }
+// The packed inputs of layer l: QKV (l = L: the LM head), gate/up, down, O.
+__device__ __forceinline__ uint8_t *pk_x(const KP &P, int l) { return P.pk + (int64_t)l * pk_bytes(P.h); }
+__device__ __forceinline__ uint8_t *pk_m(const KP &P, int l) {
+  return P.pk + (int64_t)(P.L + 1 + l) * pk_bytes(P.h);
+}
+__device__ __forceinline__ uint8_t *pk_u(const KP &P, int l) {
+  return P.pk + (int64_t)(2 * P.L + 1) * pk_bytes(P.h) + (int64_t)l * pk_bytes(P.ffn);
+}
+__device__ __forceinline__ uint8_t *pk_o(const KP &P, int l) {
+  return P.pk + (int64_t)(2 * P.L + 1) * pk_bytes(P.h) + (int64_t)P.L * pk_bytes(P.ffn) +
+         (int64_t)l * pk_bytes(P.Hq * P.d);
+}
+
+// Write 8 consecutive GEMM input values of sequence b as hi and lo bf16.
+__device__ __forceinline__ void pk_store8(uint8_t *pk, int K, int k8, int b, const float (&v)[8]) {
+  v4i hw, lw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
+    const uint16_t l0 = f2bf(v[2 * i] - bf16f(h0)), l1 = f2bf(v[2 * i + 1] - bf16f(h1));
+    hw[i] = (int)((uint32_t)h0 | ((uint32_t)h1 << 16));
+    lw[i] = (int)((uint32_t)l0 | ((uint32_t)l1 << 16));
+  }
+  const Rsrc r = mkbuf(uni_ptr(pk), (uint32_t)pk_bytes(K));
+  st128<CP_SC1>(r, pk_off(k8, b), hw);
+  st128<CP_SC1>(r, pk_off(k8, 8 + b), lw);
+}
+
+// Per-workgroup sums of squares: index 2l = the QKV input of layer l (2L:
+// the LM head's), 2l + 1 = the gate/up input of layer l.
+__device__ __forceinline__ float *ssq_at(const KP &P, int idx, int lam) {
+  return P.ssq + ((int64_t)idx * P.W + lam) * P.B;
+}
+
+// ---------------------------------------------------------------------------
+// row groups: up to 16 rows of one weight matrix at a fixed stride
+
+struct MbRg {
+  uint64_t base;  // address of the group's first row
+  int32_t nr;     // rows (0: none)
+  int32_t rs;     // bytes from one row to the next
+  int32_t o0;     // output index of the first row (QKV: RoPE pair index)
+};
+
+// The k-th run of at most 16 RoPE pairs of a QKV task that stays inside one
+// q/k/v head; returns its length (0 past the last) and its first pair.
+__device__ __forceinline__ int qkv_group(const KP &P, const Task &t, int k, int *p0) {
+  const int half = P.d >> 1;
+  int p = t.r0;
+  for (int i = 0; p < t.r1; ++i) {
+    const int n = min(16, min(t.r1, (p / half + 1) * half) - p);
+    if (i == k) { *p0 = p; return n; }
+    p += n;
+  }
+  *p0 = t.r1;
+  return 0;
+}
+
+// Row groups of a task: QKV and gate/up list (A, B) partners next to each
+// other (A = RoPE rows j / gate rows, B = rows j + d/2 / up rows).
+__device__ __forceinline__ int mb_nrg(const KP &P, const Task &t) {
+  const int rows = t.r1 - t.r0;
+  if (t.op == OP_QKV) {
+    int n = 0, p;
+    while (qkv_group(P, t, n, &p) > 0) ++n;
+    return 2 * n;
+  }
+  if (t.op == OP_GU) return 2 * ((rows + 15) >> 4);
+  return (rows + 15) >> 4;
+}
+
+__device__ __forceinline__ MbRg mb_rg(const KP &P, const Task &t, int j) {
+  const DevLayer &Lw = P.layers[min(t.layer, P.L - 1)];
+  const int h2 = P.h * 2;
+  if (t.op == OP_QKV) {
+    int p;
+    const int n = qkv_group(P, t, j >> 1, &p);
+    const int half = P.d >> 1, gh = p / half, g = gh / (P.G + 2), hh = gh % (P.G + 2);
+    const int jj = p % half + (j & 1) * half;
+    const uint16_t *m;
+    int64_t row;
+    if (hh < P.G) { m = (const uint16_t *)Lw.wq; row = (int64_t)(g * P.G + hh) * P.d + jj; }
+    else { m = (const uint16_t *)(hh == P.G ? Lw.wk : Lw.wv); row = (int64_t)g * P.d + jj; }
+    return MbRg{(uint64_t)(m + row * P.h), n, h2, p};
+  }
+  if (t.op == OP_GU) {
+    const int r = t.r0 + 16 * (j >> 1), n = max(0, min(16, t.r1 - r));
+    const uint16_t *m = (const uint16_t *)((j & 1) ? Lw.wu : Lw.wg);
+    return MbRg{(uint64_t)(m + (int64_t)r * P.h), n, h2, r};
+  }
+  const int r = t.r0 + 16 * j, n = max(0, min(16, t.r1 - r));
+  if (t.op == OP_OPROJ) {
+    const int K = P.Hq * P.d;
+    return MbRg{(uint64_t)((const uint16_t *)Lw.wo + (int64_t)r * K), n, K * 2, r};
+  }
+  if (t.op == OP_DOWN)
+    return MbRg{(uint64_t)((const uint16_t *)Lw.wd + (int64_t)r * P.ffn), n, P.ffn * 2, r};
+  return MbRg{(uint64_t)(P.lm_head + (int64_t)r * P.h), n, h2, r};  // OP_LM
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM stream of one batch of NB row groups.
+//
+// Split-K over the wavefronts: wavefront w takes 32-column blocks
+// [nkb * w / nw, nkb * (w + 1) / nw) of every row group of the batch.  Per
+// block it loads one 16-byte A fragment per row group (16 rows x 64 bytes,
+// streaming) and one B fragment (the 1 KB packed input block, device scope)
+// and issues NB MFMAs.  A ring of D blocks is kept in flight; the A
+// fragments of the first D blocks are issued before the dependency wait
+// (weights never wait for activations), the B fragments after it.  At the
+// end each wavefront folds hi + lo (lanes c and c + 8 of a 16-lane row) and
+// writes its 16 x B partials of every row group to
+// ys[((wave * NB + j) * 8 + b) * 16 + row].
+template <int NB, int D>
+__device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nrg, const uint8_t *act, int K,
+                                          const Waiter *wait, float *ys) {
+  const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
+  Rsrc ra[NB];
+  uint32_t vo[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    MbRg g{0, 0, 0, 0};
+    if (j0 + j < nrg) g = mb_rg(P, t, j0 + j);
+    const int nr = rfl(g.nr), rs = rfl(g.rs);
+    ra[j] = mkbuf64(rfl64(g.base), (uint32_t)(nr * rs));
+    // rows past nr fall outside the buffer and read 0
+    vo[j] = (uint32_t)((lane & 15) * rs + (lane >> 4) * 16);
+  }
+  const int nkb = K >> 5;
+  const int kb0 = nkb * wave / nw, n = nkb * (wave + 1) / nw - kb0;
+  const Rsrc rb = mkbuf(act, (uint32_t)nkb * 1024u);
+  const uint32_t bo = (uint32_t)lane * 16u;
+  v4i a[D][NB], bq[D];
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < n) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) a[s][j] = ld128s<CP_W>(ra[j], vo[j], (uint32_t)(kb0 + s) * 64u);
+    }
+  if (wait && !(*wait)(P)) return false;
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < n) bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)(kb0 + s) * 1024u);
+  auto consume = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = mfma_16x16x32(a[s][j], bq[s], acc[j]);
+  };
+  auto issue = [&](int s, int kb) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) a[s][j] = ld128s<CP_W>(ra[j], vo[j], (uint32_t)kb * 64u);
+    bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)kb * 1024u);
+  };
+  const int m = n >= D ? (n - D) / D : 0;  // rounds whose every issue lies inside the span
+  for (int q = 0; q < m; ++q) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      consume(s);
+      issue(s, kb0 + (q + 1) * D + s);
+    }
+  }
+  const int rem = n - m * D;  // 0 <= rem < 2D
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    if (s < rem) consume(s);
+    if (s + D < rem) issue(s, kb0 + (m + 1) * D + s);
+  }
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s + D < rem) consume(s);
+  const int c = lane & 15;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = acc[j][i] + dpp<0x128>(acc[j][i]);  // row_ror:8: hi + lo
+    if (c < P.B)
+      *reinterpret_cast<float4 *>(ys + ((wave * NB + j) * 8 + c) * 16 + 4 * (lane >> 4)) =
+          float4{v[0], v[1], v[2], v[3]};
+  }
+  return true;
+}
+
+// Output (row i of row group j, sequence b) of a batch of nb row groups:
+// the wavefronts' partials added in wavefront order.
+__device__ __forceinline__ float mb_y(const float *ys, int nb, int nw, int j, int b, int i) {
+  float v[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) v[w] = w < nw ? ys[((w * nb + j) * 8 + b) * 16 + i] : 0.f;
+  float y = 0.f;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) y += v[w];
+  return y;
+}
+
+// 1 / rms of each sequence's input from the producers' sums of squares
+// (wavefront b sums sequence b's W partials in workgroup order).
+__device__ __forceinline__ void mb_norm_scales(const KP &P, int idx, int K, float *rs) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  if (wave < P.B) {
+    float s = 0.f;
+    for (int w = lane; w < P.W; w += 64) s += ld_sc1(ssq_at(P, idx, w) + wave);
+    s = wave_sum(s);
+    if (lane == 0) rs[wave] = 1.0f / sqrtf(s / (float)K + P.eps);
+  }
+}
+
+__device__ __forceinline__ int mb_tok(const int *toks, int b) { return toks[b]; }
+
+// Buffer descriptors are scalar: every access below takes a per-workgroup
+// base and a per-lane byte offset (a per-lane base would make the compiler
+// loop over the lanes' distinct descriptors).
+
+__device__ __forceinline__ void bf8(v4i w, float (&o)[8]) {
+  o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+  o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
+}
+__device__ __forceinline__ void f8(v4i a, v4i c, float (&x)[8]) {
+  const float4 p = __builtin_bit_cast(float4, a), q = __builtin_bit_cast(float4, c);
+  x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w; x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+}
+// Rows r..r+7 of sequence b of a layer's [B][h] fp32 vector (device scope).
+__device__ __forceinline__ void ld8_vec(const KP &P, const float *vec, int b, int r, float (&x)[8]) {
+  const Rsrc rr = mkbuf(uni_ptr(vec), (uint32_t)P.B * P.h * 4);
+  const uint32_t o = ((uint32_t)b * P.h + r) * 4;
+  f8(ld128<CP_SC1>(rr, o), ld128<CP_SC1>(rr, o + 16), x);
+}
+__device__ __forceinline__ void st8_vec(const KP &P, float *vec, int b, int r, const float (&v)[8]) {
+  const Rsrc rr = mkbuf(uni_ptr(vec), (uint32_t)P.B * P.h * 4);
+  const uint32_t o = ((uint32_t)b * P.h + r) * 4;
+  st128<CP_SC1>(rr, o, __builtin_bit_cast(v4i, float4{v[0], v[1], v[2], v[3]}));
+  st128<CP_SC1>(rr, o + 16, __builtin_bit_cast(v4i, float4{v[4], v[5], v[6], v[7]}));
+}
+
+// The residual entering layer l at rows r..r+7 of sequence b.
+__device__ __forceinline__ void mb_x_in(const KP &P, int l, int b, int r, const int *toks, float (&x)[8]) {
+  if (l == 0) {
+    const Rsrc re = mkbuf(P.embed, (uint32_t)P.V * P.h * 2);
+    bf8(ld128<CP_DEF>(re, ((uint32_t)mb_tok(toks, b) * P.h + r) * 2), x);
+  } else {
+    ld8_vec(P, P.x_out + vec_off(P, l - 1, 0, P.h), b, r, x);
+  }
+}
+
+__device__ __forceinline__ void mb_gain8(const KP &P, const uint16_t *g, int r, float (&o)[8]) {
+  bf8(ld128<CP_DEF>(mkbuf(uni_ptr(g), (uint32_t)P.h * 2), (uint32_t)r * 2), o);
+}
+
+// LDS of the micro-batch GEMM tasks: ys[nw * 8 * 8 * 16] | rs[8] | ssq[8] |
+// per-thread partials[512].
+struct MbLds {
+  float *ys, *rs, *ssq, *ep;
+};
+__device__ __forceinline__ MbLds mb_lds(const KP &P, float *lds) {
+  float *ys = lds, *rs = ys + P.nw * 8 * 8 * 16;
+  return MbLds{ys, rs, rs + 8, rs + 16};
+}
+
+// One GEMM task: batches of up to 8 row groups, each streamed, reduced and
+// finished by its operator's epilogue.
+__device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int step, const int *toks, float *lds,
+                                        const Waiter &wait) {
+  const int l = t.layer, op = t.op, tid = threadIdx.x, T = P.nthr, nw = P.nw, B = P.B;
+  const MbLds M = mb_lds(P, lds);
+  const int nrg = rfl(mb_nrg(P, t));
+  const int nb = nrg <= 1 ? 1 : nrg <= 2 ? 2 : nrg <= 4 ? 4 : 8;
+  const uint8_t *act;
+  int K, nidx = -1;  // sums of squares this task's input is normalised with
+  if (op == OP_QKV) { act = pk_x(P, l); K = P.h; nidx = 2 * l; }
+  else if (op == OP_GU) { act = pk_m(P, l); K = P.h; nidx = 2 * l + 1; }
+  else if (op == OP_DOWN) { act = pk_u(P, l); K = P.ffn; }
+  else if (op == OP_OPROJ) { act = pk_o(P, l); K = P.Hq * P.d; }
+  else { act = pk_x(P, P.L); K = P.h; nidx = 2 * P.L; }
+  if (tid < 8) M.ssq[tid] = 0.f;
+  // LM: each sequence's running best, kept by wavefront b
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  bool nan = false;
+  bool waited = false;
+  for (int j0 = 0; j0 < max(nrg, 1); j0 += nb) {
+    const Waiter *wp = waited ? nullptr : &wait;
+    bool ok;
+    if (nb == 1) ok = mb_stream<1, 12>(P, t, j0, nrg, act, K, wp, M.ys);
+    else if (nb == 2) ok = mb_stream<2, 8>(P, t, j0, nrg, act, K, wp, M.ys);
+    else if (nb == 4) ok = mb_stream<4, 5>(P, t, j0, nrg, act, K, wp, M.ys);
+    else ok = mb_stream<8, 2>(P, t, j0, nrg, act, K, wp, M.ys);
+    if (!ok) return false;
+    if (!waited) {
+      if (nidx >= 0) mb_norm_scales(P, nidx, K, M.rs);
+      else if (tid < 8) M.rs[tid] = 1.f;
+      waited = true;
+    }
+    __syncthreads();
+    wait.mark(1);
+    const float *ys = M.ys;
+    switch (op) {
+      case OP_QKV: {
+        const int half = P.d >> 1;
+        for (int e = tid; e < (nb >> 1) * 16 * B; e += T) {
+          const int b = e % B, i = (e / B) % 16, k = e / (16 * B), jA = 2 * k;
+          if (j0 + jA >= nrg) continue;
+          int p;
+          const int n = qkv_group(P, t, (j0 + jA) >> 1, &p);
+          if (i >= n) continue;
+          p += i;
+          const int gh = p / half, g = gh / (P.G + 2), hh = gh % (P.G + 2), jj = p % half;
+          const float r = M.rs[b];
+          float a = r * mb_y(ys, nb, nw, jA, b, i), c = r * mb_y(ys, nb, nw, jA + 1, b, i);
+          const int pos = P.pos0v[b] + step;
+          if (hh <= P.G) {  // RoPE on q and k
+            const float cs = P.rope[(int64_t)pos * half + jj];
+            const float sn = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + jj];
+            const float a2 = a * cs - c * sn, c2 = c * cs + a * sn;
+            a = a2; c = c2;
+          }
+          if (hh < P.G) {
+            float *qd = P.q + vec_off(P, l, b, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
+            st_sc1(qd + jj, a);
+            st_sc1(qd + jj + half, c);
+          } else {  // the layer's K or V cache of every sequence under one descriptor each
+            const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
+            const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
+            const uint32_t o0 = (uint32_t)((((int64_t)b * P.Hkv + g) * P.max_ctx + pos) * P.d + jj) * 2;
+            if (hh == P.G) {
+              const Rsrc rr = mkbuf(P.kc + lbase, bytes);
+              st16<CP_SC1>(rr, o0, f2bf(a));
+              st16<CP_SC1>(rr, o0 + (uint32_t)half * 2, f2bf(c));
+            } else {
+              const Rsrc rv = mkbuf(P.vc + lbase, bytes);
+              st16<CP_SC1>(rv, o0, f2bf(a));
+              st16<CP_SC1>(rv, o0 + (uint32_t)half * 2, f2bf(c));
+            }
+          }
+        }
+        break;
+      }
+      case OP_GU: {
+        for (int e = tid; e < (nb >> 1) * 2 * B; e += T) {
+          const int b = e % B, o = (e / B) & 1, k = e / (2 * B), jA = 2 * k;
+          const int r0 = t.r0 + 16 * ((j0 + jA) >> 1) + 8 * o;
+          if (j0 + jA >= nrg || r0 >= t.r1) continue;
+          const float r = M.rs[b];
+          float u[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            u[i] = silu(r * mb_y(ys, nb, nw, jA, b, 8 * o + i)) * (r * mb_y(ys, nb, nw, jA + 1, b, 8 * o + i));
+          pk_store8(pk_u(P, l), P.ffn, r0 >> 3, b, u);
+        }
+        break;
+      }
+      case OP_OPROJ:
+      case OP_DOWN: {
+        const bool down = op == OP_DOWN;
+        const uint16_t *gain = !down ? (const uint16_t *)P.layers[l].ffn_norm
+                               : l + 1 < P.L ? (const uint16_t *)P.layers[l + 1].attn_norm : P.final_norm;
+        uint8_t *dst = down ? pk_x(P, l + 1) : pk_m(P, l);
+        const int ne = nb * 2 * B;
+        for (int e = tid; e < ne; e += T) {
+          const int b = e % B, o = (e / B) & 1, j = e / (2 * B);
+          const int r0 = t.r0 + 16 * (j0 + j) + 8 * o;
+          float sq = 0.f;
+          if (j0 + j < nrg && r0 < t.r1) {
+            float x[8], g[8];
+            if (down) ld8_vec(P, P.xmid + vec_off(P, l, 0, P.h), b, r0, x);
+            else mb_x_in(P, l, b, r0, toks, x);
+            mb_gain8(P, gain, r0, g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] += mb_y(ys, nb, nw, j, b, 8 * o + i);
+            st8_vec(P, (down ? P.x_out : P.xmid) + vec_off(P, l, 0, P.h), b, r0, x);
+            if (down && P.chk_hidden && l == P.L - 1) {
+              float *hd = P.chk_hidden + ((int64_t)step * P.B + b) * P.h + r0;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) hd[i] = x[i];
+            }
+            float xg[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { sq = fmaf(x[i], x[i], sq); xg[i] = x[i] * g[i]; }
+            pk_store8(dst, P.h, r0 >> 3, b, xg);
+          }
+          M.ep[e] = sq;
+        }
+        __syncthreads();
+        if (tid < B) {  // this batch's sums of squares, in row order
+          float s = M.ssq[tid];
+          for (int e = tid; e < ne; e += B) s += M.ep[e];
+          M.ssq[tid] = s;
+        }
+        break;
+      }
+      default: {  // OP_LM: wavefront b keeps sequence b's best
+        const int wave = wave_id(), lane = tid & 63;
+        if (wave < B) {
+          const int b = wave;
+          for (int e = lane; e < nb * 16; e += 64) {
+            const int j = e >> 4, i = e & 15, row = t.r0 + 16 * (j0 + j) + i;
+            if (j0 + j >= nrg || row >= t.r1) continue;
+            const float y = M.rs[b] * mb_y(ys, nb, nw, j, b, i);
+            if (y != y) nan = true;
+            else argmax_merge(bv, bi, y, row);
+            if (P.chk_logits) P.chk_logits[((int64_t)step * P.B + b) * P.V + row] = y;
+          }
+        }
+        break;
+      }
+    }
+    __syncthreads();  // ys is rewritten by the next batch
+  }
+  if (op == OP_LM) {
+    const int wave = wave_id(), lane = tid & 63;
+    if (wave < B) {
+      wave_argmax_l63(bv, bi);
+      const bool wn = __any(nan);
+      if (lane == 63) {
+        st_sc1(P.lmp + 2 * ((int64_t)lam * B + wave), wn ? __builtin_nanf("") : bv);
+        st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * ((int64_t)lam * B + wave) + 1, (uint32_t)bi);
+      }
+    }
+  } else if (op == OP_OPROJ || op == OP_DOWN) {
+    if (tid < B) st_sc1(ssq_at(P, op == OP_DOWN ? 2 * (l + 1) : 2 * l + 1, lam) + tid, M.ssq[tid]);
+  }
+  return true;
+}
+
+// Embedding rows [r0, r1) of every sequence's token, packed (times the
+// first layer's attention-norm gains) for the first QKV stage, with their
+// sums of squares.
+__device__ __forceinline__ bool mb_embed(const KP &P, const Task &t, int lam, const int *toks, float *lds) {
+  const int tid = threadIdx.x, B = P.B;
+  const MbLds M = mb_lds(P, lds);
+  const uint16_t *gain = (const uint16_t *)P.layers[0].attn_norm;
+  const int n8 = (t.r1 - t.r0) >> 3;
+  if (tid < 8) M.ssq[tid] = 0.f;
+  __syncthreads();
+  for (int e0 = 0; e0 < n8 * B; e0 += P.nthr) {
+    const int e = e0 + tid;
+    float sq = 0.f;
+    if (e < n8 * B) {
+      const int b = e % B, r0 = t.r0 + 8 * (e / B);
+      float x[8], g[8], xg[8];
+      mb_x_in(P, 0, b, r0, toks, x);
+      mb_gain8(P, gain, r0, g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { sq = fmaf(x[i], x[i], sq); xg[i] = x[i] * g[i]; }
+      pk_store8(pk_x(P, 0), P.h, r0 >> 3, b, xg);
+    }
+    M.ep[tid] = sq;
+    __syncthreads();
+    if (tid < B) {  // the threads whose element e0 + k belongs to sequence tid
+      float s = M.ssq[tid];
+      for (int k = (tid - e0 % B + B) % B; k < P.nthr; k += B) s += M.ep[k];
+      M.ssq[tid] = s;
+    }
+    __syncthreads();
+  }
+  if (tid < B) st_sc1(ssq_at(P, 0, lam) + tid, M.ssq[tid]);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Attention: this workgroup's share of KV head g over all sequences.
+//
+// Step positions: sequence b attends n_b = pos_b + 1 positions.  KV head g's
+// pairs (b, t) are numbered f = pre_b + t (pre_b = n_0 + .. + n_{b-1}) up to
+// N = sum n_b; workgroup i of the head's Tw takes f in
+// [i * N / Tw, (i + 1) * N / Tw).  Its piece of sequence b leaves a record
+// (m, l, -, -, o[d]) per query head at ((l * W + lambda) * B + b).
+
+__device__ __forceinline__ int64_t mb_share(int64_t N, int Tw, int i) { return (int64_t)i * N / Tw; }
+
+// Positions [t0, t0 + cnt) of sequence b (at most cmax of them), merged into
+// the running (max, sum, output) state of the piece kept in LDS; the last
+// sub-piece writes the piece's record.
+__device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, int g, int t0, int cnt, int pos,
+                                            float *lds, const Waiter *wait, bool first, bool last, bool &ok) {
+  const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr;
+  const int wave = wave_id(), nw = P.nw, lane = tid & 63;
+  const int cpad = ((P.cmax + 63) / 64) * 64;
+  float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
+  float *Or = st + 2 * G, *Mr = Or + G * d, *Lr = Mr + G;
+  const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * d;
+  const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * d * 2);
+  const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * d * 2);
+  const int LPP = d / 8, PPW = 64 / LPP, sub = lane % LPP, grp = lane / LPP;
+  const int PASS = nw * PPW;
+  auto koff = [=](int tt) { return (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2; };
+  v4i kb[APB], vb[APB];
+#pragma unroll
+  for (int p = 0; p < APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    const bool old = tt < cnt && t0 + tt != pos;
+    kb[p] = old ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
+    vb[p] = old ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
+  }
+  if (wait && !(*wait)(P)) { ok = false; return; }
+  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
+  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
+#pragma unroll
+  for (int p = 0; p < APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    if (tt < cnt && t0 + tt == pos) {
+      kb[p] = ld128<CP_SC1>(kr, koff(tt));
+      vb[p] = ld128<CP_SC1>(vr, koff(tt));
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < cnt; base += APB * PASS) {
+    if (base > 0) {
+#pragma unroll
+      for (int p = 0; p < APB; ++p) {
+        const int tt = base + p * PASS + wave * PPW + grp;
+        kb[p] = tt < cnt ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < APB; ++p) {
+      const int tt = base + p * PASS + wave * PPW + grp;
+      if (base + p * PASS < cnt) {
+        for (int hh = 0; hh < G; ++hh) {
+          const float4 *q4 = reinterpret_cast<const float4 *>(qs + hh * d + sub * 8);
+          float s = dot8_bf16(kb[p], q4[0], q4[1], 0.f);
+          s = (LPP == 16) ? sum16(s) : sum8(s);
+          if (tt < cnt && sub == 0) sc[hh * cpad + tt] = s;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int hh = wave; hh < G; hh += nw) {
+    float m = -INFINITY;
+    for (int i = lane; i < cnt; i += 64) m = fmaxf(m, sc[hh * cpad + i]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int i = lane; i < cnt; i += 64) {
+      const float e = expf(sc[hh * cpad + i] - m);
+      sc[hh * cpad + i] = e;
+      s += e;
+    }
+    s = wave_sum(s);
+    if (lane == 0) { st[2 * hh] = m; st[2 * hh + 1] = s; }
+  }
+  __syncthreads();
+  float acc[8][8];
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  for (int base = 0; base < cnt; base += APB * PASS) {
+    if (base > 0) {
+#pragma unroll
+      for (int p = 0; p < APB; ++p) {
+        const int tt = base + p * PASS + wave * PPW + grp;
+        vb[p] = tt < cnt ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < APB; ++p) {
+      const int tt = base + p * PASS + wave * PPW + grp;
+      if (tt < cnt) {
+        const v4i vw = vb[p];
+        const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
+                            bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh)
+          if (hh < G) {
+            const float pr = sc[hh * cpad + tt];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, v[e], acc[hh][e]);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh)
+    if (hh < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[hh][e];
+        if (LPP == 8) v += dpp<0x128>(v);  // row_ror:8
+        acc[hh][e] = xrow_sum(v);
+      }
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh)
+      if (hh < G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ored[(wave * G + hh) * d + sub * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  const int rec = d + PREC_O;
+  float *pdst = P.part + (((int64_t)l * P.W + lam) * P.B + b) * G * rec;
+  for (int i = tid; i < G * d; i += T) {
+    const int hh = i / d, j = i % d;
+    float s = 0.f;
+    float ov[MAXW];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) s += ov[w];
+    if (!first) {
+      const float m = st[2 * hh], M = fmaxf(Mr[hh], m);
+      s = Or[i] * expf(Mr[hh] - M) + s * expf(m - M);
+    }
+    Or[i] = s;
+    if (last) st_sc1(pdst + hh * rec + PREC_O + j, s);
+  }
+  __syncthreads();
+  for (int hh = tid; hh < G; hh += T) {
+    float m = st[2 * hh], ls = st[2 * hh + 1];
+    if (!first) {
+      const float M = fmaxf(Mr[hh], m);
+      ls = Lr[hh] * expf(Mr[hh] - M) + ls * expf(m - M);
+      m = M;
+    }
+    Mr[hh] = m;
+    Lr[hh] = ls;
+    if (last) {
+      st_sc1(pdst + hh * rec, m);
+      st_sc1(pdst + hh * rec + 1, ls);
+    }
+  }
+  __syncthreads();  // the LDS is reused by the next sub-piece
+}
+
+__device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int step, float *lds,
+                                        const Waiter &wait) {
+  const int g = t.aux, i = t.r0, Tw = t.r1;
+  int64_t N = 0;
+  for (int b = 0; b < P.B; ++b) N += P.pos0v[b] + step + 1;
+  const int64_t f0 = mb_share(N, Tw, i), f1 = mb_share(N, Tw, i + 1);
+  bool ok = true, first = true;
+  int64_t pre = 0;
+  for (int b = 0; b < P.B && ok; ++b) {
+    const int pos = P.pos0v[b] + step;
+    const int64_t lo = max(f0, pre), hi = min(f1, pre + pos + 1);
+    // the piece in sub-pieces of at most cmax positions
+    for (int64_t c0 = lo; c0 < hi && ok; c0 += P.cmax) {
+      const int n = (int)min((int64_t)P.cmax, hi - c0);
+      mb_attn_sub(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, first ? &wait : nullptr, c0 == lo,
+                  c0 + n == hi, ok);
+      first = false;
+    }
+    pre += pos + 1;
+  }
+  if (first && ok) ok = wait(P);  // no piece: still ordered after the producers
+  return ok;
+}
+
+// Combine: elements [r0, r1) of KV head g's (sequence, query head, dim)
+// space, 8 dims per group of 32 lanes.  The lanes of a group take the
+// records of the sequence's workgroups (lane r: the r-th, r + 32-th, ...),
+// merge them pairwise with the running-max rescaling, and reduce across the
+// group; lane 0 packs the 8 outputs for the O projection.
+__device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const Waiter &wait) {
+  if (!wait(P)) return false;
+  const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = threadIdx.x;
+  const int rec = d + PREC_O, gd = G * d;
+  const int ngr = (t.r1 - t.r0) >> 3, gpp = P.nthr >> 5;
+  int64_t N = 0;
+  for (int b = 0; b < P.B; ++b) N += P.pos0v[b] + step + 1;
+  for (int q0 = 0; q0 < ngr; q0 += gpp) {
+    const int grp = q0 + (tid >> 5), sub = tid & 31;
+    const bool act = grp < ngr;
+    const int e = t.r0 + 8 * grp, b = act ? e / gd : 0, k = e % gd, hh = k / d, j0 = k % d;
+    int64_t pre = 0;
+    for (int bb = 0; bb < b; ++bb) pre += P.pos0v[bb] + step + 1;
+    const int64_t nb = P.pos0v[b] + step + 1;
+    // workgroups holding f = pre and f = pre + nb - 1
+    const int i_lo = (int)(((pre + 1) * Tw - 1) / N), i_hi = (int)(((pre + nb) * Tw - 1) / N);
+    // the layer's records under one descriptor; record (wg, b, hh) at a per-lane offset
+    const Rsrc rr = mkbuf(P.part + (int64_t)l * P.W * P.B * G * rec, (uint32_t)P.W * P.B * G * rec * 4);
+    float M = -INFINITY, Ls = 0.f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = i_lo + sub; act && i <= i_hi; i += 32) {
+      if (mb_share(N, Tw, i) >= mb_share(N, Tw, i + 1)) continue;  // empty share: no record
+      const uint32_t ro = (uint32_t)((((g * Tw + i) * P.B + b) * G + hh) * rec) * 4;
+      const float4 ml = __builtin_bit_cast(float4, ld128<CP_SC1>(rr, ro));
+      const float4 oa = __builtin_bit_cast(float4, ld128<CP_SC1>(rr, ro + (PREC_O + j0) * 4));
+      const float4 ob = __builtin_bit_cast(float4, ld128<CP_SC1>(rr, ro + (PREC_O + j0 + 4) * 4));
+      const float m = ml.x, ls = ml.y;
+      const float o[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+      const float Mn = fmaxf(M, m);
+      const float a = M == -INFINITY ? 0.f : expf(M - Mn), c = expf(m - Mn);
+      Ls = Ls * a + ls * c;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) O[q] = O[q] * a + o[q] * c;
+      M = Mn;
+    }
+#pragma unroll
+    for (int x = 16; x >= 1; x >>= 1) {  // across the 32 lanes of the group
+      const float Mo = __shfl_xor(M, x), Lo = __shfl_xor(Ls, x);
+      float Oo[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Oo[q] = __shfl_xor(O[q], x);
+      const float Mn = fmaxf(M, Mo);
+      const float a = M == -INFINITY ? 0.f : expf(M - Mn), c = Mo == -INFINITY ? 0.f : expf(Mo - Mn);
+      Ls = Ls * a + Lo * c;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) O[q] = O[q] * a + Oo[q] * c;
+      M = Mn;
+    }
+    if (act && sub == 0) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = O[q] / Ls;
+      pk_store8(pk_o(P, l), P.Hq * d, ((g * G + hh) * d + j0) >> 3, b, v);
+    }
+  }
+  return true;
+}
+
+// Each sequence's greedy token from the W partials (wavefront b reads
+// sequence b's); toks[b] = -1 on NaN.
+__device__ __forceinline__ void mb_reduce(const KP &P, int *toks) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  __syncthreads();
+  if (wave < P.B) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    bool nan = false;
+    for (int i = lane; i < P.W; i += 64) {
+      const int64_t o = 2 * ((int64_t)i * P.B + wave);
+      const float v = ld_sc1(P.lmp + o);
+      const int ix = (int)ld_flag(reinterpret_cast<const uint32_t *>(P.lmp) + o + 1);
+      if (v != v) nan = true;
+      else argmax_merge(bv, bi, v, ix);
+    }
+    wave_argmax_l63(bv, bi);
+    const bool anynan = __any(nan);
+    if (lane == 63) toks[wave] = anynan ? -1 : bi;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool mb_run_task(const Task &t, int lam, int step, const int *toks, float *lds,
+                                            const Waiter &wait) {
+  const KP &P = kp_fresh();
+  switch (t.op) {
+    case OP_EMBED: return mb_embed(P, t, lam, toks, lds);
+    case OP_ATTN: return mb_attn(P, t, lam, step, lds, wait);
+    case OP_COMB: return mb_comb(P, t, step, wait);
+    default: return mb_gemm(P, t, lam, step, toks, lds, wait);
+  }
+}
+
+// The micro-batch resident kernel (and, with P.persistent = 0, its
+// per-operator baseline: one stage of one step per launch).
+extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ int sh[8];
+  __shared__ int toks[8];
+  const bool res = P.persistent != 0;
+  const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
+  const int tid = threadIdx.x;
+  if (res && tid == 0) {
+    const uint32_t x = xcc_id();
+    P.xcc[lam] = x;
+    if (P.W % P.X == 0 && (int)x != (int)(blockIdx.x % P.X))
+      __hip_atomic_fetch_add(&P.status->xcc_mismatch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int s_begin = res ? 0 : P.b_step, s_end = res ? P.n_steps : P.b_step + 1;
+  const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
+  if (tid < P.B) {  // the first step's tokens (the baseline: its step's)
+    const int s = s_begin;
+    toks[tid] = P.forced ? P.forced[(int64_t)s * P.B + tid] : (s == 0 ? P.in_tok[tid] : P.tok_slot[tid]);
+  }
+  __syncthreads();
+  for (int s = s_begin; s < s_end; ++s) {
+    const uint32_t ep = P.epoch_base + (uint32_t)s + 1u;
+    if (res && P.forced && tid < P.B) toks[tid] = P.forced[(int64_t)s * P.B + tid];
+    __syncthreads();
+    int bad = 0, badtok = 0;
+    for (int b = 0; b < P.B; ++b)
+      if (toks[b] < 0 || toks[b] >= P.V) { bad = 1; badtok = toks[b]; }
+    if (bad) {
+      if (tid == 0) latch_error(P, PRE_DEV_BAD_TOKEN, s, -1, -1, (uint32_t)badtok, 0);
+      return;
+    }
+    for (int si = si0; si < si1; ++si) {
+      const Task t = P.tasks[(int64_t)si * P.W + lam];
+      const int tr = res && P.trace != nullptr;
+      const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
+      const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
+      if (!mb_run_task(t, lam, s, toks, lds, wait)) return;
+      if (res) {
+        signal_slot(P, t.signal, ep, false);
+        if (tr) trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
+      }
+    }
+    if (!res) return;
+    const bool need = (!P.forced && s + 1 < P.n_steps) || lam == 0;
+    if (need) {
+      const int s_lm = P.n_si - 1;
+      if (!wait_slots(P, s_lm * P.W, (s_lm + 1) * P.W, ep, s, s_lm, sh)) return;
+      mb_reduce(P, toks);
+      for (int b = 0; b < P.B; ++b)
+        if (toks[b] < 0) {
+          if (tid == 0) latch_error(P, PRE_DEV_NAN, s, s_lm, -1, 0, 0);
+          return;
+        }
+      if (lam == 0 && tid < P.B) P.out_tok[(int64_t)s * P.B + tid] = toks[tid];
+      __syncthreads();
+    }
+  }
+}
+
+// Baseline: each sequence's greedy token of step `step` (one workgroup).
+extern "C" __global__ void __launch_bounds__(512) pre_k_argmax_mb(KP P, int step) {
+  __shared__ int toks[8];
+  mb_reduce(P, toks);
+  if (threadIdx.x < P.B) {
+    const int nt = toks[threadIdx.x];
+    if (nt < 0) latch_error(P, PRE_DEV_NAN, step, P.n_si - 1, -1, 0, 0);
+    P.tok_slot[threadIdx.x] = nt < 0 ? 0 : nt;
+    P.out_tok[(int64_t)step * P.B + threadIdx.x] = nt;
+  }
+}
+
+// Debug: D = A (16 x 32) * B (32 x 16) through mfma_16x16x32 with the lane
+// layout the GEMM stream assumes (A, B row-major bf16; D row-major fp32).
+extern "C" __global__ void pre_k_mfma_probe(const uint16_t *A, const uint16_t *Bm, float *Dm) {
+  const int l = threadIdx.x & 63, r = l & 15, kq = l >> 4;
+  v4i a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (int)((uint32_t)A[r * 32 + kq * 8 + 2 * i] | ((uint32_t)A[r * 32 + kq * 8 + 2 * i + 1] << 16));
+    b[i] = (int)((uint32_t)Bm[(kq * 8 + 2 * i) * 16 + r] | ((uint32_t)Bm[(kq * 8 + 2 * i + 1) * 16 + r] << 16));
+  }
+  const f32x4_t d = mfma_16x16x32(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Dm[(4 * kq + i) * 16 + r] = d[i];
+}

@@ -29,8 +29,12 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (c->head_dim != 64 && c->head_dim != 128) return PRE_ERR_SHAPE;
   if (c->hidden % 8 || (c->n_q_heads * c->head_dim) % 8) return PRE_ERR_SHAPE;
   if (c->batch > 8) return PRE_ERR_SHAPE;
-  if (c->batch != 1) return PRE_ERR_UNSUPPORTED;
   const bool moe = c->n_experts > 0;
+  const bool mb = c->batch > 1;
+  // micro-batch: dense models whose GEMM inputs come in whole 32-column
+  // blocks of the packed MFMA layout
+  if (mb && (moe || c->hidden % 32 || c->ffn_dim % 32 || (c->n_q_heads * c->head_dim) % 32))
+    return PRE_ERR_UNSUPPORTED;
   if (moe) {
     if (c->expert_dtype != 1 || c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 16 ||
         c->n_shared < 0 || c->n_shared > 4 || c->expert_ffn < 16 || c->expert_ffn % 16 ||
@@ -42,6 +46,7 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   D->L = c->n_layers; D->h = c->hidden; D->Hq = c->n_q_heads; D->Hkv = c->n_kv_heads;
   D->d = c->head_dim; D->ffn = c->ffn_dim; D->V = c->vocab; D->B = c->batch;
   D->max_ctx = c->max_ctx;
+  D->mb = mb;
   D->E = moe ? c->n_experts : 0; D->top_k = moe ? c->top_k : 0;
   D->n_shared = moe ? c->n_shared : 0; D->effn = moe ? c->expert_ffn : 0; D->moe = moe;
   D->G = c->n_q_heads / c->n_kv_heads;
@@ -65,8 +70,11 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   }
   if (D->W < 1 || D->W > 4096) return PRE_ERR_SHAPE;
   D->X = 8;
-  const int bg = D->B * D->Hkv;
+  const int bg = mb ? D->Hkv : D->B * D->Hkv;
   if (D->Hkv > 8 || D->W < bg) return PRE_ERR_SHAPE;
+  // micro-batch: the attention work of KV head g lies on workgroups
+  // [g * W / Hkv, (g + 1) * W / Hkv)
+  if (mb && D->W % D->Hkv) return PRE_ERR_SHAPE;
   D->Tg = D->W / bg;
   // KV head g's QKV pairs, attention chunks and O-projection slice occupy
   // lambdas [g * W/8, (g + 1) * W/8): one XCD, when there are 8 KV heads and
@@ -75,17 +83,23 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // about 128 positions per attention chunk at the longest context, at most
   // one chunk per workgroup of the (sequence, KV head)'s share
   D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 128)));
+  if (mb) D->NC = 1;  // the micro-batch attention split follows the contexts of each step
   if (D->NC > D->Tg) return PRE_ERR_SHAPE;
   D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
   if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
-  D->stages_per_layer = moe ? 6 : 5;
-  D->n_si = D->L * D->stages_per_layer + 1;
+  D->stages_per_layer = (moe || mb) ? 6 : 5;
+  // micro-batch: an embedding stage first, then per layer QKV, ATTN, COMB,
+  // OPROJ, GU, DOWN, then the LM head
+  D->n_si = D->L * D->stages_per_layer + (mb ? 2 : 1);
   // longest staged GEMV input; the fp8 expert-down chunks of the last slot
   // read up to (slots - 1) * effn + effn rounded up to whole 1024-column chunks
   const int nk = D->top_k + D->n_shared;
   D->kmax = pad_to(std::max({D->h, D->Hq * D->d, D->F, moe ? D->E : 0,
                              moe ? (nk - 1) * D->effn + pad_to(D->effn, 1024) : 0}), 1024);
-  D->cmax = cdiv(D->max_ctx, D->NC);
+  // micro-batch: a workgroup's share of one KV head's positions of all sequences
+  // (in sub-pieces of at most 16K / G positions: the scores stay within 64 KB of LDS)
+  D->cmax = mb ? std::min(cdiv(D->B * D->max_ctx, D->Tg) + 1, std::max(64, 16384 / D->G))
+               : cdiv(D->max_ctx, D->NC);
   const int waves = D->threads / 64;
   {
     // results (2 per row pair) of the largest task of any GEMV stage
@@ -107,6 +121,13 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   int64_t gemv = (int64_t)D->segoff + 80 * 12;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
+  if (mb) {
+    // MFMA stages: per-wavefront partials of up to 8 row groups x 8 sequences
+    // x 16 rows, the sequences' norm scales and sums, per-thread partials;
+    // attention: the running state of a piece (output, max, sum)
+    gemv = (int64_t)waves * 8 * 8 * 16 + 1024;
+    attn += (int64_t)D->G * D->d + 4 * D->G;
+  }
   D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);
   if (D->lds_bytes > 160 * 1024) return PRE_ERR_SHAPE;
   D->eps = c->rms_eps;
@@ -134,7 +155,19 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->x_emb = take((int64_t)D.B * D.h * f);
   Lo->a_norm = take((int64_t)D.B * D.kmax * f);
   Lo->tok = take((int64_t)D.B * 4 * 4);
-  Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers)
+  Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers, micro-batch)
+  if (D.mb) {
+    // packed bf16 hi/lo GEMM inputs: 1 KB per 32 columns; per layer the QKV
+    // input (plus the LM head's), the gate/up input, the down input and the
+    // O-projection input
+    const int64_t kh = D.h / 32 * 1024, kf = (int64_t)D.ffn / 32 * 1024, ko = (int64_t)D.Hq * D.d / 32 * 1024;
+    Lo->pk = take((2 * (int64_t)D.L + 1) * kh + D.L * (kf + ko));
+    Lo->ssq = take((2 * (int64_t)D.L + 1) * D.W * D.B * f);
+    // attention records of every (workgroup, sequence) of a layer
+    Lo->part = take((int64_t)D.L * D.W * D.B * D.G * (D.d + 4) * f);
+  } else {
+    Lo->pk = Lo->ssq = 0;
+  }
   Lo->total = off;
 }
 
@@ -146,7 +179,86 @@ static inline void split(int64_t n, int W, int t, int32_t *lo, int32_t *hi) {
 
 static inline int32_t slot(const Dims &D, int si, int i) { return si * D.W + i; }
 
+// Balanced split of n items (a multiple of 8) in whole groups of 8.
+static inline void split8(int64_t n, int W, int t, int32_t *lo, int32_t *hi) {
+  const int64_t u = n / 8;
+  *lo = (int32_t)(8 * (u * t / W));
+  *hi = (int32_t)(8 * (u * (t + 1) / W));
+}
+
+// Micro-batch table.  Per step: EMBED; per layer QKV, ATTN, COMB, OPROJ,
+// GU, DOWN; LM.  Every stage has one task per workgroup.  KV head g's QKV
+// rows, attention share and combine lie on workgroups [g * Tw, (g + 1) * Tw)
+// (Tw = W / Hkv, lambda XCD-major), the other stages split rows evenly.
+static void build_tasks_mb(const Dims &D, std::vector<Task> &T) {
+  const int W = D.W, Tw = D.Tg;
+  T.assign((size_t)D.n_si * W, Task{});
+  auto at = [&](int si, int lam) -> Task & { return T[(size_t)si * W + lam]; };
+  auto all = [&](Task &t, int si_prod) { t.wait_lo = slot(D, si_prod, 0); t.wait_hi = slot(D, si_prod, W); };
+  const int P = D.qkv_pairs, PG = P / D.Hkv;
+  for (int lam = 0; lam < W; ++lam) {
+    Task &t = at(0, lam);
+    t.op = OP_EMBED; t.layer = 0;
+    split8(D.h, W, lam, &t.r0, &t.r1);
+    t.wait_lo = t.wait_hi = 0;  // the step's tokens are known to every workgroup
+    t.signal = slot(D, 0, lam);
+  }
+  for (int l = 0; l < D.L; ++l) {
+    const int s_q = 1 + 6 * l, s_a = s_q + 1, s_c = s_q + 2, s_o = s_q + 3, s_gu = s_q + 4, s_dn = s_q + 5;
+    for (int lam = 0; lam < W; ++lam) {
+      Task &q = at(s_q, lam);
+      q.op = OP_QKV; q.layer = l;
+      split(P, W, lam, &q.r0, &q.r1);
+      all(q, s_q - 1);  // EMBED or the previous layer's DOWN
+      q.signal = slot(D, s_q, lam);
+      const int g = lam / Tw, i = lam % Tw;
+      Task &a = at(s_a, lam);
+      a.op = OP_ATTN; a.layer = l; a.aux = g; a.r0 = i; a.r1 = Tw;
+      int lo = -1, hi = -1;  // QKV tasks whose pairs meet KV head g's
+      for (int w = 0; w < W; ++w) {
+        int32_t x0, x1;
+        split(P, W, w, &x0, &x1);
+        if (x0 < x1 && x0 < (g + 1) * PG && x1 > g * PG) {
+          if (lo < 0) lo = w;
+          hi = w + 1;
+        }
+      }
+      a.wait_lo = slot(D, s_q, lo); a.wait_hi = slot(D, s_q, hi);
+      a.signal = slot(D, s_a, lam);
+      Task &c = at(s_c, lam);
+      c.op = OP_COMB; c.layer = l; c.aux = g;
+      split8((int64_t)D.B * D.G * D.d, Tw, i, &c.r0, &c.r1);
+      c.wait_lo = slot(D, s_a, g * Tw); c.wait_hi = slot(D, s_a, (g + 1) * Tw);
+      c.signal = slot(D, s_c, lam);
+      Task &o = at(s_o, lam);
+      o.op = OP_OPROJ; o.layer = l; o.aux = -1;
+      split8(D.h, W, lam, &o.r0, &o.r1);
+      all(o, s_c);
+      o.signal = slot(D, s_o, lam);
+      Task &gu = at(s_gu, lam);
+      gu.op = OP_GU; gu.layer = l;
+      split8(D.ffn, W, lam, &gu.r0, &gu.r1);
+      all(gu, s_o);
+      gu.signal = slot(D, s_gu, lam);
+      Task &dn = at(s_dn, lam);
+      dn.op = OP_DOWN; dn.layer = l;
+      split8(D.h, W, lam, &dn.r0, &dn.r1);
+      all(dn, s_gu);
+      dn.signal = slot(D, s_dn, lam);
+    }
+  }
+  const int s_lm = D.n_si - 1;
+  for (int lam = 0; lam < W; ++lam) {
+    Task &t = at(s_lm, lam);
+    t.op = OP_LM; t.layer = D.L;
+    split(D.V, W, lam, &t.r0, &t.r1);
+    all(t, s_lm - 1);
+    t.signal = slot(D, s_lm, lam);
+  }
+}
+
 void build_tasks(const Dims &D, std::vector<Task> &T) {
+  if (D.mb) { build_tasks_mb(D, T); return; }
   const int W = D.W, spl = D.stages_per_layer;
   T.assign((size_t)D.n_si * W, Task{});
   auto at = [&](int si, int lam) -> Task & { return T[(size_t)si * W + lam]; };
@@ -247,6 +359,12 @@ void build_tasks(const Dims &D, std::vector<Task> &T) {
 
 // Expected op of a stage instance.
 static int32_t op_of_stage(const Dims &D, int si) {
+  if (D.mb) {
+    static const int32_t mbs[6] = {OP_QKV, OP_ATTN, OP_COMB, OP_OPROJ, OP_GU, OP_DOWN};
+    if (si == 0) return OP_EMBED;
+    if (si == D.n_si - 1) return OP_LM;
+    return mbs[(si - 1) % 6];
+  }
   if (si == D.L * D.stages_per_layer) return OP_LM;
   const int k = si % D.stages_per_layer;
   static const int32_t dense[5] = {OP_QKV, OP_ATTN, OP_OPROJ, OP_GU, OP_DOWN};
@@ -275,7 +393,84 @@ static int64_t coverage_target(const Dims &D, int32_t op) {
 //  (sequence, KV head) has each chunk exactly once; 7 every consumer waits on
 //  all producers of its input; 8 every workgroup takes part in every GEMV
 //  stage (this orders slot reuse across steps); 9 layer numbers.
+// The micro-batch table: checks 1-4 and 9 as below; 5 row coverage (in
+// whole groups of 8 where the output is packed) and the combine's element
+// coverage per KV head; 6 every KV head has Tw attention tasks numbered
+// 0..Tw-1; 7 producer sets; 8 no empty task slot.
+static int validate_mb(const Dims &D, const std::vector<Task> &T) {
+  const int W = D.W, n_slots = D.n_si * W, Tw = D.Tg;
+  if ((int64_t)T.size() != (int64_t)D.n_si * W) return 1;
+  for (int si = 0; si < D.n_si; ++si)
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      if (t.op == OP_NONE) return 8;
+      if (t.op != op_of_stage(D, si)) return 2;
+      if (t.signal != si * W + lam) return 4;
+      if (t.wait_lo < 0 || t.wait_hi < t.wait_lo || t.wait_hi > si * W) return 3;
+      const int want_layer = si == 0 ? 0 : (t.op == OP_LM ? D.L : (si - 1) / 6);
+      if (t.layer != want_layer) return 9;
+    }
+  const int PG = D.qkv_pairs / D.Hkv;
+  for (int si = 0; si < D.n_si; ++si) {
+    const int32_t op = op_of_stage(D, si);
+    const Task *row = &T[(size_t)si * W];
+    if (op == OP_ATTN) {
+      for (int lam = 0; lam < W; ++lam)
+        if (row[lam].aux != lam / Tw || row[lam].r0 != lam % Tw || row[lam].r1 != Tw) return 6;
+      continue;
+    }
+    if (op == OP_COMB) {
+      const int64_t n = (int64_t)D.B * D.G * D.d;
+      for (int g = 0; g < D.Hkv; ++g) {
+        int64_t next = 0;
+        for (int i = 0; i < Tw; ++i) {
+          const Task &t = row[g * Tw + i];
+          if (t.aux != g || t.r0 != next || t.r1 < t.r0 || t.r0 % 8 || t.r1 % 8) return 5;
+          next = t.r1;
+        }
+        if (next != n) return 5;
+      }
+      continue;
+    }
+    const int64_t n = op == OP_EMBED || op == OP_OPROJ || op == OP_DOWN ? D.h
+                      : op == OP_GU ? D.ffn : op == OP_QKV ? D.qkv_pairs : D.V;
+    const bool by8 = op != OP_QKV && op != OP_LM;
+    int64_t next = 0;
+    for (int lam = 0; lam < W; ++lam) {  // contiguous, in workgroup order
+      const Task &t = row[lam];
+      if (t.r0 != next || t.r1 < t.r0 || (by8 && (t.r0 % 8 || t.r1 % 8))) return 5;
+      next = t.r1;
+    }
+    if (next != n) return 5;
+  }
+  for (int si = 0; si < D.n_si; ++si) {
+    const int32_t op = op_of_stage(D, si);
+    for (int lam = 0; lam < W; ++lam) {
+      const Task &t = T[(size_t)si * W + lam];
+      bool ok = true;
+      if (op == OP_EMBED) {
+        ok = t.wait_lo == t.wait_hi;
+      } else if (op == OP_ATTN) {
+        const int g = t.aux;
+        for (int q = 0; q < W && ok; ++q) {
+          const Task &p = T[(size_t)(si - 1) * W + q];
+          if (p.r0 < p.r1 && p.r0 < (g + 1) * PG && p.r1 > g * PG)
+            ok = t.wait_lo <= (si - 1) * W + q && t.wait_hi > (si - 1) * W + q;
+        }
+      } else if (op == OP_COMB) {
+        ok = t.wait_lo <= (si - 1) * W + t.aux * Tw && t.wait_hi >= (si - 1) * W + (t.aux + 1) * Tw;
+      } else {
+        ok = t.wait_lo <= (si - 1) * W && t.wait_hi >= si * W;
+      }
+      if (!ok) return 7;
+    }
+  }
+  (void)n_slots;
+  return 0;
+}
+
 int validate(const Dims &D, const std::vector<Task> &T) {
+  if (D.mb) return validate_mb(D, T);
   const int W = D.W, n_slots = D.n_si * W;
   if ((int64_t)T.size() != (int64_t)D.n_si * W) return 1;
   std::vector<int> setter_si(n_slots, -1);

@@ -32,13 +32,15 @@ enum Op : int32_t {
   OP_EGU = 7,    // expert gate/up row pairs (slot k of the chosen experts)
   OP_EDOWN = 8,  // expert down rows summed over chosen experts + residual
   OP_LM = 9,     // LM-head rows + per-task argmax
+  OP_EMBED = 10, // micro-batch: embedding rows of every sequence, packed for the QKV stage
+  OP_COMB = 11,  // micro-batch: attention chunk combine of one KV head, packed for the O projection
 };
 
 // One task: 8 x int32 = 32 bytes.
 struct Task {
   int32_t op, layer;
   int32_t r0, r1;     // row / pair range [r0, r1); ATTN: r0 = chunk, r1 = chunks
-  int32_t aux;        // ATTN, OPROJ: sequence * n_kv_heads + kv head
+  int32_t aux;        // ATTN, OPROJ: sequence * n_kv_heads + kv head (micro-batch ATTN, COMB: kv head)
   int32_t wait_lo, wait_hi;  // ready slots [lo, hi) that must reach this step's epoch
   int32_t signal;     // slot set to the epoch when done (ATTN: set by the combiner)
 };
@@ -65,6 +67,7 @@ struct DevStatus {
 struct Layout {
   int64_t status, flags, layers, tasks, rope, xcc;
   int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid;
+  int64_t pk, ssq;  // micro-batch: packed GEMM inputs, per-workgroup sums of squares
   int64_t total;
 };
 
@@ -75,14 +78,15 @@ struct Dims {
   int32_t G;          // query heads per KV head
   int32_t qkv_pairs;  // RoPE pairs of all QKV rows: Hkv * (G + 2) * d / 2
   int32_t F;          // width of the FFN activation slot (ffn or (top_k+n_shared)*effn)
+  int32_t mb;         // micro-batch path (batch > 1): MFMA GEMM stages, balanced attention
   int32_t W, X, NC;   // workgroups, XCDs, attention chunks per (sequence, KV head)
   int32_t local;      // QKV->attention->O-projection hand-offs stay inside one XCD's L2
-  int32_t Tg;         // workgroups per (sequence, KV head): W / (batch * n_kv_heads)
+  int32_t Tg;         // workgroups per (sequence, KV head): W / (batch * n_kv_heads); micro-batch: per KV head
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded
   int32_t ymax;       // most GEMV results one task produces (x waves: LDS partials)
   int32_t segoff;     // LDS float offset of the GEMV segment table (room for the chunk combine before it)
-  int32_t cmax;       // longest attention chunk (positions)
+  int32_t cmax;       // longest attention chunk (positions; micro-batch: longest piece of one workgroup)
   int32_t lds_bytes;  // dynamic LDS per workgroup
   float eps, theta;
 };

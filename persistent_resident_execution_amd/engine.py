@@ -104,11 +104,14 @@ def lib():
         L.pre_plan_validate.argtypes = [C.POINTER(Config), vp, i32]
         L.pre_step_bytes.restype = C.c_int64
         L.pre_step_bytes.argtypes = [C.POINTER(Config), C.POINTER(i32)]
-        L.pre_debug_fp8_decode.argtypes = [vp, vp, C.c_int, vp]
-        L.pre_debug_layout.argtypes = [vp, vp]
-        L.pre_debug_lane_ops.argtypes = [vp, vp, vp]
-        L.pre_debug_gemv.argtypes = [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp]
-        L.pre_debug_copy.argtypes = [vp, vp, C.c_size_t, vp]
+        # debug entries (not part of the C ABI header)
+        debug = {"pre_debug_fp8_decode": [vp, vp, C.c_int, vp], "pre_debug_layout": [vp, vp],
+                 "pre_debug_lane_ops": [vp, vp, vp],
+                 "pre_debug_gemv": [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp],
+                 "pre_debug_copy": [vp, vp, C.c_size_t, vp], "pre_debug_mfma": [vp, vp, vp, vp]}
+        for name, at in debug.items():
+            if hasattr(L, name):
+                getattr(L, name).argtypes = at
         _lib = L
     return _lib
 
@@ -253,12 +256,12 @@ class Engine:
                                           buf.element_size()), "set_trace")
 
     LAYOUT = ["status", "flags", "layers", "tasks", "rope", "xcc", "x_out", "pbuf", "q", "u", "rl",
-              "part", "lmp", "x_emb", "a_norm", "tok", "total"]
+              "part", "lmp", "x_emb", "a_norm", "tok", "xmid", "pk", "ssq", "total"]
 
     def debug_slot(self, name, count, dtype=torch.float32, offset=0):
         """A view of a workspace region (debugging)."""
         import numpy as np
-        off = np.zeros(17, np.int64)
+        off = np.zeros(len(self.LAYOUT), np.int64)
         _check(lib().pre_debug_layout(self.h, C.c_void_p(off.ctypes.data)), "debug_layout")
         start = int(off[self.LAYOUT.index(name)]) + offset
         esz = torch.tensor([], dtype=dtype).element_size()
@@ -307,3 +310,15 @@ def debug_copy(src, dst):
     n = src.numel() * src.element_size()
     assert n == dst.numel() * dst.element_size() and n % 16 == 0
     _check(lib().pre_debug_copy(_ptr(src), _ptr(dst), n, _stream()), "debug_copy")
+
+
+def debug_mfma(a, b):
+    """A (16 x 32) @ B (32 x 16), bf16 in, fp32 out, through the matrix-core
+    instruction with the operand lane layout the micro-batch GEMMs use."""
+    A = a.to(device="cuda", dtype=torch.bfloat16).contiguous()
+    Bm = b.to(device="cuda", dtype=torch.bfloat16).contiguous()
+    assert A.shape == (16, 32) and Bm.shape == (32, 16)
+    out = torch.zeros((16, 16), dtype=torch.float32, device="cuda")
+    _check(lib().pre_debug_mfma(_ptr(A), _ptr(Bm), _ptr(out), _stream()), "debug_mfma")
+    torch.cuda.synchronize()
+    return out.cpu()

@@ -94,6 +94,13 @@ SMALL_MHA = ModelConfig("small_mha", n_layers=2, hidden=256, n_q_heads=4, n_kv_h
 # hand-offs are in use; ragged hidden and ffn.
 SMALL_GQA8 = ModelConfig("small_gqa8", n_layers=2, hidden=640, n_q_heads=16, n_kv_heads=8,
                          head_dim=64, ffn_dim=1200, vocab=1777, max_ctx=288)
+# Micro-batch shapes (GEMM inputs in whole 32-column blocks, as the packed
+# matrix-core layout needs; rows still ragged against the 16-row groups and
+# the workgroup split): 8 sequences, and 3.
+SMALL_MB = ModelConfig("small_mb", n_layers=2, hidden=384, n_q_heads=6, n_kv_heads=2,
+                       head_dim=64, ffn_dim=1056, vocab=2003, max_ctx=320, batch=8)
+SMALL_MB3 = ModelConfig("small_mb3", n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=4,
+                        head_dim=64, ffn_dim=544, vocab=1500, max_ctx=200, batch=3)
 
 
 # --------------------------------------------------------------------------

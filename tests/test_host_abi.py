@@ -100,10 +100,59 @@ def test_plans_validate(lib, m, grid):
     assert info.workspace_bytes > 0
 
 
-def test_microbatch_reported_unsupported(lib):
-    with pytest.raises(E.PreError) as ei:
-        E.plan_describe(synth.WORKLOADS["dense8b_mb8"].model)
+MB = [synth.WORKLOADS["dense8b_mb8"].model, synth.SMALL_MB, synth.SMALL_MB3]
+
+
+@pytest.mark.parametrize("m", MB, ids=lambda m: m.name)
+@pytest.mark.parametrize("grid", [0, 8, 16, 40, 256])
+def test_microbatch_plans_validate(lib, m, grid):
+    """The micro-batch table: an embedding stage, six stages per layer, the LM
+    head; every KV head's attention and combine on its own block of Tw
+    workgroups; rows in whole groups of 8 where outputs are packed."""
+    info, T = E.plan_describe(m, with_tasks=True, grid_wgs=grid)
+    assert info.validator == 0
+    W = info.n_wgs
+    assert W % m.n_kv_heads == 0
+    assert info.n_stage_inst == 6 * m.n_layers + 2
+    Tw = W // m.n_kv_heads
+    ops = [T[si * W][0] for si in range(info.n_stage_inst)]
+    assert ops[0] == 10 and ops[-1] == 9 and ops[1:7] == [1, 2, 11, 3, 4, 5]
+    attn, comb = T[2 * W:3 * W], T[3 * W:4 * W]
+    for lam in range(W):
+        assert attn[lam][4] == lam // Tw and attn[lam][2] == lam % Tw and attn[lam][3] == Tw
+        assert comb[lam][4] == lam // Tw
+        assert comb[lam][5] == 2 * W + (lam // Tw) * Tw and comb[lam][6] == comb[lam][5] + Tw
+    for si in (0, 4, 5, 6):  # EMBED, OPROJ, GU, DOWN: row ranges in groups of 8
+        for lam in range(W):
+            assert T[si * W + lam][2] % 8 == 0 and T[si * W + lam][3] % 8 == 0
+
+
+def test_microbatch_plan_validator_catches_mistakes(lib):
+    m = synth.SMALL_MB
+    info, T = E.plan_describe(m, with_tasks=True, grid_wgs=16)
+    W = info.n_wgs
+    bad = T.copy()
+    bad[3 * W + 1][5] += 1  # a combine that no longer waits on all of its head's attention
+    assert E.plan_validate(m, bad, grid_wgs=16) == 7
+    bad = T.copy()
+    bad[5 * W + 2][3] -= 8  # a gate/up row group nobody computes
+    assert E.plan_validate(m, bad, grid_wgs=16) == 5
+    bad = T.copy()
+    bad[2 * W + 3][2] = 0  # two attention shares with the same index
+    assert E.plan_validate(m, bad, grid_wgs=16) == 6
+
+
+def test_microbatch_unsupported_and_bad_shapes(lib):
+    from dataclasses import replace
+    with pytest.raises(E.PreError) as ei:  # routed experts at batch > 1
+        E.plan_describe(replace(synth.SMALL_MOE, batch=2))
     assert ei.value.code == -6
+    with pytest.raises(E.PreError) as ei:  # ffn not in whole 32-column blocks
+        E.plan_describe(replace(synth.SMALL_DENSE, batch=2))
+    assert ei.value.code == -6
+    with pytest.raises(E.PreError) as ei:  # KV heads' workgroup blocks must be equal
+        E.plan_describe(synth.SMALL_MB3, grid_wgs=10)
+    assert ei.value.code == -2
 
 
 def test_attention_and_o_projection_are_xcd_local_on_the_8b_shape(lib):
