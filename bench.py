@@ -51,6 +51,16 @@ def setup(workload, device="cuda", seed=0, prefill="engine", **eng_kw):
     t0 = time.time()
     W = synth.gen_weights(m, seed=seed, device=device)
     P = w.contexts[0]
+    if m.batch > 1:
+        # micro-batch: each sequence at its own context; the cache is the
+        # seeded synthetic one (the prefill of unequal lengths is not a
+        # lockstep decode), the first tokens seeded
+        kc, vc = synth.gen_kv_cache(m, max(w.contexts), seed=seed + 1, device=device)
+        eng = E.Engine(m, W, kc, vc, **eng_kw)
+        g0 = synth.gen_tokens(m.vocab, m.batch, seed=seed + 2, device=device)
+        log(f"[bench] {workload}: weights + synthetic cache of contexts {list(w.contexts)} "
+            f"in {time.time() - t0:.1f}s")
+        return w, m, W, kc, vc, eng, g0
     if prefill == "synthetic":
         kc, vc = synth.gen_kv_cache(m, P, seed=seed + 1, device=device)
     else:
@@ -79,18 +89,19 @@ def launches_per_token_per_op(m):
 
 
 def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
-    """Median/min seconds of one call of n_steps from position P; also returns
-    the per-call event times."""
+    """Seconds of each of `repeats` calls of n_steps from position(s) P (an
+    int, or one per sequence); also returns the tokens of the last call."""
     import torch
     stream = torch.cuda.current_stream()
-    out = torch.empty((max(n_steps, warmup_steps, 1), 1), dtype=torch.int32, device="cuda")
+    pos = list(P) if isinstance(P, (list, tuple)) else [P]
+    out = torch.empty((max(n_steps, warmup_steps, 1), len(pos)), dtype=torch.int32, device="cuda")
     if warmup_steps:
-        eng.set_positions([P])
+        eng.set_positions(pos)
         fn(warmup_steps, in_tokens=g0, out_tokens=out[:warmup_steps])
         torch.cuda.synchronize()
     times = []
     for _ in range(repeats):
-        eng.set_positions([P])
+        eng.set_positions(pos)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -99,32 +110,39 @@ def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / 1e3)
     eng.status()
-    return times, out[:n_steps, 0].cpu()
+    return times, out[:n_steps].cpu()
 
 
 def cpu_baseline(m, W, P, budget_s=15.0, max_steps=64):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    decode steps at context P of the same model (weights copied to the host;
-    the cache is a seeded synthetic one -- its values do not change the work)."""
+    decode steps of the same model (weights copied to the host; the cache is
+    a seeded synthetic one -- its values do not change the work) at context P,
+    or, for a micro-batch, whole steps = one decode of every sequence at its
+    own context (the oracle decodes sequences one at a time)."""
     import numpy as np
     import oracle
     from persistent_resident_execution_amd import synth
     t0 = time.time()
     om = oracle.OracleModel(m, synth.weights_to_numpy(W))
-    kc_t, vc_t = synth.gen_kv_cache(m, P, seed=1, device="cpu")
-    kc = synth.to_bits(kc_t)[:, 0]
-    vc = synth.to_bits(vc_t)[:, 0]
+    pos = list(P) if isinstance(P, (list, tuple)) else [P]
+    kc_t, vc_t = synth.gen_kv_cache(m, max(pos), seed=1, device="cpu")
+    kc_all, vc_all = synth.to_bits(kc_t), synth.to_bits(vc_t)
+    caches = [(np.ascontiguousarray(kc_all[:, b]), np.ascontiguousarray(vc_all[:, b])) for b in range(len(pos))]
     log(f"[bench] oracle set-up {time.time() - t0:.1f}s ({oracle.num_threads()} threads)")
-    tok, steps, t_start = 1, 0, time.time()
+    toks, steps, t_start = [1] * len(pos), 0, time.time()
     while steps < max_steps:
-        tok, _, _ = om.decode_step(kc, vc, int(tok), P + steps, want_logits=False, want_hidden=False)
+        for b, (kc, vc) in enumerate(caches):
+            toks[b], _, _ = om.decode_step(kc, vc, int(toks[b]), pos[b] + steps, want_logits=False,
+                                           want_hidden=False)
         steps += 1
         if time.time() - t_start >= budget_s:
             break
     el = time.time() - t_start
-    return {"value": round(el / steps * 1e6, 1), "unit": "us/token", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{steps} decode step(s) of the same {m.name} decoder at context {P}, batch 1, "
+    what = (f"context {pos[0]}, batch 1" if len(pos) == 1 else
+            f"contexts {pos}, one step = every sequence")
+    return {"value": round(el / steps * 1e6, 1), "unit": "us/step" if len(pos) > 1 else "us/token",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{steps} decode step(s) of the same {m.name} decoder at {what}, "
                       f"fp64 C oracle, {el:.1f}s wall"}
 
 
@@ -186,24 +204,30 @@ def main():
         torch.cuda.synchronize()
         del a, b
     w, m, W, kc, vc, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill)
-    P, K = w.contexts[0], args.steps
-    log(f"[bench] timing {args.repeats} x {K} persistent steps from position {P}")
+    mb = m.batch > 1
+    P, K = (list(w.contexts) if mb else w.contexts[0]), args.steps
+    pos = P if mb else [P]
+    log(f"[bench] timing {args.repeats} x {K} persistent steps from position(s) {P}")
     tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
     t_med = statistics.median(tp)
-    bytes_call = sum(E.step_bytes(m, [P + s]) for s in range(K))
+    bytes_call = sum(E.step_bytes(m, [p + s for p in pos]) for s in range(K))
     us_tok = t_med / K * 1e6
     gbps = bytes_call / t_med / 1e9
     result = {
-        "metric": "decode us/token (batch 1) + achieved HBM GB/s as % of MI355X peak",
-        "value": round(us_tok, 2), "unit": "us/token", "n_gpus": 1, "steps": K,
+        "metric": ("decode us/step (micro-batch " + str(m.batch) + ") + achieved HBM GB/s as % of MI355X peak"
+                   if mb else "decode us/token (batch 1) + achieved HBM GB/s as % of MI355X peak"),
+        "value": round(us_tok, 2), "unit": "us/step" if mb else "us/token", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(us_tok / 1e3, 4), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 weights/KV, fp32 compute",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, random prompt tokens)",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("bf16 weights/KV, bf16 hi+lo activations on the matrix cores, fp32 accumulate" if mb
+                  else "bf16 weights/KV, fp32 compute"),
+        "data": ("synthetic (seeded N(0,0.02) bf16 weights, seeded N(0,1) K/V cache, seeded first tokens)"
+                 if mb else "synthetic (seeded N(0,0.02) bf16 weights, random prompt tokens)"),
         "config": {"workload": w.note, "layers": m.n_layers, "hidden": m.hidden,
                    "heads": f"{m.n_q_heads}q/{m.n_kv_heads}kv x {m.head_dim}",
                    "ffn": m.ffn_dim, "vocab": m.vocab, "context": P, "batch": m.batch,
                    "parallelism": "single GPU, one workgroup per CU"},
-        "tokens_per_s": round(K / t_med, 1),
+        "tokens_per_s": round(K * m.batch / t_med, 1),
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "repeats_us_per_token": [round(t / K * 1e6, 2) for t in tp],
@@ -222,7 +246,7 @@ def main():
                                      "persistent_speedup": round(ub / us_tok, 3),
                                      "same_tokens": bool((btoks == toks).all())}
     eng.close()
-    if not args.no_tiny:
+    if not args.no_tiny and not mb:
         log("[bench] tiny decoder persistent vs per-op")
         result["tiny"] = tiny_comparison()
     if not args.no_cpu:

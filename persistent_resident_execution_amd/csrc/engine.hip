@@ -60,6 +60,7 @@ struct KP {
   int32_t local;         // XCD-local hand-offs (QKV -> attention -> O projection)
   // micro-batch
   int32_t pos0v[8];      // each sequence's position at the call's first step
+  int32_t mbst;          // longest GEMM input staged in LDS (columns; longer ones stream from memory)
   uint8_t *pk;           // packed GEMM inputs
   float *ssq;            // per-workgroup sums of squares of the normalised inputs
 };
@@ -1671,6 +1672,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.pk = D.mb ? (uint8_t *)(ws + Lo.pk) : nullptr;
   P.ssq = D.mb ? (float *)(ws + Lo.ssq) : nullptr;
   for (int b = 0; b < D.B; ++b) P.pos0v[b] = e->pos[b];
+  P.mbst = D.mbst;
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;

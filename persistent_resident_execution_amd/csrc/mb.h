@@ -153,96 +153,116 @@ __device__ __forceinline__ MbRg mb_rg(const KP &P, const Task &t, int j) {
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM stream of one batch of NB row groups.
+// The GEMM stream of one batch of nb row groups (nb = 1, 2, 4 or 8).
 //
-// Split-K over the wavefronts: wavefront w takes 32-column blocks
-// [nkb * w / nw, nkb * (w + 1) / nw) of every row group of the batch.  Per
-// block it loads one 16-byte A fragment per row group (16 rows x 64 bytes,
-// streaming) and one B fragment (the 1 KB packed input block, device scope)
-// and issues NB MFMAs.  A ring of D blocks is kept in flight; the A
-// fragments of the first D blocks are issued before the dependency wait
-// (weights never wait for activations), the B fragments after it.  At the
-// end each wavefront folds hi + lo (lanes c and c + 8 of a 16-lane row) and
-// writes its 16 x B partials of every row group to
-// ys[((wave * NB + j) * 8 + b) * 16 + row].
-template <int NB, int D>
-__device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nrg, const uint8_t *act, int K,
-                                          const Waiter *wait, float *ys) {
+// Wavefront w takes row group jr = w % nb of the batch and k-part
+// kp = w / nb of the nw / nb equal parts of the 32-column blocks (with 8
+// row groups every wavefront owns one group over all of K; with one group
+// the eight wavefronts split K).  Per block it loads one 16-byte A fragment
+// (16 rows x 64 bytes, streaming) and takes the B fragment -- the 1 KB
+// packed input block -- from the copy staged in LDS (inputs up to the
+// staging size) or from device memory, then issues one MFMA.  Each
+// wavefront thus streams 16 rows, contiguously along each row: few
+// concurrent row streams per CU keep the weight fetches page-friendly.  A
+// ring of D blocks of A fragments is kept in flight; the first D are issued
+// before the dependency wait (weights never wait for activations), then
+// the wait, the staging of the input (STAGED) and the loop.  At the end each
+// wavefront folds hi + lo (lanes c and c + 8 of a 16-lane row) and writes
+// its 16 x B partials to ys[((kp * nb + jr) * 8 + b) * 16 + row].
+template <bool STAGED, int D>
+__device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nb, int nrg, const uint8_t *act,
+                                          float *lact, int K, const Waiter *wait, float *ys) {
   const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
-  Rsrc ra[NB];
-  uint32_t vo[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    MbRg g{0, 0, 0, 0};
-    if (j0 + j < nrg) g = mb_rg(P, t, j0 + j);
-    const int nr = rfl(g.nr), rs = rfl(g.rs);
-    ra[j] = mkbuf64(rfl64(g.base), (uint32_t)(nr * rs));
-    // rows past nr fall outside the buffer and read 0
-    vo[j] = (uint32_t)((lane & 15) * rs + (lane >> 4) * 16);
-  }
+  const int jr = wave % nb, kp = wave / nb, nkp = nw / nb;
+  MbRg g{0, 0, 0, 0};
+  if (j0 + jr < nrg) g = mb_rg(P, t, j0 + jr);
+  const int nr = rfl(g.nr), rs = rfl(g.rs);
+  // rows past nr fall outside the buffer and read 0
+  const Rsrc ra = mkbuf64(rfl64(g.base), (uint32_t)(nr * rs));
+  const uint32_t vo = (uint32_t)((lane & 15) * rs + (lane >> 4) * 16);
   const int nkb = K >> 5;
-  const int kb0 = nkb * wave / nw, n = nkb * (wave + 1) / nw - kb0;
-  const Rsrc rb = mkbuf(act, (uint32_t)nkb * 1024u);
+  const int kb0 = nkb * kp / nkp, n = nkb * (kp + 1) / nkp - kb0;
+  const Rsrc rb = mkbuf(uni_ptr(act), (uint32_t)nkb * 1024u);
   const uint32_t bo = (uint32_t)lane * 16u;
-  v4i a[D][NB], bq[D];
-  f32x4_t acc[NB];
+  v4i a[D], bq[STAGED ? 1 : D];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // The first D blocks are issued unconditionally (a slot past the span gets
+  // an offset outside every buffer and reads 0 without touching memory), so
+  // every path into the loop has the same loads in flight.
+  constexpr uint32_t OOB = 0x80000000u;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < D; ++s) a[s] = ld128s<CP_W>(ra, vo, s < n ? (uint32_t)(kb0 + s) * 64u : OOB);
+  if (wait) {
+    if (!(*wait)(P)) return false;
+    if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
+      const int n16 = nkb * 64;
+      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {
+        v4i x[16];
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < n) {
+        for (int k = 0; k < 16; ++k)
+          x[k] = i0 + k * P.nthr < n16 ? ld128<CP_SC1>(rb, (uint32_t)(i0 + k * P.nthr) * 16u) : v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < NB; ++j) a[s][j] = ld128s<CP_W>(ra[j], vo[j], (uint32_t)(kb0 + s) * 64u);
+        for (int k = 0; k < 16; ++k)
+          if (i0 + k * P.nthr < n16) reinterpret_cast<v4i *>(lact)[i0 + k * P.nthr] = x[k];
+      }
+      __syncthreads();
     }
-  if (wait && !(*wait)(P)) return false;
+  }
+  if (!STAGED) {
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < n) bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)(kb0 + s) * 1024u);
-  auto consume = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = mfma_16x16x32(a[s][j], bq[s], acc[j]);
+    for (int s = 0; s < D; ++s) bq[s] = ld128s<CP_SC1>(rb, bo, s < n ? (uint32_t)(kb0 + s) * 1024u : OOB);
+  }
+  auto consume = [&](int s, int kb) {
+    const v4i b = STAGED ? reinterpret_cast<const v4i *>(lact)[kb * 64 + lane] : bq[STAGED ? 0 : s];
+    acc = mfma_16x16x32(a[s], b, acc);
   };
   auto issue = [&](int s, int kb) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) a[s][j] = ld128s<CP_W>(ra[j], vo[j], (uint32_t)kb * 64u);
-    bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)kb * 1024u);
+    a[s] = ld128s<CP_W>(ra, vo, (uint32_t)kb * 64u);
+    if (!STAGED) bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)kb * 1024u);
   };
   const int m = n >= D ? (n - D) / D : 0;  // rounds whose every issue lies inside the span
-  for (int q = 0; q < m; ++q) {
+  // The first round is peeled: it still has the prologue's order of loads in
+  // flight; the loop after it sees the steady order only, so its waits are
+  // exact (one slot at a time).
+  if (m > 0) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      consume(s);
-      issue(s, kb0 + (q + 1) * D + s);
+      consume(s, kb0 + s);
+      issue(s, kb0 + D + s);
+    }
+    for (int q = 1; q < m; ++q) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        consume(s, kb0 + q * D + s);
+        issue(s, kb0 + (q + 1) * D + s);
+      }
     }
   }
   const int rem = n - m * D;  // 0 <= rem < 2D
 #pragma unroll
   for (int s = 0; s < D; ++s) {
-    if (s < rem) consume(s);
+    if (s < rem) consume(s, kb0 + m * D + s);
     if (s + D < rem) issue(s, kb0 + (m + 1) * D + s);
   }
 #pragma unroll
   for (int s = 0; s < D; ++s)
-    if (s + D < rem) consume(s);
+    if (s + D < rem) consume(s, kb0 + (m + 1) * D + s);
   const int c = lane & 15;
+  float v[4];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[j][i] + dpp<0x128>(acc[j][i]);  // row_ror:8: hi + lo
-    if (c < P.B)
-      *reinterpret_cast<float4 *>(ys + ((wave * NB + j) * 8 + c) * 16 + 4 * (lane >> 4)) =
-          float4{v[0], v[1], v[2], v[3]};
-  }
+  for (int i = 0; i < 4; ++i) v[i] = acc[i] + dpp<0x128>(acc[i]);  // row_ror:8: hi + lo
+  if (c < P.B)
+    *reinterpret_cast<float4 *>(ys + ((kp * nb + jr) * 8 + c) * 16 + 4 * (lane >> 4)) = float4{v[0], v[1], v[2], v[3]};
+  (void)nkp;
   return true;
 }
 
 // Output (row i of row group j, sequence b) of a batch of nb row groups:
-// the wavefronts' partials added in wavefront order.
-__device__ __forceinline__ float mb_y(const float *ys, int nb, int nw, int j, int b, int i) {
+// the nkp k-parts' partials added in order.
+__device__ __forceinline__ float mb_y(const float *ys, int nb, int nkp, int j, int b, int i) {
   float v[MAXW];
 #pragma unroll
-  for (int w = 0; w < MAXW; ++w) v[w] = w < nw ? ys[((w * nb + j) * 8 + b) * 16 + i] : 0.f;
+  for (int w = 0; w < MAXW; ++w) v[w] = w < nkp ? ys[((w * nb + j) * 8 + b) * 16 + i] : 0.f;
   float y = 0.f;
 #pragma unroll
   for (int w = 0; w < MAXW; ++w) y += v[w];
@@ -302,14 +322,14 @@ __device__ __forceinline__ void mb_gain8(const KP &P, const uint16_t *g, int r, 
   bf8(ld128<CP_DEF>(mkbuf(uni_ptr(g), (uint32_t)P.h * 2), (uint32_t)r * 2), o);
 }
 
-// LDS of the micro-batch GEMM tasks: ys[nw * 8 * 8 * 16] | rs[8] | ssq[8] |
-// per-thread partials[512].
+// LDS of the micro-batch GEMM tasks: ys[nw * 8 * 16] | rs[8] | ssq[8] |
+// per-thread partials[512] | staged packed input (K * 8 floats).
 struct MbLds {
-  float *ys, *rs, *ssq, *ep;
+  float *ys, *rs, *ssq, *ep, *act;
 };
 __device__ __forceinline__ MbLds mb_lds(const KP &P, float *lds) {
-  float *ys = lds, *rs = ys + P.nw * 8 * 8 * 16;
-  return MbLds{ys, rs, rs + 8, rs + 16};
+  float *ys = lds, *rs = ys + P.nw * 8 * 16;
+  return MbLds{ys, rs, rs + 8, rs + 16, rs + 16 + 512};
 }
 
 // One GEMM task: batches of up to 8 row groups, each streamed, reduced and
@@ -319,7 +339,8 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   const int l = t.layer, op = t.op, tid = threadIdx.x, T = P.nthr, nw = P.nw, B = P.B;
   const MbLds M = mb_lds(P, lds);
   const int nrg = rfl(mb_nrg(P, t));
-  const int nb = nrg <= 1 ? 1 : nrg <= 2 ? 2 : nrg <= 4 ? 4 : 8;
+  const int nb = min(nw, nrg <= 1 ? 1 : nrg <= 2 ? 2 : nrg <= 4 ? 4 : 8);  // row groups per batch
+  const int nkp = nw / nb;  // k-parts per row group
   const uint8_t *act;
   int K, nidx = -1;  // sums of squares this task's input is normalised with
   if (op == OP_QKV) { act = pk_x(P, l); K = P.h; nidx = 2 * l; }
@@ -335,11 +356,8 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   bool waited = false;
   for (int j0 = 0; j0 < max(nrg, 1); j0 += nb) {
     const Waiter *wp = waited ? nullptr : &wait;
-    bool ok;
-    if (nb == 1) ok = mb_stream<1, 12>(P, t, j0, nrg, act, K, wp, M.ys);
-    else if (nb == 2) ok = mb_stream<2, 8>(P, t, j0, nrg, act, K, wp, M.ys);
-    else if (nb == 4) ok = mb_stream<4, 5>(P, t, j0, nrg, act, K, wp, M.ys);
-    else ok = mb_stream<8, 2>(P, t, j0, nrg, act, K, wp, M.ys);
+    const bool ok = K <= P.mbst ? mb_stream<true, 16>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys)
+                                : mb_stream<false, 12>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys);
     if (!ok) return false;
     if (!waited) {
       if (nidx >= 0) mb_norm_scales(P, nidx, K, M.rs);
@@ -361,7 +379,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
           p += i;
           const int gh = p / half, g = gh / (P.G + 2), hh = gh % (P.G + 2), jj = p % half;
           const float r = M.rs[b];
-          float a = r * mb_y(ys, nb, nw, jA, b, i), c = r * mb_y(ys, nb, nw, jA + 1, b, i);
+          float a = r * mb_y(ys, nb, nkp, jA, b, i), c = r * mb_y(ys, nb, nkp, jA + 1, b, i);
           const int pos = P.pos0v[b] + step;
           if (hh <= P.G) {  // RoPE on q and k
             const float cs = P.rope[(int64_t)pos * half + jj];
@@ -399,7 +417,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
           float u[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            u[i] = silu(r * mb_y(ys, nb, nw, jA, b, 8 * o + i)) * (r * mb_y(ys, nb, nw, jA + 1, b, 8 * o + i));
+            u[i] = silu(r * mb_y(ys, nb, nkp, jA, b, 8 * o + i)) * (r * mb_y(ys, nb, nkp, jA + 1, b, 8 * o + i));
           pk_store8(pk_u(P, l), P.ffn, r0 >> 3, b, u);
         }
         break;
@@ -421,7 +439,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
             else mb_x_in(P, l, b, r0, toks, x);
             mb_gain8(P, gain, r0, g);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] += mb_y(ys, nb, nw, j, b, 8 * o + i);
+            for (int i = 0; i < 8; ++i) x[i] += mb_y(ys, nb, nkp, j, b, 8 * o + i);
             st8_vec(P, (down ? P.x_out : P.xmid) + vec_off(P, l, 0, P.h), b, r0, x);
             if (down && P.chk_hidden && l == P.L - 1) {
               float *hd = P.chk_hidden + ((int64_t)step * P.B + b) * P.h + r0;
@@ -450,7 +468,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
           for (int e = lane; e < nb * 16; e += 64) {
             const int j = e >> 4, i = e & 15, row = t.r0 + 16 * (j0 + j) + i;
             if (j0 + j >= nrg || row >= t.r1) continue;
-            const float y = M.rs[b] * mb_y(ys, nb, nw, j, b, i);
+            const float y = M.rs[b] * mb_y(ys, nb, nkp, j, b, i);
             if (y != y) nan = true;
             else argmax_merge(bv, bi, y, row);
             if (P.chk_logits) P.chk_logits[((int64_t)step * P.B + b) * P.V + row] = y;

@@ -87,6 +87,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (D->NC > D->Tg) return PRE_ERR_SHAPE;
   D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
   if (D->threads % 64 || D->threads < 128 || D->threads > 512) return PRE_ERR_SHAPE;
+  // micro-batch: wavefronts split a batch's row groups evenly (a power of
+  // two), and the LM head keeps one wavefront per sequence
+  if (mb && ((D->threads & (D->threads - 1)) || D->threads < 64 * D->B)) return PRE_ERR_SHAPE;
   D->stages_per_layer = (moe || mb) ? 6 : 5;
   // micro-batch: an embedding stage first, then per layer QKV, ATTN, COMB,
   // OPROJ, GU, DOWN, then the LM head
@@ -122,10 +125,14 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
   if (mb) {
-    // MFMA stages: per-wavefront partials of up to 8 row groups x 8 sequences
-    // x 16 rows, the sequences' norm scales and sums, per-thread partials;
-    // attention: the running state of a piece (output, max, sum)
-    gemv = (int64_t)waves * 8 * 8 * 16 + 1024;
+    // MFMA stages: per-wavefront partials (8 sequences x 16 rows), the
+    // sequences' norm scales and sums, per-thread partials, and the packed
+    // input (32 bytes per column) when the hidden-size inputs fit beside
+    // them; attention: the running state of a piece (output, max, sum)
+    const int64_t base = (int64_t)waves * 8 * 16 + 16 + 512;
+    const int64_t kst = std::max(D->h, D->Hq * D->d);
+    D->mbst = (base + kst * 8) * 4 <= 150 * 1024 ? (int32_t)kst : 0;
+    gemv = base + (int64_t)D->mbst * 8;
     attn += (int64_t)D->G * D->d + 4 * D->G;
   }
   D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);
