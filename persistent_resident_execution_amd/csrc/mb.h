@@ -196,7 +196,7 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
     if (!(*wait)(P)) return false;
     if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
       const int n16 = nkb * 64;
-      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {
+      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
         v4i x[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k)
@@ -544,6 +544,9 @@ __device__ __forceinline__ int64_t mb_share(int64_t N, int Tw, int i) { return (
 // Positions [t0, t0 + cnt) of sequence b (at most cmax of them), merged into
 // the running (max, sum, output) state of the piece kept in LDS; the last
 // sub-piece writes the piece's record.
+// MG: query heads per KV head the accumulators are sized for (G <= MG);
+// MB_APB: passes per batch of K or V rows.
+template <int MG, int MB_APB>
 __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, int g, int t0, int cnt, int pos,
                                             float *lds, const Waiter *wait, bool first, bool last, bool &ok) {
   const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr;
@@ -555,86 +558,41 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
   const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * d * 2);
   const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * d * 2);
   const int LPP = d / 8, PPW = 64 / LPP, sub = lane % LPP, grp = lane / LPP;
-  const int PASS = nw * PPW;
+  const int PASS = nw * PPW, STEP = MB_APB * PASS;
   auto koff = [=](int tt) { return (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2; };
-  v4i kb[APB], vb[APB];
+  // positions past the sub-piece read nothing (an offset outside the buffer)
+  auto load = [&](const Rsrc &r, v4i (&x)[MB_APB], int base) {
 #pragma unroll
-  for (int p = 0; p < APB; ++p) {
-    const int tt = p * PASS + wave * PPW + grp;
-    const bool old = tt < cnt && t0 + tt != pos;
-    kb[p] = old ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
-    vb[p] = old ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
-  }
-  if (wait && !(*wait)(P)) { ok = false; return; }
-  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
-  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
-#pragma unroll
-  for (int p = 0; p < APB; ++p) {
-    const int tt = p * PASS + wave * PPW + grp;
-    if (tt < cnt && t0 + tt == pos) {
-      kb[p] = ld128<CP_SC1>(kr, koff(tt));
-      vb[p] = ld128<CP_SC1>(vr, koff(tt));
+    for (int p = 0; p < MB_APB; ++p) {
+      const int tt = base + p * PASS + wave * PPW + grp;
+      x[p] = ld128<CP_SC1>(r, tt < cnt ? koff(tt) : 0x80000000u);
     }
-  }
-  __syncthreads();
-  for (int base = 0; base < cnt; base += APB * PASS) {
-    if (base > 0) {
+  };
+  auto scores = [&](const v4i (&x)[MB_APB], int base) {
 #pragma unroll
-      for (int p = 0; p < APB; ++p) {
-        const int tt = base + p * PASS + wave * PPW + grp;
-        kb[p] = tt < cnt ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < APB; ++p) {
+    for (int p = 0; p < MB_APB; ++p) {
       const int tt = base + p * PASS + wave * PPW + grp;
       if (base + p * PASS < cnt) {
         for (int hh = 0; hh < G; ++hh) {
           const float4 *q4 = reinterpret_cast<const float4 *>(qs + hh * d + sub * 8);
-          float s = dot8_bf16(kb[p], q4[0], q4[1], 0.f);
-          s = (LPP == 16) ? sum16(s) : sum8(s);
-          if (tt < cnt && sub == 0) sc[hh * cpad + tt] = s;
+          float sv = dot8_bf16(x[p], q4[0], q4[1], 0.f);
+          sv = (LPP == 16) ? sum16(sv) : sum8(sv);
+          if (tt < cnt && sub == 0) sc[hh * cpad + tt] = sv;
         }
       }
     }
-  }
-  __syncthreads();
-  for (int hh = wave; hh < G; hh += nw) {
-    float m = -INFINITY;
-    for (int i = lane; i < cnt; i += 64) m = fmaxf(m, sc[hh * cpad + i]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int i = lane; i < cnt; i += 64) {
-      const float e = expf(sc[hh * cpad + i] - m);
-      sc[hh * cpad + i] = e;
-      s += e;
-    }
-    s = wave_sum(s);
-    if (lane == 0) { st[2 * hh] = m; st[2 * hh + 1] = s; }
-  }
-  __syncthreads();
-  float acc[8][8];
+  };
+  float acc[MG][8];
+  auto pv = [&](const v4i (&x)[MB_APB], int base) {
 #pragma unroll
-  for (int hh = 0; hh < 8; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  for (int base = 0; base < cnt; base += APB * PASS) {
-    if (base > 0) {
-#pragma unroll
-      for (int p = 0; p < APB; ++p) {
-        const int tt = base + p * PASS + wave * PPW + grp;
-        vb[p] = tt < cnt ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < APB; ++p) {
+    for (int p = 0; p < MB_APB; ++p) {
       const int tt = base + p * PASS + wave * PPW + grp;
       if (tt < cnt) {
-        const v4i vw = vb[p];
+        const v4i vw = x[p];
         const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
                             bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh)
+        for (int hh = 0; hh < MG; ++hh)
           if (hh < G) {
             const float pr = sc[hh * cpad + tt];
 #pragma unroll
@@ -642,9 +600,66 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
           }
       }
     }
+  };
+  // the cached rows of the first batch, before the wait
+  v4i kb[MB_APB], vb[MB_APB], kn[MB_APB], vn[MB_APB];
+#pragma unroll
+  for (int p = 0; p < MB_APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    const bool old = tt < cnt && t0 + tt != pos;
+    kb[p] = ld128<CP_SC1>(kr, old ? koff(tt) : 0x80000000u);
+    vb[p] = ld128<CP_SC1>(vr, old ? koff(tt) : 0x80000000u);
+  }
+  if (wait && !(*wait)(P)) { ok = false; return; }
+  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
+  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
+#pragma unroll
+  for (int p = 0; p < MB_APB; ++p) {
+    const int tt = p * PASS + wave * PPW + grp;
+    if (tt < cnt && t0 + tt == pos) {  // the row this step's QKV stage wrote
+      kb[p] = ld128<CP_SC1>(kr, koff(tt));
+      vb[p] = ld128<CP_SC1>(vr, koff(tt));
+    }
+  }
+  __syncthreads();
+  // scores: the next batch's K rows are in flight while one batch is used
+  for (int base = 0; base < cnt; base += 2 * STEP) {
+    load(kr, kn, base + STEP);
+    scores(kb, base);
+    if (base + STEP >= cnt) break;
+    load(kr, kb, base + 2 * STEP);
+    scores(kn, base + STEP);
+  }
+  load(vr, vn, STEP);  // the second V batch, during the softmax
+  __syncthreads();
+  for (int hh = wave; hh < G; hh += nw) {
+    float m = -INFINITY;
+    for (int i = lane; i < cnt; i += 64) m = fmaxf(m, sc[hh * cpad + i]);
+    m = wave_max(m);
+    float sm = 0.f;
+    for (int i = lane; i < cnt; i += 64) {
+      const float e = expf(sc[hh * cpad + i] - m);
+      sc[hh * cpad + i] = e;
+      sm += e;
+    }
+    sm = wave_sum(sm);
+    if (lane == 0) { st[2 * hh] = m; st[2 * hh + 1] = sm; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < MG; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  // o = sum_t p_t V_t, two V batches in flight
+  for (int base = 0; base < cnt; base += 2 * STEP) {
+    pv(vb, base);
+    if (base + STEP >= cnt) break;
+    load(vr, vb, base + 2 * STEP);
+    pv(vn, base + STEP);
+    load(vr, vn, base + 3 * STEP);
   }
 #pragma unroll
-  for (int hh = 0; hh < 8; ++hh)
+  for (int hh = 0; hh < MG; ++hh)
     if (hh < G) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -655,7 +670,7 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
     }
   if (grp == 0) {
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
+    for (int hh = 0; hh < MG; ++hh)
       if (hh < G)
 #pragma unroll
         for (int e = 0; e < 8; ++e) ored[(wave * G + hh) * d + sub * 8 + e] = acc[hh][e];
@@ -710,8 +725,12 @@ __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int
     // the piece in sub-pieces of at most cmax positions
     for (int64_t c0 = lo; c0 < hi && ok; c0 += P.cmax) {
       const int n = (int)min((int64_t)P.cmax, hi - c0);
-      mb_attn_sub(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, first ? &wait : nullptr, c0 == lo,
-                  c0 + n == hi, ok);
+      if (P.G <= 4)
+        mb_attn_sub<4, 4>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, first ? &wait : nullptr, c0 == lo,
+                       c0 + n == hi, ok);
+      else
+        mb_attn_sub<8, 3>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, first ? &wait : nullptr, c0 == lo,
+                       c0 + n == hi, ok);
       first = false;
     }
     pre += pos + 1;
