@@ -212,6 +212,7 @@ def main():
     pos = P if mb else [P]
     log(f"[bench] timing {args.repeats} x {K} persistent steps from position(s) {P}")
     tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
+    kern = "pre_persistent_mb" if mb else "pre_persistent"
     t_med = statistics.median(tp)
     bytes_call = sum(E.step_bytes(m, [p + s for p in pos]) for s in range(K))
     us_tok = t_med / K * 1e6
@@ -236,8 +237,8 @@ def main():
         "repeats_us_per_token": [round(t / K * 1e6, 2) for t in tp],
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": profiling.traffic_for(args.workload, K),
-                     "kernel": "pre_persistent", "bytes_per_launch": bytes_call,
+                     "traffic": profiling.traffic_for(args.workload, K, kern),
+                     "kernel": kern, "bytes_per_launch": bytes_call,
                      "launch_ms": round(t_med * 1e3, 3)},
     }
     if not args.no_baseline:

@@ -7,7 +7,8 @@ profiles/, and read them back for the benchmark.
     python -m persistent_resident_execution_amd.profiling counters DIR --out FILE --command "..."
 
 `stats` condenses a `rocprofv3 --kernel-trace --stats` run: calls and
-durations per kernel, plus every pre_persistent dispatch from the trace.
+durations per kernel, plus every dispatch of the resident kernel from the
+trace (--kernel: pre_persistent, or pre_persistent_mb for a micro-batch).
 
 `traffic` takes two `--pmc` runs of the same command, one collecting
 FETCH_SIZE and one WRITE_SIZE (both KiB per dispatch).  The command runs
@@ -61,20 +62,20 @@ def _short(name, n=60):
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def summarize_stats(d, out, command):
+def summarize_stats(d, out, command, kernel=KERNEL):
     rows = _csv(d, "kernel_stats.csv")
     trace = _csv(d, "kernel_trace.csv")
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-            if r["Kernel_Name"] == KERNEL]
+            if r["Kernel_Name"] == kernel]
     lines = [f"# rocprofv3 kernel trace + stats", f"command: {command}", f"source_sha256: {source_hash()}", "",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>12s} {'min_us':>12s} {'max_us':>12s} {'pct':>6s}"]
     for r in rows:
         lines.append(f"{_short(r['Name']):60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} "
                      f"{float(r['MinNs']) / 1e3:12.1f} {float(r['MaxNs']) / 1e3:12.1f} "
                      f"{float(r['Percentage']):6.2f}")
-    lines += ["", f"{KERNEL} dispatches (us): " + ", ".join(f"{x:.1f}" for x in durs)]
+    lines += ["", f"{kernel} dispatches (us): " + ", ".join(f"{x:.1f}" for x in durs)]
     if durs:
-        lines.append(f"{KERNEL} mean_us: {statistics.mean(durs):.1f}")
+        lines.append(f"{kernel} mean_us: {statistics.mean(durs):.1f}")
     _write(out, lines)
 
 
@@ -89,10 +90,10 @@ def _last_dispatch_value(rows, kernel, counter):
     return vals[max(vals)], len(vals)
 
 
-def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, steps):
+def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, steps, kernel=KERNEL):
     fr, wr = _csv(fetch_dir, "counter_collection.csv"), _csv(write_dir, "counter_collection.csv")
-    f_k, nf = _last_dispatch_value(fr, KERNEL, "FETCH_SIZE")
-    w_k, nw = _last_dispatch_value(wr, KERNEL, "WRITE_SIZE")
+    f_k, nf = _last_dispatch_value(fr, kernel, "FETCH_SIZE")
+    w_k, nw = _last_dispatch_value(wr, kernel, "WRITE_SIZE")
     f_c, _ = _last_dispatch_value(fr, COPY_KERNEL, "FETCH_SIZE")
     w_c, _ = _last_dispatch_value(wr, COPY_KERNEL, "WRITE_SIZE")
     ff, fw = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
@@ -103,22 +104,23 @@ def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, 
              f"copy_bytes: {copy_bytes}",
              f"copy_FETCH_SIZE_KiB: {f_c:.1f}", f"copy_WRITE_SIZE_KiB: {w_c:.1f}",
              f"fetch_scale: {ff:.4f}", f"write_scale: {fw:.4f}",
-             f"kernel_FETCH_SIZE_KiB: {f_k:.1f}  (last of {nf} {KERNEL} dispatches)",
-             f"kernel_WRITE_SIZE_KiB: {w_k:.1f}  (last of {nw} {KERNEL} dispatches)",
+             f"kernel: {kernel}",
+             f"kernel_FETCH_SIZE_KiB: {f_k:.1f}  (last of {nf} {kernel} dispatches)",
+             f"kernel_WRITE_SIZE_KiB: {w_k:.1f}  (last of {nw} {kernel} dispatches)",
              f"fetch_bytes_per_launch: {fetch_b:.0f}", f"write_bytes_per_launch: {write_b:.0f}",
              f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
              f"traffic_bytes_per_step: {(fetch_b + write_b) / steps:.0f}"]
     _write(out, lines)
 
 
-def summarize_counters(d, out, command):
+def summarize_counters(d, out, command, kernel=KERNEL):
     rows = _csv(d, "counter_collection.csv")
-    names = sorted({r["Counter_Name"] for r in rows if r["Kernel_Name"] == KERNEL})
+    names = sorted({r["Counter_Name"] for r in rows if r["Kernel_Name"] == kernel})
     lines = ["# rocprofv3 --pmc counters of the last decode launch", f"command: {command}",
              f"source_sha256: {source_hash()}"]
     vals = {}
     for n in names:
-        v, cnt = _last_dispatch_value(rows, KERNEL, n)
+        v, cnt = _last_dispatch_value(rows, kernel, n)
         vals[n] = v
         lines.append(f"{n}: {v:.0f}  (last of {cnt} dispatches)")
     if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
@@ -149,10 +151,10 @@ def read_summary(path) -> dict:
     return res
 
 
-def traffic_for(workload, steps):
+def traffic_for(workload, steps, kernel=KERNEL):
     """Measured HBM bytes of one launch of `steps` steps, or None when no
     summary matches this workload, step count and the current sources."""
-    s = read_summary(os.path.join(ROOT, "profiles", f"{KERNEL}_{workload}_traffic.txt"))
+    s = read_summary(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt"))
     if not s or s.get("workload") != workload or s.get("steps") != str(steps):
         return None
     if s.get("source_sha256") != source_hash():
@@ -167,6 +169,7 @@ def main():
     a.add_argument("dir")
     a.add_argument("--out", required=True)
     a.add_argument("--command", required=True)
+    a.add_argument("--kernel", default=KERNEL)
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
@@ -175,18 +178,20 @@ def main():
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--workload", required=True)
     b.add_argument("--steps", type=int, required=True)
+    b.add_argument("--kernel", default=KERNEL)
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--out", required=True)
     c.add_argument("--command", required=True)
+    c.add_argument("--kernel", default=KERNEL)
     args = ap.parse_args()
     if args.cmd == "stats":
-        summarize_stats(args.dir, args.out, args.command)
+        summarize_stats(args.dir, args.out, args.command, args.kernel)
     elif args.cmd == "traffic":
         summarize_traffic(args.fetch_dir, args.write_dir, args.out, args.command, args.copy_bytes,
-                          args.workload, args.steps)
+                          args.workload, args.steps, args.kernel)
     else:
-        summarize_counters(args.dir, args.out, args.command)
+        summarize_counters(args.dir, args.out, args.command, args.kernel)
 
 
 if __name__ == "__main__":
