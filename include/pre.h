@@ -88,9 +88,12 @@ extern "C" {
  * attention partials from producer to consumer through the XCD's own L2
  * when every consumer sits on the producer's XCD (8 KV heads, a grid that is
  * a multiple of 8: KV head g's QKV rows, attention chunks and output
- * projection slice all run on XCD g); -1 = always hand off at device scope.
- * The persistent kernel checks the placement it assumes and latches
- * PRE_DEV_PLACEMENT if the hardware put a workgroup elsewhere. */
+ * projection slice all run on XCD g), or, when the grid fits one XCD's CUs
+ * (small models; the default grid of a small model is capped at that), run
+ * every workgroup on XCD 0 and hand every flag over in its L2; -1 = always
+ * hand off at device scope, no placement.  The persistent kernel checks the
+ * placement it assumes and latches PRE_DEV_PLACEMENT if the hardware put a
+ * workgroup elsewhere. */
 typedef struct pre_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t batch, max_ctx;
@@ -224,7 +227,7 @@ const char *pre_strerror(int code);
  * aux, wait_lo, wait_hi, signal) in table order when h_tasks is non-NULL. */
 typedef struct pre_plan_info {
   int32_t n_stage_inst, n_wgs, n_slots, n_tasks, attn_splits, validator;
-  int32_t xcd_local;  /* 1 if the XCD-local hand-offs are in use */
+  int32_t xcd_local;  /* 1: per-KV-head XCD-local hand-offs; 2: every workgroup on one XCD; 0: none */
   int64_t workspace_bytes;
 } pre_plan_info;
 int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int32_t *h_tasks,

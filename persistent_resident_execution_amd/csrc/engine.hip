@@ -58,6 +58,7 @@ struct KP {
   int32_t persistent;
   int32_t b_si, b_step;  // baseline launches: the stage and step to run
   int32_t local;         // XCD-local hand-offs (QKV -> attention -> O projection)
+  int32_t onexcd;        // every workgroup on XCD 0: every hand-off in that XCD's L2
   // micro-batch
   int32_t pos0v[8];      // each sequence's position at the call's first step
   int32_t mbst;          // longest GEMM input staged in LDS (columns; longer ones stream from memory)
@@ -163,6 +164,25 @@ __device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep, 
   }
 }
 
+// A result other workgroups read: written through at device scope, or, with
+// one-XCD placement (every reader shares this XCD's L2), left in the L2,
+// where the readers' device-scope loads find it without a memory round trip.
+__device__ __forceinline__ void st_out(const KP &P, float *p, float v) {
+  if (P.onexcd)
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    st_sc1(p, v);
+}
+__device__ __forceinline__ void st_out16(const KP &P, Rsrc r, uint32_t off, uint16_t v) {
+  if (P.onexcd) st16<CP_SC0>(r, off, v);
+  else st16<CP_SC1>(r, off, v);
+}
+__device__ __forceinline__ void st_out128(const KP &P, Rsrc r, uint32_t off, v4i v) {
+  if (P.onexcd) st128<CP_SC0>(r, off, v);
+  else st128<CP_SC1>(r, off, v);
+}
+
 // ---------------------------------------------------------------------------
 // staging a GEMV input vector into LDS (fp32), optionally RMS-normalised
 
@@ -249,7 +269,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
           }
         reinterpret_cast<float4 *>(xs)[i] = s.gain ? scaled(f, g[k]) : f;
         if (s.dump && i >= s.d0 && i < s.d1)
-          st128<CP_SC1>(rd, (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
+          st_out128(P, rd, (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
         ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
         ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
       }
@@ -457,18 +477,18 @@ __device__ __forceinline__ int st_begin(PStream<FP8, D, CP> &S, const Seg *tab, 
 // lane 63 writes the wavefront's partials of that pair to
 // ys[(pair * nw + wave) * 2 + {0, 1}].
 template <bool FP8, int D, int CP>
-__device__ __forceinline__ void st_compute(PStream<FP8, D, CP> &S, int jj, bool span_end, const float *xs,
-                                           float *ys) {
+__device__ __forceinline__ void st_compute_w(PStream<FP8, D, CP> &S, int jj, v4i w0, v4i w1, bool span_end,
+                                             const float *xs, float *ys) {
   const int lane = threadIdx.x & 63;
   const float *xb = xs + (FP8 ? S.xo[jj] + S.cc * 1024 + lane * 16 : S.cc * 512 + lane * 8);
   if (FP8) {
-    S.acc[0] = fmaf(S.sc[jj][0], dot16_fp8(S.buf[jj][0], xb), S.acc[0]);
-    S.acc[1] = fmaf(S.sc[jj][1], dot16_fp8(S.buf[jj][1], xb), S.acc[1]);
+    S.acc[0] = fmaf(S.sc[jj][0], dot16_fp8(w0, xb), S.acc[0]);
+    S.acc[1] = fmaf(S.sc[jj][1], dot16_fp8(w1, xb), S.acc[1]);
   } else {
     const float4 *x4 = reinterpret_cast<const float4 *>(xb);
     const float4 x0 = x4[0], x1 = x4[1];
-    S.acc[0] = dot8_bf16(S.buf[jj][0], x0, x1, S.acc[0]);
-    S.acc[1] = dot8_bf16(S.buf[jj][1], x0, x1, S.acc[1]);
+    S.acc[0] = dot8_bf16(w0, x0, x1, S.acc[0]);
+    S.acc[1] = dot8_bf16(w1, x0, x1, S.acc[1]);
   }
   const bool row_end = ++S.cc == S.nch;
   if (row_end || span_end) {
@@ -477,6 +497,11 @@ __device__ __forceinline__ void st_compute(PStream<FP8, D, CP> &S, int jj, bool 
     if (lane == 63) *reinterpret_cast<float2 *>(ys + (S.cg * S.nw + S.wave) * 2) = y;
     if (row_end) { S.cc = 0; ++S.cg; }
   }
+}
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_compute(PStream<FP8, D, CP> &S, int jj, bool span_end, const float *xs,
+                                           float *ys) {
+  st_compute_w(S, jj, S.buf[jj][0], S.buf[jj][1], span_end, xs, ys);
 }
 
 // Consume the span of n units.  Full rounds of the ring first (one issue per
@@ -973,7 +998,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     if (op == OP_EGU) {
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
       for (int i = tid; i < rows; i += P.nthr)
-        st_sc1(u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
+        st_out(P, u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
     } else {
       const int nk = P.top_k + P.n_shared, np = (rows + 1) >> 1;
       float *xo = P.x_out + vec_off(P, l, 0, P.h) + t.r0;
@@ -982,7 +1007,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         float acc = 0.f;
         for (int k = 0; k < nk; ++k) acc = fmaf(selw[k], ys_get(ys, k * np + (i >> 1), i & 1, nw), acc);
         const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + acc;
-        st_sc1(xo + i, v);
+        st_out(P, xo + i, v);
         if (hid) hid[i] = v;
       }
     }
@@ -1003,20 +1028,20 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         }
         if (hh < P.G) {
           float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
-          st_sc1(qd + j, a);
-          st_sc1(qd + j + half, b);
+          st_out(P, qd + j, a);
+          st_out(P, qd + j + half, b);
         } else {  // the layer's K or V cache of every KV head under one descriptor each
           const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
           const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
           const uint32_t o0 = (uint32_t)(((int64_t)g * P.max_ctx + pos) * P.d + j) * 2, o1 = o0 + (uint32_t)half * 2;
           if (hh == P.G) {
             const Rsrc r = mkbuf(P.kc + lbase, bytes);
-            st16<CP_SC1>(r, o0, f2bf(a));
-            st16<CP_SC1>(r, o1, f2bf(b));
+            st_out16(P, r, o0, f2bf(a));
+            st_out16(P, r, o1, f2bf(b));
           } else {
             const Rsrc r = mkbuf(P.vc + lbase, bytes);
-            st16<CP_SC1>(r, o0, f2bf(a));
-            st16<CP_SC1>(r, o1, f2bf(b));
+            st_out16(P, r, o0, f2bf(a));
+            st_out16(P, r, o1, f2bf(b));
           }
         }
       }
@@ -1025,13 +1050,13 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     case OP_OPROJ: {
       const int b = t.aux / P.Hkv, g = t.aux % P.Hkv;
       float *dst = P.pbuf + ((int64_t)(l * P.B + b) * P.Hkv + g) * P.h + t.r0;
-      for (int i = tid; i < rows; i += P.nthr) st_sc1(dst + i, ys_row(ys, i, nw));
+      for (int i = tid; i < rows; i += P.nthr) st_out(P, dst + i, ys_row(ys, i, nw));
       return true;
     }
     case OP_GU: {
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
       for (int i = tid; i < rows; i += P.nthr)
-        st_sc1(u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
+        st_out(P, u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
       return true;
     }
     case OP_DOWN: {
@@ -1039,14 +1064,14 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       float *hid = (P.chk_hidden && l == P.L - 1) ? P.chk_hidden + (int64_t)step * P.B * P.h + t.r0 : nullptr;
       for (int i = tid; i < rows; i += P.nthr) {
         const float v = (i == tid ? res0 : mid_elem(P, l, tok, t.r0 + i)) + ys_row(ys, i, nw);
-        st_sc1(xo + i, v);
+        st_out(P, xo + i, v);
         if (hid) hid[i] = v;
       }
       return true;
     }
     case OP_ROUTER: {
       float *rl = P.rl + vec_off(P, l, 0, P.E) + t.r0;
-      for (int i = tid; i < rows; i += P.nthr) st_sc1(rl + i, rs * ys_row(ys, i, nw));
+      for (int i = tid; i < rows; i += P.nthr) st_out(P, rl + i, rs * ys_row(ys, i, nw));
       return true;
     }
     default: {  // OP_LM
@@ -1073,8 +1098,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         int ix = 0x7fffffff, anynan = 0;
         for (int w = 0; w < nw; ++w) { anynan |= wn[w]; argmax_merge(v, ix, wv[w], wi[w]); }
         if (anynan) v = __builtin_nanf("");
-        st_sc1(P.lmp + 2 * lam, v);
-        st_flag(reinterpret_cast<uint32_t *>(P.lmp) + 2 * lam + 1, (uint32_t)ix);
+        st_out(P, P.lmp + 2 * lam, v);
+        st_out(P, P.lmp + 2 * lam + 1, __builtin_bit_cast(float, (uint32_t)ix));
       }
       return true;
     }
@@ -1253,11 +1278,11 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
     for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) s += ov[w];
-    st_sc1(pdst + hh * rec + PREC_O + j, s);
+    st_out(P, pdst + hh * rec + PREC_O + j, s);
   }
   for (int hh = tid; hh < G; hh += T) {
-    st_sc1(pdst + hh * rec, st[2 * hh]);
-    st_sc1(pdst + hh * rec + 1, st[2 * hh + 1]);
+    st_out(P, pdst + hh * rec, st[2 * hh]);
+    st_out(P, pdst + hh * rec + 1, st[2 * hh + 1]);
   }
   return true;
 }
@@ -1316,20 +1341,23 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
   const bool res = P.persistent != 0;
-  const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
+  // one-XCD placement: the grid has 8 blocks per workgroup and only the
+  // blocks dispatched to XCD 0 (b % 8 == 0) take part; the others leave
+  if (res && P.onexcd && blockIdx.x % P.X != 0) return;
+  const int lam = !res ? blockIdx.x : P.onexcd ? blockIdx.x / P.X : lambda_of_block(blockIdx.x, P.W, P.X);
   if (res) {
     // the XCD this workgroup runs on; the task placement assumes block b on
     // XCD b % 8, and the XCD-local hand-offs need it
     if (threadIdx.x == 0) {
       const uint32_t x = xcc_id();
       P.xcc[lam] = x;
-      const int bad = P.W % P.X == 0 && (int)x != (int)(blockIdx.x % P.X);
+      const int bad = (P.W % P.X == 0 || P.onexcd) && (int)x != (int)(blockIdx.x % P.X);
       if (bad) __hip_atomic_fetch_add(&P.status->xcc_mismatch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (bad && P.local) latch_error(P, PRE_DEV_PLACEMENT, 0, -1, lam, x, blockIdx.x % P.X);
+      if (bad && (P.local || P.onexcd)) latch_error(P, PRE_DEV_PLACEMENT, 0, -1, lam, x, blockIdx.x % P.X);
       sh[2] = bad;
     }
     __syncthreads();
-    if (P.local && sh[2]) return;
+    if ((P.local || P.onexcd) && sh[2]) return;
   }
   const int s_end = res ? P.n_steps : P.b_step + 1;
   const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
@@ -1349,7 +1377,7 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
       const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
       if (!run_task(t, lam, s, pos, tok, lds, wait)) return;
       if (res) {
-        signal_slot(P, t.signal, ep, P.local && (t.op == OP_QKV || t.op == OP_ATTN));
+        signal_slot(P, t.signal, ep, P.onexcd || (P.local && (t.op == OP_QKV || t.op == OP_ATTN)));
         if (tr) trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
       }
     }
@@ -1571,7 +1599,7 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, D.threads, dyn) != hipSuccess)
     return PRE_ERR_HIP;
-  if (per_cu < 1 || (int64_t)per_cu * cus < D.W) return PRE_ERR_SHAPE;
+  if (per_cu < 1 || (int64_t)per_cu * cus < (int64_t)D.W * (D.onexcd ? D.X : 1)) return PRE_ERR_SHAPE;
 
   std::vector<DevLayer> dl(D.L);
   for (int l = 0; l < D.L; ++l) std::memcpy(&dl[l], &w->layers[l], sizeof(DevLayer));
@@ -1677,6 +1705,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;
   P.local = D.local;
+  P.onexcd = persistent ? D.onexcd : 0;  // the per-operator launches spread over every XCD
 }
 
 static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in, const int32_t *d_forced,
@@ -1709,7 +1738,8 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 32, 0xffffffffu);
   void *args[] = {&P};
   const void *kern = e->D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
-  hipError_t err = hipLaunchCooperativeKernel(kern, dim3(e->D.W), dim3(e->D.threads), args, (unsigned)e->lds_dyn,
+  const unsigned nblk = (unsigned)(e->D.W * (e->D.onexcd ? e->D.X : 1));  // one-XCD: 8 blocks per workgroup
+  hipError_t err = hipLaunchCooperativeKernel(kern, dim3(nblk), dim3(e->D.threads), args, (unsigned)e->lds_dyn,
                                               (hipStream_t)stream);
   if (err != hipSuccess) return PRE_ERR_HIP;
   e->epoch_base += (uint32_t)n_steps;

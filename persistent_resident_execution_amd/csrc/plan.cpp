@@ -67,6 +67,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
       lb += 6 * (int64_t)c->ffn_dim * h;
     const int64_t by_size = std::max<int64_t>(8, lb / (32 * 1024) / 8 * 8);
     D->W = (int32_t)std::min<int64_t>(n_cus, by_size);
+    // a small model (at most two XCDs' worth of workgroups) is latency-bound:
+    // it runs on one XCD, where every hand-off stays in that XCD's L2
+    if (!mb && D->W <= 2 * (n_cus / 8)) D->W = std::min(D->W, n_cus / 8);
   }
   if (D->W < 1 || D->W > 4096) return PRE_ERR_SHAPE;
   D->X = 8;
@@ -80,6 +83,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // lambdas [g * W/8, (g + 1) * W/8): one XCD, when there are 8 KV heads and
   // the grid splits evenly over the 8 XCDs
   D->local = c->xcd_local >= 0 && D->Hkv == D->X && D->B == 1 && D->W % D->X == 0;
+  // every workgroup on XCD 0 when the grid fits one XCD's CUs (and the
+  // per-head placement does not apply)
+  D->onexcd = c->xcd_local >= 0 && !D->local && D->B == 1 && D->W <= n_cus / 8;
   // about 128 positions per attention chunk at the longest context, at most
   // one chunk per workgroup of the (sequence, KV head)'s share
   D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 128)));
@@ -615,7 +621,7 @@ extern "C" int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int3
   out->n_tasks = (int32_t)T.size();
   out->attn_splits = D.NC;
   out->validator = pre::validate(D, T);
-  out->xcd_local = D.local;
+  out->xcd_local = D.local ? 1 : D.onexcd ? 2 : 0;
   out->workspace_bytes = Lo.total;
   if (h_tasks)
     for (int32_t i = 0; i < max_tasks && i < (int32_t)T.size(); ++i)

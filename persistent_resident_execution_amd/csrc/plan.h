@@ -81,6 +81,7 @@ struct Dims {
   int32_t mb;         // micro-batch path (batch > 1): MFMA GEMM stages, balanced attention
   int32_t W, X, NC;   // workgroups, XCDs, attention chunks per (sequence, KV head)
   int32_t local;      // QKV->attention->O-projection hand-offs stay inside one XCD's L2
+  int32_t onexcd;     // every workgroup on XCD 0 (small grids): every hand-off stays in its L2
   int32_t Tg;         // workgroups per (sequence, KV head): W / (batch * n_kv_heads); micro-batch: per KV head
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded

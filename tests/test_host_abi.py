@@ -234,16 +234,21 @@ def test_step_bytes_8b_order_of_magnitude(lib):
 
 @pytest.mark.parametrize("m,grid,flag,want", [
     (synth.DENSE8B, 0, 0, 1), (synth.DENSE8B, 64, 0, 1), (synth.DENSE8B, 0, -1, 0),
-    (synth.DENSE8B, 100, 0, 0), (synth.MOE, 0, 0, 1), (synth.TINY, 0, 0, 0),
-    (synth.SMALL_GQA8, 0, 0, 1), (synth.SMALL_GQA8, 40, 0, 1), (synth.SMALL_GQA8, 36, 0, 0)],
+    (synth.DENSE8B, 100, 0, 0), (synth.MOE, 0, 0, 1), (synth.TINY, 0, 0, 2), (synth.TINY, 0, -1, 0),
+    (synth.TINY, 64, 0, 0), (synth.TINY, 24, 0, 2), (synth.SMALL_DENSE, 40, 0, 0), (synth.SMALL_DENSE, 32, 0, 2),
+    (synth.SMALL_GQA8, 40, 0, 1), (synth.SMALL_GQA8, 36, 0, 0), (synth.SMALL_GQA8, 12, 0, 2)],
     ids=lambda v: str(getattr(v, "name", v)))
 def test_xcd_local_mode_only_where_each_head_fits_one_xcd(lib, m, grid, flag, want):
-    """The L2-local hand-offs are used only with 8 KV heads on a grid that
-    splits evenly over the 8 XCDs; there every QKV, attention and O-projection
-    task of head g, and every slot it waits on, lies in XCD g's lambda range."""
+    """The per-head L2-local hand-offs (1) are used only with 8 KV heads on a
+    grid that splits evenly over the 8 XCDs; there every QKV, attention and
+    O-projection task of head g, and every slot it waits on, lies in XCD g's
+    lambda range.  Otherwise a grid that fits one XCD's 32 CUs runs there
+    entirely (2); the default grid of a small model is capped at 32."""
     info, T = E.plan_describe(m, with_tasks=True, grid_wgs=grid, xcd_local=flag)
     assert info.xcd_local == want
-    if not want:
+    if want == 2:
+        assert info.n_wgs <= 32
+    if want != 1:
         return
     W, per = info.n_wgs, info.n_wgs // 8
     spl = 6 if m.is_moe else 5
