@@ -60,3 +60,45 @@ def test_full_size_decode_matches_oracle(oracle_lib, workload):
             break
         tok = nxt
     eng.close()
+
+
+MB_STEPS = 2
+
+
+def test_full_size_microbatch_matches_oracle(oracle_lib):
+    """The micro-batch workload at full size (8B shape, 8 sequences at
+    contexts 512..8192) in the benchmark's launch configuration: every
+    sequence's logits and hidden state of 2 free-running steps against the
+    oracle decoding that sequence alone from the same cache bytes."""
+    w = synth.WORKLOADS["dense8b_mb8"]
+    m, ctx = w.model, list(w.contexts)
+    _say(f"[full-size] dense8b_mb8: weights on the GPU, host copies, caches of contexts {ctx}")
+    W = synth.gen_weights(m, seed=0, device="cuda")
+    om = oracle_lib.OracleModel(m, synth.weights_to_numpy(W))
+    kc, vc = synth.gen_kv_cache(m, max(ctx), seed=1, device="cuda")
+    eng = E.Engine(m, W, kc, vc)
+    eng.set_positions(ctx)
+    tok0 = synth.gen_tokens(m.vocab, m.batch, seed=5, device="cuda")
+    lg = torch.zeros((MB_STEPS, m.batch, m.vocab), dtype=torch.float32, device="cuda")
+    hd = torch.zeros((MB_STEPS, m.batch, m.hidden), dtype=torch.float32, device="cuda")
+    kc_h, vc_h = synth.to_bits(kc), synth.to_bits(vc)  # before the decode appends
+    out = eng.decode(MB_STEPS, in_tokens=tok0, logits=lg, hidden=hd)
+    torch.cuda.synchronize()
+    eng.status()
+    toks, lgs, hds = out.cpu().numpy(), lg.cpu().numpy(), hd.cpu().numpy()
+    eng.close()
+    del W, kc, vc, lg, hd
+    torch.cuda.empty_cache()
+    _say(f"  GPU tokens {toks.tolist()}; oracle per sequence follows")
+    t0 = tok0.cpu().numpy()
+    for b in range(m.batch):
+        kb = np.ascontiguousarray(kc_h[:, b])
+        vb = np.ascontiguousarray(vc_h[:, b])
+        tok = int(t0[b])
+        for s in range(MB_STEPS):
+            nxt, ref_lg, ref_hd = om.decode_step(kb, vb, tok, ctx[b] + s)
+            cont, rec = parity.compare_step(s, int(toks[s, b]), lgs[s, b], hds[s, b], nxt, ref_lg, ref_hd)
+            _say(f"  sequence {b} (context {ctx[b]}) step {s}: {rec}")
+            if not cont:
+                break
+            tok = nxt
