@@ -91,10 +91,56 @@ __device__ __forceinline__ void latch_error(const KP &P, int kind, int step, int
 // Spin (wave 0) until flags[lo..hi) >= ep; all threads return the same
 // verdict.  Bounded by the watchdog; leaves early if another workgroup
 // aborted.
+template <bool PIPE = false>
 __device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t ep, int step,
                                            int stage, int *sh) {
   if (lo >= hi) return true;
-  if (threadIdx.x < 64) {
+  if (PIPE && threadIdx.x < 64 && hi - lo <= 256) {
+    // Up to 256 producers: two polls in flight.  Each check uses the older
+    // poll while the newer one is already on its way, so a flag that lands
+    // is seen about half a memory round trip sooner than with one poll at a
+    // time.
+    const int lane = threadIdx.x;
+    const uint64_t t0 = now_ticks();
+    int verdict = 1, iter = 0;
+    auto poll = [&](uint32_t (&v)[4]) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = lo + lane + 64 * k;
+        v[k] = i < hi ? ld_flag(P.flags + i) : ep;
+      }
+    };
+    auto done = [&](const uint32_t (&v)[4]) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ok &= (int32_t)(v[k] - ep) >= 0;
+      return __all(ok);
+    };
+    uint32_t a[4], b[4];
+    poll(a);
+    while (true) {
+      poll(b);
+      if (done(a)) break;
+      poll(a);
+      if (done(b)) break;
+      if ((++iter & 7) == 0) {
+        if (ld_flag(&P.status->abort)) { verdict = 0; break; }
+        if (now_ticks() - t0 > P.watchdog_ticks) {
+          uint32_t seen = ep;
+          int bad = -1;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if ((int32_t)(b[k] - ep) < 0 && lo + lane + 64 * k < hi) { seen = b[k]; bad = lo + lane + 64 * k; }
+          const uint64_t m = __ballot(bad >= 0);
+          const int first = __ffsll((unsigned long long)m) - 1;
+          if (lane == first) latch_error(P, PRE_DEV_TIMEOUT, step, stage, bad, seen, ep);
+          verdict = 0;
+          break;
+        }
+      }
+    }
+    if (lane == 0) sh[0] = verdict;
+  } else if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const uint64_t t0 = now_ticks();
     int verdict = 1, iter = 0;
@@ -131,14 +177,17 @@ __device__ __forceinline__ bool wait_slots(const KP &P, int lo, int hi, uint32_t
 // Timestamps are taken only when a trace buffer is set: reading the clock is
 // a scalar-memory round trip that the barrier after it would make every
 // wavefront wait for.
-struct Waiter {
+// PIPE: two polls in flight (the batch-1 kernel; the micro-batch kernel's
+// register budget keeps the single poll).
+template <bool PIPE>
+struct WaiterT {
   int active, lo, hi, step, stage;
   uint32_t ep;
   int *sh;
   int tr;  // tracing on
   __device__ __forceinline__ bool operator()(const KP &P) const {
     if (!active) return true;
-    const bool ok = wait_slots(P, lo, hi, ep, step, stage, sh);
+    const bool ok = wait_slots<PIPE>(P, lo, hi, ep, step, stage, sh);
     if (tr && threadIdx.x == 0) sh[3] = (int)(uint32_t)now_ticks();  // trace: end of the wait
     return ok;
   }
@@ -147,6 +196,8 @@ struct Waiter {
     if (tr && threadIdx.x == 0) sh[4 + k] = (int)(uint32_t)now_ticks();
   }
 };
+using Waiter = WaiterT<true>;
+using MbWaiter = WaiterT<false>;
 
 // Publish: every thread's stores are complete, then one flag store.  When
 // all of the flag's readers are on this XCD (the QKV and attention stages

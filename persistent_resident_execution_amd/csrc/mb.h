@@ -171,7 +171,7 @@ __device__ __forceinline__ MbRg mb_rg(const KP &P, const Task &t, int j) {
 // its 16 x B partials to ys[((kp * nb + jr) * 8 + b) * 16 + row].
 template <bool STAGED, int D>
 __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nb, int nrg, const uint8_t *act,
-                                          float *lact, int K, const Waiter *wait, float *ys) {
+                                          float *lact, int K, const MbWaiter *wait, float *ys) {
   const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
   const int jr = wave % nb, kp = wave / nb, nkp = nw / nb;
   MbRg g{0, 0, 0, 0};
@@ -335,7 +335,7 @@ __device__ __forceinline__ MbLds mb_lds(const KP &P, float *lds) {
 // One GEMM task: batches of up to 8 row groups, each streamed, reduced and
 // finished by its operator's epilogue.
 __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int step, const int *toks, float *lds,
-                                        const Waiter &wait) {
+                                        const MbWaiter &wait) {
   const int l = t.layer, op = t.op, tid = threadIdx.x, T = P.nthr, nw = P.nw, B = P.B;
   const MbLds M = mb_lds(P, lds);
   const int nrg = rfl(mb_nrg(P, t));
@@ -355,7 +355,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   bool nan = false;
   bool waited = false;
   for (int j0 = 0; j0 < max(nrg, 1); j0 += nb) {
-    const Waiter *wp = waited ? nullptr : &wait;
+    const MbWaiter *wp = waited ? nullptr : &wait;
     const bool ok = K <= P.mbst ? mb_stream<true, 16>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys)
                                 : mb_stream<false, 12>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys);
     if (!ok) return false;
@@ -548,7 +548,7 @@ __device__ __forceinline__ int64_t mb_share(int64_t N, int Tw, int i) { return (
 // MB_APB: passes per batch of K or V rows.
 template <int MG, int MB_APB>
 __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, int g, int t0, int cnt, int pos,
-                                            float *lds, const Waiter *wait, bool first, bool last, bool &ok) {
+                                            float *lds, const MbWaiter *wait, bool first, bool last, bool &ok) {
   const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr;
   const int wave = wave_id(), nw = P.nw, lane = tid & 63;
   const int cpad = ((P.cmax + 63) / 64) * 64;
@@ -712,7 +712,7 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
 }
 
 __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int step, float *lds,
-                                        const Waiter &wait) {
+                                        const MbWaiter &wait) {
   const int g = t.aux, i = t.r0, Tw = t.r1;
   int64_t N = 0;
   for (int b = 0; b < P.B; ++b) N += P.pos0v[b] + step + 1;
@@ -744,7 +744,7 @@ __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int
 // records of the sequence's workgroups (lane r: the r-th, r + 32-th, ...),
 // merge them pairwise with the running-max rescaling, and reduce across the
 // group; lane 0 packs the 8 outputs for the O projection.
-__device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const Waiter &wait) {
+__device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const MbWaiter &wait) {
   if (!wait(P)) return false;
   const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = threadIdx.x;
   const int rec = d + PREC_O, gd = G * d;
@@ -825,7 +825,7 @@ __device__ __forceinline__ void mb_reduce(const KP &P, int *toks) {
 }
 
 __device__ __forceinline__ bool mb_run_task(const Task &t, int lam, int step, const int *toks, float *lds,
-                                            const Waiter &wait) {
+                                            const MbWaiter &wait) {
   const KP &P = kp_fresh();
   switch (t.op) {
     case OP_EMBED: return mb_embed(P, t, lam, toks, lds);
@@ -872,7 +872,7 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
       const Task t = P.tasks[(int64_t)si * P.W + lam];
       const int tr = res && P.trace != nullptr;
       const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
-      const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
+      const MbWaiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
       if (!mb_run_task(t, lam, s, toks, lds, wait)) return;
       if (res) {
         signal_slot(P, t.signal, ep, false);
