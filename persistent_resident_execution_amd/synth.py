@@ -101,6 +101,10 @@ SMALL_MB = ModelConfig("small_mb", n_layers=2, hidden=384, n_q_heads=6, n_kv_hea
                        head_dim=64, ffn_dim=1056, vocab=2003, max_ctx=320, batch=8)
 SMALL_MB3 = ModelConfig("small_mb3", n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=4,
                         head_dim=64, ffn_dim=544, vocab=1500, max_ctx=200, batch=3)
+# Seven query heads per KV head and 128-dim heads: the micro-batch attention
+# variant that reads q from LDS (more than four query heads per KV head).
+SMALL_MB_G7 = ModelConfig("small_mb_g7", n_layers=2, hidden=512, n_q_heads=14, n_kv_heads=2,
+                          head_dim=128, ffn_dim=832, vocab=1201, max_ctx=240, batch=5)
 
 
 # --------------------------------------------------------------------------

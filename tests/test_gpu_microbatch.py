@@ -145,3 +145,14 @@ def test_microbatch_of_three(oracle_lib):
     res, kc_h, vc_h = S.run(ctx, 4)
     wl, wh = S.check(ctx, res, kc_h, vc_h)
     _say(f"  max dlogit {wl:.2e}, max hidden rel {wh:.2e}")
+
+
+def test_microbatch_seven_query_heads(oracle_lib):
+    """Seven query heads per 128-dim KV head (q read from LDS in attention),
+    five sequences, one of them at context 0."""
+    _say("[test] micro-batch 5, seven query heads per KV head")
+    S = MbSetup(oracle_lib, synth.SMALL_MB_G7)
+    ctx = [3, 150, 60, 0, 201]
+    res, kc_h, vc_h = S.run(ctx, 4)
+    wl, wh = S.check(ctx, res, kc_h, vc_h)
+    _say(f"  max dlogit {wl:.2e}, max hidden rel {wh:.2e}")

@@ -100,7 +100,7 @@ def test_plans_validate(lib, m, grid):
     assert info.workspace_bytes > 0
 
 
-MB = [synth.WORKLOADS["dense8b_mb8"].model, synth.SMALL_MB, synth.SMALL_MB3]
+MB = [synth.WORKLOADS["dense8b_mb8"].model, synth.SMALL_MB, synth.SMALL_MB3, synth.SMALL_MB_G7]
 
 
 @pytest.mark.parametrize("m", MB, ids=lambda m: m.name)
