@@ -825,116 +825,52 @@ __device__ __forceinline__ Geo segs_fp8(const KP &P, const Task &t, const int *s
 
 // Combine the NC chunk partials of (sequence b, KV head g) into
 // xs[0 .. G*d): o_h = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c with
-// M = max_c m_c.  The partial block [NC][G][rec] is contiguous (a record is
-// m, l, two unused words, o[d]: 16-byte aligned); it is read with 16-byte
-// loads into the LDS behind xs, all in flight at once (in slices of chunks
-// when it does not fit), so the combine costs one device round trip.
-__device__ __forceinline__ void attn_combine_lds(const KP &P, int l, int bg, float *lds, int lds_n, float *xs) {
+// M = max_c m_c.  A record is m, l, two unused words, o[d] (16-byte
+// aligned).  Each thread forms its output elements straight from the
+// records: up to 16 chunks per round with all their loads in flight (the
+// m, l pair of a head is one address for the whole wavefront), the running
+// max carried across rounds -- one memory round trip for up to 16 chunks,
+// no LDS staging and no barrier.
+__device__ __forceinline__ void attn_combine(const KP &P, int l, int bg, float *xs) {
   const int b = bg / P.Hkv, g = bg % P.Hkv, G = P.G, d = P.d, NC = P.NC, rec = d + PREC_O;
   const int tid = threadIdx.x, T = P.nthr;
-  const float *src = P.part + (((int64_t)l * P.B + b) * P.Hkv + g) * NC * G * rec;
-  const int go = (G * d + 3) & ~3;
-  float *wt = lds + go;          // [NC][G] e^{m - M}
-  float *den = wt + NC * G;      // [G] sum, [G] max
-  float *blk = lds + ((go + NC * G + 2 * G + 3) & ~3);
-  const int per = NC * G * (rec + 1) <= lds_n ? NC : max(1, min(NC, (lds_n - (int)(blk - lds)) / (G * rec)));
-  const Rsrc r = mkbuf(src, (uint32_t)NC * G * rec * 4);
-  if (per == NC) {
-    // the whole block fits: one bulk load, then every output element forms
-    // its head's maximum and weighted sums itself (no further barrier)
-    float *bk = lds;
-    const int nf = NC * G * rec, n16 = nf / 4;
-    for (int i = tid; i < n16; i += 16 * T) {
-      v4i a[16];
+  const Rsrc r = mkbuf(uni_ptr(P.part + (((int64_t)l * P.B + b) * P.Hkv + g) * NC * G * rec),
+                       (uint32_t)NC * G * rec * 4);
+  for (int i = tid; i < G * d; i += T) {
+    const int hh = i / d, j = i - hh * d;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int c0 = 0; c0 < NC; c0 += 16) {
+      v2i ml[16];
+      float ov[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t base = c0 + k < NC ? (uint32_t)(((c0 + k) * G + hh) * rec) * 4 : 0x80000000u;
+        ml[k] = ld64<CP_SC1>(r, base);
+        ov[k] = ldf<CP_SC1>(r, base + (uint32_t)(PREC_O + j) * 4);
+      }
+      float mv[16], Mn = M;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int mb = ml[k].x;  // copied out as a value before the bit cast
+        mv[k] = c0 + k < NC ? __int_as_float(mb) : -INFINITY;
+        Mn = fmaxf(Mn, mv[k]);
+      }
+      if (Mn != M) {  // rescale what earlier rounds summed (nothing in the first)
+        const float sc = expf(M - Mn);
+        num *= sc;
+        den *= sc;
+        M = Mn;
+      }
 #pragma unroll
       for (int k = 0; k < 16; ++k)
-        a[k] = i + k * T < n16 ? ld128<CP_SC1>(r, (uint32_t)(i + k * T) * 16) : v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (i + k * T < n16) reinterpret_cast<v4i *>(bk)[i + k * T] = a[k];
-    }
-    __syncthreads();
-    const int cs = G * rec;  // stride between chunks
-    // e^{m_c - M} of every (chunk, head), once
-    float *wt = bk + nf;
-    for (int i = tid; i < NC * G; i += T) {
-      const int hh = i % G;
-      const float *bh = bk + hh * rec;
-      float Mx = -INFINITY;
-#pragma unroll 4
-      for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, bh[cc * cs]);
-      wt[i] = expf(bk[(i / G) * cs + hh * rec] - Mx);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid + q * T;
-      if (i < G * d) {
-        const int hh = i / d, j = i - hh * d;
-        const float *bh = bk + hh * rec;
-        float num = 0.f, den = 0.f;
-#pragma unroll 4
-        for (int cc = 0; cc < NC; ++cc) {
-          const float w = wt[cc * G + hh];
-          num = fmaf(w, bh[cc * cs + PREC_O + j], num);
-          den = fmaf(w, bh[cc * cs + 1], den);
+        if (c0 + k < NC) {
+          const int lb = ml[k].y;
+          const float w = expf(mv[k] - M);
+          num = fmaf(w, ov[k], num);
+          den = fmaf(w, __int_as_float(lb), den);
         }
-        xs[i] = num / den;
-      }
     }
-    return;
-  }
-  // sliced: the chunk partials are staged a few chunks at a time
-  float num[4] = {0.f, 0.f, 0.f, 0.f}, dsum = 0.f;
-  for (int c0 = 0; c0 < NC; c0 += per) {
-    const int c1 = min(NC, c0 + per), nf = (c1 - c0) * G * rec;  // nf is even
-    const uint32_t base = (uint32_t)c0 * G * rec * 4;
-    for (int i = tid * 2; i < nf; i += 16 * T) {
-      v2i a[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = i + k * 2 * T;
-        a[k] = e < nf ? ld64<CP_SC1>(r, base + (uint32_t)e * 4) : v2i{0, 0};
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = i + k * 2 * T;
-        if (e < nf) *reinterpret_cast<float2 *>(blk + e) = __builtin_bit_cast(float2, a[k]);
-      }
-    }
-    __syncthreads();
-    if (c0 == 0) {  // the maxima; every slice after the first must reload them
-      if (tid < G) {
-        float Mx = -INFINITY;
-        if (per == NC)
-          for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, blk[(cc * G + tid) * rec]);
-        else
-          for (int cc = 0; cc < NC; ++cc) Mx = fmaxf(Mx, ldf<CP_SC1>(r, (uint32_t)(cc * G + tid) * rec * 4));
-        den[G + tid] = Mx;
-      }
-      __syncthreads();
-    }
-    for (int i = tid; i < (c1 - c0) * G; i += T) wt[c0 * G + i] = expf(blk[i * rec] - den[G + i % G]);
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid + q * T;
-      if (i < G * d) {
-        const int hh = i / d, j = i % d;
-        for (int cc = c0; cc < c1; ++cc)
-          num[q] = fmaf(wt[cc * G + hh], blk[((cc - c0) * G + hh) * rec + PREC_O + j], num[q]);
-      }
-    }
-    if (tid < G)
-      for (int cc = c0; cc < c1; ++cc) dsum = fmaf(wt[cc * G + tid], blk[((cc - c0) * G + tid) * rec + 1], dsum);
-    __syncthreads();
-  }
-  if (tid < G) den[tid] = dsum;
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = tid + q * T;
-    if (i < G * d) xs[i] = num[q] / den[i / d];
+    xs[i] = num / den;
   }
 }
 
@@ -1001,13 +937,10 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   bool normed = false;  // RMSNorm folded into the staging: results scale by norm_scale
   int Kst = 0;
   if (op == OP_OPROJ) {
-    // combine into xs[0..K); its scratch lies behind the padded input, up to
-    // the segment table, and overlaps ys, which is cleared again afterwards
+    // combine into xs[0..K) and zero the padding of the last chunk
     const int Kp = (G.K + 511) & ~511;
-    attn_combine_lds(P, l, t.aux, lds + Kp, (int)(reinterpret_cast<float *>(M.seg) - lds) - Kp, M.xs);
-    __syncthreads();
+    attn_combine(P, l, t.aux, M.xs);
     for (int i = G.K + tid; i < Kp; i += P.nthr) M.xs[i] = 0.f;
-    ys_clear(M.ys, G.NG, nw, P.nthr);
     __syncthreads();
   } else {
     Src src{P.a_norm, nullptr, nullptr, 0, 0, nullptr};  // the baseline's normalised input

@@ -122,11 +122,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   }
   // GEMV phase: staged input, per-row results, reduction scratch, segment
   // table (80 entries of 12 words); the output projection's chunk combine
-  // needs its input (padded to 512) plus every chunk record of its KV head
-  // and one weight per record ahead of the table.  Attention phase: q,
-  // scores, per-wave output partials, softmax stats.
-  const int64_t comb = pad_to(D->G * D->d, 512) + (int64_t)D->NC * D->G * (D->d + 5);
-  D->segoff = (int32_t)pad_to(std::max<int64_t>((int64_t)D->kmax + (int64_t)D->ymax * waves + 256, comb), 4);
+  // writes its result into the staged input and needs no scratch.
+  // Attention phase: q, scores, per-wave output partials, softmax stats.
+  D->segoff = (int32_t)pad_to((int64_t)D->kmax + (int64_t)D->ymax * waves + 256, 4);
   int64_t gemv = (int64_t)D->segoff + 80 * 12;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;

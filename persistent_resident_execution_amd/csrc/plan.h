@@ -86,7 +86,7 @@ struct Dims {
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded
   int32_t ymax;       // most GEMV results one task produces (x waves: LDS partials)
-  int32_t segoff;     // LDS float offset of the GEMV segment table (room for the chunk combine before it)
+  int32_t segoff;     // LDS float offset of the GEMV segment table
   int32_t mbst;       // micro-batch: longest GEMM input staged in LDS (0: none)
   int32_t cmax;       // longest attention chunk (positions; micro-batch: longest piece of one workgroup)
   int32_t lds_bytes;  // dynamic LDS per workgroup

@@ -71,10 +71,7 @@ def _gemv_lds_bytes(m, W, threads=512):
     else:
         y += [2 * _cdiv(m.ffn_dim, W)]
     ymax = _cdiv(max(y), 64) * 64
-    G = m.n_q_heads // m.n_kv_heads
-    nc = min(Tg, max(1, _cdiv(m.max_ctx, 128)))
-    comb = _cdiv(G * m.head_dim, 512) * 512 + nc * G * (m.head_dim + 5)  # input + chunk records + weights
-    return (_cdiv(max(kmax + ymax * (threads // 64) + 256, comb), 4) * 4 + 80 * 12) * 4
+    return (_cdiv(kmax + ymax * (threads // 64) + 256, 4) * 4 + 80 * 12) * 4
 
 
 ALL = [w.model for w in synth.WORKLOADS.values() if w.model.batch == 1] + [
