@@ -272,9 +272,13 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
       v4i a[8];
       v2i g[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
-        g[j] = s.gain ? ld64<CP_DEF>(rg, (uint32_t)(i + j * T) * 8) : v2i{0, 0};
+      for (int j = 0; j < 8; ++j) {  // loads past the input are not issued
+        a[j] = v4i{0, 0, 0, 0};
+        g[j] = v2i{0, 0};
+        if (i + j * T < n4) {
+          a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
+          if (s.gain) g[j] = ld64<CP_DEF>(rg, (uint32_t)(i + j * T) * 8);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -968,7 +972,9 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         }
       }
     }
-    stage_vec(P, M.xs, M.red, src, K, P.kmax);
+    // zero padding up to what the stream reads: whole 512-column chunks
+    // (fp8 expert slots start at their own offsets: up to kmax)
+    stage_vec(P, M.xs, M.red, src, K, FP8 ? P.kmax : min(P.kmax, (K + 1023) & ~1023));
     normed = src.gain != nullptr;
     Kst = K;
   }
