@@ -169,9 +169,10 @@ __device__ __forceinline__ MbRg mb_rg(const KP &P, const Task &t, int j) {
 // the wait, the staging of the input (STAGED) and the loop.  At the end each
 // wavefront folds hi + lo (lanes c and c + 8 of a 16-lane row) and writes
 // its 16 x B partials to ys[((kp * nb + jr) * 8 + b) * 16 + row].
-template <bool STAGED, int D>
+template <bool STAGED, int D, class AfterWait, class AfterStage>
 __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nb, int nrg, const uint8_t *act,
-                                          float *lact, int K, const MbWaiter *wait, float *ys) {
+                                          float *lact, int K, const MbWaiter *wait, float *ys,
+                                          const AfterWait &after_wait, const AfterStage &after_stage) {
   const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
   const int jr = wave % nb, kp = wave / nb, nkp = nw / nb;
   MbRg g{0, 0, 0, 0};
@@ -194,6 +195,7 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
   for (int s = 0; s < D; ++s) a[s] = ld128s<CP_W>(ra, vo, s < n ? (uint32_t)(kb0 + s) * 64u : OOB);
   if (wait) {
     if (!(*wait)(P)) return false;
+    after_wait();  // loads of the producers' other results, in flight with the staging
     if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
       const int n16 = nkb * 64;
       for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
@@ -207,6 +209,7 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
       }
       __syncthreads();
     }
+    after_stage();  // (their values: landed with the staging)
   }
   if (!STAGED) {
 #pragma unroll
@@ -349,6 +352,26 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   else if (op == OP_OPROJ) { act = pk_o(P, l); K = P.Hq * P.d; }
   else { act = pk_x(P, P.L); K = P.h; nidx = 2 * P.L; }
   if (tid < 8) M.ssq[tid] = 0.f;
+  // The producers' sums of squares of this input (wavefront b, sequence b),
+  // loaded once the input is staged, in flight with the weight stream, and
+  // folded into the norm scales after it.
+  float sq4[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool early_ss = nidx >= 0 && P.W <= 256 && K <= P.mbst;  // staged inputs only
+  auto load_ss = [&]() {
+    const int wave = wave_id(), lane = tid & 63;
+    if (early_ss && wave < B) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (lane + 64 * k < P.W) sq4[k] = ld_sc1(ssq_at(P, nidx, lane + 64 * k) + wave);
+    }
+  };
+  auto fold_ss = [&]() {
+    const int wave = wave_id(), lane = tid & 63;
+    if (early_ss && wave < B) {
+      const float s = wave_sum(sq4[0] + sq4[1] + sq4[2] + sq4[3]);
+      if (lane == 0) M.rs[wave] = 1.0f / sqrtf(s / (float)K + P.eps);
+    }
+  };
   // LM: each sequence's running best, kept by wavefront b
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -356,12 +379,18 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   bool waited = false;
   for (int j0 = 0; j0 < max(nrg, 1); j0 += nb) {
     const MbWaiter *wp = waited ? nullptr : &wait;
-    const bool ok = K <= P.mbst ? mb_stream<true, 16>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys)
-                                : mb_stream<false, 12>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys);
+    const bool ok =
+        K <= P.mbst ? mb_stream<true, 16>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, load_ss)
+                    : mb_stream<false, 12>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, [] {});
     if (!ok) return false;
     if (!waited) {
-      if (nidx >= 0) mb_norm_scales(P, nidx, K, M.rs);
-      else if (tid < 8) M.rs[tid] = 1.f;
+      if (early_ss) {
+        fold_ss();
+      } else if (nidx >= 0) {
+        mb_norm_scales(P, nidx, K, M.rs);
+      } else if (tid < 8) {
+        M.rs[tid] = 1.f;
+      }
       waited = true;
     }
     __syncthreads();
