@@ -5,6 +5,7 @@ profiles/, and read them back for the benchmark.
     python -m persistent_resident_execution_amd.profiling traffic FETCH_DIR WRITE_DIR --out FILE \\
         --command "..." --copy-bytes N --workload W --steps K
     python -m persistent_resident_execution_amd.profiling counters DIR --out FILE --command "..."
+    python -m persistent_resident_execution_amd.profiling l2xcd DIR --out FILE --command "..."
 
 `stats` condenses a `rocprofv3 --kernel-trace --stats` run: calls and
 durations per kernel, plus every dispatch of the resident kernel from the
@@ -21,6 +22,11 @@ still hash the same.
 
 `counters` lists any other counters of the last pre_persistent dispatch
 (L2 hits and misses, GPU-active cycles).
+
+`l2xcd` reads a `rocprofv3 --pmc TCC_HIT TCC_MISS --output-format json`
+run, where each dispatch carries one record per counter instance (16 L2
+channels x 8 XCDs, in the order the counter's instance list gives), and
+writes the L2 hit rate of each XCD for the last dispatch of the kernel.
 """
 from __future__ import annotations
 
@@ -131,6 +137,54 @@ def summarize_counters(d, out, command, kernel=KERNEL):
     _write(out, lines)
 
 
+def summarize_l2_per_xcd(d, out, command, kernel=KERNEL):
+    import json
+    hits = sorted(glob.glob(os.path.join(d, "**", "*.json"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *.json under {d}")
+    with open(hits[0]) as fh:
+        doc = json.load(fh)
+    top = doc["rocprofiler-sdk-tool"][0] if "rocprofiler-sdk-tool" in doc else doc
+    # counter id -> (name, XCD index of each instance, in record order)
+    ctr = {}
+    for c in top["counters"]:
+        xcd = []
+        for inst in c.get("instances", []):
+            dims = {x["dimension_name"]: x["index"] for x in inst["dimensions"]}
+            xcd.append(dims.get("DIMENSION_XCC", 0))
+        ctr[c["id"]["handle"]] = (c["name"], xcd)
+    def is_kernel(sym):
+        for key in ("formatted_kernel_name", "demangled_kernel_name", "truncated_kernel_name", "kernel_name"):
+            nm = str(sym.get(key, ""))
+            if nm == kernel or nm == kernel + ".kd" or nm.startswith(kernel + "("):
+                return True
+        return False
+    ids = {k.get("kernel_id") for k in top.get("kernel_symbols", []) if is_kernel(k)}
+    last = None
+    for rec in top["callback_records"]["counter_collection"]:
+        if rec["dispatch_data"]["dispatch_info"]["kernel_id"] in ids:
+            last = rec
+    if last is None:
+        raise RuntimeError(f"no dispatch of {kernel}")
+    per = {}  # name -> [per-XCD sum]
+    seen = {}
+    for r in last["records"]:
+        cid = r["counter_id"]["handle"]
+        name, xcd = ctr[cid]
+        i = seen.get(cid, 0)
+        seen[cid] = i + 1
+        per.setdefault(name, [0.0] * 8)[xcd[i] if i < len(xcd) else 0] += float(r["value"])
+    h, m = per.get("TCC_HIT", [0.0] * 8), per.get("TCC_MISS", [0.0] * 8)
+    lines = ["# L2 hit rate per XCD of the last decode launch (rocprofv3 --pmc, per-instance records)",
+             f"command: {command}", f"source_sha256: {source_hash()}", f"kernel: {kernel}"]
+    for x in range(8):
+        t = h[x] + m[x]
+        lines.append(f"xcd{x}: hit {h[x]:.0f} miss {m[x]:.0f} hit_rate {h[x] / t if t else 0.0:.4f}")
+    th, tm = sum(h), sum(m)
+    lines.append(f"all: hit {th:.0f} miss {tm:.0f} hit_rate {th / (th + tm) if th + tm else 0.0:.4f}")
+    _write(out, lines)
+
+
 def _write(out, lines):
     os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     with open(out, "w") as fh:
@@ -184,12 +238,19 @@ def main():
     c.add_argument("--out", required=True)
     c.add_argument("--command", required=True)
     c.add_argument("--kernel", default=KERNEL)
+    e = sub.add_parser("l2xcd")
+    e.add_argument("dir")
+    e.add_argument("--out", required=True)
+    e.add_argument("--command", required=True)
+    e.add_argument("--kernel", default=KERNEL)
     args = ap.parse_args()
     if args.cmd == "stats":
         summarize_stats(args.dir, args.out, args.command, args.kernel)
     elif args.cmd == "traffic":
         summarize_traffic(args.fetch_dir, args.write_dir, args.out, args.command, args.copy_bytes,
                           args.workload, args.steps, args.kernel)
+    elif args.cmd == "l2xcd":
+        summarize_l2_per_xcd(args.dir, args.out, args.command, args.kernel)
     else:
         summarize_counters(args.dir, args.out, args.command, args.kernel)
 
