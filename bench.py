@@ -15,8 +15,10 @@ position and the median is reported.  Inputs are resident in HBM.
 Also reported: the roofline of the persistent kernel (algorithmic bytes per
 launch over the launch time measured with HIP events on the launch stream,
 against 8 TB/s), the one-kernel-per-operator baseline on the same workload,
-the tiny-decoder persistent vs baseline latency, and the CPU oracle timed on
-a bounded sample (cpu_baseline).
+the rate of a read-only streaming kernel measured on the same box, reported
+beside the decode rate (stream_reference), the tiny-decoder persistent vs
+baseline latency, and the CPU oracle timed on a bounded sample
+(cpu_baseline).
 """
 from __future__ import annotations
 
@@ -175,6 +177,39 @@ def tiny_comparison(repeats=5):
             "launches_per_token_per_op": launches_per_token_per_op(m), "launches_per_token_persistent": 1 / n}
 
 
+def stream_reference(gbps, mib=2048, repeats=5):
+    """The library's streamed GEMV alone (y = W x over a 2 GiB bf16 matrix,
+    4096 columns, one workgroup per CU, streaming loads), best ring depth:
+    a read-only streaming rate measured on this machine, reported beside the
+    decode rate (not instead of the 8 TB/s peak)."""
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    K = 4096
+    rows = (mib << 20) // (K * 2)
+    W = torch.zeros((rows, K), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(K, dtype=torch.float32, device="cuda")
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    best = {}
+    for variant, ring in ((3, 4), (5, 8), (7, 12)):
+        E.debug_gemv(variant, W, x, y)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            E.debug_gemv(variant, W, x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        best[ring] = W.numel() * 2 / statistics.median(ts) / 1e9
+    del W, x, y
+    torch.cuda.empty_cache()
+    ring, ref = max(best.items(), key=lambda kv: kv[1])
+    return {"kernel": "pre_k_gemv_bench", "bytes": rows * K * 2, "gbps": round(ref, 1),
+            "ring_units": ring, "gbps_by_ring": {str(k): round(v, 1) for k, v in best.items()},
+            "decode_frac_of_stream": round(gbps / ref, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +220,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle sample")
     ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timing")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-decoder comparison")
+    ap.add_argument("--no-stream", action="store_true", help="skip the read-only stream reference")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -250,6 +286,9 @@ def main():
                                      "persistent_speedup": round(ub / us_tok, 3),
                                      "same_tokens": bool((btoks == toks).all())}
     eng.close()
+    if not args.no_stream:
+        log("[bench] read-only stream reference")
+        result["stream_reference"] = stream_reference(gbps)
     if not args.no_tiny and not mb:
         log("[bench] tiny decoder persistent vs per-op")
         result["tiny"] = tiny_comparison()
