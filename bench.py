@@ -177,6 +177,40 @@ def tiny_comparison(repeats=5):
             "launches_per_token_per_op": launches_per_token_per_op(m), "launches_per_token_persistent": 1 / n}
 
 
+def phases(args, w, m, eng, g0, P, K):
+    """Busy and idle time per stage from the kernel's timestamp ring (one
+    traced launch of K steps after a warm-up; the first traced step is
+    skipped), written as a text summary."""
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    from persistent_resident_execution_amd import profiling
+    info, _ = E.plan_describe(m, grid_wgs=args.grid)
+    nsi, W = info.n_stage_inst, info.n_wgs
+    tr = torch.zeros(K * nsi * W * 8, dtype=torch.int32, device="cuda")
+    eng.set_trace(tr)
+    t, _ = time_calls(eng, eng.decode, K, g0, P, 1, args.warmup)
+    eng.set_trace(None)
+    rec = tr.view(K, nsi, W, 8).cpu().numpy()
+    if m.batch > 1:
+        names, spl, first = ["embed", "qkv", "attn", "comb", "oproj", "gu", "down", "lm"], 6, 1
+    elif m.is_moe:
+        names, spl, first = ["qkv", "attn", "oproj", "router", "egu", "edown", "lm"], 6, 0
+    else:
+        names, spl, first = ["qkv", "attn", "oproj", "gu", "down", "lm"], 5, 0
+    lines = [f"# per-stage wait / busy / phases (us) from the in-kernel timestamp ring, {w.note}",
+             "command: python3 bench.py " + " ".join(sys.argv[1:]),
+             f"traced: {K} steps in one launch ({t[0] / K * 1e6:.1f} us/step with the ring on), "
+             f"{W} workgroups; means over steps 2..{K} and layers",
+             "wait = task begin -> producers ready; busy = the rest of the task; span = first begin -> "
+             "last end over the workgroups"]
+    lines += profiling.phase_table(rec, names, m.n_layers, spl, first,
+                                   profiling.PHASES_MB if m.batch > 1 else profiling.PHASES)
+    with open(args.phases, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    eng.close()
+
+
 def stream_reference(gbps, mib=2048, repeats=5):
     """The library's streamed GEMV alone (y = W x over a 2 GiB bf16 matrix,
     4096 columns, one workgroup per CU, streaming loads), best ring depth:
@@ -221,6 +255,9 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timing")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-decoder comparison")
     ap.add_argument("--no-stream", action="store_true", help="skip the read-only stream reference")
+    ap.add_argument("--phases", default="",
+                    help="instead of timing: trace --steps steps with the in-kernel timestamp ring and "
+                         "write the per-stage wait/busy/phase summary to this file")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -246,6 +283,9 @@ def main():
     mb = m.batch > 1
     P, K = (list(w.contexts) if mb else w.contexts[0]), args.steps
     pos = P if mb else [P]
+    if args.phases:
+        phases(args, w, m, eng, g0, P, K)
+        return
     log(f"[bench] timing {args.repeats} x {K} persistent steps from position(s) {P}")
     tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
     kern = "pre_persistent_mb" if mb else "pre_persistent"

@@ -185,6 +185,80 @@ def summarize_l2_per_xcd(d, out, command, kernel=KERNEL):
     _write(out, lines)
 
 
+# Phases of each task kind in the trace ring: (name, mark index that ends
+# it); the last phase ends with the task (END).
+END = -1
+PHASES = {"qkv": [("stage", 0), ("stream", 1), ("epi", END)],
+          "attn": [("q+kv", 0), ("scores+softmax", 1), ("pv+reduce", 2), ("store", END)],
+          "oproj": [("combine", 0), ("stream", 1), ("epi", END)],
+          "gu": [("stage", 0), ("stream", 1), ("epi", END)], "down": [("stage", 0), ("stream", 1), ("epi", END)],
+          "router": [("stage", 0), ("stream", 1), ("epi", END)], "egu": [("stage", 0), ("stream", 1), ("epi", END)],
+          "edown": [("stage", 0), ("stream", 1), ("epi", END)], "lm": [("stage", 0), ("stream", 1), ("epi", END)]}
+# the micro-batch kernel marks only the end of its GEMM streams (input
+# staging included); its attention and combine tasks set no marks
+PHASES_MB = {k: [("stream", 1), ("epi", END)] for k in ("qkv", "oproj", "gu", "down", "lm")}
+
+
+def phase_table(rec, stage_names, n_layers, stages_per_layer, first, phases=None):
+    """Per task kind, means over the traced steps (the first one skipped) and
+    layers, in µs: the wait for producers (begin -> wait end), the work after
+    it (busy) split at the task's phase marks, and the span of the stage
+    (earliest begin to latest end over the workgroups); plus the per-layer
+    critical-path deltas (latest end of a stage minus latest end of the one
+    before).  rec: uint32 trace records [steps][stage instances][W][8].
+    stage_names: the per-layer kinds in order, optionally preceded by
+    "embed" (stage instance 0) and followed by "lm" (the last one); kind k
+    of layer l is stage instance first + l * stages_per_layer + k.  A stage
+    without a dependency wait (embed) reports its whole task as busy."""
+    import numpy as np
+    phases = PHASES if phases is None else phases
+    a = rec.astype(np.int64) & 0xffffffff
+    steps, nsi = a.shape[0], a.shape[1]
+    kinds = [n for n in stage_names if n not in ("embed", "lm")]
+    lines = []
+    for nm in stage_names:
+        if nm == "lm":
+            sis = [nsi - 1]
+        elif nm == "embed":
+            sis = [0]
+        else:
+            k = kinds.index(nm)
+            sis = [first + l * stages_per_layer + k for l in range(n_layers)]
+        wait, busy, span, ph = [], [], [], []
+        for s in range(1, steps):
+            for si in sis:
+                r = a[s, si]
+                r = r[r[:, 1] != 0]
+                if len(r) == 0:
+                    continue
+                w0 = r[:, 1] if nm == "embed" else r[:, 2]
+                wait.append(float(np.mean(w0 - r[:, 1])))
+                busy.append(float(np.mean(r[:, 3] - w0)))
+                span.append(float(r[:, 3].max() - r[:, 1].min()))
+                spec = phases.get(nm, [])
+                if spec:
+                    pts = [w0] + [r[:, 3] if m == END else r[:, 4 + m] for _, m in spec]
+                    ph.append([float(np.mean(pts[j + 1] - pts[j])) for j in range(len(spec))])
+        if not busy:
+            continue
+        us = lambda v: round(float(np.mean(v)) / 100.0, 2)  # noqa: E731  (100 MHz ticks)
+        line = f"{nm:7s} wait {us(wait):7.2f}  busy {us(busy):7.2f}  span {us(span):7.2f}"
+        if ph:
+            pm = np.mean(np.array(ph), axis=0) / 100.0
+            line += "  | " + "  ".join(f"{n} {v:.2f}" for (n, _), v in zip(phases[nm], pm))
+        lines.append(line)
+    # d[j]: latest end of stage instance j + 1 minus that of instance j
+    ends = np.array([[a[s, si][:, 3].max() for si in range(nsi)] for s in range(1, steps)], dtype=np.float64)
+    d = np.diff(ends, axis=1).mean(axis=0) / 100.0
+    per = []
+    for k in range(stages_per_layer):
+        v = [d[first + l * stages_per_layer + k - 1] for l in range(n_layers)
+             if first + l * stages_per_layer + k >= 1]
+        per.append(float(np.mean(v)) if v else 0.0)
+    lines.append("critical-path deltas per layer (us): " + "  ".join(f"{n} {v:.2f}" for n, v in zip(kinds, per)))
+    return lines
+
+
 def _write(out, lines):
     os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     with open(out, "w") as fh:
