@@ -41,11 +41,6 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
                                                  c, 0, 0, 0);
 }
 
-template <int CP>
-__device__ __forceinline__ v4i ld128s(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
-}
-
 // Byte offset of the 16 bytes that hold columns k8 * 8 .. + 7 of GEMM input
 // column `col` (sequence b: col b = hi, col 8 + b = lo).
 __device__ __forceinline__ uint32_t pk_off(int k8, int col) {
@@ -156,56 +151,79 @@ __device__ __forceinline__ MbRg mb_rg(const KP &P, const Task &t, int j) {
 // The GEMM stream of one batch of nb row groups (nb = 1, 2, 4 or 8).
 //
 // Wavefront w takes row group jr = w % nb of the batch and k-part
-// kp = w / nb of the nw / nb equal parts of the 32-column blocks (with 8
+// kp = w / nb of the nw / nb equal parts of the 128-column steps (with 8
 // row groups every wavefront owns one group over all of K; with one group
-// the eight wavefronts split K).  Per block it loads one 16-byte A fragment
-// (16 rows x 64 bytes, streaming) and takes the B fragment -- the 1 KB
-// packed input block -- from the copy staged in LDS (inputs up to the
-// staging size) or from device memory, then issues one MFMA.  Each
-// wavefront thus streams 16 rows, contiguously along each row: few
-// concurrent row streams per CU keep the weight fetches page-friendly.  A
-// ring of D blocks of A fragments is kept in flight; the first D are issued
-// before the dependency wait (weights never wait for activations), then
-// the wait, the staging of the input (STAGED) and the loop.  At the end each
-// wavefront folds hi + lo (lanes c and c + 8 of a 16-lane row) and writes
-// its 16 x B partials to ys[((kp * nb + jr) * 8 + b) * 16 + row].
-template <bool STAGED, int D, class AfterWait, class AfterStage>
+// the eight wavefronts split K).
+//
+// Operand mapping ("diagonal"): the 16 rows of the MFMA's A operand are
+// (weight row rho = i / 4, column quarter h = i % 4) of a set of 4 weight
+// rows, so one 16-byte load per lane covers 4 rows x 256 contiguous bytes
+// (the 16-rows x 64-bytes footprint of the plain mapping streams markedly
+// slower).  The 16 B columns are (input column c = j / 4, quarter h = j % 4)
+// of 4 packed input columns.  Entry (i, j) of the product is a true partial
+// dot product only where h(i) = h(j); the other entries are discarded, so a
+// 128-column step of 16 rows takes 4 loads (row sets s) and 16 MFMAs
+// (4 row sets x {hi, lo} x {sequences 0-3, 4-7}), against 4 MFMAs for the
+// plain mapping -- the matrix cores have that headroom.  hi and lo share an
+// accumulator.  A ring of DS steps of A fragments is kept in flight; the
+// first DS are issued before the dependency wait (weights never wait for
+// activations), then the wait, the staging of the input (STAGED) and the
+// loop.  At the end each lane keeps its diagonal entry, a quad of lanes adds
+// the four quarters, and the 16 x B partials go to
+// ys[((kp * nb + jr) * 8 + b) * 16 + row].
+template <bool STAGED, int DS, class AfterWait, class AfterStage>
 __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nb, int nrg, const uint8_t *act,
                                           float *lact, int K, const MbWaiter *wait, float *ys,
                                           const AfterWait &after_wait, const AfterStage &after_stage) {
   const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
+  const int ii = lane & 15, q = lane >> 4, h = ii & 3;
   const int jr = wave % nb, kp = wave / nb, nkp = nw / nb;
   MbRg g{0, 0, 0, 0};
   if (j0 + jr < nrg) g = mb_rg(P, t, j0 + jr);
   const int nr = rfl(g.nr), rs = rfl(g.rs);
   // rows past nr fall outside the buffer and read 0
   const Rsrc ra = mkbuf64(rfl64(g.base), (uint32_t)(nr * rs));
-  const uint32_t vo = (uint32_t)((lane & 15) * rs + (lane >> 4) * 16);
-  const int nkb = K >> 5;
-  const int kb0 = nkb * kp / nkp, n = nkb * (kp + 1) / nkp - kb0;
+  const int nkb = K >> 5, nks = (nkb + 3) >> 2;
+  const int ks0 = nks * kp / nkp, n = nks * (kp + 1) / nkp - ks0;
   const Rsrc rb = mkbuf(uni_ptr(act), (uint32_t)nkb * 1024u);
-  const uint32_t bo = (uint32_t)lane * 16u;
-  v4i a[D], bq[STAGED ? 1 : D];
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // The first D blocks are issued unconditionally (a slot past the span gets
-  // an offset outside every buffer and reads 0 without touching memory), so
-  // every path into the loop has the same loads in flight.
+  // Every out-of-range marker sits in the per-lane offset (the one the
+  // buffer range check covers), set by masks rather than branches so the
+  // ring's waits stay exact: steps past the span, and weight quarters of the
+  // last step past the K / 32 blocks (input quarters there lie outside the
+  // input buffer, or are zero in the staged copy).
   constexpr uint32_t OOB = 0x80000000u;
+  const uint32_t va = (uint32_t)((ii >> 2) * rs + h * 64 + q * 16);  // row set 0, step 0
+  const uint32_t vb = (uint32_t)(h * 1024 + q * 256 + (ii >> 2) * 16);  // packed column c, quarter h
+  auto span_mask = [&](int st) -> uint32_t { return (uint32_t)(st >= n) * OOB; };
+  auto a_off = [&](int st, int s, uint32_t sm) -> uint32_t {  // step st of the span, row set s
+    const int ks = ks0 + st;
+    return (va + (uint32_t)(4 * s * rs) + (uint32_t)ks * 256u) | sm | ((uint32_t)(ks * 4 + h >= nkb) * OOB);
+  };
+  // B fragment f: bit 0 = lo, bit 1 = sequences 4..7
+  auto b_off = [&](int st, int f) -> uint32_t {
+    return vb + (uint32_t)((f & 1) * 128 + (f >> 1) * 64) + (uint32_t)(ks0 + st) * 4096u;
+  };
+  v4i a[DS][4], bq[STAGED ? 1 : DS][4];
+  f32x4_t acc[4][2];
 #pragma unroll
-  for (int s = 0; s < D; ++s) a[s] = ld128s<CP_W>(ra, vo, s < n ? (uint32_t)(kb0 + s) * 64u : OOB);
+  for (int s = 0; s < 4; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < DS; ++st)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[st][s] = ld128<CP_W>(ra, a_off(st, s, span_mask(st)));
   if (wait) {
     if (!(*wait)(P)) return false;
     after_wait();  // loads of the producers' other results, in flight with the staging
     if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
-      const int n16 = nkb * 64;
-      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
+      const int n16 = nkb * 64, m16 = nks * 256;  // (zeros up to the last whole step)
+      for (int i0 = threadIdx.x; i0 < m16; i0 += 16 * P.nthr) {  // 4096 columns: one round
         v4i x[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k)
           x[k] = i0 + k * P.nthr < n16 ? ld128<CP_SC1>(rb, (uint32_t)(i0 + k * P.nthr) * 16u) : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-          if (i0 + k * P.nthr < n16) reinterpret_cast<v4i *>(lact)[i0 + k * P.nthr] = x[k];
+          if (i0 + k * P.nthr < m16) reinterpret_cast<v4i *>(lact)[i0 + k * P.nthr] = x[k];
       }
       __syncthreads();
     }
@@ -213,50 +231,74 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
   }
   if (!STAGED) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) bq[s] = ld128s<CP_SC1>(rb, bo, s < n ? (uint32_t)(kb0 + s) * 1024u : OOB);
+    for (int st = 0; st < DS; ++st)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bq[STAGED ? 0 : st][f] = ld128<CP_SC1>(rb, b_off(st, f) | span_mask(st));
   }
-  auto consume = [&](int s, int kb) {
-    const v4i b = STAGED ? reinterpret_cast<const v4i *>(lact)[kb * 64 + lane] : bq[STAGED ? 0 : s];
-    acc = mfma_16x16x32(a[s], b, acc);
+  auto consume = [&](int slot, int st) {
+    v4i b[4];
+    if (STAGED) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = reinterpret_cast<const v4i *>(lact)[b_off(st, f) >> 4];
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = bq[STAGED ? 0 : slot][f];
+    }
+    // the accumulator changes with every MFMA: no back-to-back dependence
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[s][f >> 1] = mfma_16x16x32(a[slot][s], b[f], acc[s][f >> 1]);
   };
-  auto issue = [&](int s, int kb) {
-    a[s] = ld128s<CP_W>(ra, vo, (uint32_t)kb * 64u);
-    if (!STAGED) bq[s] = ld128s<CP_SC1>(rb, bo, (uint32_t)kb * 1024u);
+  // (inside the span: issues of the steady loop and the tail)
+  auto issue = [&](int slot, int st) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[slot][s] = ld128<CP_W>(ra, a_off(st, s, 0u));
+    if (!STAGED) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bq[STAGED ? 0 : slot][f] = ld128<CP_SC1>(rb, b_off(st, f));
+    }
   };
-  const int m = n >= D ? (n - D) / D : 0;  // rounds whose every issue lies inside the span
+  const int m = n >= DS ? (n - DS) / DS : 0;  // rounds whose every issue lies inside the span
   // The first round is peeled: it still has the prologue's order of loads in
   // flight; the loop after it sees the steady order only, so its waits are
   // exact (one slot at a time).
   if (m > 0) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-      consume(s, kb0 + s);
-      issue(s, kb0 + D + s);
+    for (int s = 0; s < DS; ++s) {
+      consume(s, s);
+      issue(s, DS + s);
     }
-    for (int q = 1; q < m; ++q) {
+    for (int r = 1; r < m; ++r) {
 #pragma unroll
-      for (int s = 0; s < D; ++s) {
-        consume(s, kb0 + q * D + s);
-        issue(s, kb0 + (q + 1) * D + s);
+      for (int s = 0; s < DS; ++s) {
+        consume(s, r * DS + s);
+        issue(s, (r + 1) * DS + s);
       }
     }
   }
-  const int rem = n - m * D;  // 0 <= rem < 2D
+  const int rem = n - m * DS;  // 0 <= rem < 2 DS
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
-    if (s < rem) consume(s, kb0 + m * D + s);
-    if (s + D < rem) issue(s, kb0 + (m + 1) * D + s);
+  for (int s = 0; s < DS; ++s) {
+    if (s < rem) consume(s, m * DS + s);
+    if (s + DS < rem) issue(s, (m + 1) * DS + s);
   }
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s + D < rem) consume(s, kb0 + (m + 1) * D + s);
-  const int c = lane & 15;
-  float v[4];
+  for (int s = 0; s < DS; ++s)
+    if (s + DS < rem) consume(s, (m + 1) * DS + s);
+  // diagonal entries: lane (q, 4c + h) holds row 4s + q, column c of
+  // sequence set m, quarter h, in element h
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = acc[i] + dpp<0x128>(acc[i]);  // row_ror:8: hi + lo
-  if (c < P.B)
-    *reinterpret_cast<float4 *>(ys + ((kp * nb + jr) * 8 + c) * 16 + 4 * (lane >> 4)) = float4{v[0], v[1], v[2], v[3]};
-  (void)nkp;
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const f32x4_t x = acc[s][ms];
+      float v = h == 0 ? x[0] : h == 1 ? x[1] : h == 2 ? x[2] : x[3];
+      v += dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+      v += dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+      const int b = 4 * ms + (ii >> 2);
+      if (h == 0 && b < P.B) ys[((kp * nb + jr) * 8 + b) * 16 + 4 * s + q] = v;
+    }
   return true;
 }
 
@@ -380,8 +422,8 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   for (int j0 = 0; j0 < max(nrg, 1); j0 += nb) {
     const MbWaiter *wp = waited ? nullptr : &wait;
     const bool ok =
-        K <= P.mbst ? mb_stream<true, 16>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, load_ss)
-                    : mb_stream<false, 12>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, [] {});
+        K <= P.mbst ? mb_stream<true, 3>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, load_ss)
+                    : mb_stream<false, 3>(P, t, j0, nb, nrg, act, M.act, K, wp, M.ys, [] {}, [] {});
     if (!ok) return false;
     if (!waited) {
       if (early_ss) {

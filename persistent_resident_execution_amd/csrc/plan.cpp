@@ -134,7 +134,8 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
     // input (32 bytes per column) when the hidden-size inputs fit beside
     // them; attention: the running state of a piece (output, max, sum)
     const int64_t base = (int64_t)waves * 8 * 16 + 16 + 512;
-    const int64_t kst = std::max(D->h, D->Hq * D->d);
+    // (staged in whole 128-column steps: the tail past K is zero-filled)
+    const int64_t kst = pad_to(std::max(D->h, D->Hq * D->d), 128);
     D->mbst = (base + kst * 8) * 4 <= 150 * 1024 ? (int32_t)kst : 0;
     gemv = base + (int64_t)D->mbst * 8;
     attn += (int64_t)D->G * D->d + 4 * D->G;
