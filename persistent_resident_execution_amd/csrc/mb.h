@@ -14,9 +14,11 @@
 //    bf16 weights are exact in the fp32 accumulator, so the result carries
 //    about 16 bits of the activation (better than one fp32 rounding of a
 //    long dot product needs).  16 columns = 8 sequences x (hi, lo).
-//  * The producers write their outputs straight into that packed layout:
-//    32 GEMM columns per 1 KB block, [block][k8 of 4][column of 16][8 bf16],
-//    so lane l of an MFMA reads its 16 bytes at block * 1024 + l * 16.  The
+//  * The producers write their outputs straight into that packed layout,
+//    ordered for the stream's operand mapping (below): 128 GEMM columns per
+//    4 KB step, [fragment f][k-group q of 4][column c of 4][quarter h of
+//    4][8 bf16], so the 16 bytes lane l of an MFMA takes for fragment f of
+//    step s sit at s * 4096 + f * 1024 + l * 16.  The
 //    RMSNorm that precedes a projection is folded as in the batch-1 tiles:
 //    the producer packs x * g and leaves its share of sum(x^2) per sequence;
 //    the consumer scales its outputs by 1 / rms.
@@ -42,11 +44,16 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
 }
 
 // Byte offset of the 16 bytes that hold columns k8 * 8 .. + 7 of GEMM input
-// column `col` (sequence b: col b = hi, col 8 + b = lo).
+// column `col` (sequence b: col b = hi, col 8 + b = lo).  Within step
+// k8 / 16: quarter h = (k8 % 16) / 4, k-group q = k8 % 4; column col is
+// c = col % 4 of fragment f (bit 0: col / 8, bit 1: (col / 4) % 2).
 __device__ __forceinline__ uint32_t pk_off(int k8, int col) {
-  return (((uint32_t)k8 >> 2) * 64u + ((uint32_t)k8 & 3u) * 16u + (uint32_t)col) * 16u;
+  const uint32_t k = (uint32_t)k8, c = (uint32_t)col;
+  const uint32_t f = ((c >> 3) & 1u) | (((c >> 2) & 1u) << 1);
+  return (k >> 4) * 4096u + f * 1024u + (k & 3u) * 256u + (c & 3u) * 64u + ((k >> 2) & 3u) * 16u;
 }
-__device__ __forceinline__ int64_t pk_bytes(int K) { return (int64_t)(K >> 5) * 1024; }
+// (whole steps; the columns past K stay zero)
+__device__ __forceinline__ int64_t pk_bytes(int K) { return (int64_t)((K + 127) >> 7) * 4096; }
 // The packed inputs of layer l: QKV (l = L: the LM head), gate/up, down, O.
 __device__ __forceinline__ uint8_t *pk_x(const KP &P, int l) { return P.pk + (int64_t)l * pk_bytes(P.h); }
 __device__ __forceinline__ uint8_t *pk_m(const KP &P, int l) {
@@ -185,23 +192,21 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
   const Rsrc ra = mkbuf64(rfl64(g.base), (uint32_t)(nr * rs));
   const int nkb = K >> 5, nks = (nkb + 3) >> 2;
   const int ks0 = nks * kp / nkp, n = nks * (kp + 1) / nkp - ks0;
-  const Rsrc rb = mkbuf(uni_ptr(act), (uint32_t)nkb * 1024u);
+  const Rsrc rb = mkbuf(uni_ptr(act), (uint32_t)nks * 4096u);
   // Every out-of-range marker sits in the per-lane offset (the one the
   // buffer range check covers), set by masks rather than branches so the
   // ring's waits stay exact: steps past the span, and weight quarters of the
-  // last step past the K / 32 blocks (input quarters there lie outside the
-  // input buffer, or are zero in the staged copy).
+  // last step past the K / 32 blocks (the input there is zero).
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t va = (uint32_t)((ii >> 2) * rs + h * 64 + q * 16);  // row set 0, step 0
-  const uint32_t vb = (uint32_t)(h * 1024 + q * 256 + (ii >> 2) * 16);  // packed column c, quarter h
   auto span_mask = [&](int st) -> uint32_t { return (uint32_t)(st >= n) * OOB; };
   auto a_off = [&](int st, int s, uint32_t sm) -> uint32_t {  // step st of the span, row set s
     const int ks = ks0 + st;
     return (va + (uint32_t)(4 * s * rs) + (uint32_t)ks * 256u) | sm | ((uint32_t)(ks * 4 + h >= nkb) * OOB);
   };
-  // B fragment f: bit 0 = lo, bit 1 = sequences 4..7
+  // B fragment f (bit 0 = lo, bit 1 = sequences 4..7): 1 KB, lane-linear
   auto b_off = [&](int st, int f) -> uint32_t {
-    return vb + (uint32_t)((f & 1) * 128 + (f >> 1) * 64) + (uint32_t)(ks0 + st) * 4096u;
+    return (uint32_t)(ks0 + st) * 4096u + (uint32_t)f * 1024u + (uint32_t)lane * 16u;
   };
   v4i a[DS][4], bq[STAGED ? 1 : DS][4];
   f32x4_t acc[4][2];
@@ -215,15 +220,15 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
     if (!(*wait)(P)) return false;
     after_wait();  // loads of the producers' other results, in flight with the staging
     if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
-      const int n16 = nkb * 64, m16 = nks * 256;  // (zeros up to the last whole step)
-      for (int i0 = threadIdx.x; i0 < m16; i0 += 16 * P.nthr) {  // 4096 columns: one round
+      const int n16 = nks * 256;
+      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
         v4i x[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k)
           x[k] = i0 + k * P.nthr < n16 ? ld128<CP_SC1>(rb, (uint32_t)(i0 + k * P.nthr) * 16u) : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-          if (i0 + k * P.nthr < m16) reinterpret_cast<v4i *>(lact)[i0 + k * P.nthr] = x[k];
+          if (i0 + k * P.nthr < n16) reinterpret_cast<v4i *>(lact)[i0 + k * P.nthr] = x[k];
       }
       __syncthreads();
     }

@@ -169,10 +169,11 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->tok = take((int64_t)D.B * 4 * 4);
   Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers, micro-batch)
   if (D.mb) {
-    // packed bf16 hi/lo GEMM inputs: 1 KB per 32 columns; per layer the QKV
-    // input (plus the LM head's), the gate/up input, the down input and the
-    // O-projection input
-    const int64_t kh = D.h / 32 * 1024, kf = (int64_t)D.ffn / 32 * 1024, ko = (int64_t)D.Hq * D.d / 32 * 1024;
+    // packed bf16 hi/lo GEMM inputs: 4 KB per 128 columns (whole steps, the
+    // tail left zero); per layer the QKV input (plus the LM head's), the
+    // gate/up input, the down input and the O-projection input
+    const int64_t kh = (int64_t)cdiv(D.h, 128) * 4096, kf = (int64_t)cdiv(D.ffn, 128) * 4096,
+                  ko = (int64_t)cdiv(D.Hq * D.d, 128) * 4096;
     Lo->pk = take((2 * (int64_t)D.L + 1) * kh + D.L * (kf + ko));
     Lo->ssq = take((2 * (int64_t)D.L + 1) * D.W * D.B * f);
     // attention records of every (workgroup, sequence) of a layer
