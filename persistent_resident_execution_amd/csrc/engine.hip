@@ -684,36 +684,46 @@ __device__ __forceinline__ void wave_argmax_l63(float &bv, int &bi) {
 // id), then the n_shared shared experts with weight 1.  Every workgroup
 // that needs the choice computes it; the inputs and the order of operations
 // are the same everywhere, so all of them agree.  sel/selw in LDS.
+//
+// The selection is one parallel pass, not k rounds of an argmax: expert e's
+// rank is the number of experts ahead of it in the order (logit descending,
+// lower id first on ties, a NaN logit last), counted by tpe threads of
+// consecutive lanes over E / tpe experts each; ranks below top_k are the
+// choice, in that order.  (A NaN logit makes the softmax sum NaN, so every
+// weight is NaN and the LM head's NaN check reports it.)
 __device__ __forceinline__ void route(const KP &P, int l, int *sel, float *selw, float *scratch) {
-  const int tid = threadIdx.x, T = P.nthr;
-  const float *rl = P.rl + vec_off(P, l, 0, P.E);
-  for (int i = tid; i < P.E; i += T) scratch[i] = ld_sc1(rl + i);
+  const int tid = threadIdx.x, T = P.nthr, E = P.E, lane = tid & 63;
+  const float *rl = P.rl + vec_off(P, l, 0, E);
+  for (int i = tid; i < E; i += T) scratch[i] = ld_sc1(rl + i);
   __syncthreads();
-  if (tid < 64) {
-    const int lane = tid;
-    float m = -INFINITY;
-    for (int i = lane; i < P.E; i += 64) m = fmaxf(m, scratch[i]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int i = lane; i < P.E; i += 64) s += expf(scratch[i] - m);
-    s = wave_sum(s);
-    uint32_t taken = 0;  // bit li: local index lane + 64 * li already chosen (E <= 1024)
-    for (int k = 0; k < P.top_k; ++k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff, li = 0;
-      for (int i = lane; i < P.E; i += 64, ++li)
-        if (!((taken >> li) & 1u) && (scratch[i] > bv || (scratch[i] == bv && i < bi))) { bv = scratch[i]; bi = i; }
-      wave_argmax_l63(bv, bi);
-      // a NaN logit leaves no winner: expert E-1 keeps the addresses valid and
-      // the NaN weight reaches the LM head's NaN check
-      const int win = min(__builtin_amdgcn_readlane(bi, 63), P.E - 1);
-      const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 63));
-      if ((win & 63) == lane) taken |= 1u << (win >> 6);
-      if (lane == 0) { sel[k] = win; selw[k] = expf(wv - m) / s; }
+  // softmax statistics: every wavefront, in the same order
+  float m = -INFINITY;
+  for (int i = lane; i < E; i += 64) m = fmaxf(m, scratch[i]);
+  m = wave_max(m);
+  float s = 0.f;
+  for (int i = lane; i < E; i += 64) s += expf(scratch[i] - m);
+  s = wave_sum(s);
+  int tpe = 1;  // threads per expert: T / E rounded down to a power of two, at most 64
+  while (tpe < 64 && tpe * 2 * E <= T) tpe *= 2;
+  const int part = tid & (tpe - 1), per = T / tpe;
+  for (int base = 0; base < E; base += per) {  // (the same trip count in every lane)
+    const int e = base + tid / tpe;
+    const float ve = e < E ? scratch[e] : 0.f;
+    const float ke = ve != ve ? -INFINITY : ve;
+    int c = 0;
+    for (int j = part; j < E; j += tpe) {
+      const float vj = scratch[j];
+      const float kj = vj != vj ? -INFINITY : vj;
+      c += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
     }
-    if (lane == 0)
-      for (int k = 0; k < P.n_shared; ++k) { sel[P.top_k + k] = k; selw[P.top_k + k] = 1.0f; }
+    for (int o = 1; o < tpe; o <<= 1) c += __shfl_xor(c, o);
+    if (e < E && part == 0 && c < P.top_k) {
+      sel[c] = e;
+      selw[c] = expf(ve - m) / s;
+    }
   }
+  if (tid == 0)
+    for (int k = 0; k < P.n_shared; ++k) { sel[P.top_k + k] = k; selw[P.top_k + k] = 1.0f; }
   __syncthreads();
 }
 
