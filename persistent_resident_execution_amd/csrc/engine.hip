@@ -1137,137 +1137,248 @@ __device__ __forceinline__ int reduce_lm(const KP &P, int *sh) {
 // tasks) and q are read after it.  Writes the chunk's (max, sum,
 // unnormalised output) per head; the output projection combines the chunks.
 
-constexpr int APB = 5;  // attention passes whose K/V rows are held in registers
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
-                                           const Waiter &wait) {
-  const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, c = t.r0, NC = t.r1;
-  const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr;
-  const int wave = wave_id(), nw = P.nw, lane = tid & 63;
-  const int n = pos + 1, C = (n + NC - 1) / NC, t0 = c * C;
-  const int cnt = max(0, min(n, t0 + C) - t0);
-  const int cpad = ((P.cmax + 63) / 64) * 64;
-  float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
-  const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * d;
-  const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * d * 2);
-  const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * d * 2);
-  const int LPP = d / 8, PPW = 64 / LPP, sub = lane % LPP, grp = lane / LPP;
-  const int PASS = nw * PPW;
-  auto koff = [=](int tt) { return (uint32_t)((int64_t)(t0 + tt) * d + sub * 8) * 2; };
-  // cached rows of the first batch, before the wait
-  v4i kb[APB], vb[APB];
+// D(16x16) += A(16 rows x 32) * B(32 x 16 columns).  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each as the 8 consecutive k of
+// group l / 16; it receives D rows 4 * (l / 16) .. + 3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// Attention of one piece on the matrix cores: positions [t0, t0 + cnt) of
+// sequence b, KV head g, layer l, all G query heads (cnt <= the score
+// buffer's cpad columns).  NQ = d / 32 column quarters of a head; NS = sets
+// of 16 / NQ query heads in the score columns.
+//  * Scores, with the diagonal operand mapping of the micro-batch GEMM
+//    stream: A row i = (position i / NQ, quarter i % NQ) of 16 / NQ
+//    consecutive cached K rows -- one 16-byte load per lane reads them
+//    whole, 1 KB contiguous -- and B column j = (query head j / NQ, quarter
+//    j % NQ), the scaled q as hi + lo bf16 parts.  The diagonal entries,
+//    added over the quarters, are the scores; they go to sc[head][position].
+//    The first RA loads are issued before the wait with the step's newest
+//    row left out, and that row is reloaded after it.
+//  * Softmax per head (max, exponentials, sum into st[2h], st[2h + 1]; max
+//    -1e30 for an empty piece), with zeros to whole 32-position chunks.
+//  * o = sum_t p_t V_t in chunks of 32 positions: A rows (head, hi/lo part of
+//    p), B column j = one of the head's dimensions, the 8 positions of a
+//    k-group packed from 8 V loads (each lane loads its own 8-dimension slice
+//    of 8 consecutive rows, so the packing stays in the lane).  Wavefront w
+//    leaves its share in ored[(w * G + h) * d + j].
+// VPRE: each wavefront's first V chunk is also loaded before the wait (the
+// newest row again left out and reloaded), for short pieces whose V rows
+// would otherwise arrive only after the scores.  Ends after a barrier; false
+// if the wait was aborted.  Phase marks 0-2 after the scores, the softmax
+// and the weighted sums.
+template <int NQ, int NS, bool VPRE, class WaitT>
+__device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int t0, int cnt, int pos, float *sc,
+                                          int cpad, float *ored, float *st, const WaitT *wait) {
+  constexpr int D = 32 * NQ;  // head dimension
+  constexpr int PL = 16 / NQ;  // positions per K load
+  constexpr int RA = 8;  // K loads in flight per wavefront
+  constexpr uint32_t OOB = 0x80000000u;
+  const int G = P.G;
+  const int wave = wave_id(), nw = P.nw, lane = threadIdx.x & 63, ii = lane & 15, qg = lane >> 4;
+  const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * D;
+  const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * D * 2);
+  const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * D * 2);
+  // K load u: positions u * PL ..; this lane's row and 16 bytes.  Before the
+  // wait the row this step's QKV stage writes is left out (reloaded after).
+  auto koff = [&](int u, bool pre) -> uint32_t {
+    const int tt = u * PL + ii / NQ;
+    const bool in = tt < cnt && !(pre && t0 + tt == pos);
+    return in ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + (uint32_t)((ii % NQ) * 64 + qg * 16) : OOB;
+  };
+  const int nL = (cnt + PL - 1) / PL;
+  const int nk = nL > wave ? (nL - wave + nw - 1) / nw : 0;  // this wavefront's loads u = wave + nw * k
+  // V chunk c (positions c * 32 ..): load r of this lane = position
+  // c * 32 + 8 qg + r, dimensions 8 (ii % (D / 8)) ..
+  const uint32_t vcol = (uint32_t)(ii % (D / 8)) * 16u;
+  auto vload = [&](v4i (&x)[8], int c, bool pre) {
 #pragma unroll
-  for (int p = 0; p < APB; ++p) {
-    const int tt = p * PASS + wave * PPW + grp;
-    const bool old = tt < cnt && t0 + tt != pos;
-    kb[p] = old ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
-    vb[p] = old ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
-  }
-  if (!wait(P)) return false;
-  // q of the group and the newest row
-  const float *qsrc = P.q + vec_off(P, l, b, P.Hq * d) + (int64_t)g * G * d;
-  for (int i = tid; i < G * d; i += T) qs[i] = ld_sc1(qsrc + i) * P.attn_scale;
+    for (int r = 0; r < 8; ++r) {
+      const int tt = c * 32 + 8 * qg + r;
+      const bool in = tt < cnt && !(pre && t0 + tt == pos);
+      x[r] = ld128<CP_SC1>(vr, in ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + vcol : OOB);
+    }
+  };
+  const int nC = (cnt + 31) >> 5;
+  const int nkc = nC > wave ? (nC - wave + nw - 1) / nw : 0;  // this wavefront's chunks c = wave + nw * k
+  v4i ka[RA], va[8], vn[8];
 #pragma unroll
-  for (int p = 0; p < APB; ++p) {
-    const int tt = p * PASS + wave * PPW + grp;
-    if (tt < cnt && t0 + tt == pos) {
-      kb[p] = ld128<CP_SC1>(kr, koff(tt));
-      vb[p] = ld128<CP_SC1>(vr, koff(tt));
+  for (int s = 0; s < RA; ++s) ka[s] = ld128<CP_SC1>(kr, koff(wave + nw * s, true));
+  if (VPRE) vload(va, wave, true);
+  if (wait && !(*wait)(P)) return false;
+  if (t0 <= pos && pos < t0 + cnt) {  // the newest row, now written
+    const int up = (pos - t0) / PL;
+    if (up % nw == wave && up / nw < RA) {
+#pragma unroll
+      for (int s = 0; s < RA; ++s)
+        if (s == up / nw) ka[s] = ld128<CP_SC1>(kr, koff(up, false));
+    }
+    const int tp = pos - t0 - 32 * wave;  // in this wavefront's first V chunk: load (tp % 8) of every lane
+    if (VPRE && tp >= 0 && tp < 32) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r == (tp & 7)) {
+          const int tt = 32 * wave + 8 * qg + r;
+          va[r] = ld128<CP_SC1>(vr, tt < cnt ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + vcol : OOB);
+        }
     }
   }
-  __syncthreads();
-  wait.mark(0);
-  // scores
-  for (int base = 0; base < cnt; base += APB * PASS) {
-    if (base > 0) {
+  // q as the score columns: set s, column j = (head s * 16 / NQ + j / NQ, quarter j % NQ)
+  v4i qh[NS], ql[NS];
+  {
+    // (written by other workgroups this step: read at device scope; absent heads read 0)
+    const Rsrc rq = mkbuf(uni_ptr(P.q + vec_off(P, l, b, P.Hq * D) + (int64_t)g * G * D), (uint32_t)(G * D * 4));
 #pragma unroll
-      for (int p = 0; p < APB; ++p) {
-        const int tt = base + p * PASS + wave * PPW + grp;
-        kb[p] = tt < cnt ? ld128<CP_SC1>(kr, koff(tt)) : v4i{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) {
+      const int hh = s * (16 / NQ) + ii / NQ;
+      const uint32_t qo = hh < G ? (uint32_t)(hh * D + (ii % NQ) * 32 + qg * 8) * 4u : OOB;
+      const float4 x0 = __builtin_bit_cast(float4, ld128<CP_SC1>(rq, qo));
+      const float4 x1 = __builtin_bit_cast(float4, ld128<CP_SC1>(rq, qo + 16u));
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = x[2 * i] * P.attn_scale, a1 = x[2 * i + 1] * P.attn_scale;
+        const uint16_t h0 = f2bf(a0), h1 = f2bf(a1);
+        const uint16_t l0 = f2bf(a0 - bf16f(h0)), l1 = f2bf(a1 - bf16f(h1));
+        qh[s][i] = (int)((uint32_t)h0 | ((uint32_t)h1 << 16));
+        ql[s][i] = (int)((uint32_t)l0 | ((uint32_t)l1 << 16));
       }
     }
+  }
+  // scores of K load u (positions u * PL ..) into sc
+  auto scores = [&](const v4i &a, int u) {
 #pragma unroll
-    for (int p = 0; p < APB; ++p) {
-      const int tt = base + p * PASS + wave * PPW + grp;
-      if (base + p * PASS < cnt) {
-        for (int hh = 0; hh < G; ++hh) {
-          const float4 *q4 = reinterpret_cast<const float4 *>(qs + hh * d + sub * 8);
-          float s = dot8_bf16(kb[p], q4[0], q4[1], 0.f);
-          s = (LPP == 16) ? sum16(s) : sum8(s);
-          if (tt < cnt && sub == 0) sc[hh * cpad + tt] = s;
+    for (int s = 0; s < NS; ++s) {
+      f32x4_t c = mfma_16x16x32(a, qh[s], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      c = mfma_16x16x32(a, ql[s], c);
+      if (NQ == 4) {  // lane (qg, 4c + h): position qg, head c, quarter h in element h
+        const int h = ii & 3;
+        float v = h == 0 ? c[0] : h == 1 ? c[1] : h == 2 ? c[2] : c[3];
+        v += dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+        v += dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+        const int tt = u * PL + qg, hh = s * 4 + (ii >> 2);
+        if (h == 0 && tt < cnt && hh < G) sc[hh * cpad + tt] = v;
+      } else {  // lane (qg, 2c + h): positions 2 qg (element h) and 2 qg + 1 (element 2 + h), head c
+        const int h = ii & 1;
+        float v0 = h ? c[1] : c[0], v1 = h ? c[3] : c[2];
+        v0 += dpp<0xB1>(v0);
+        v1 += dpp<0xB1>(v1);
+        const int tt = u * PL + 2 * qg, hh = s * 8 + (ii >> 1);
+        if (h == 0 && hh < G) {
+          if (tt < cnt) sc[hh * cpad + tt] = v0;
+          if (tt + 1 < cnt) sc[hh * cpad + tt + 1] = v1;
         }
       }
     }
+  };
+  for (int k0 = 0; k0 < nk; k0 += RA) {
+#pragma unroll
+    for (int s = 0; s < RA; ++s) {
+      if (k0 + s < nk) scores(ka[s], wave + nw * (k0 + s));
+      ka[s] = ld128<CP_SC1>(kr, koff(wave + nw * (k0 + s + RA), false));
+    }
   }
+  if (!VPRE) vload(va, wave, false);  // the first V chunk, during the softmax
   __syncthreads();
-  // per-head max and exponentials
+  if (wait) wait->mark(0);
   for (int hh = wave; hh < G; hh += nw) {
     float m = -INFINITY;
     for (int i = lane; i < cnt; i += 64) m = fmaxf(m, sc[hh * cpad + i]);
     m = wave_max(m);
-    float s = 0.f;
+    float sm = 0.f;
     for (int i = lane; i < cnt; i += 64) {
       const float e = expf(sc[hh * cpad + i] - m);
       sc[hh * cpad + i] = e;
-      s += e;
+      sm += e;
     }
-    s = wave_sum(s);
-    if (lane == 0) { st[2 * hh] = cnt > 0 ? m : -1e30f; st[2 * hh + 1] = s; }
+    for (int i = cnt + lane; i < nC * 32; i += 64) sc[hh * cpad + i] = 0.f;  // whole chunks
+    sm = wave_sum(sm);
+    if (lane == 0) { st[2 * hh] = cnt > 0 ? m : -1e30f; st[2 * hh + 1] = sm; }
   }
   __syncthreads();
-  wait.mark(1);
-  // o = sum_t p_t V_t: a lane owns 8 dims of one position per pass
-  float acc[8][8];
+  if (wait) wait->mark(1);
+  f32x4_t acc[D / 16];
 #pragma unroll
-  for (int hh = 0; hh < 8; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  for (int base = 0; base < cnt; base += APB * PASS) {
-    if (base > 0) {
-#pragma unroll
-      for (int p = 0; p < APB; ++p) {
-        const int tt = base + p * PASS + wave * PPW + grp;
-        vb[p] = tt < cnt ? ld128<CP_SC1>(vr, koff(tt)) : v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < APB; ++p) {
-      const int tt = base + p * PASS + wave * PPW + grp;
-      if (tt < cnt) {
-        const v4i vw = vb[p];
-        const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
-                            bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh)
-          if (hh < G) {
-            const float pr = sc[hh * cpad + tt];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, v[e], acc[hh][e]);
-          }
-      }
-    }
-  }
-  // reduce the PPW position groups of the wave (lanes sub, sub + LPP, ...):
-  // the two 8-lane halves of a row first when LPP = 8, then across rows
-#pragma unroll
-  for (int hh = 0; hh < 8; ++hh)
+  for (int m = 0; m < D / 16; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto pv = [&](const v4i (&x)[8], int c) {
+    // A: row ii = (head ii / 2, part ii % 2) of p, positions c * 32 + 8 qg ..
+    const int hh = ii >> 1;
+    float p[8];
     if (hh < G) {
+      const float4 *p4 = reinterpret_cast<const float4 *>(sc + hh * cpad + c * 32 + 8 * qg);
+      const float4 p0 = p4[0], p1 = p4[1];
+      p[0] = p0.x; p[1] = p0.y; p[2] = p0.z; p[3] = p0.w; p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[hh][e];
-        if (LPP == 8) v += dpp<0x128>(v);  // row_ror:8
-        acc[hh][e] = xrow_sum(v);
-      }
+      for (int e = 0; e < 8; ++e) p[e] = 0.f;
     }
-  if (grp == 0) {
+    v4i pa;
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
-      if (hh < G)
+    for (int i = 0; i < 4; ++i) {
+      uint16_t w0 = f2bf(p[2 * i]), w1 = f2bf(p[2 * i + 1]);
+      if (ii & 1) { w0 = f2bf(p[2 * i] - bf16f(w0)); w1 = f2bf(p[2 * i + 1] - bf16f(w1)); }
+      pa[i] = (int)((uint32_t)w0 | ((uint32_t)w1 << 16));
+    }
+    // B for output dimension 8 (ii % (D / 8)) + e: element e of the 8 rows
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ored[(wave * G + hh) * d + sub * 8 + e] = acc[hh][e];
+    for (int m = 0; m < D / 16; ++m) {
+      v4i bw;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v4i &X = x[2 * u], &Y = x[2 * u + 1];
+        uint32_t xa, ya;
+        if (NQ == 4) {
+          xa = (uint32_t)X[m >> 1];
+          ya = (uint32_t)Y[m >> 1];
+        } else {  // D = 64: lanes ii >= 8 take dimensions 4..7 of their slice
+          xa = (uint32_t)(ii >= 8 ? X[(m >> 1) + 2] : X[m >> 1]);
+          ya = (uint32_t)(ii >= 8 ? Y[(m >> 1) + 2] : Y[m >> 1]);
+        }
+        bw[u] = (int)((m & 1) ? (xa >> 16) | (ya & 0xffff0000u) : (xa & 0xffffu) | (ya << 16));
+      }
+      acc[m] = mfma_16x16x32(pa, bw, acc[m]);
+    }
+  };
+  for (int k = 0; k < nkc; k += 2) {
+    vload(vn, wave + nw * (k + 1), false);
+    pv(va, wave + nw * k);
+    if (k + 1 >= nkc) break;
+    vload(va, wave + nw * (k + 2), false);
+    pv(vn, wave + nw * (k + 1));
+  }
+  // this wavefront's partial outputs: rows 4 qg + e = (head 2 qg + e / 2, part e % 2)
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) {
+    const int dim = NQ == 4 ? ii * 8 + m : (ii & 7) * 8 + m + 4 * (ii >> 3);
+    const int h0 = 2 * qg, h1 = 2 * qg + 1;
+    if (h0 < G) ored[(wave * G + h0) * D + dim] = acc[m][0] + acc[m][1];
+    if (h1 < G) ored[(wave * G + h1) * D + dim] = acc[m][2] + acc[m][3];
   }
   __syncthreads();
-  wait.mark(2);
+  if (wait) wait->mark(2);
+  return true;
+}
+
+// One attention chunk task: chunk c of NC of (sequence b, KV head g)'s
+// positions, all G query heads, on the matrix cores; the record (m, l, -, -,
+// o[d]) per head goes to the O-projection task's combine.
+__device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
+                                           const Waiter &wait) {
+  const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, c = t.r0, NC = t.r1;
+  const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr, nw = P.nw;
+  const int n = pos + 1, C = (n + NC - 1) / NC, t0 = c * C;
+  const int cnt = max(0, min(n, t0 + C) - t0);
+  const int cpad = ((P.cmax + 63) / 64) * 64;
+  float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
+  const bool ok = d == 64    ? attn_core<2, 1, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait)
+                  : G <= 4 ? attn_core<4, 1, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait)
+                           : attn_core<4, 2, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait);
+  if (!ok) return false;
   const int rec = d + PREC_O;
   float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * rec;
   for (int i = tid; i < G * d; i += T) {

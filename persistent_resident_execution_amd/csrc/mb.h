@@ -32,17 +32,6 @@
 // ---------------------------------------------------------------------------
 // MFMA operands and the packed layout
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// D(16x16) += A(16 rows x 32) * B(32 x 16 columns).  Lane l supplies row
-// (l % 16) of A and column (l % 16) of B, each as the 8 consecutive k of
-// group l / 16; it receives D rows 4 * (l / 16) .. + 3 of column l % 16.
-__device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                 c, 0, 0, 0);
-}
-
 // Byte offset of the 16 bytes that hold columns k8 * 8 .. + 7 of GEMM input
 // column `col` (sequence b: col b = hi, col 8 + b = lo).  Within step
 // k8 / 16: quarter h = (k8 % 16) / 4, k-group q = k8 % 4; column col is
@@ -619,8 +608,11 @@ __device__ __forceinline__ int64_t mb_share(int64_t N, int Tw, int i) { return (
 
 // Positions [t0, t0 + cnt) of sequence b (at most cmax of them), merged into
 // the running (max, sum, output) state of the piece kept in LDS; the last
-// sub-piece writes the piece's record.  Both products run on the matrix
-// cores (NQ = d / 32 column quarters of a head; NS = sets of 16 / NQ query
+// sub-piece writes the piece's record.  (The scheme of attn_core, the
+// batch-1 chunk task's attention, kept as its own copy: instantiating that
+// shared template in this register-bound kernel moved its register
+// allocation and made the step about 2% slower.)  Both products run on the
+// matrix cores (NQ = d / 32 column quarters of a head; NS = sets of 16 / NQ query
 // heads in the score columns):
 //  * Scores, with the same diagonal operand mapping as the GEMM stream: A
 //    row i = (position i / NQ, quarter i % NQ) of 16 / NQ consecutive cached
