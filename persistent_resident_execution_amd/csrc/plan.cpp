@@ -87,8 +87,10 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // per-head placement does not apply)
   D->onexcd = c->xcd_local >= 0 && !D->local && D->B == 1 && D->W <= n_cus / 8;
   // about 128 positions per attention chunk at the longest context, at most
-  // one chunk per workgroup of the (sequence, KV head)'s share
-  D->NC = c->attn_splits > 0 ? c->attn_splits : std::min(D->Tg, std::max(1, cdiv(c->max_ctx, 128)));
+  // 16 chunks (longer chunks cost the matrix-core attention little, and the
+  // O projection's combine reads one record per chunk) and at most one chunk
+  // per workgroup of the (sequence, KV head)'s share
+  D->NC = c->attn_splits > 0 ? c->attn_splits : std::min({D->Tg, 16, std::max(1, cdiv(c->max_ctx, 128))});
   if (mb) D->NC = 1;  // the micro-batch attention split follows the contexts of each step
   if (D->NC > D->Tg) return PRE_ERR_SHAPE;
   D->threads = c->wg_threads > 0 ? c->wg_threads : 512;
