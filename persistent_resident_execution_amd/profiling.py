@@ -189,7 +189,7 @@ def summarize_l2_per_xcd(d, out, command, kernel=KERNEL):
 # it); the last phase ends with the task (END).
 END = -1
 PHASES = {"qkv": [("stage", 0), ("stream", 1), ("epi", END)],
-          "attn": [("q+kv", 0), ("scores+softmax", 1), ("pv+reduce", 2), ("store", END)],
+          "attn": [("q+scores", 0), ("softmax", 1), ("pv", 2), ("store", END)],
           "oproj": [("combine", 0), ("stream", 1), ("epi", END)],
           "gu": [("stage", 0), ("stream", 1), ("epi", END)], "down": [("stage", 0), ("stream", 1), ("epi", END)],
           "router": [("stage", 0), ("stream", 1), ("epi", END)], "egu": [("stage", 0), ("stream", 1), ("epi", END)],

@@ -33,7 +33,7 @@ def test_phase_table_batch1():
     qkv = lines[0].split()
     assert qkv[:7] == ["qkv", "wait", "0.50", "busy", "1.50", "span", "2.03"]
     assert "stage 0.28  stream 0.70  epi 0.52" in lines[0]
-    assert "pv+reduce 0.20  store 0.32" in lines[1]
+    assert "pv 0.20  store 0.32" in lines[1]
     # stage ends 300 ticks apart: 3 us per stage on the critical path
     assert lines[-1].endswith("qkv 3.00  attn 3.00  oproj 3.00  gu 3.00  down 3.00")
 
