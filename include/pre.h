@@ -83,8 +83,8 @@ extern "C" {
  * grid_wgs: workgroups that take part (0 = one per CU, or fewer -- one per
  * 32 KB of a layer's weights, a multiple of 8 -- for small models);
  * wg_threads: threads per workgroup (0 = 512).  attn_splits: KV chunks per KV
- * head and sequence (0 = about one per 128 positions of max_ctx, at most the
- * workgroups per KV head).  xcd_local: 0 = hand the q/K/V rows and the
+ * head and sequence (0 = about one per 128 positions of max_ctx, at most 16
+ * and at most the workgroups per KV head).  xcd_local: 0 = hand the q/K/V rows and the
  * attention partials from producer to consumer through the XCD's own L2
  * when every consumer sits on the producer's XCD (8 KV heads, a grid that is
  * a multiple of 8: KV head g's QKV rows, attention chunks and output
