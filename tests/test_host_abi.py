@@ -177,6 +177,19 @@ def test_attention_and_o_projection_are_xcd_local_on_the_8b_shape(lib):
         assert lo == W + aux * per and hi == lo + info.attn_splits  # that head's chunk tasks
 
 
+@pytest.mark.parametrize("wl,want", [("dense8b_ctx1024", 12), ("dense8b_ctx8192", 16), ("moe", 16),
+                                     ("tiny", 2), ("dense8b_mb8", 1)])
+def test_default_attention_split(lib, wl, want):
+    """Default KV chunks per (sequence, KV head): about one per 128 positions
+    of max_ctx, at most 16 and at most the workgroups per KV head; one for the
+    micro-batch (its split follows the step's contexts)."""
+    m = synth.WORKLOADS[wl].model
+    info, _ = E.plan_describe(m)
+    assert info.attn_splits == want
+    info, _ = E.plan_describe(m, attn_splits=3) if m.batch == 1 else (info, None)
+    assert info.attn_splits == (3 if m.batch == 1 else 1)
+
+
 def _planted(m, mutate):
     info, T = E.plan_describe(m, with_tasks=True)
     T = T.copy()
