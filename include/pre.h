@@ -72,6 +72,10 @@ extern "C" {
 #define PRE_DEV_NAN 3       /* a NaN logit reached the argmax               */
 #define PRE_DEV_PLACEMENT 4 /* a workgroup ran on another XCD than the
                                XCD-local hand-offs assume (see xcd_local)   */
+#define PRE_DEV_CONTEXT 5   /* a sequence's position was negative, or the
+                               call's steps would pass max_ctx (slot = the
+                               sequence, observed = its position, expected =
+                               max_ctx)                                      */
 
 /* ---- model configuration ---------------------------------------------- */
 /* Plain data, read once at create.  n_experts == 0 means a dense SwiGLU FFN
@@ -127,9 +131,18 @@ typedef struct pre_weights {
 
 /* KV cache (device): k and v are bf16 [n_layers][batch][n_kv_heads][max_ctx]
  * [head_dim].  Positions below a sequence's current position must hold its
- * K/V (post-RoPE K); the engine appends at the current position. */
+ * K/V (post-RoPE K); the engine appends at the current position.
+ * d_ctx_len (device, int32 [batch], 4-byte aligned, caller-owned, may be
+ * NULL): sequence b's current position = the number of its cached tokens.
+ * Every decode call reads it on the device at its start and advances it by
+ * n_steps on the device at its end, so the host never tracks positions
+ * (the pages' split of prefill and decode: a decode engine takes over a
+ * cache that another engine filled -- SemiAnalysis TileRT digest, "PD
+ * separation").  With NULL the engine keeps its own device array in the
+ * workspace, starting at 0. */
 typedef struct pre_kv {
   void *k, *v;
+  int32_t *d_ctx_len;
 } pre_kv;
 
 /* Optional per-call outputs for checking (device, may be NULL):

@@ -48,7 +48,9 @@ struct KP {
   float *x_out, *pbuf, *q, *u, *rl, *part, *lmp, *x_emb, *a_norm, *xmid;
   int32_t *tok_slot;
   // this call
-  int32_t n_steps, pos0;
+  int32_t n_steps;
+  int32_t *ctx_len;      // [B] each sequence's position (= cached tokens) at the call's start;
+                         // read by every workgroup at the start, advanced at the end
   uint32_t epoch_base, watchdog_ticks;
   const int32_t *in_tok, *forced;
   int32_t *out_tok;
@@ -57,10 +59,11 @@ struct KP {
   uint32_t trace_cap;
   int32_t persistent;
   int32_t b_si, b_step;  // baseline launches: the stage and step to run
+  int32_t b_nsteps;      // baseline: steps of the whole call (the position check)
   int32_t local;         // XCD-local hand-offs (QKV -> attention -> O projection)
   int32_t onexcd;        // every workgroup on XCD 0: every hand-off in that XCD's L2
+  int32_t drop_slot;     // debug: the task setting this ready flag skips the store (-1: none)
   // micro-batch
-  int32_t pos0v[8];      // each sequence's position at the call's first step
   int32_t mbst;          // longest GEMM input staged in LDS (columns; longer ones stream from memory)
   uint8_t *pk;           // packed GEMM inputs
   float *ssq;            // per-workgroup sums of squares of the normalised inputs
@@ -209,7 +212,7 @@ using MbWaiter = WaiterT<false>;
 __device__ __forceinline__ void signal_slot(const KP &P, int slot, uint32_t ep, bool local) {
   drain();
   __syncthreads();
-  if (threadIdx.x == 0 && slot >= 0) {
+  if (threadIdx.x == 0 && slot >= 0 && slot != P.drop_slot) {
     if (local) __builtin_amdgcn_raw_buffer_store_b32(ep, mkbuf(P.flags + slot, 4), 0, 0, CP_SC0);
     else st_flag(P.flags + slot, ep);
   }
@@ -1409,6 +1412,19 @@ __device__ __forceinline__ void trace_rec(const KP &P, int step, int si, int lam
   for (int k = 0; k < 4; ++k) r[4 + k] = (uint32_t)sh[4 + k];
 }
 
+// Sequence b's position at the start of the call, checked against the
+// cache: every step of the call must stay below max_ctx.  Every workgroup
+// reads the same value and takes the same branch, so on an error they all
+// leave (one latches PRE_DEV_CONTEXT) and no wait is left pending.  Returns
+// -1 on an error.
+__device__ __forceinline__ int call_position(const KP &P, int b) {
+  const int p = __builtin_amdgcn_readfirstlane((int)ld_flag(reinterpret_cast<const uint32_t *>(P.ctx_len) + b));
+  const int n = P.persistent ? P.n_steps : P.b_nsteps;
+  if (p >= 0 && (int64_t)p + n <= P.max_ctx) return p;
+  if (threadIdx.x == 0 && blockIdx.x == 0) latch_error(P, PRE_DEV_CONTEXT, 0, -1, b, (uint32_t)p, (uint32_t)P.max_ctx);
+  return -1;
+}
+
 __device__ __forceinline__ bool token_ok(const KP &P, int tok, int step) {
   if (tok >= 0 && tok < P.V) return true;
   if (threadIdx.x == 0) latch_error(P, PRE_DEV_BAD_TOKEN, step, -1, -1, (uint32_t)tok, 0);
@@ -1472,10 +1488,14 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   }
   const int s_end = res ? P.n_steps : P.b_step + 1;
   const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
+  // the position of the call's first step, from the device array (every
+  // workgroup reads it here; workgroup 0 advances it after the last step)
+  const int pos0 = call_position(P, 0);
+  if (pos0 < 0) return;
   int tok = res ? (P.forced ? P.forced[0] : P.in_tok[0]) : P.tok_slot[1];
   for (int s = res ? 0 : P.b_step; s < s_end; ++s) {
     const uint32_t ep = P.epoch_base + (uint32_t)s + 1u;
-    const int pos = P.pos0 + s;
+    const int pos = pos0 + s;
     if (res) {
       if (P.forced) tok = P.forced[(int64_t)s * P.B];
       if (!token_ok(P, tok, s)) return;
@@ -1508,6 +1528,9 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
       if (!P.forced) tok = nt;
     }
   }
+  // Workgroup 0 has seen every workgroup's LM flag of the last step, so every
+  // workgroup has read the start position: advance it.
+  if (lam == 0 && threadIdx.x == 0) st_flag(reinterpret_cast<uint32_t *>(P.ctx_len), (uint32_t)(pos0 + P.n_steps));
 }
 
 // the micro-batch task set and kernel
@@ -1545,6 +1568,16 @@ extern "C" __global__ void __launch_bounds__(512) pre_k_argmax(KP P, int step) {
     if (nt < 0) latch_error(P, PRE_DEV_NAN, step, P.n_si - 1, -1, 0, 0);
     P.tok_slot[0] = nt < 0 ? 0 : nt;
     P.out_tok[(int64_t)step * P.B] = nt;
+  }
+}
+
+// Baseline: every sequence's position advances by the call's steps (the
+// last launch of the call, after every stage has read the start positions).
+extern "C" __global__ void pre_k_advance(KP P, int n) {
+  const int b = threadIdx.x;
+  if (b < P.B) {
+    const int p = P.ctx_len[b];
+    if (p >= 0 && (int64_t)p + n <= P.max_ctx) P.ctx_len[b] = p + n;
   }
 }
 
@@ -1620,7 +1653,7 @@ struct pre_engine {
   size_t ws_bytes;
   pre_kv kv;
   const void *embed, *final_norm, *lm_head;
-  int32_t pos[8];
+  int32_t *ctx;  // device position array [B]: the caller's, or the workspace's own
   uint32_t epoch_base;
   uint32_t watchdog_ms;
   int lds_dyn;
@@ -1630,6 +1663,7 @@ struct pre_engine {
   uint32_t *trace;
   size_t trace_bytes;
   int device;
+  int32_t drop_slot;  // debug: ready flag never published (-1: none)
 };
 
 static inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
@@ -1684,11 +1718,10 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   if (rc != PRE_OK) return rc;
   if (!w->embed || !w->final_norm || !w->lm_head || !kv->k || !kv->v) return PRE_ERR_ARG;
   if (!al16(w->embed) || !al16(w->final_norm) || !al16(w->lm_head) || !al16(kv->k) || !al16(kv->v) ||
-      !al16(d_workspace))
+      !al16(d_workspace) || ((uintptr_t)kv->d_ctx_len & 3))
     return PRE_ERR_ALIGN;
   for (int l = 0; l < D.L; ++l)
     if ((rc = check_layer(D, w->layers[l])) != PRE_OK) return rc;
-  if ((int64_t)D.max_ctx * D.d * 2 >= (1ll << 32)) return PRE_ERR_SHAPE;
   Layout Lo;
   build_layout(D, &Lo);
   if ((int64_t)ws_bytes < Lo.total) return PRE_ERR_WORKSPACE;
@@ -1744,7 +1777,7 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   e->embed = w->embed;
   e->final_norm = w->final_norm;
   e->lm_head = w->lm_head;
-  std::memset(e->pos, 0, sizeof(e->pos));
+  e->ctx = kv->d_ctx_len ? kv->d_ctx_len : (int32_t *)(ws + Lo.ctx);
   e->epoch_base = 0;
   const char *wd = std::getenv("PRE_WATCHDOG_MS");
   e->watchdog_ms = wd ? (uint32_t)std::max(1, std::atoi(wd)) : 2000u;
@@ -1754,22 +1787,29 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   e->trace = nullptr;
   e->trace_bytes = 0;
   e->device = dev;
+  e->drop_slot = -1;
   e->lw.assign(w->layers, w->layers + D.L);
   *out = e;
   return PRE_OK;
 }
 
+// Host helpers over the device position array: both wait for the device
+// (every queued call has advanced the positions) before they copy.
 extern "C" int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
   for (int b = 0; b < e->D.B; ++b)
     if (h_pos[b] < 0 || h_pos[b] >= e->D.max_ctx) return PRE_ERR_CONTEXT;
-  for (int b = 0; b < e->D.B; ++b) e->pos[b] = h_pos[b];
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(e->ctx, h_pos, sizeof(int32_t) * e->D.B, hipMemcpyHostToDevice) != hipSuccess)
+    return PRE_ERR_HIP;
   return PRE_OK;
 }
 
 extern "C" int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
-  for (int b = 0; b < e->D.B; ++b) h_pos[b] = e->pos[b];
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(h_pos, e->ctx, sizeof(int32_t) * e->D.B, hipMemcpyDeviceToHost) != hipSuccess)
+    return PRE_ERR_HIP;
   return PRE_OK;
 }
 
@@ -1810,7 +1850,8 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.xmid = (float *)(ws + Lo.xmid);
   P.pk = D.mb ? (uint8_t *)(ws + Lo.pk) : nullptr;
   P.ssq = D.mb ? (float *)(ws + Lo.ssq) : nullptr;
-  for (int b = 0; b < D.B; ++b) P.pos0v[b] = e->pos[b];
+  P.ctx_len = e->ctx;
+  P.drop_slot = e->drop_slot;
   P.mbst = D.mbst;
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
@@ -1825,8 +1866,7 @@ static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in,
   if (n_steps == 0) return PRE_OK;  // nothing to do; the buffers are not read
   if (!d_out || (!d_in && !d_forced)) return PRE_ERR_ARG;
   if (e->broken) return PRE_ERR_BROKEN;
-  for (int b = 0; b < e->D.B; ++b)
-    if ((int64_t)e->pos[b] + n_steps > e->D.max_ctx) return PRE_ERR_CONTEXT;
+  if (n_steps > e->D.max_ctx) return PRE_ERR_CONTEXT;  // (positions live on the device: checked there)
   return PRE_OK;
 }
 
@@ -1838,7 +1878,6 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   KP P;
   fill_kp(e, P, 1);
   P.n_steps = n_steps;
-  P.pos0 = e->pos[0];
   P.epoch_base = e->epoch_base;
   P.in_tok = d_in_tokens;
   P.forced = d_forced;
@@ -1854,7 +1893,6 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
                                               (hipStream_t)stream);
   if (err != hipSuccess) return PRE_ERR_HIP;
   e->epoch_base += (uint32_t)n_steps;
-  for (int b = 0; b < e->D.B; ++b) e->pos[b] += n_steps;
   return PRE_OK;
 }
 
@@ -1870,7 +1908,7 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
   P.out_tok = d_out_tokens;
   P.chk_logits = chk ? chk->logits : nullptr;
   P.chk_hidden = chk ? chk->hidden : nullptr;
-  P.pos0 = e->pos[0];
+  P.b_nsteps = n_steps;
   hipStream_t st = (hipStream_t)stream;
   const Dims &D = e->D;
   const dim3 blk(D.threads);
@@ -1900,8 +1938,8 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
     stage(D.n_si - 1, s);
     hipLaunchKernelGGL(pre_k_argmax, dim3(1), dim3(64), 0, st, P, s);
   }
+  hipLaunchKernelGGL(pre_k_advance, dim3(1), dim3(64), 0, st, P, n_steps);
   if (hipGetLastError() != hipSuccess) return PRE_ERR_HIP;
-  for (int b = 0; b < D.B; ++b) e->pos[b] += n_steps;
   return PRE_OK;
 }
 
@@ -2030,13 +2068,25 @@ extern "C" int pre_debug_mfma(const void *d_a, const void *d_b, float *d_d, void
 
 // Debug: byte offsets of the workspace regions (status, flags, layers, tasks,
 // rope, xcc, x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid, pk,
-// ssq, total) -- 20 int64 values.
+// ssq, ctx, total) -- 21 int64 values.
 extern "C" int pre_debug_layout(const pre_engine *e, int64_t *out) {
   if (!e || !out) return PRE_ERR_ARG;
   const Layout &L = e->Lo;
-  const int64_t v[20] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u,
-                         L.rl, L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.xmid, L.pk, L.ssq, L.total};
-  for (int i = 0; i < 20; ++i) out[i] = v[i];
+  const int64_t v[21] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u, L.rl,
+                         L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.xmid, L.pk, L.ssq, L.ctx, L.total};
+  for (int i = 0; i < 21; ++i) out[i] = v[i];
+  return PRE_OK;
+}
+
+// Debug: from the next decode call on, the task that sets ready flag `slot`
+// (an index into the step's slots, 0 .. n_slots-1) skips the store; -1 turns
+// this off.  Every consumer of that flag then waits until the watchdog fires,
+// latches PRE_DEV_TIMEOUT and raises the abort word, and every other
+// workgroup leaves at its next wait: the way to exercise the watchdog path
+// with every kernel still ending normally.
+extern "C" int pre_debug_drop_signal(pre_engine *e, int32_t slot) {
+  if (!e || slot < -1 || slot >= e->D.n_si * e->D.W) return PRE_ERR_ARG;
+  e->drop_slot = slot;
   return PRE_OK;
 }
 

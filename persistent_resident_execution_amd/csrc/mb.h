@@ -445,7 +445,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
           const int gh = p / half, g = gh / (P.G + 2), hh = gh % (P.G + 2), jj = p % half;
           const float r = M.rs[b];
           float a = r * mb_y(ys, nb, nkp, jA, b, i), c = r * mb_y(ys, nb, nkp, jA + 1, b, i);
-          const int pos = P.pos0v[b] + step;
+          const int pos = toks[8 + b] + step;
           if (hh <= P.G) {  // RoPE on q and k
             const float cs = P.rope[(int64_t)pos * half + jj];
             const float sn = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + jj];
@@ -839,16 +839,17 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
   __syncthreads();  // the LDS is reused by the next sub-piece
 }
 
-__device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int step, float *lds,
+__device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int step, const int *toks, float *lds,
                                         const MbWaiter &wait) {
   const int g = t.aux, i = t.r0, Tw = t.r1;
+  const int *pos0v = toks + 8;
   int64_t N = 0;
-  for (int b = 0; b < P.B; ++b) N += P.pos0v[b] + step + 1;
+  for (int b = 0; b < P.B; ++b) N += pos0v[b] + step + 1;
   const int64_t f0 = mb_share(N, Tw, i), f1 = mb_share(N, Tw, i + 1);
   bool ok = true, first = true;
   int64_t pre = 0;
   for (int b = 0; b < P.B && ok; ++b) {
-    const int pos = P.pos0v[b] + step;
+    const int pos = pos0v[b] + step;
     const int64_t lo = max(f0, pre), hi = min(f1, pre + pos + 1);
     // the piece in sub-pieces of at most cmax positions
     for (int64_t c0 = lo; c0 < hi && ok; c0 += P.cmax) {
@@ -873,20 +874,21 @@ __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int
 // records of the sequence's workgroups (lane r: the r-th, r + 32-th, ...),
 // merge them pairwise with the running-max rescaling, and reduce across the
 // group; lane 0 packs the 8 outputs for the O projection.
-__device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const MbWaiter &wait) {
+__device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const int *toks, const MbWaiter &wait) {
   if (!wait(P)) return false;
   const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = threadIdx.x;
+  const int *pos0v = toks + 8;
   const int rec = d + PREC_O, gd = G * d;
   const int ngr = (t.r1 - t.r0) >> 3, gpp = P.nthr >> 5;
   int64_t N = 0;
-  for (int b = 0; b < P.B; ++b) N += P.pos0v[b] + step + 1;
+  for (int b = 0; b < P.B; ++b) N += pos0v[b] + step + 1;
   for (int q0 = 0; q0 < ngr; q0 += gpp) {
     const int grp = q0 + (tid >> 5), sub = tid & 31;
     const bool act = grp < ngr;
     const int e = t.r0 + 8 * grp, b = act ? e / gd : 0, k = e % gd, hh = k / d, j0 = k % d;
     int64_t pre = 0;
-    for (int bb = 0; bb < b; ++bb) pre += P.pos0v[bb] + step + 1;
-    const int64_t nb = P.pos0v[b] + step + 1;
+    for (int bb = 0; bb < b; ++bb) pre += pos0v[bb] + step + 1;
+    const int64_t nb = pos0v[b] + step + 1;
     // workgroups holding f = pre and f = pre + nb - 1
     const int i_lo = (int)(((pre + 1) * Tw - 1) / N), i_hi = (int)(((pre + nb) * Tw - 1) / N);
     // the layer's records under one descriptor; record (wg, b, hh) at a per-lane offset
@@ -958,8 +960,8 @@ __device__ __forceinline__ bool mb_run_task(const Task &t, int lam, int step, co
   const KP &P = kp_fresh();
   switch (t.op) {
     case OP_EMBED: return mb_embed(P, t, lam, toks, lds);
-    case OP_ATTN: return mb_attn(P, t, lam, step, lds, wait);
-    case OP_COMB: return mb_comb(P, t, step, wait);
+    case OP_ATTN: return mb_attn(P, t, lam, step, toks, lds, wait);
+    case OP_COMB: return mb_comb(P, t, step, toks, wait);
     default: return mb_gemm(P, t, lam, step, toks, lds, wait);
   }
 }
@@ -969,7 +971,7 @@ __device__ __forceinline__ bool mb_run_task(const Task &t, int lam, int step, co
 extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
-  __shared__ int toks[8];
+  __shared__ int toks[16];  // [0, 8): the step's tokens; [8, 16): the sequences' positions at the call's start
   const bool res = P.persistent != 0;
   const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
   const int tid = threadIdx.x;
@@ -984,6 +986,14 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
   if (tid < P.B) {  // the first step's tokens (the baseline: its step's)
     const int s = s_begin;
     toks[tid] = P.forced ? P.forced[(int64_t)s * P.B + tid] : (s == 0 ? P.in_tok[tid] : P.tok_slot[tid]);
+  }
+  // every sequence's start position (workgroup 0 advances them after the
+  // last step); all workgroups see the same values and leave together on an
+  // error
+  for (int b = 0; b < P.B; ++b) {
+    const int p = call_position(P, b);
+    if (p < 0) return;
+    if (tid == 0) toks[8 + b] = p;
   }
   __syncthreads();
   for (int s = s_begin; s < s_end; ++s) {
@@ -1023,6 +1033,8 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
       __syncthreads();
     }
   }
+  if (res && lam == 0 && tid < P.B)
+    st_flag(reinterpret_cast<uint32_t *>(P.ctx_len) + tid, (uint32_t)(toks[8 + tid] + P.n_steps));
 }
 
 // Baseline: each sequence's greedy token of step `step` (one workgroup).

@@ -29,6 +29,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (c->head_dim != 64 && c->head_dim != 128) return PRE_ERR_SHAPE;
   if (c->hidden % 8 || (c->n_q_heads * c->head_dim) % 8) return PRE_ERR_SHAPE;
   if (c->batch > 8) return PRE_ERR_SHAPE;
+  // the K/V append addresses a layer's whole cache through one buffer
+  // descriptor (32-bit size and offsets), the attention one head's
+  if ((int64_t)c->batch * c->n_kv_heads * c->max_ctx * c->head_dim * 2 >= (1ll << 32)) return PRE_ERR_SHAPE;
   const bool moe = c->n_experts > 0;
   const bool mb = c->batch > 1;
   // micro-batch: dense models whose GEMM inputs come in whole 32-column
@@ -170,6 +173,7 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->a_norm = take((int64_t)D.B * D.kmax * f);
   Lo->tok = take((int64_t)D.B * 4 * 4);
   Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers, micro-batch)
+  Lo->ctx = take((int64_t)D.B * 4);
   if (D.mb) {
     // packed bf16 hi/lo GEMM inputs: 4 KB per 128 columns (whole steps, the
     // tail left zero); per layer the QKV input (plus the LM head's), the

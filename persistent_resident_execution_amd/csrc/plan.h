@@ -68,6 +68,7 @@ struct Layout {
   int64_t status, flags, layers, tasks, rope, xcc;
   int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid;
   int64_t pk, ssq;  // micro-batch: packed GEMM inputs, per-workgroup sums of squares
+  int64_t ctx;      // the engine's own position array [B] (used when the caller passes none)
   int64_t total;
 };
 

@@ -21,7 +21,7 @@ PRE_OK = 0
 ERRORS = {-1: "PRE_ERR_ARG", -2: "PRE_ERR_SHAPE", -3: "PRE_ERR_ALIGN", -4: "PRE_ERR_WORKSPACE",
           -5: "PRE_ERR_HIP", -6: "PRE_ERR_UNSUPPORTED", -7: "PRE_ERR_DEVICE", -8: "PRE_ERR_BROKEN",
           -9: "PRE_ERR_CONTEXT"}
-DEV_ERRORS = {0: "ok", 1: "timeout", 2: "bad token", 3: "nan"}
+DEV_ERRORS = {0: "ok", 1: "timeout", 2: "bad token", 3: "nan", 4: "placement", 5: "context"}
 
 
 class PreError(RuntimeError):
@@ -53,7 +53,7 @@ class Weights(C.Structure):
 
 
 class KV(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("d_ctx_len", C.c_void_p)]
 
 
 class Check(C.Structure):
@@ -108,7 +108,8 @@ def lib():
         debug = {"pre_debug_fp8_decode": [vp, vp, C.c_int, vp], "pre_debug_layout": [vp, vp],
                  "pre_debug_lane_ops": [vp, vp, vp],
                  "pre_debug_gemv": [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp],
-                 "pre_debug_copy": [vp, vp, C.c_size_t, vp], "pre_debug_mfma": [vp, vp, vp, vp]}
+                 "pre_debug_copy": [vp, vp, C.c_size_t, vp], "pre_debug_mfma": [vp, vp, vp, vp],
+                 "pre_debug_drop_signal": [vp, i32]}
         for name, at in debug.items():
             if hasattr(L, name):
                 getattr(L, name).argtypes = at
@@ -164,6 +165,94 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+# ---- argument checks ----------------------------------------------------------
+# The C ABI receives raw device pointers and cannot tell a host tensor, a wrong
+# dtype or a short buffer from a good one; any of these would make a kernel
+# read or write out of bounds.  Every tensor is checked here before a call.
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def check_tensor(t, name, dtype, shape=None, numel=None, device_type="cuda"):
+    """t must be a contiguous tensor of `dtype` on a `device_type` device,
+    of exactly `shape` (if given) and at least `numel` elements (if given)."""
+    _need(torch.is_tensor(t), f"{name}: expected a tensor, got {type(t).__name__}")
+    _need(t.device.type == device_type, f"{name}: on {t.device}, expected a {device_type} tensor")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    _need(t.dtype in dts, f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dts))}")
+    _need(t.is_contiguous(), f"{name}: not contiguous")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None:
+        _need(t.numel() >= numel, f"{name}: {t.numel()} elements, needs at least {numel}")
+
+
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def weight_shapes(m: synth.ModelConfig) -> dict:
+    """Expected (dtype, shape) of every weight tensor (top level and per layer)."""
+    h, d, bf = m.hidden, m.head_dim, torch.bfloat16
+    top = {"embed": (bf, (m.vocab, h)), "final_norm": (bf, (h,)), "lm_head": (bf, (m.vocab, h))}
+    lay = {"attn_norm": (bf, (h,)), "wq": (bf, (m.n_q_heads * d, h)), "wk": (bf, (m.n_kv_heads * d, h)),
+           "wv": (bf, (m.n_kv_heads * d, h)), "wo": (bf, (h, m.n_q_heads * d)), "ffn_norm": (bf, (h,))}
+    if m.is_moe:
+        f, E, S = m.expert_ffn, m.n_experts, m.n_shared
+        fb, hb = (f + 127) // 128, (h + 127) // 128
+        lay["router"] = (bf, (E, h))
+        for pre, n in (("e_", E), ("s_", S)):
+            if n == 0:
+                continue
+            lay[pre + "wg"] = (FP8_DTYPES, (n, f, h))
+            lay[pre + "wu"] = (FP8_DTYPES, (n, f, h))
+            lay[pre + "wd"] = (FP8_DTYPES, (n, h, f))
+            lay[pre + "sg"] = (bf, (n, fb, hb))
+            lay[pre + "su"] = (bf, (n, fb, hb))
+            lay[pre + "sd"] = (bf, (n, hb, fb))
+    else:
+        f = m.ffn_dim
+        lay.update({"wg": (bf, (f, h)), "wu": (bf, (f, h)), "wd": (bf, (h, f))})
+    return {"top": top, "layer": lay}
+
+
+def check_model_args(m: synth.ModelConfig, weights: dict, k_cache, v_cache, ctx_len=None,
+                     device_type="cuda"):
+    """Weights, cache and position array of an engine, before create."""
+    ws = weight_shapes(m)
+    for n, (dt, sh) in ws["top"].items():
+        check_tensor(weights.get(n), n, dt, shape=sh, device_type=device_type)
+    _need(len(weights.get("layers", [])) == m.n_layers, f"weights: {m.n_layers} layers expected")
+    for l, lw in enumerate(weights["layers"]):
+        for n, (dt, sh) in ws["layer"].items():
+            check_tensor(lw.get(n), f"layers[{l}].{n}", dt, shape=sh, device_type=device_type)
+    kv_shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
+    check_tensor(k_cache, "k_cache", torch.bfloat16, shape=kv_shape, device_type=device_type)
+    check_tensor(v_cache, "v_cache", torch.bfloat16, shape=kv_shape, device_type=device_type)
+    if ctx_len is not None:
+        check_tensor(ctx_len, "ctx_len", torch.int32, shape=(m.batch,), device_type=device_type)
+
+
+def check_decode_args(m: synth.ModelConfig, n_steps, in_tokens, forced, out_tokens, logits, hidden,
+                      device_type="cuda"):
+    """The buffers of one decode call, sized for n_steps steps of m.batch sequences."""
+    _need(isinstance(n_steps, int) and n_steps >= 0, f"n_steps: {n_steps!r} is not a count")
+    if n_steps == 0:
+        return
+    B = m.batch
+    _need(in_tokens is not None or forced is not None, "in_tokens or forced is required")
+    if in_tokens is not None:
+        check_tensor(in_tokens, "in_tokens", torch.int32, numel=B, device_type=device_type)
+    if forced is not None:
+        check_tensor(forced, "forced", torch.int32, numel=n_steps * B, device_type=device_type)
+    check_tensor(out_tokens, "out_tokens", torch.int32, numel=n_steps * B, device_type=device_type)
+    if logits is not None:
+        check_tensor(logits, "logits", torch.float32, numel=n_steps * B * m.vocab, device_type=device_type)
+    if hidden is not None:
+        check_tensor(hidden, "hidden", torch.float32, numel=n_steps * B * m.hidden, device_type=device_type)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return C.c_void_p(s.cuda_stream)
@@ -177,15 +266,20 @@ class Engine:
     """
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
-                 wg_threads=0, attn_splits=0, stream=None, xcd_local=0):
+                 wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None):
         self.m = m
+        self.h = None
+        check_model_args(m, weights, k_cache, v_cache, ctx_len)
+        dev = k_cache.device
+        for t in [weights["embed"], v_cache] + ([ctx_len] if ctx_len is not None else []):
+            _need(t.device == dev, f"every tensor must be on {dev}, found one on {t.device}")
         self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local)
         L = lib()
         nbytes = C.c_size_t()
         _check(L.pre_workspace_size(C.byref(self.cfg), C.byref(nbytes)), "workspace_size")
-        dev = k_cache.device
         self.workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=dev)
-        self._keep = [weights, k_cache, v_cache]
+        self.ctx_len = ctx_len
+        self._keep = [weights, k_cache, v_cache, ctx_len]
         self.layers = (LayerW * m.n_layers)()
         for l, lw in enumerate(weights["layers"]):
             for n in LAYER_FIELDS:
@@ -194,7 +288,8 @@ class Engine:
                     setattr(self.layers[l], n, t.data_ptr())
         self.w = Weights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
                          weights["lm_head"].data_ptr(), self.layers)
-        self.kv = KV(k_cache.data_ptr(), v_cache.data_ptr())
+        self.kv = KV(k_cache.data_ptr(), v_cache.data_ptr(),
+                     ctx_len.data_ptr() if ctx_len is not None else None)
         h = C.c_void_p()
         _check(L.pre_engine_create(C.byref(self.cfg), C.byref(self.w), C.byref(self.kv),
                                    C.c_void_p(self.workspace.data_ptr()), nbytes.value,
@@ -213,6 +308,12 @@ class Engine:
 
     # -- decode ----------------------------------------------------------------
     def _run(self, fn, n_steps, in_tokens, forced, out_tokens, logits, hidden, stream):
+        _need(self.h is not None, "engine is closed")
+        check_decode_args(self.m, n_steps, in_tokens, forced, out_tokens, logits, hidden)
+        dev = self.workspace.device
+        for t in (in_tokens, forced, out_tokens, logits, hidden):
+            _need(t is None or t.device == dev, f"every buffer must be on {dev}, found one on "
+                                                f"{None if t is None else t.device}")
         chk = Check(logits.data_ptr() if logits is not None else None,
                     hidden.data_ptr() if hidden is not None else None)
         _check(fn(self.h, int(n_steps), _ptr(in_tokens), _ptr(forced), _ptr(out_tokens),
@@ -255,8 +356,13 @@ class Engine:
         _check(lib().pre_engine_set_trace(self.h, _ptr(buf), 0 if buf is None else buf.numel() *
                                           buf.element_size()), "set_trace")
 
+    def debug_drop_signal(self, slot):
+        """Debug: the task setting ready flag `slot` skips the store from the
+        next call on (-1: off) -- drives the watchdog path."""
+        _check(lib().pre_debug_drop_signal(self.h, int(slot)), "debug_drop_signal")
+
     LAYOUT = ["status", "flags", "layers", "tasks", "rope", "xcc", "x_out", "pbuf", "q", "u", "rl",
-              "part", "lmp", "x_emb", "a_norm", "tok", "xmid", "pk", "ssq", "total"]
+              "part", "lmp", "x_emb", "a_norm", "tok", "xmid", "pk", "ssq", "ctx", "total"]
 
     def debug_slot(self, name, count, dtype=torch.float32, offset=0):
         """A view of a workspace region (debugging)."""

@@ -71,26 +71,21 @@ class MbSetup:
         return res, kc_h, vc_h
 
     def check(self, ctx, res, kc_h, vc_h, forced=None):
-        """Per sequence: the oracle's own free-running decode (or the forced
-        tokens) from the same cache, compared step by step."""
+        """Per sequence: the oracle decoding that sequence alone from the same
+        cache, teacher-forced on the GPU's tokens (or on the forced tokens),
+        every step compared."""
         tok0, toks, lgs, hds = res
-        steps = toks.shape[0]
         worst_l = worst_h = 0.0
         for b in range(self.m.batch):
             kb = np.ascontiguousarray(kc_h[:, b])
             vb = np.ascontiguousarray(vc_h[:, b])
-            tok = int(tok0[b])
-            for s in range(steps):
-                if forced is not None:
-                    tok = int(forced[s, b])
-                nxt, rl, rh = self.om.decode_step(kb, vb, tok, ctx[b] + s)
-                cont, rec = parity.compare_step(s, int(toks[s, b]), lgs[s, b], hds[s, b], nxt, rl, rh)
-                worst_l = max(worst_l, rec.get("max_dlogit", 0.0))
-                worst_h = max(worst_h, rec.get("hidden_rel", 0.0))
-                if not cont and forced is None:
-                    _say(f"  sequence {b}: streams parted at a near-tie at step {s}")
-                    break
-                tok = nxt
+            recs = parity.check_forced(self.om, kb, vb, ctx[b], int(tok0[b]), toks[:, b], lgs[:, b], hds[:, b],
+                                       inputs=None if forced is None else forced[:, b])
+            worst_l = max([worst_l] + [r["max_dlogit"] for r in recs])
+            worst_h = max([worst_h] + [r["hidden_rel"] for r in recs])
+            ties = [r["step"] for r in recs if r.get("near_tie")]
+            if ties:
+                _say(f"  sequence {b}: near-tie token differences at steps {ties}")
         return worst_l, worst_h
 
 

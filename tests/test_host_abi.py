@@ -269,3 +269,85 @@ def test_xcd_local_mode_only_where_each_head_fits_one_xcd(lib, m, grid, flag, wa
                 if op == 0 or lo >= hi or k == 0:
                     continue
                 assert all((s % W) // per == lam // per for s in range(lo, hi)), (layer, k, lam)
+
+
+def test_kv_descriptor_size_bound(lib):
+    """The K/V append addresses a layer's whole cache with a 32-bit buffer
+    size: a configuration whose layer cache reaches 4 GiB is refused, the
+    largest one below passes.  (At batch 1 the attention chunk's LDS bounds
+    max_ctx long before that.)"""
+    import dataclasses
+    m = synth.DENSE8B  # 8 KV heads x 128 dims: 4 KB per position and sequence
+    per_pos = m.n_kv_heads * m.head_dim * 2
+    for batch in (4, 8):
+        limit = (1 << 32) // (per_pos * batch)  # first max_ctx whose layer cache is 4 GiB
+        ok = dataclasses.replace(m, batch=batch, max_ctx=limit - 1)
+        bad = dataclasses.replace(m, batch=batch, max_ctx=limit)
+        assert E.plan_describe(ok)[0].validator == 0
+        with pytest.raises(E.PreError) as ei:
+            E.plan_describe(bad)
+        assert ei.value.code == -2
+
+
+def _host_weights(m):
+    import torch
+    W = synth.gen_weights(m, seed=0, device="cpu")
+    shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
+    return W, torch.zeros(shape, dtype=torch.bfloat16), torch.zeros(shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("m", [synth.TINY, synth.SMALL_MOE], ids=lambda m: m.name)
+def test_engine_arguments_are_checked_before_any_call(m):
+    """The binding hands raw pointers to the C ABI, so it checks every tensor
+    first: device, dtype, contiguity and shape/size.  Exercised here on host
+    tensors with the device check set to the host (the binding uses 'cuda')."""
+    import torch
+    W, kc, vc = _host_weights(m)
+    E.check_model_args(m, W, kc, vc, device_type="cpu")  # good arguments pass
+    with pytest.raises(ValueError, match="expected a cuda tensor"):
+        E.check_model_args(m, W, kc, vc)
+    bad = [("k_cache", lambda: (W, kc[:, :, :, :-1], vc)),
+           ("v_cache", lambda: (W, kc, vc.float())),
+           ("k_cache", lambda: (W, kc.transpose(3, 4), vc)),
+           ("embed", lambda: ({**W, "embed": W["embed"][:-1]}, kc, vc)),
+           ("lm_head", lambda: ({**W, "lm_head": W["lm_head"].float()}, kc, vc)),
+           ("layers[1].wq", lambda: ({**W, "layers": [W["layers"][0], {**W["layers"][1],
+                                      "wq": W["layers"][1]["wq"].t()}]}, kc, vc)),
+           ("weights", lambda: ({**W, "layers": W["layers"][:1]}, kc, vc))]
+    if m.is_moe:
+        bad.append(("layers[0].e_sd", lambda: ({**W, "layers": [{**W["layers"][0],
+                                                 "e_sd": W["layers"][0]["e_sd"][:, :-1]}] + W["layers"][1:]},
+                                               kc, vc)))
+    for name, make in bad:
+        with pytest.raises(ValueError, match=re.escape(name)):
+            E.check_model_args(m, *make(), device_type="cpu")
+    with pytest.raises(ValueError, match="ctx_len"):
+        E.check_model_args(m, W, kc, vc, ctx_len=torch.zeros(m.batch, dtype=torch.int64), device_type="cpu")
+
+
+def test_decode_arguments_are_checked_before_any_call():
+    import torch
+    m = synth.SMALL_MB3  # batch 3
+    n, B, V, h = 4, m.batch, m.vocab, m.hidden
+    i32 = lambda k: torch.zeros(k, dtype=torch.int32)  # noqa: E731
+    good = dict(in_tokens=i32(B), forced=None, out_tokens=i32(n * B),
+                logits=torch.zeros(n * B * V), hidden=torch.zeros(n * B * h))
+    E.check_decode_args(m, n, device_type="cpu", **good)
+    E.check_decode_args(m, 0, None, None, None, None, None, device_type="cpu")  # nothing is read
+    with pytest.raises(ValueError, match="expected a cuda tensor"):
+        E.check_decode_args(m, n, **good)
+    cases = [("in_tokens", dict(in_tokens=torch.zeros(B, dtype=torch.int64))),
+             ("in_tokens", dict(in_tokens=i32(B - 1))),
+             ("forced", dict(forced=i32(n * B - 1))),
+             ("out_tokens", dict(out_tokens=i32(n * B - 1))),
+             ("logits", dict(logits=torch.zeros(n * B * V - 1))),
+             ("hidden", dict(hidden=torch.zeros(n * B * h, dtype=torch.float64))),
+             ("hidden", dict(hidden=torch.zeros(2 * n * B * h)[::2])),
+             ("in_tokens or forced", dict(in_tokens=None)),
+             ("n_steps", None)]
+    for name, change in cases:
+        with pytest.raises(ValueError, match=re.escape(name)):
+            if change is None:
+                E.check_decode_args(m, -1, device_type="cpu", **good)
+            else:
+                E.check_decode_args(m, n, device_type="cpu", **{**good, **change})
