@@ -179,6 +179,23 @@ int pre_workspace_size(const pre_config *cfg, size_t *bytes);
 int pre_engine_create(const pre_config *cfg, const pre_weights *w, const pre_kv *kv,
                       void *d_workspace, size_t ws_bytes, void *stream, pre_engine **out);
 
+/* The engine without a caller workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same as pre_engine_create, but the workspace is
+ * a static device array of the library, PRE_STATIC_WORKSPACE_BYTES per GPU
+ * (each GPU the library runs on holds its copy until the process ends).  It
+ * allocates no device memory: no hipMalloc/hipFree or allocating library
+ * routine is called (host bookkeeping uses the C++ heap).  Configurations
+ * whose workspace (pre_workspace_size) exceeds the array return
+ * PRE_ERR_WORKSPACE; the batch-1 workloads here need 0.1-22 MB.  The used
+ * part of the array is cleared at create.  All engines created this way on
+ * one GPU share the array: each create takes it over, and calls on an engine
+ * created earlier on that GPU then return PRE_ERR_BROKEN; calls on one GPU
+ * that overlap in time race. */
+#define PRE_STATIC_WORKSPACE_BYTES (32u << 20)
+int pre_engine_create_static(const pre_config *cfg, const pre_weights *w, const pre_kv *kv, void *stream,
+                             pre_engine **out);
+
 /* Set / read the position each sequence decodes at next (host-side state:
  * h_pos[batch]).  A position is also the number of cached tokens. */
 int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos);

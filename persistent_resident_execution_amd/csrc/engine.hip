@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/pre.h"
@@ -1664,7 +1665,10 @@ struct pre_engine {
   size_t trace_bytes;
   int device;
   int32_t drop_slot;  // debug: ready flag never published (-1: none)
+  uint32_t static_gen;  // non-zero: created over the static workspace, with this generation
 };
+
+static bool static_taken_over(const pre_engine *e);
 
 static inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -1706,8 +1710,61 @@ static int check_layer(const Dims &D, const pre_layer_w &L) {
   return PRE_OK;
 }
 
+static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_kv *kv, void *d_workspace,
+                         size_t ws_bytes, void *stream, pre_engine **out, uint32_t static_gen);
+
 extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, const pre_kv *kv,
                                  void *d_workspace, size_t ws_bytes, void *stream, pre_engine **out) {
+  return create_engine(cfg, w, kv, d_workspace, ws_bytes, stream, out, 0);
+}
+
+// ---- the engine over the library's static workspace ----------------------
+// For callers that cannot allocate device memory.  The workspace is this
+// file-scope device array; each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array: its device address is looked up once per device
+// (hipGetSymbolAddress with that device current) and only that address is
+// ever used.  Engines created over it share it: each create takes it over
+// (a generation count per device), and calls on an engine created before
+// the latest one on that device return PRE_ERR_BROKEN.
+static __device__ __align__(256) char scratch[PRE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+uint32_t g_scratch_gen[kMaxDevices];
+}  // namespace
+
+extern "C" int pre_engine_create_static(const pre_config *cfg, const pre_weights *w, const pre_kv *kv,
+                                        void *stream, pre_engine **out) {
+  if (!out) return PRE_ERR_ARG;
+  *out = nullptr;
+  if (!cfg) return PRE_ERR_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PRE_ERR_HIP;
+  size_t need = 0;
+  int rc = pre_workspace_size(cfg, &need);
+  if (rc != PRE_OK) return rc;
+  if (need > (size_t)PRE_STATIC_WORKSPACE_BYTES) return PRE_ERR_WORKSPACE;
+  void *ptr;
+  uint32_t gen;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void *p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PRE_ERR_HIP;
+      g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+    gen = ++g_scratch_gen[dev];
+    if (gen == 0) gen = ++g_scratch_gen[dev];
+  }
+  return create_engine(cfg, w, kv, ptr, (size_t)PRE_STATIC_WORKSPACE_BYTES, stream, out, gen);
+}
+
+static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_kv *kv, void *d_workspace,
+                         size_t ws_bytes, void *stream, pre_engine **out, uint32_t static_gen) {
   if (!out) return PRE_ERR_ARG;
   *out = nullptr;
   if (!cfg || !w || !kv || !d_workspace || !w->layers) return PRE_ERR_ARG;
@@ -1788,6 +1845,7 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
   e->trace_bytes = 0;
   e->device = dev;
   e->drop_slot = -1;
+  e->static_gen = static_gen;
   e->lw.assign(w->layers, w->layers + D.L);
   *out = e;
   return PRE_OK;
@@ -1797,6 +1855,7 @@ extern "C" int pre_engine_create(const pre_config *cfg, const pre_weights *w, co
 // (every queued call has advanced the positions) before they copy.
 extern "C" int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
+  if (static_taken_over(e)) return PRE_ERR_BROKEN;
   for (int b = 0; b < e->D.B; ++b)
     if (h_pos[b] < 0 || h_pos[b] >= e->D.max_ctx) return PRE_ERR_CONTEXT;
   if (hipDeviceSynchronize() != hipSuccess ||
@@ -1807,6 +1866,7 @@ extern "C" int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos) {
 
 extern "C" int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
+  if (static_taken_over(e)) return PRE_ERR_BROKEN;
   if (hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(h_pos, e->ctx, sizeof(int32_t) * e->D.B, hipMemcpyDeviceToHost) != hipSuccess)
     return PRE_ERR_HIP;
@@ -1865,7 +1925,7 @@ static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in,
   if (!e || n_steps < 0) return PRE_ERR_ARG;
   if (n_steps == 0) return PRE_OK;  // nothing to do; the buffers are not read
   if (!d_out || (!d_in && !d_forced)) return PRE_ERR_ARG;
-  if (e->broken) return PRE_ERR_BROKEN;
+  if (e->broken || static_taken_over(e)) return PRE_ERR_BROKEN;
   if (n_steps > e->D.max_ctx) return PRE_ERR_CONTEXT;  // (positions live on the device: checked there)
   return PRE_OK;
 }
@@ -1943,8 +2003,15 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
   return PRE_OK;
 }
 
+static bool static_taken_over(const pre_engine *e) {
+  if (!e->static_gen) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_gen[e->device] != e->static_gen;
+}
+
 extern "C" int pre_engine_status(pre_engine *e, pre_status *out) {
   if (!e || !out) return PRE_ERR_ARG;
+  if (static_taken_over(e)) return PRE_ERR_BROKEN;
   DevStatus ds;
   if (hipStreamSynchronize(e->stream) != hipSuccess ||
       hipMemcpy(&ds, e->ws + e->Lo.status, sizeof(ds), hipMemcpyDeviceToHost) != hipSuccess)
@@ -1966,6 +2033,7 @@ extern "C" int pre_engine_status(pre_engine *e, pre_status *out) {
 
 extern "C" int pre_engine_reset(pre_engine *e, void *stream) {
   if (!e) return PRE_ERR_ARG;
+  if (static_taken_over(e)) return PRE_ERR_BROKEN;
   hipStream_t st = (hipStream_t)stream;
   const Layout &Lo = e->Lo;
   if (hipMemsetAsync(e->ws + Lo.status, 0, sizeof(DevStatus), st) != hipSuccess ||
@@ -2006,7 +2074,8 @@ extern "C" const char *pre_strerror(int code) {
     case PRE_ERR_HIP: return "HIP runtime call failed";
     case PRE_ERR_UNSUPPORTED: return "configuration valid but not built";
     case PRE_ERR_DEVICE: return "device latched an error (see pre_engine_status)";
-    case PRE_ERR_BROKEN: return "engine broken by an earlier device error; reset it";
+    case PRE_ERR_BROKEN:
+      return "engine broken by an earlier device error (reset it), or its static workspace was taken over";
     case PRE_ERR_CONTEXT: return "position would reach max_ctx";
     default: return "unknown error";
   }

@@ -72,7 +72,7 @@ class PlanInfo(C.Structure):
 
 
 # Every function the header declares (checked by the CPU test suite).
-EXPORTS = ["pre_workspace_size", "pre_engine_create", "pre_engine_set_positions",
+EXPORTS = ["pre_workspace_size", "pre_engine_create", "pre_engine_create_static", "pre_engine_set_positions",
            "pre_engine_get_positions", "pre_engine_decode", "pre_baseline_decode",
            "pre_engine_status", "pre_engine_reset", "pre_engine_set_watchdog",
            "pre_engine_set_trace", "pre_engine_destroy", "pre_strerror", "pre_plan_describe",
@@ -89,6 +89,8 @@ def lib():
         L.pre_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(C.c_size_t)]
         L.pre_engine_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KV), vp,
                                         C.c_size_t, vp, C.POINTER(vp)]
+        L.pre_engine_create_static.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KV), vp,
+                                               C.POINTER(vp)]
         L.pre_engine_set_positions.argtypes = [vp, C.POINTER(i32)]
         L.pre_engine_get_positions.argtypes = [vp, C.POINTER(i32)]
         for f in (L.pre_engine_decode, L.pre_baseline_decode):
@@ -266,18 +268,24 @@ class Engine:
     """
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
-                 wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None):
+                 wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None,
+                 static_workspace=False):
+        """static_workspace: create with pre_engine_create_static (the
+        library's static device workspace; no allocation) instead of a
+        workspace tensor."""
         self.m = m
         self.h = None
         check_model_args(m, weights, k_cache, v_cache, ctx_len)
         dev = k_cache.device
         for t in [weights["embed"], v_cache] + ([ctx_len] if ctx_len is not None else []):
             _need(t.device == dev, f"every tensor must be on {dev}, found one on {t.device}")
+        self.device = dev
         self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local)
         L = lib()
         nbytes = C.c_size_t()
         _check(L.pre_workspace_size(C.byref(self.cfg), C.byref(nbytes)), "workspace_size")
-        self.workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=dev)
+        self.workspace = None if static_workspace else torch.empty(int(nbytes.value), dtype=torch.uint8,
+                                                                   device=dev)
         self.ctx_len = ctx_len
         self._keep = [weights, k_cache, v_cache, ctx_len]
         self.layers = (LayerW * m.n_layers)()
@@ -291,9 +299,13 @@ class Engine:
         self.kv = KV(k_cache.data_ptr(), v_cache.data_ptr(),
                      ctx_len.data_ptr() if ctx_len is not None else None)
         h = C.c_void_p()
-        _check(L.pre_engine_create(C.byref(self.cfg), C.byref(self.w), C.byref(self.kv),
-                                   C.c_void_p(self.workspace.data_ptr()), nbytes.value,
-                                   _stream(stream), C.byref(h)), "engine_create")
+        if static_workspace:
+            _check(L.pre_engine_create_static(C.byref(self.cfg), C.byref(self.w), C.byref(self.kv),
+                                              _stream(stream), C.byref(h)), "engine_create_static")
+        else:
+            _check(L.pre_engine_create(C.byref(self.cfg), C.byref(self.w), C.byref(self.kv),
+                                       C.c_void_p(self.workspace.data_ptr()), nbytes.value,
+                                       _stream(stream), C.byref(h)), "engine_create")
         self.h = h
 
     # -- positions -----------------------------------------------------------
@@ -310,7 +322,7 @@ class Engine:
     def _run(self, fn, n_steps, in_tokens, forced, out_tokens, logits, hidden, stream):
         _need(self.h is not None, "engine is closed")
         check_decode_args(self.m, n_steps, in_tokens, forced, out_tokens, logits, hidden)
-        dev = self.workspace.device
+        dev = self.device
         for t in (in_tokens, forced, out_tokens, logits, hidden):
             _need(t is None or t.device == dev, f"every buffer must be on {dev}, found one on "
                                                 f"{None if t is None else t.device}")
@@ -324,7 +336,7 @@ class Engine:
         """One persistent launch of n_steps; returns out_tokens [n_steps, batch] (int32)."""
         if out_tokens is None:
             out_tokens = torch.empty((n_steps, self.m.batch), dtype=torch.int32,
-                                     device=self.workspace.device)
+                                     device=self.device)
         self._run(lib().pre_engine_decode, n_steps, in_tokens, forced, out_tokens, logits, hidden,
                   stream)
         return out_tokens
@@ -333,7 +345,7 @@ class Engine:
                         hidden=None, stream=None):
         if out_tokens is None:
             out_tokens = torch.empty((n_steps, self.m.batch), dtype=torch.int32,
-                                     device=self.workspace.device)
+                                     device=self.device)
         self._run(lib().pre_baseline_decode, n_steps, in_tokens, forced, out_tokens, logits,
                   hidden, stream)
         return out_tokens
