@@ -1,28 +1,33 @@
 """Decode benchmark: µs/token and achieved HBM bandwidth of the persistent
-decode kernel on one MI355X.
+decode kernel on one MI355X, for every workload configuration.
 
-    python bench.py [--gpus 1] [--steps 256] [--warmup 32] [--workload dense8b_ctx1024]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense8b_ctx1024]
+                    [--configs all|none|name,name,...]
 
-One "step" is one decode step (one token) through the whole hot path.  The
-default workload is the 8B-shape dense decoder at batch 1: 32 layers, hidden
-4096, 32 query / 8 KV heads of 128, SwiGLU 14336, vocabulary 128256, bf16
-weights ~N(0, 0.02) from seed 0, the KV cache prefilled on the GPU from 1024
-random tokens, then greedy decode.  The timed region is ONE engine call of
---steps steps (one persistent kernel launch), bracketed by device
-synchronisation; it is repeated --repeats times from the same prefilled
-position and the median is reported.  Inputs are resident in HBM.
+One "step" is one decode step (one token per sequence) through the whole hot
+path.  The headline workload is the 8B-shape dense decoder at batch 1: 32
+layers, hidden 4096, 32 query / 8 KV heads of 128, SwiGLU 14336, vocabulary
+128256, bf16 weights ~N(0, 0.02) from seed 0, the KV cache filled on the GPU
+by the engine itself from 1024 random tokens, then greedy decode.  The timed
+region is ONE engine call of K steps (one persistent kernel launch) starting
+at the prefilled position, bracketed by device synchronisation and timed
+with HIP events on the launch stream; it is repeated --repeats times from the
+same position and the median is reported.  Inputs are resident in HBM.
 
-Also reported: the roofline of the persistent kernel (algorithmic bytes per
-launch over the launch time measured with HIP events on the launch stream,
-against 8 TB/s), the one-kernel-per-operator baseline on the same workload,
-the rate of a read-only streaming kernel measured on the same box, reported
-beside the decode rate (stream_reference), the tiny-decoder persistent vs
-baseline latency, and the CPU oracle timed on a bounded sample
-(cpu_baseline).
+The same run measures the other workloads the same way under "configs":
+context 8192 (engine prefill of 8192 tokens), the MoE decoder (engine prefill
+of 4096 tokens), the micro-batch of 8 (seeded synthetic caches at contexts
+512..8192) and the tiny decoder (engine prefill of 128 tokens).  Each entry
+carries its µs per step, its roofline (algorithmic bytes of the timed launch
+over its HIP-event time, against 8 TB/s; HBM traffic from the committed
+rocprofv3 counter summary when one matches the current kernel sources), the
+one-kernel-per-operator path on the same call, and the CPU oracle timed on a
+bounded sample of the same workload (cpu_baseline).
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import statistics
@@ -33,72 +38,78 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+CONFIG_ORDER = ["dense8b_ctx8192", "moe", "dense8b_mb8", "tiny"]
+# what each path computes in (the "dtype" of its line)
+DTYPE_B1 = ("bf16 weights and K/V cache; GEMV products and sums in fp32; attention scores and P.V on the "
+            "matrix cores with q and p split into bf16 hi+lo parts (about 16 significant bits), fp32 accumulate")
+DTYPE_MOE = DTYPE_B1.replace("bf16 weights", "bf16 attention/router weights, fp8 e4m3 experts with bf16 "
+                             "128x128 block scales (decoded exactly to fp32)")
+DTYPE_MB = ("bf16 weights and K/V cache; every GEMM and attention product on the matrix cores with the "
+            "activations split into bf16 hi+lo parts (about 16 significant bits), fp32 accumulate")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(workload, device="cuda", seed=0, prefill="engine", **eng_kw):
-    """Weights, cache and engine of a workload.  prefill="engine" fills the
-    cache by teacher-forced decode of the workload's random prompt (the
-    workload as specified); "synthetic" writes seeded N(0,1) K/V rows instead
-    and decodes from token 1 -- the same bytes and flops per step, without a
-    prefill launch (used for profiler runs that must see only timed launches)."""
+def setup(workload, W=None, device="cuda", seed=0, prefill="engine", **eng_kw):
+    """Weights (reused if given: same shapes), cache, position array and engine
+    of a workload.  prefill="engine" fills the cache by teacher-forced decode
+    of the workload's random prompt (the workload as specified); "synthetic"
+    writes seeded N(0,1) K/V rows instead and decodes from token 1 -- the same
+    bytes and flops per step, without a prefill launch (used for profiler runs
+    that must see only timed launches).  A micro-batch always uses the
+    synthetic cache: a lockstep prefill cannot give eight different lengths."""
     import torch
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import synth
     w = synth.WORKLOADS[workload]
     m = w.model
     t0 = time.time()
-    W = synth.gen_weights(m, seed=seed, device=device)
-    P = w.contexts[0]
-    if m.batch > 1:
-        # micro-batch: each sequence at its own context; the cache is the
-        # seeded synthetic one (the prefill of unequal lengths is not a
-        # lockstep decode), the first tokens seeded
-        kc, vc = synth.gen_kv_cache(m, max(w.contexts), seed=seed + 1, device=device)
-        eng = E.Engine(m, W, kc, vc, **eng_kw)
-        g0 = synth.gen_tokens(m.vocab, m.batch, seed=seed + 2, device=device)
-        log(f"[bench] {workload}: weights + synthetic cache of contexts {list(w.contexts)} "
-            f"in {time.time() - t0:.1f}s")
-        return w, m, W, kc, vc, eng, g0
-    if prefill == "synthetic":
-        kc, vc = synth.gen_kv_cache(m, P, seed=seed + 1, device=device)
+    if W is None:
+        W = synth.gen_weights(m, seed=seed, device=device)
+    pos = list(w.contexts)
+    ctx = torch.zeros(m.batch, dtype=torch.int32, device=device)
+    if m.batch > 1 or prefill == "synthetic":
+        kc, vc = synth.gen_kv_cache(m, max(pos), seed=seed + 1, device=device)
     else:
         shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
         kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
         vc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-    eng = E.Engine(m, W, kc, vc, **eng_kw)
-    if prefill == "synthetic":
+    eng = E.Engine(m, W, kc, vc, ctx_len=ctx, **eng_kw)
+    if m.batch > 1:
+        g0 = synth.gen_tokens(m.vocab, m.batch, seed=seed + 2, device=device)
+        how = f"synthetic caches of contexts {pos}"
+    elif prefill == "synthetic":
         g0 = torch.ones(1, dtype=torch.int32, device=device)
+        how = f"synthetic cache of {pos[0]} positions"
     else:
-        prompt = synth.gen_tokens(m.vocab, P, seed=seed, device=device)
-        eng.set_positions([0])
-        out = eng.decode(P, forced=prompt.view(P, 1))  # cache filled by the engine itself
+        prompt = synth.gen_tokens(m.vocab, pos[0], seed=seed, device=device)
+        out = eng.decode(pos[0], forced=prompt.view(-1, 1))  # cache filled by the engine itself
         torch.cuda.synchronize()
         eng.status()
         g0 = out[-1].contiguous()
-    log(f"[bench] {workload}: weights + {prefill} prefill of {P} tokens in {time.time() - t0:.1f}s")
-    return w, m, W, kc, vc, eng, g0
+        how = f"engine prefill of {pos[0]} tokens"
+    log(f"[bench] {workload}: weights + {how} in {time.time() - t0:.1f}s")
+    return w, m, W, (kc, vc, ctx), eng, g0
 
 
-def launches_per_token_per_op(m):
+def launches_per_step_per_op(m):
     """Kernels the one-kernel-per-operator path launches per step.  Batch 1:
     embedding; per layer two norms and one launch per task stage (5 dense, 6
     MoE); final norm, LM head, argmax.  Micro-batch: the embedding stage, six
-    stages per layer, the LM head and the argmax."""
+    stages per layer, the LM head and the argmax.  (Plus one position-advance
+    launch per call.)"""
     if m.batch > 1:
         return 6 * m.n_layers + 3
     return (8 if m.is_moe else 7) * m.n_layers + 4
 
 
-def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
-    """Seconds of each of `repeats` calls of n_steps from position(s) P (an
-    int, or one per sequence); also returns the tokens of the last call."""
+def time_calls(eng, fn, n_steps, g0, pos, repeats, warmup_steps):
+    """Seconds of each of `repeats` calls of n_steps from positions `pos`
+    (HIP events on the launch stream); also the tokens of the last call."""
     import torch
     stream = torch.cuda.current_stream()
-    pos = list(P) if isinstance(P, (list, tuple)) else [P]
     out = torch.empty((max(n_steps, warmup_steps, 1), len(pos)), dtype=torch.int32, device="cuda")
     if warmup_steps:
         eng.set_positions(pos)
@@ -114,83 +125,164 @@ def time_calls(eng, fn, n_steps, g0, P, repeats, warmup_steps):
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / 1e3)
+        del e0, e1
     eng.status()
     return times, out[:n_steps].cpu()
 
 
-def cpu_baseline(m, W, P, budget_s=15.0, max_steps=64):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(m, W, pos, budget_s=12.0, single_thread_steps=0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    decode steps of the same model (weights copied to the host; the cache is
-    a seeded synthetic one -- its values do not change the work) at context P,
-    or, for a micro-batch, whole steps = one decode of every sequence at its
-    own context (the oracle decodes sequences one at a time)."""
+    decode steps of the same model (weights copied to the host; the cache is a
+    seeded synthetic one -- its values do not change the work) at the
+    workload's context(s); for a micro-batch one step = one decode of every
+    sequence at its own context (the oracle decodes sequences one at a time).
+    With single_thread_steps > 0, that many steps are also timed on one
+    thread."""
     import numpy as np
     import oracle
     from persistent_resident_execution_amd import synth
     t0 = time.time()
     om = oracle.OracleModel(m, synth.weights_to_numpy(W))
-    pos = list(P) if isinstance(P, (list, tuple)) else [P]
     kc_t, vc_t = synth.gen_kv_cache(m, max(pos), seed=1, device="cpu")
     kc_all, vc_all = synth.to_bits(kc_t), synth.to_bits(vc_t)
+    del kc_t, vc_t
     caches = [(np.ascontiguousarray(kc_all[:, b]), np.ascontiguousarray(vc_all[:, b])) for b in range(len(pos))]
-    log(f"[bench] oracle set-up {time.time() - t0:.1f}s ({oracle.num_threads()} threads)")
-    toks, steps, t_start = [1] * len(pos), 0, time.time()
-    while steps < max_steps:
-        for b, (kc, vc) in enumerate(caches):
-            toks[b], _, _ = om.decode_step(kc, vc, int(toks[b]), pos[b] + steps, want_logits=False,
-                                           want_hidden=False)
-        steps += 1
-        if time.time() - t_start >= budget_s:
-            break
-    el = time.time() - t_start
-    what = (f"context {pos[0]}, batch 1" if len(pos) == 1 else
-            f"contexts {pos}, one step = every sequence")
-    return {"value": round(el / steps * 1e6, 1), "unit": "us/step" if len(pos) > 1 else "us/token",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{steps} decode step(s) of the same {m.name} decoder at {what}, "
-                      f"fp64 C oracle, {el:.1f}s wall"}
+    del kc_all, vc_all
+    threads = oracle.num_threads()
+    log(f"[bench] oracle set-up {time.time() - t0:.1f}s ({threads} threads)")
+
+    def run(max_steps, budget):
+        toks, steps, ts = [1] * len(pos), 0, time.time()
+        while steps < max_steps:
+            for b, (kc, vc) in enumerate(caches):
+                toks[b], _, _ = om.decode_step(kc, vc, int(toks[b]), pos[b] + steps, want_logits=False,
+                                               want_hidden=False)
+            steps += 1
+            if time.time() - ts >= budget:
+                break
+        return steps, time.time() - ts
+
+    steps, el = run(64, budget_s)
+    unit = "us/step" if len(pos) > 1 else "us/token"
+    what = f"context {pos[0]}, batch 1" if len(pos) == 1 else f"contexts {pos}, one step = every sequence"
+    res = {"value": round(el / steps * 1e6, 1), "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": f"{steps} decode step(s) of the same {m.name} decoder at {what}, fp64 C oracle, "
+                     f"{el:.1f}s wall on {threads} threads", "cpu_model": cpu_model(),
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if single_thread_steps:
+        oracle.set_num_threads(1)
+        try:
+            s1, e1 = run(single_thread_steps, 0.0)
+        finally:
+            oracle.set_num_threads(threads)
+        res["single_thread"] = {"value": round(e1 / s1 * 1e6, 1), "unit": unit, "steps": s1}
+    del om, caches
+    gc.collect()
+    return res
 
 
-def tiny_comparison(repeats=5):
-    """Persistent vs one-kernel-per-op on the tiny decoder (latency bound)."""
+def roofline(m, pos, K, t_med, kernel, workload):
+    """Algorithmic bytes of one launch of K steps from positions pos over its
+    HIP-event time, against the 8 TB/s peak; HBM traffic from the committed
+    counter summary (per step, times K) while it matches the kernel sources."""
+    from persistent_resident_execution_amd import engine as E
+    from persistent_resident_execution_amd import profiling
+    bytes_call = sum(E.step_bytes(m, [p + s for p in pos]) for s in range(K))
+    gbps = bytes_call / t_med / 1e9
+    tr = profiling.traffic_for(workload, K, kernel)
+    return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": tr["bytes_per_launch"] if tr else None,
+            "traffic_basis": tr["basis"] if tr else "no counter summary for the current kernel sources",
+            "kernel": kernel, "bytes_per_launch": bytes_call,
+            "bytes_per_step_mean": round(bytes_call / K), "launch_ms": round(t_med * 1e3, 3)}
+
+
+def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps=0):
+    """Everything reported for one workload; returns (entry, weights)."""
     import torch
-    _, m, _, _, _, eng, g0 = setup("tiny")
-    P, n = 128, 64
-    tp, _ = time_calls(eng, eng.decode, n, g0, P, repeats, 8)
-    tb, _ = time_calls(eng, eng.baseline_decode, n, g0, P, repeats, 8)
-    res = {}
-    for grid in (8, 16, 32, 64):
-        e2 = __import__("persistent_resident_execution_amd.engine", fromlist=["Engine"]).Engine(
-            m, eng._keep[0], eng._keep[1], eng._keep[2], grid_wgs=grid)
-        t, _ = time_calls(e2, e2.decode, n, g0, P, repeats, 8)
-        res[grid] = statistics.median(t) / n * 1e6
-        e2.close()
-    up = statistics.median(tp) / n * 1e6
-    ub = statistics.median(tb) / n * 1e6
-    best_grid = min(res, key=res.get)
+    w, m, W, bufs, eng, g0 = setup(workload, W, grid_wgs=args.grid, prefill=args.prefill)
+    mb = m.batch > 1
+    pos = list(w.contexts)
+    K = args.steps if args.steps > 0 else w.steps
+    log(f"[bench] {workload}: timing {args.repeats} x {K} persistent steps from position(s) {pos}")
+    tp, toks = time_calls(eng, eng.decode, K, g0, pos, args.repeats, args.warmup)
+    kern = "pre_persistent_mb" if mb else "pre_persistent"
+    t_med = statistics.median(tp)
+    us = t_med / K * 1e6
+    unit = "us/step" if mb else "us/token"
+    e = {"workload": w.note, "value": round(us, 2), "unit": unit,
+         "window": {"steps": K, "start_positions": pos,
+                    "note": f"one launch of {K} greedy steps from the prefilled position(s)"},
+         "tokens_per_s": round(K * m.batch / t_med, 1),
+         "repeats_us_per_step": [round(t / K * 1e6, 2) for t in tp],
+         "dtype": DTYPE_MB if mb else (DTYPE_MOE if m.is_moe else DTYPE_B1),
+         "roofline": roofline(m, pos, K, t_med, kern, workload)}
+    if baseline:
+        log(f"[bench] {workload}: the one-kernel-per-operator path")
+        tb, btoks = time_calls(eng, eng.baseline_decode, K, g0, pos, max(1, args.repeats // 2), 0)
+        ub = statistics.median(tb) / K * 1e6
+        e["per_op_baseline"] = {unit.replace("/", "_per_"): round(ub, 2),
+                                "launches_per_step": launches_per_step_per_op(m),
+                                "persistent_speedup": round(ub / us, 3),
+                                "same_tokens": bool((btoks == toks).all())}
     eng.close()
+    del eng, bufs, g0, toks
+    gc.collect()
     torch.cuda.synchronize()
-    return {"persistent_us_per_token": round(up, 2), "per_op_us_per_token": round(ub, 2),
-            "speedup": round(ub / up, 2),
-            "persistent_us_per_token_by_grid": {str(k): round(v, 2) for k, v in res.items()},
-            "best_grid": best_grid, "best_speedup": round(ub / min(up, res[best_grid]), 2),
-            "launches_per_token_per_op": launches_per_token_per_op(m), "launches_per_token_persistent": 1 / n}
+    torch.cuda.empty_cache()
+    if cpu:
+        log(f"[bench] {workload}: CPU oracle sample")
+        e["cpu_baseline"] = cpu_baseline(m, W, pos, single_thread_steps=single_thread_steps)
+    return e, W
 
 
-def phases(args, w, m, eng, g0, P, K):
+def tiny_grids(args, entry):
+    """The tiny decoder's persistent µs/token at a few grid sizes (its
+    default grid is one XCD's 32 CUs)."""
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    w, m, W, bufs, eng, g0 = setup("tiny")
+    eng.close()
+    pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
+    res = {}
+    for grid in (8, 16, 64):
+        e2 = E.Engine(m, W, bufs[0], bufs[1], grid_wgs=grid, ctx_len=bufs[2])
+        t, _ = time_calls(e2, e2.decode, K, g0, pos, args.repeats, 8)
+        res[str(grid)] = round(statistics.median(t) / K * 1e6, 2)
+        e2.close()
+    res["32 (default)"] = entry["value"]
+    del eng, bufs, W
+    torch.cuda.empty_cache()
+    return res
+
+
+def phases(args):
     """Busy and idle time per stage from the kernel's timestamp ring (one
     traced launch of K steps after a warm-up; the first traced step is
     skipped), written as a text summary."""
     import torch
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import profiling
+    w, m, W, bufs, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill)
+    pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
     info, _ = E.plan_describe(m, grid_wgs=args.grid)
-    nsi, W = info.n_stage_inst, info.n_wgs
-    tr = torch.zeros(K * nsi * W * 8, dtype=torch.int32, device="cuda")
+    nsi, nW = info.n_stage_inst, info.n_wgs
+    tr = torch.zeros(K * nsi * nW * 8, dtype=torch.int32, device="cuda")
     eng.set_trace(tr)
-    t, _ = time_calls(eng, eng.decode, K, g0, P, 1, args.warmup)
+    t, _ = time_calls(eng, eng.decode, K, g0, pos, 1, args.warmup)
     eng.set_trace(None)
-    rec = tr.view(K, nsi, W, 8).cpu().numpy()
+    rec = tr.view(K, nsi, nW, 8).cpu().numpy()
     if m.batch > 1:
         names, spl, first = ["embed", "qkv", "attn", "comb", "oproj", "gu", "down", "lm"], 6, 1
     elif m.is_moe:
@@ -200,7 +292,7 @@ def phases(args, w, m, eng, g0, P, K):
     lines = [f"# per-stage wait / busy / phases (us) from the in-kernel timestamp ring, {w.note}",
              "command: python3 bench.py " + " ".join(sys.argv[1:]),
              f"traced: {K} steps in one launch ({t[0] / K * 1e6:.1f} us/step with the ring on), "
-             f"{W} workgroups; means over steps 2..{K} and layers",
+             f"{nW} workgroups; means over steps 2..{K} and layers",
              "wait = task begin -> producers ready; busy = the rest of the task; span = first begin -> "
              "last end over the workgroups"]
     lines += profiling.phase_table(rec, names, m.n_layers, spl, first,
@@ -247,17 +339,19 @@ def stream_reference(gbps, mib=2048, repeats=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="steps per timed launch (0: each workload's own step count)")
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--repeats", type=int, default=5)
-    ap.add_argument("--workload", default="dense8b_ctx1024")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle sample")
-    ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timing")
-    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-decoder comparison")
+    ap.add_argument("--workload", default="dense8b_ctx1024", help="the headline workload")
+    ap.add_argument("--configs", default="all",
+                    help="other workloads measured in the same run: all, none, or a comma list")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle samples")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the per-op baseline timings")
     ap.add_argument("--no-stream", action="store_true", help="skip the read-only stream reference")
     ap.add_argument("--phases", default="",
-                    help="instead of timing: trace --steps steps with the in-kernel timestamp ring and "
-                         "write the per-stage wait/busy/phase summary to this file")
+                    help="instead of timing: trace --steps steps of --workload with the in-kernel timestamp "
+                         "ring and write the per-stage wait/busy/phase summary to this file")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -269,72 +363,81 @@ def main():
         sys.exit(2)
     import torch
     from persistent_resident_execution_amd import engine as E
-    from persistent_resident_execution_amd import profiling
     torch.cuda.set_device(0)
-
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        a = torch.ones(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        E.debug_copy(a, b)
+    try:
+        if args.calibrate_copy_mib:
+            n = args.calibrate_copy_mib << 20
+            a = torch.ones(n, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            E.debug_copy(a, b)
+            torch.cuda.synchronize()
+            del a, b
+        if args.phases:
+            phases(args)
+            return
+        run_main(args)
+    finally:
+        # release every device allocation while the runtime (and a profiler
+        # wrapped around this process) is still fully up
+        gc.collect()
         torch.cuda.synchronize()
-        del a, b
-    w, m, W, kc, vc, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill)
+        torch.cuda.empty_cache()
+        sys.stdout.flush()
+
+
+def run_main(args):
+    import torch
+    from persistent_resident_execution_amd import synth
+    head = args.workload
+    cpu = not args.no_cpu
+    e, W = measure(head, args, baseline=not args.no_baseline, cpu=cpu,
+                   single_thread_steps=1 if head.startswith("dense8b") or head == "tiny" else 0)
+    m = synth.WORKLOADS[head].model
     mb = m.batch > 1
-    P, K = (list(w.contexts) if mb else w.contexts[0]), args.steps
-    pos = P if mb else [P]
-    if args.phases:
-        phases(args, w, m, eng, g0, P, K)
-        return
-    log(f"[bench] timing {args.repeats} x {K} persistent steps from position(s) {P}")
-    tp, toks = time_calls(eng, eng.decode, K, g0, P, args.repeats, args.warmup)
-    kern = "pre_persistent_mb" if mb else "pre_persistent"
-    t_med = statistics.median(tp)
-    bytes_call = sum(E.step_bytes(m, [p + s for p in pos]) for s in range(K))
-    us_tok = t_med / K * 1e6
-    gbps = bytes_call / t_med / 1e9
     result = {
         "metric": ("decode us/step (micro-batch " + str(m.batch) + ") + achieved HBM GB/s as % of MI355X peak"
                    if mb else "decode us/token (batch 1) + achieved HBM GB/s as % of MI355X peak"),
-        "value": round(us_tok, 2), "unit": "us/step" if mb else "us/token", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(us_tok / 1e3, 4), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16 weights/KV, bf16 hi+lo activations on the matrix cores, fp32 accumulate" if mb
-                  else "bf16 weights/KV, fp32 compute"),
+        "value": e["value"], "unit": e["unit"], "n_gpus": 1, "steps": e["window"]["steps"],
+        "warmup": args.warmup, "ms_per_step": round(e["value"] / 1e3, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": e["dtype"],
         "data": ("synthetic (seeded N(0,0.02) bf16 weights, seeded N(0,1) K/V cache, seeded first tokens)"
-                 if mb else "synthetic (seeded N(0,0.02) bf16 weights, random prompt tokens)"),
-        "config": {"workload": w.note, "layers": m.n_layers, "hidden": m.hidden,
-                   "heads": f"{m.n_q_heads}q/{m.n_kv_heads}kv x {m.head_dim}",
-                   "ffn": m.ffn_dim, "vocab": m.vocab, "context": P, "batch": m.batch,
+                 if mb else "synthetic (seeded N(0,0.02) bf16 weights, random prompt tokens prefilled by the "
+                            "engine)"),
+        "config": {"workload": e["workload"], "timed": e["window"]["note"],
+                   "start_positions": e["window"]["start_positions"], "layers": m.n_layers,
+                   "hidden": m.hidden, "heads": f"{m.n_q_heads}q/{m.n_kv_heads}kv x {m.head_dim}",
+                   "ffn": m.ffn_dim, "vocab": m.vocab, "batch": m.batch,
                    "parallelism": "single GPU, one workgroup per CU"},
-        "tokens_per_s": round(K * m.batch / t_med, 1),
-        "hbm_gbps_algorithmic": round(gbps, 1),
-        "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
-        "repeats_us_per_token": [round(t / K * 1e6, 2) for t in tp],
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": profiling.traffic_for(args.workload, K, kern),
-                     "kernel": kern, "bytes_per_launch": bytes_call,
-                     "launch_ms": round(t_med * 1e3, 3)},
+        "tokens_per_s": e["tokens_per_s"],
+        "hbm_gbps_algorithmic": e["roofline"]["achieved"],
+        "hbm_frac_of_peak": e["roofline"]["frac"],
+        "repeats_us_per_step": e["repeats_us_per_step"],
+        "roofline": e["roofline"],
     }
-    if not args.no_baseline:
-        log("[bench] timing the one-kernel-per-op baseline")
-        tb, btoks = time_calls(eng, eng.baseline_decode, K, g0, P, max(1, args.repeats // 2), 0)
-        ub = statistics.median(tb) / K * 1e6
-        result["per_op_baseline"] = {("us_per_step" if mb else "us_per_token"): round(ub, 2),
-                                     "launches_per_token": launches_per_token_per_op(m),
-                                     "persistent_speedup": round(ub / us_tok, 3),
-                                     "same_tokens": bool((btoks == toks).all())}
-    eng.close()
+    for k in ("per_op_baseline", "cpu_baseline"):
+        if k in e:
+            result[k] = e[k]
     if not args.no_stream:
         log("[bench] read-only stream reference")
-        result["stream_reference"] = stream_reference(gbps)
-    if not args.no_tiny and not mb:
-        log("[bench] tiny decoder persistent vs per-op")
-        result["tiny"] = tiny_comparison()
-    if not args.no_cpu:
-        log("[bench] CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(m, W, P)
+        result["stream_reference"] = stream_reference(e["roofline"]["achieved"])
+    names = CONFIG_ORDER if args.configs == "all" else ([] if args.configs == "none" else args.configs.split(","))
+    configs = {}
+    for name in names:
+        if name == head:
+            continue
+        mm = synth.WORKLOADS[name].model
+        same = (mm.n_layers, mm.hidden, mm.vocab, mm.ffn_dim, mm.n_experts) == (
+            m.n_layers, m.hidden, m.vocab, m.ffn_dim, m.n_experts)
+        ce, W2 = measure(name, args, W=W if same else None, baseline=not args.no_baseline, cpu=cpu,
+                         single_thread_steps=4 if name == "tiny" else 0)
+        if name == "tiny":
+            ce["by_grid_us_per_token"] = tiny_grids(args, ce)
+        configs[name] = ce
+        del W2
+        gc.collect()
+        torch.cuda.empty_cache()
+    if configs:
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 

@@ -90,6 +90,7 @@ def lib():
         L.orc_prefill.restype = C.c_int
         L.orc_prefill.argtypes = [C.POINTER(OrcConfig), C.POINTER(OrcWeights), vp, vp, i64, vp, i32]
         L.orc_num_threads.restype = C.c_int
+        L.orc_set_num_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -194,6 +195,11 @@ def topk(p, k):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- whole model --------------------------------------------------------------

@@ -110,8 +110,10 @@ int orc_forward_full(const orc_config *c, const orc_weights *w, const int32_t *t
 int orc_prefill(const orc_config *c, const orc_weights *w, uint16_t *kc, uint16_t *vc,
                 int64_t layer_stride, const int32_t *tokens, int n);
 
-/* Number of OpenMP threads the oracle uses. */
+/* Number of OpenMP threads the oracle uses, and a way to change it (timing
+ * only: every sum is sequential whatever the thread count). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -280,14 +280,20 @@ def read_summary(path) -> dict:
 
 
 def traffic_for(workload, steps, kernel=KERNEL):
-    """Measured HBM bytes of one launch of `steps` steps, or None when no
-    summary matches this workload, step count and the current sources."""
+    """HBM bytes of one launch of `steps` steps from the committed counter
+    summary of this workload: its measured bytes per step (FETCH_SIZE +
+    WRITE_SIZE of a profiled launch, scaled by the copy kernel's reading)
+    times `steps`.  None when there is no summary or the kernel sources have
+    changed since it was taken."""
     s = read_summary(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt"))
-    if not s or s.get("workload") != workload or s.get("steps") != str(steps):
+    if not s or s.get("workload") != workload:
         return None
     if s.get("source_sha256") != source_hash():
         return None
-    return int(float(s["traffic_bytes_per_launch"]))
+    per_step = float(s["traffic_bytes_per_step"])
+    return {"bytes_per_launch": int(per_step * steps), "bytes_per_step": int(per_step),
+            "basis": f"measured {int(per_step)} bytes/step over a profiled launch of {s.get('steps')} steps, "
+                     f"times {steps} steps"}
 
 
 def main():
