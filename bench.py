@@ -211,7 +211,8 @@ def roofline(m, pos, K, t_med, kernel, workload):
 def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps=0):
     """Everything reported for one workload; returns (entry, weights)."""
     import torch
-    w, m, W, bufs, eng, g0 = setup(workload, W, grid_wgs=args.grid, prefill=args.prefill)
+    w, m, W, bufs, eng, g0 = setup(workload, W, grid_wgs=args.grid, prefill=args.prefill,
+                                   attn_splits=args.attn_splits)
     mb = m.batch > 1
     pos = list(w.contexts)
     K = args.steps if args.steps > 0 else w.steps
@@ -274,9 +275,10 @@ def phases(args):
     import torch
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import profiling
-    w, m, W, bufs, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill)
+    w, m, W, bufs, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill,
+                                   attn_splits=args.attn_splits)
     pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
-    info, _ = E.plan_describe(m, grid_wgs=args.grid)
+    info, _ = E.plan_describe(m, grid_wgs=args.grid, attn_splits=args.attn_splits)
     nsi, nW = info.n_stage_inst, info.n_wgs
     tr = torch.zeros(K * nsi * nW * 8, dtype=torch.int32, device="cuda")
     eng.set_trace(tr)
@@ -353,6 +355,7 @@ def main():
                     help="instead of timing: trace --steps steps of --workload with the in-kernel timestamp "
                          "ring and write the per-stage wait/busy/phase summary to this file")
     ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--attn-splits", type=int, default=0, help="attention chunks per KV head (0: default)")
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first copy this many MiB with the library's copy kernel (counter calibration)")

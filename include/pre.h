@@ -64,6 +64,8 @@ extern "C" {
 #define PRE_ERR_BROKEN (-8)      /* engine poisoned by an earlier device
                                     error; call pre_engine_reset first       */
 #define PRE_ERR_CONTEXT (-9)     /* positions + n_steps would pass max_ctx    */
+#define PRE_ERR_BUSY (-10)       /* a serving loop holds the engine, or the
+                                    request ring has no free slot            */
 
 /* Device error kinds in pre_status.error. */
 #define PRE_DEV_OK 0
@@ -245,6 +247,61 @@ int pre_engine_set_trace(pre_engine *e, void *d_buf, size_t bytes);
 
 /* Free the host-side state (no device memory is owned). */
 int pre_engine_destroy(pre_engine *e);
+
+/* ---- the serving loop: one resident launch, requests through a ring ------
+ * The resident kernel stays on the GPU between requests and takes them from
+ * a ring of descriptors in coherent host memory: the host writes a
+ * descriptor and marks it ready, the kernel's scheduler (workgroup 0) polls
+ * the ring, claims the oldest ready slot, and every workgroup decodes the
+ * request -- its prompt teacher-forced, then greedy tokens fed back on the
+ * device until the EOS token or the budget -- while workgroup 0 streams the
+ * tokens into the slot.  Each slot moves FREE -> READY (host) -> RUNNING ->
+ * DONE (kernel) -> FREE (host).  Sources: "Persistent execution paradigm"
+ * section 4 (a resident kernel that polls for work on the device) and
+ * section 5.6 (a GPU-resident scheduler over a ring with a per-slot state
+ * machine); XL-Persistent-Kernel, the request lifecycle (prompt, decode,
+ * stop at EOS or budget) and device-resident request descriptors.  Batch-1
+ * engines only (micro-batch engines return PRE_ERR_UNSUPPORTED).  While the
+ * loop runs it holds every CU: the engine's other calls return PRE_ERR_BUSY,
+ * and the caller must not wait on other GPU work of the device until
+ * pre_serve_stop. */
+typedef struct pre_server pre_server;
+typedef struct pre_serve_stats {
+  int32_t steps;   /* decode steps the loop ran */
+  int32_t served;  /* requests it finished (without a request error) */
+  int32_t error;   /* the device error latched by the loop (PRE_DEV_*) */
+} pre_serve_stats;
+
+/* Allocate the ring (n_slots slots, prompts of up to max_prompt tokens, up
+ * to max_out generated tokens each; coherent pinned host memory owned by
+ * the server) and launch the resident loop on `stream`.  The loop ends by
+ * itself after idle_ms milliseconds without a request (a bound for callers
+ * that never stop it).  The engine's ready-flag epochs and device positions
+ * continue across the loop. */
+int pre_serve_start(pre_engine *e, int32_t n_slots, int32_t max_prompt, int32_t max_out, uint32_t idle_ms,
+                    void *stream, pre_server **out);
+
+/* Submit a request (host only, no GPU call): n_prompt >= 1 tokens (h_prompt,
+ * host), decoded from position pos (the number of tokens already cached for
+ * the sequence; -1 = the engine's current position), then up to budget
+ * greedy tokens, stopping after a token equal to eos (-1: none).  The last
+ * prompt token's greedy successor is the first output.  *slot receives the
+ * slot to poll.  PRE_ERR_BUSY if every slot is taken, PRE_ERR_DEVICE if the
+ * loop has ended; a request the kernel finds invalid (its steps would pass
+ * max_ctx) is finished with that error in its slot and the loop goes on. */
+int pre_serve_submit(pre_server *s, const int32_t *h_prompt, int32_t n_prompt, int32_t pos, int32_t budget,
+                     int32_t eos, int32_t *slot);
+
+/* Copy up to max_tokens of the slot's tokens produced so far into h_tokens;
+ * *n_out = how many exist, *done = 1 once the request is finished (the slot
+ * is then freed; *err = its PRE_DEV_* error or 0).  Returns PRE_ERR_DEVICE
+ * if the loop ended before finishing the request. */
+int pre_serve_poll(pre_server *s, int32_t slot, int32_t *h_tokens, int32_t max_tokens, int32_t *n_out,
+                   int32_t *done, int32_t *err);
+
+/* Ask the loop to end, wait for the kernel, report its counts and free the
+ * ring and the server. */
+int pre_serve_stop(pre_server *s, pre_serve_stats *stats);
 
 /* Static description of an error code. */
 const char *pre_strerror(int code);

@@ -68,6 +68,13 @@ struct KP {
   int32_t mbst;          // longest GEMM input staged in LDS (columns; longer ones stream from memory)
   uint8_t *pk;           // packed GEMM inputs
   float *ssq;            // per-workgroup sums of squares of the normalised inputs
+  // serving loop: the request ring (coherent host memory) and the
+  // scheduler's broadcast area in the workspace
+  uint32_t *ring;        // header (16 words) then ring_slots slots of ring_words words
+  int32_t *cmd;          // workspace: command sequence number and the claimed request
+  int32_t *req_tok;      // workspace: the claimed request's prompt [max_ctx]
+  int32_t ring_slots, ring_prompt, ring_out, ring_words;
+  uint32_t idle_ticks;   // the loop ends after this long without a request
 };
 
 
@@ -1537,6 +1544,9 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
 // the micro-batch task set and kernel
 #include "mb.h"
 
+// the serving loop (request ring)
+#include "serve.h"
+
 // ---------------------------------------------------------------------------
 // baseline: one kernel per operator, stream order as the only sync
 
@@ -1666,6 +1676,7 @@ struct pre_engine {
   int device;
   int32_t drop_slot;  // debug: ready flag never published (-1: none)
   uint32_t static_gen;  // non-zero: created over the static workspace, with this generation
+  int serving;          // a serving loop holds the GPU: other calls return PRE_ERR_BUSY
 };
 
 static bool static_taken_over(const pre_engine *e);
@@ -1793,7 +1804,9 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
   const void *kern = D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess ||
+  if ((!D.mb && hipFuncSetAttribute((const void *)pre_serve, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
+                    hipSuccess) ||
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
     return PRE_ERR_HIP;
@@ -1846,6 +1859,7 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   e->device = dev;
   e->drop_slot = -1;
   e->static_gen = static_gen;
+  e->serving = 0;
   e->lw.assign(w->layers, w->layers + D.L);
   *out = e;
   return PRE_OK;
@@ -1855,6 +1869,7 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
 // (every queued call has advanced the positions) before they copy.
 extern "C" int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
+  if (e->serving) return PRE_ERR_BUSY;
   if (static_taken_over(e)) return PRE_ERR_BROKEN;
   for (int b = 0; b < e->D.B; ++b)
     if (h_pos[b] < 0 || h_pos[b] >= e->D.max_ctx) return PRE_ERR_CONTEXT;
@@ -1866,6 +1881,7 @@ extern "C" int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos) {
 
 extern "C" int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos) {
   if (!e || !h_pos) return PRE_ERR_ARG;
+  if (e->serving) return PRE_ERR_BUSY;
   if (static_taken_over(e)) return PRE_ERR_BROKEN;
   if (hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(h_pos, e->ctx, sizeof(int32_t) * e->D.B, hipMemcpyDeviceToHost) != hipSuccess)
@@ -1925,6 +1941,7 @@ static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in,
   if (!e || n_steps < 0) return PRE_ERR_ARG;
   if (n_steps == 0) return PRE_OK;  // nothing to do; the buffers are not read
   if (!d_out || (!d_in && !d_forced)) return PRE_ERR_ARG;
+  if (e->serving) return PRE_ERR_BUSY;
   if (e->broken || static_taken_over(e)) return PRE_ERR_BROKEN;
   if (n_steps > e->D.max_ctx) return PRE_ERR_CONTEXT;  // (positions live on the device: checked there)
   return PRE_OK;
@@ -2011,6 +2028,7 @@ static bool static_taken_over(const pre_engine *e) {
 
 extern "C" int pre_engine_status(pre_engine *e, pre_status *out) {
   if (!e || !out) return PRE_ERR_ARG;
+  if (e->serving) return PRE_ERR_BUSY;
   if (static_taken_over(e)) return PRE_ERR_BROKEN;
   DevStatus ds;
   if (hipStreamSynchronize(e->stream) != hipSuccess ||
@@ -2033,6 +2051,7 @@ extern "C" int pre_engine_status(pre_engine *e, pre_status *out) {
 
 extern "C" int pre_engine_reset(pre_engine *e, void *stream) {
   if (!e) return PRE_ERR_ARG;
+  if (e->serving) return PRE_ERR_BUSY;
   if (static_taken_over(e)) return PRE_ERR_BROKEN;
   hipStream_t st = (hipStream_t)stream;
   const Layout &Lo = e->Lo;
@@ -2064,6 +2083,136 @@ extern "C" int pre_engine_destroy(pre_engine *e) {
   return PRE_OK;
 }
 
+// ---- the serving loop (request ring) -------------------------------------
+
+struct pre_server {
+  pre_engine *e;
+  uint32_t *ring_h;  // coherent host memory (the host's view)
+  uint32_t *ring_d;  // the same memory as the kernel addresses it
+  int32_t slots, max_prompt, max_out, words;
+  int32_t next_seq;
+  hipStream_t stream;
+};
+
+static inline uint32_t ring_ld(const uint32_t *p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
+static inline void ring_st(uint32_t *p, uint32_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+
+extern "C" int pre_serve_start(pre_engine *e, int32_t n_slots, int32_t max_prompt, int32_t max_out,
+                               uint32_t idle_ms, void *stream, pre_server **out) {
+  if (!out) return PRE_ERR_ARG;
+  *out = nullptr;
+  if (!e || n_slots < 1 || n_slots > 64 || max_prompt < 1 || max_out < 1 || idle_ms == 0) return PRE_ERR_ARG;
+  if (e->D.mb) return PRE_ERR_UNSUPPORTED;
+  if (e->serving) return PRE_ERR_BUSY;
+  if (e->broken || static_taken_over(e)) return PRE_ERR_BROKEN;
+  if (max_prompt > e->D.max_ctx || max_out > e->D.max_ctx) return PRE_ERR_CONTEXT;
+  const int32_t words = (16 + max_prompt + max_out + 15) / 16 * 16;
+  const size_t bytes = 4 * ((size_t)RING_HDR + (size_t)n_slots * words);
+  void *h = nullptr, *d = nullptr;
+  if (hipHostMalloc(&h, bytes, hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess || !h) return PRE_ERR_HIP;
+  std::memset(h, 0, bytes);
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || !d) {
+    (void)hipHostFree(h);
+    return PRE_ERR_HIP;
+  }
+  KP P;
+  fill_kp(e, P, 1);
+  P.epoch_base = e->epoch_base;
+  P.ring = (uint32_t *)d;
+  P.cmd = (int32_t *)(e->ws + e->Lo.cmd);
+  P.req_tok = (int32_t *)(e->ws + e->Lo.req);
+  P.ring_slots = n_slots;
+  P.ring_prompt = max_prompt;
+  P.ring_out = max_out;
+  P.ring_words = words;
+  P.idle_ticks = (uint32_t)std::min<uint64_t>((uint64_t)idle_ms * 100000ull, 0xffffffffull);
+  hipStream_t st = (hipStream_t)stream;
+  void *args[] = {&P};
+  const unsigned nblk = (unsigned)(e->D.W * (e->D.onexcd ? e->D.X : 1));
+  if (hipMemsetAsync(P.cmd, 0, 64, st) != hipSuccess ||
+      hipLaunchCooperativeKernel((const void *)pre_serve, dim3(nblk), dim3(e->D.threads), args,
+                                 (unsigned)e->lds_dyn, st) != hipSuccess) {
+    (void)hipHostFree(h);
+    return PRE_ERR_HIP;
+  }
+  pre_server *s = new pre_server();
+  s->e = e;
+  s->ring_h = (uint32_t *)h;
+  s->ring_d = (uint32_t *)d;
+  s->slots = n_slots;
+  s->max_prompt = max_prompt;
+  s->max_out = max_out;
+  s->words = words;
+  s->next_seq = 1;
+  s->stream = st;
+  e->serving = 1;
+  *out = s;
+  return PRE_OK;
+}
+
+extern "C" int pre_serve_submit(pre_server *s, const int32_t *h_prompt, int32_t n_prompt, int32_t pos,
+                                int32_t budget, int32_t eos, int32_t *slot) {
+  if (!s || !h_prompt || !slot || n_prompt < 1 || n_prompt > s->max_prompt || budget < 1 ||
+      budget > s->max_out || pos < -1)
+    return PRE_ERR_ARG;
+  const Dims &D = s->e->D;
+  for (int i = 0; i < n_prompt; ++i)
+    if (h_prompt[i] < 0 || h_prompt[i] >= D.V) return PRE_ERR_ARG;
+  if (pos >= 0 && (int64_t)pos + n_prompt + budget - 1 > D.max_ctx) return PRE_ERR_CONTEXT;
+  if (ring_ld(s->ring_h + 1) == 2u) return PRE_ERR_DEVICE;  // the loop has ended
+  for (int i = 0; i < s->slots; ++i) {
+    uint32_t *sl = s->ring_h + RING_HDR + (size_t)i * s->words;
+    if (ring_ld(sl) != (uint32_t)SLOT_FREE) continue;
+    for (int k = 0; k < n_prompt; ++k) sl[16 + k] = (uint32_t)h_prompt[k];
+    sl[1] = (uint32_t)n_prompt;
+    sl[2] = (uint32_t)pos;
+    sl[3] = (uint32_t)budget;
+    sl[4] = (uint32_t)eos;
+    sl[5] = 0u;
+    sl[6] = 0u;
+    sl[7] = (uint32_t)s->next_seq++;
+    ring_st(sl, SLOT_READY);  // published after every field above
+    *slot = i;
+    return PRE_OK;
+  }
+  return PRE_ERR_BUSY;
+}
+
+extern "C" int pre_serve_poll(pre_server *s, int32_t slot, int32_t *h_tokens, int32_t max_tokens, int32_t *n_out,
+                              int32_t *done, int32_t *err) {
+  if (!s || slot < 0 || slot >= s->slots || !n_out || !done || max_tokens < 0 || (max_tokens && !h_tokens))
+    return PRE_ERR_ARG;
+  uint32_t *sl = s->ring_h + RING_HDR + (size_t)slot * s->words;
+  const uint32_t state = ring_ld(sl);
+  if (state == (uint32_t)SLOT_FREE) return PRE_ERR_ARG;
+  const int32_t n = (int32_t)ring_ld(sl + 5);  // tokens written before the count
+  for (int i = 0; i < n && i < max_tokens; ++i) h_tokens[i] = (int32_t)sl[16 + s->max_prompt + i];
+  *n_out = n;
+  *done = state == (uint32_t)SLOT_DONE;
+  if (err) *err = *done ? (int32_t)sl[6] : 0;
+  if (*done) ring_st(sl, SLOT_FREE);
+  else if (ring_ld(s->ring_h + 1) == 2u) return PRE_ERR_DEVICE;  // the loop ended before this request
+  return PRE_OK;
+}
+
+extern "C" int pre_serve_stop(pre_server *s, pre_serve_stats *stats) {
+  if (!s) return PRE_ERR_ARG;
+  ring_st(s->ring_h, 1u);
+  const hipError_t err = hipStreamSynchronize(s->stream);
+  pre_engine *e = s->e;
+  const uint32_t steps = ring_ld(s->ring_h + 2);
+  if (stats) {
+    stats->steps = (int32_t)steps;
+    stats->served = (int32_t)ring_ld(s->ring_h + 3);
+    stats->error = (int32_t)ring_ld(s->ring_h + 4);
+  }
+  e->epoch_base += steps;
+  e->serving = 0;
+  (void)hipHostFree(s->ring_h);
+  delete s;
+  return err == hipSuccess ? PRE_OK : PRE_ERR_HIP;
+}
+
 extern "C" const char *pre_strerror(int code) {
   switch (code) {
     case PRE_OK: return "ok";
@@ -2077,6 +2226,7 @@ extern "C" const char *pre_strerror(int code) {
     case PRE_ERR_BROKEN:
       return "engine broken by an earlier device error (reset it), or its static workspace was taken over";
     case PRE_ERR_CONTEXT: return "position would reach max_ctx";
+    case PRE_ERR_BUSY: return "busy: a serving loop holds the engine, or the request ring is full";
     default: return "unknown error";
   }
 }

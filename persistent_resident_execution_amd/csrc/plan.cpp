@@ -174,6 +174,8 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->tok = take((int64_t)D.B * 4 * 4);
   Lo->xmid = take((int64_t)D.L * D.B * D.h * f);  // post-attention residual (MoE layers, micro-batch)
   Lo->ctx = take((int64_t)D.B * 4);
+  Lo->cmd = take(64);
+  Lo->req = take((int64_t)D.max_ctx * 4);
   if (D.mb) {
     // packed bf16 hi/lo GEMM inputs: 4 KB per 128 columns (whole steps, the
     // tail left zero); per layer the QKV input (plus the LM head's), the

@@ -69,6 +69,7 @@ struct Layout {
   int64_t x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid;
   int64_t pk, ssq;  // micro-batch: packed GEMM inputs, per-workgroup sums of squares
   int64_t ctx;      // the engine's own position array [B] (used when the caller passes none)
+  int64_t cmd, req;  // serving loop: the scheduler's command words, the claimed prompt [max_ctx]
   int64_t total;
 };
 

@@ -20,7 +20,7 @@ _lib = None
 PRE_OK = 0
 ERRORS = {-1: "PRE_ERR_ARG", -2: "PRE_ERR_SHAPE", -3: "PRE_ERR_ALIGN", -4: "PRE_ERR_WORKSPACE",
           -5: "PRE_ERR_HIP", -6: "PRE_ERR_UNSUPPORTED", -7: "PRE_ERR_DEVICE", -8: "PRE_ERR_BROKEN",
-          -9: "PRE_ERR_CONTEXT"}
+          -9: "PRE_ERR_CONTEXT", -10: "PRE_ERR_BUSY"}
 DEV_ERRORS = {0: "ok", 1: "timeout", 2: "bad token", 3: "nan", 4: "placement", 5: "context"}
 
 
@@ -65,6 +65,10 @@ class Status(C.Structure):
         ("observed", C.c_uint32), ("expected", C.c_uint32), ("xcc_mismatch", C.c_int32)]
 
 
+class ServeStats(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("steps", "served", "error")]
+
+
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_stage_inst", "n_wgs", "n_slots", "n_tasks",
                                          "attn_splits", "validator", "xcd_local")] + [
@@ -76,7 +80,8 @@ EXPORTS = ["pre_workspace_size", "pre_engine_create", "pre_engine_create_static"
            "pre_engine_get_positions", "pre_engine_decode", "pre_baseline_decode",
            "pre_engine_status", "pre_engine_reset", "pre_engine_set_watchdog",
            "pre_engine_set_trace", "pre_engine_destroy", "pre_strerror", "pre_plan_describe",
-           "pre_plan_validate", "pre_step_bytes"]
+           "pre_plan_validate", "pre_step_bytes", "pre_serve_start", "pre_serve_submit", "pre_serve_poll",
+           "pre_serve_stop"]
 
 
 def lib():
@@ -104,6 +109,11 @@ def lib():
         L.pre_strerror.argtypes = [C.c_int]
         L.pre_plan_describe.argtypes = [C.POINTER(Config), C.POINTER(PlanInfo), vp, i32]
         L.pre_plan_validate.argtypes = [C.POINTER(Config), vp, i32]
+        L.pre_serve_start.argtypes = [vp, i32, i32, i32, C.c_uint32, vp, C.POINTER(vp)]
+        L.pre_serve_submit.argtypes = [vp, C.POINTER(i32), i32, i32, i32, i32, C.POINTER(i32)]
+        L.pre_serve_poll.argtypes = [vp, i32, C.POINTER(i32), i32, C.POINTER(i32), C.POINTER(i32),
+                                     C.POINTER(i32)]
+        L.pre_serve_stop.argtypes = [vp, C.POINTER(ServeStats)]
         L.pre_step_bytes.restype = C.c_int64
         L.pre_step_bytes.argtypes = [C.POINTER(Config), C.POINTER(i32)]
         # debug entries (not part of the C ABI header)
@@ -393,6 +403,65 @@ class Engine:
     def __del__(self):
         try:
             self.close()
+        except Exception:
+            pass
+
+
+class Server:
+    """The serving loop of an engine (pre_serve_*): one resident launch that
+    takes requests from a ring in host memory until stop().  submit / poll /
+    wait touch host memory only; no GPU work of the device may be waited on
+    while the loop runs (it holds every CU)."""
+
+    def __init__(self, eng: Engine, n_slots=8, max_prompt=256, max_out=256, idle_ms=10000, stream=None):
+        self.eng, self.max_out = eng, int(max_out)
+        self.h = None
+        h = C.c_void_p()
+        _check(lib().pre_serve_start(eng.h, int(n_slots), int(max_prompt), int(max_out), int(idle_ms),
+                                     _stream(stream), C.byref(h)), "serve_start")
+        self.h = h
+
+    def submit(self, prompt, pos=0, budget=16, eos=-1):
+        """Queue a request; returns its slot."""
+        toks = [int(t) for t in prompt]
+        arr = (C.c_int32 * len(toks))(*toks)
+        slot = C.c_int32()
+        _check(lib().pre_serve_submit(self.h, arr, len(toks), int(pos), int(budget), int(eos),
+                                      C.byref(slot)), "serve_submit")
+        return slot.value
+
+    def poll(self, slot):
+        """(tokens so far, done, request error)."""
+        buf = (C.c_int32 * self.max_out)()
+        n, done, err = C.c_int32(), C.c_int32(), C.c_int32()
+        _check(lib().pre_serve_poll(self.h, int(slot), buf, self.max_out, C.byref(n), C.byref(done),
+                                    C.byref(err)), "serve_poll")
+        return list(buf[:min(n.value, self.max_out)]), bool(done.value), err.value
+
+    def wait(self, slot, timeout_s=60.0):
+        """Poll until the request is done; returns (tokens, request error)."""
+        import time
+        t0 = time.time()
+        while True:
+            toks, done, err = self.poll(slot)
+            if done:
+                return toks, err
+            if time.time() - t0 > timeout_s:
+                raise TimeoutError(f"request in slot {slot} not done after {timeout_s}s ({len(toks)} tokens)")
+            time.sleep(0.0005)
+
+    def stop(self):
+        """End the loop; returns its counts (steps, served, error)."""
+        if self.h is None:
+            return None
+        st = ServeStats()
+        h, self.h = self.h, None
+        _check(lib().pre_serve_stop(h, C.byref(st)), "serve_stop")
+        return {"steps": st.steps, "served": st.served, "error": st.error}
+
+    def __del__(self):
+        try:
+            self.stop()
         except Exception:
             pass
 
