@@ -248,6 +248,120 @@ def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps
     return e, W
 
 
+def measure_chunk(args, W):
+    """The chunk task set on the 8B shape: (1) prefill of the workload's 1024
+    prompt tokens, 8 per step, one launch, against the same prompt fed
+    through the decode path one token per step (teacher-forced, one launch);
+    (2) speculative verify rounds of the current token plus 7 drafts that
+    are the model's own greedy continuation (all accepted: 8 tokens
+    committed per round), against greedy decode of the same tokens.  Each
+    timed with HIP events on the launch stream, median of repeats."""
+    import torch
+    from persistent_resident_execution_amd import engine as E
+    from persistent_resident_execution_amd import synth
+    w = synth.WORKLOADS["dense8b_ctx1024"]
+    m, P = w.model, w.contexts[0]
+    shape = (m.n_layers, 1, m.n_kv_heads, m.max_ctx, m.head_dim)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    ctx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eng = E.Engine(m, W, kc, vc, ctx_len=ctx, chunk=8)
+    prompt = synth.gen_tokens(m.vocab, P, seed=0, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            eng.set_positions([0])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            r = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        eng.status()
+        return statistics.median(ts), r
+
+    reps = max(3, args.repeats // 2)
+    timed(lambda: eng.prefill(prompt), 1)  # warm-up
+    t_chunk, out = timed(lambda: eng.prefill(prompt), reps)
+    t_tok, out_tok = timed(lambda: eng.decode(P, forced=prompt.view(P, 1)), reps)
+    import dataclasses
+    m8 = dataclasses.replace(m, batch=8)
+    nst = (P + 7) // 8
+    bytes_pf = sum(E.step_bytes(m8, [min(s * 8 + j, P - 1) for j in range(8)]) for s in range(nst))
+    g0 = int(out[-1].item())
+    res = {"prefill": {
+        "workload": f"{w.note.split(',')[0]}: prefill of the {P}-token prompt into an empty cache",
+        "tokens": P, "chunk": 8, "us_per_token": round(t_chunk / P * 1e6, 2),
+        "tokens_per_s": round(P / t_chunk, 1),
+        "decode_path_us_per_token": round(t_tok / P * 1e6, 2),
+        "speedup_vs_decode_path": round(t_tok / t_chunk, 2),
+        "same_first_token": g0 == int(out_tok[-1, 0].item()),
+        "roofline": {"bound": "hbm", "achieved": round(bytes_pf / t_chunk / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(bytes_pf / t_chunk / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "kernel": "pre_persistent_mb", "bytes_per_launch": bytes_pf,
+                     "launch_ms": round(t_chunk * 1e3, 3)}}}
+    # verify: the model's own greedy continuation as drafts (all accepted)
+    rounds = 8
+    eng.set_positions([P])
+    g = eng.decode(rounds * 8, in_tokens=out[-1:].contiguous())
+    torch.cuda.synchronize()
+    seq = [g0] + g[:, 0].tolist()
+    chunks = [torch.tensor(seq[8 * r:8 * r + 8], dtype=torch.int32, device="cuda") for r in range(rounds)]
+    acc_all = []
+
+    def verify_rounds():
+        accs = []
+        for c in chunks:
+            _, a = eng.verify(c)
+            accs.append(a)
+        return accs
+
+    def reset_to(p):
+        eng.set_positions([p])
+
+    ts = []
+    for _ in range(reps + 1):
+        reset_to(P)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        accs = verify_rounds()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+        acc_all = [int(a.item()) for a in accs]
+    t_v = statistics.median(ts[1:])
+    reset_to(P)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    eng.decode(rounds * 8, in_tokens=out[-1:].contiguous())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_d = e0.elapsed_time(e1) / 1e3
+    committed = sum(a + 1 for a in acc_all)
+    bytes_v = sum(E.step_bytes(m8, [P + 8 * r + j for j in range(8)]) for r in range(rounds))
+    res["verify"] = {
+        "workload": f"8B-shape dense decoder, context {P}: {rounds} verify rounds of the current token plus 7 "
+                    "drafts (the model's own greedy continuation, so all are accepted), one launch per round",
+        "accepted_per_round": acc_all, "tokens_committed": committed,
+        "us_per_round": round(t_v / rounds * 1e6, 2), "us_per_committed_token": round(t_v / committed * 1e6, 2),
+        "greedy_decode_us_per_token": round(t_d / (rounds * 8) * 1e6, 2),
+        "speedup_vs_greedy_decode": round(t_d / t_v * committed / (rounds * 8), 2),
+        "roofline": {"bound": "hbm", "achieved": round(bytes_v / t_v / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(bytes_v / t_v / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "pre_persistent_mb", "bytes_per_launch": bytes_v // rounds,
+                     "launch_ms": round(t_v / rounds * 1e3, 3)}}
+    eng.close()
+    del eng, kc, vc, ctx
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
 def tiny_grids(args, entry):
     """The tiny decoder's persistent µs/token at a few grid sizes (its
     default grid is one XCD's 32 CUs)."""
@@ -425,8 +539,13 @@ def run_main(args):
         result["stream_reference"] = stream_reference(e["roofline"]["achieved"])
     names = CONFIG_ORDER if args.configs == "all" else ([] if args.configs == "none" else args.configs.split(","))
     configs = {}
+    if "chunk" in names or (args.configs == "all" and head == "dense8b_ctx1024"):
+        log("[bench] chunk task set: prefill and speculative verify on the 8B shape")
+        ch = measure_chunk(args, W)
+        configs["dense8b_prefill"] = ch["prefill"]
+        configs["dense8b_verify"] = ch["verify"]
     for name in names:
-        if name == head:
+        if name == head or name == "chunk":
             continue
         mm = synth.WORKLOADS[name].model
         same = (mm.n_layers, mm.hidden, mm.vocab, mm.ffn_dim, mm.n_experts) == (

@@ -99,7 +99,12 @@ extern "C" {
  * every workgroup on XCD 0 and hand every flag over in its L2; -1 = always
  * hand off at device scope, no placement.  The persistent kernel checks the
  * placement it assumes and latches PRE_DEV_PLACEMENT if the hardware put a
- * workgroup elsewhere. */
+ * workgroup elsewhere.
+ * chunk (batch-1 dense engines): 0 = none; 2..8 = also build the chunk
+ * task set, the micro-batch tiles run over `chunk` consecutive tokens of the
+ * engine's one sequence, used by pre_engine_prefill and pre_engine_verify
+ * (hidden, ffn_dim and n_q_heads * head_dim multiples of 32; MoE returns
+ * PRE_ERR_UNSUPPORTED). */
 typedef struct pre_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t batch, max_ctx;
@@ -107,6 +112,7 @@ typedef struct pre_config {
   int32_t n_experts, top_k, n_shared, expert_ffn, expert_dtype;
   int32_t grid_wgs, wg_threads, attn_splits;
   int32_t xcd_local;
+  int32_t chunk;
 } pre_config;
 
 /* Per-layer weights (device pointers).  Dense: wg, wu [ffn][hidden], wd
@@ -216,6 +222,35 @@ int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos);
 int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
                       const int32_t *d_forced, int32_t *d_out_tokens, const pre_check *chk,
                       void *stream);
+
+/* Prefill inside the engine: the n_tokens prompt tokens d_tokens (device)
+ * are decoded teacher-forced from the sequence's position, `chunk` tokens per
+ * step through the chunk task set -- every weight is read once per chunk,
+ * the skinny GEMMs run on the matrix cores, attention is causal inside the
+ * chunk -- in ONE launch (the last chunk may be ragged: its padding columns
+ * append nothing).  d_out_tokens[i] (device) receives the greedy successor
+ * of token i, so d_out_tokens[n_tokens - 1] is the first generated token;
+ * chk (optional) receives logits [n_tokens][vocab] and hidden states
+ * [n_tokens][hidden].  The position advances by n_tokens on the device.
+ * Sources: XL-Persistent-Kernel, the request lifecycle's prefill; the
+ * SemiAnalysis TileRT digest, the prefill/decode split.  PRE_ERR_UNSUPPORTED
+ * without a chunk task set. */
+int pre_engine_prefill(pre_engine *e, int32_t n_tokens, const int32_t *d_tokens, int32_t *d_out_tokens,
+                       const pre_check *chk, void *stream);
+
+/* Speculative verify of n_draft draft tokens in one step (n_draft + 1 <=
+ * chunk): d_tokens (device) = the current input token, then the drafts, at
+ * positions pos .. pos + n_draft.  d_out_tokens[i] receives the greedy
+ * successor of tokens 0..i; on the device, the drafts are accepted while
+ * each equals the greedy successor of the token before it, *d_accepted
+ * (device) receives their number a, the position advances by a + 1 (the
+ * current token and the accepted drafts stay in the cache; rows past them
+ * are overwritten later), and d_out_tokens[a] is the next input.  The
+ * committed tokens are exactly those of plain greedy decoding.  Sources:
+ * TileRT notes, v0.1.2-alpha.1 (multi-token prediction in the execution
+ * flow); XL-Persistent-Kernel, the lifecycle's draft and verify steps. */
+int pre_engine_verify(pre_engine *e, int32_t n_draft, const int32_t *d_tokens, int32_t *d_out_tokens,
+                      int32_t *d_accepted, const pre_check *chk, void *stream);
 
 /* The same decode as a conventional one-kernel-per-operator launch sequence
  * (seven launches per dense layer, eight per MoE layer, four per step),

@@ -66,6 +66,11 @@ struct KP {
   int32_t drop_slot;     // debug: the task setting this ready flag skips the store (-1: none)
   // micro-batch
   int32_t mbst;          // longest GEMM input staged in LDS (columns; longer ones stream from memory)
+  int32_t Bc;            // sequences of the K/V cache (a chunk of one sequence: 1)
+  int32_t chunk;         // the B columns are consecutive tokens of sequence 0 (prefill, verify)
+  int32_t chunk_n;       // chunk mode: tokens of the call (the last step may be ragged)
+  int32_t verify;        // chunk mode, one step: accept the drafts, commit the accepted tokens
+  int32_t *v_accept;     // verify: the number of accepted drafts
   uint8_t *pk;           // packed GEMM inputs
   float *ssq;            // per-workgroup sums of squares of the normalised inputs
   // serving loop: the request ring (coherent host memory) and the
@@ -1427,7 +1432,7 @@ __device__ __forceinline__ void trace_rec(const KP &P, int step, int si, int lam
 // -1 on an error.
 __device__ __forceinline__ int call_position(const KP &P, int b) {
   const int p = __builtin_amdgcn_readfirstlane((int)ld_flag(reinterpret_cast<const uint32_t *>(P.ctx_len) + b));
-  const int n = P.persistent ? P.n_steps : P.b_nsteps;
+  const int n = P.chunk ? P.chunk_n : P.persistent ? P.n_steps : P.b_nsteps;
   if (p >= 0 && (int64_t)p + n <= P.max_ctx) return p;
   if (threadIdx.x == 0 && blockIdx.x == 0) latch_error(P, PRE_DEV_CONTEXT, 0, -1, b, (uint32_t)p, (uint32_t)P.max_ctx);
   return -1;
@@ -1677,6 +1682,13 @@ struct pre_engine {
   int32_t drop_slot;  // debug: ready flag never published (-1: none)
   uint32_t static_gen;  // non-zero: created over the static workspace, with this generation
   int serving;          // a serving loop holds the GPU: other calls return PRE_ERR_BUSY
+  // chunk task set (prefill / verify): its dims, layout, offset in the
+  // workspace and its own ready-flag epochs
+  int has_chunk;
+  Dims Dc;
+  Layout Lc;
+  int64_t coff;
+  uint32_t chunk_epoch;
 };
 
 static bool static_taken_over(const pre_engine *e);
@@ -1692,16 +1704,38 @@ static int device_cus(int *cus, int *lds_max, int *dev) {
   return PRE_OK;
 }
 
+// The chunk task set of a batch-1 engine (pre_config.chunk > 0): the
+// micro-batch task table with `chunk` columns that are consecutive tokens of
+// the engine's one sequence (prefill, speculative verify).  Dense models
+// whose GEMM inputs come in whole 32-column blocks only.
+static int chunk_dims(const pre_config *cfg, int cus, Dims *Dc) {
+  if (cfg->chunk == 0) return PRE_OK;
+  if (cfg->chunk < 2 || cfg->chunk > 8) return PRE_ERR_SHAPE;
+  if (cfg->batch != 1 || cfg->n_experts > 0) return PRE_ERR_UNSUPPORTED;
+  pre_config c = *cfg;
+  c.batch = cfg->chunk;
+  c.attn_splits = 0;
+  return derive_dims(&c, cus, Dc);
+}
+
+static int64_t align256h(int64_t x) { return (x + 255) & ~int64_t(255); }
+
 extern "C" int pre_workspace_size(const pre_config *cfg, size_t *bytes) {
   if (!cfg || !bytes) return PRE_ERR_ARG;
   int cus = 256, ldsm = 0, dev = 0;
   if (cfg->grid_wgs <= 0 && device_cus(&cus, &ldsm, &dev) != PRE_OK) cus = 256;
-  Dims D;
+  Dims D, Dc;
   int rc = derive_dims(cfg, cus, &D);
   if (rc != PRE_OK) return rc;
-  Layout Lo;
+  if ((rc = chunk_dims(cfg, cus, &Dc)) != PRE_OK) return rc;
+  Layout Lo, Lc;
   build_layout(D, &Lo);
-  *bytes = (size_t)Lo.total;
+  int64_t total = Lo.total;
+  if (cfg->chunk) {
+    build_layout(Dc, &Lc);
+    total = align256h(total) + Lc.total;
+  }
+  *bytes = (size_t)total;
   return PRE_OK;
 }
 
@@ -1790,16 +1824,26 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
     return PRE_ERR_ALIGN;
   for (int l = 0; l < D.L; ++l)
     if ((rc = check_layer(D, w->layers[l])) != PRE_OK) return rc;
-  Layout Lo;
+  Layout Lo, Lc;
   build_layout(D, &Lo);
-  if ((int64_t)ws_bytes < Lo.total) return PRE_ERR_WORKSPACE;
-  std::vector<Task> T;
+  Dims Dc;
+  std::memset(&Dc, 0, sizeof(Dc));
+  std::memset(&Lc, 0, sizeof(Lc));
+  if ((rc = chunk_dims(cfg, cus, &Dc)) != PRE_OK) return rc;
+  const int64_t coff = align256h(Lo.total);
+  if (cfg->chunk) build_layout(Dc, &Lc);
+  if ((int64_t)ws_bytes < (cfg->chunk ? coff + Lc.total : Lo.total)) return PRE_ERR_WORKSPACE;
+  std::vector<Task> T, Tc;
   build_tasks(D, T);
   if (validate(D, T) != 0) return PRE_ERR_SHAPE;
+  if (cfg->chunk) {
+    build_tasks(Dc, Tc);
+    if (validate(Dc, Tc) != 0) return PRE_ERR_SHAPE;
+  }
 
   // LDS: what the tiles need, raised past half a CU's LDS so that exactly one
   // workgroup fits per CU (one resident workgroup per CU).
-  int dyn = D.lds_bytes;
+  int dyn = std::max(D.lds_bytes, cfg->chunk ? Dc.lds_bytes : 0);
   const int want = std::min(ldsm, 96 * 1024);
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
@@ -1814,6 +1858,15 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, D.threads, dyn) != hipSuccess)
     return PRE_ERR_HIP;
   if (per_cu < 1 || (int64_t)per_cu * cus < (int64_t)D.W * (D.onexcd ? D.X : 1)) return PRE_ERR_SHAPE;
+  if (cfg->chunk) {
+    int per_cu_c = 0;
+    if (hipFuncSetAttribute((const void *)pre_persistent_mb, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_c, (const void *)pre_persistent_mb, Dc.threads, dyn) !=
+            hipSuccess)
+      return PRE_ERR_HIP;
+    if (per_cu_c < 1 || (int64_t)per_cu_c * cus < (int64_t)Dc.W) return PRE_ERR_SHAPE;
+  }
 
   std::vector<DevLayer> dl(D.L);
   for (int l = 0; l < D.L; ++l) std::memcpy(&dl[l], &w->layers[l], sizeof(DevLayer));
@@ -1833,9 +1886,20 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
           hipSuccess ||
       hipMemcpyAsync(ws + Lo.tasks, T.data(), T.size() * sizeof(Task), hipMemcpyHostToDevice, st) != hipSuccess ||
       hipMemcpyAsync(ws + Lo.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice, st) !=
-          hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
+          hipSuccess)
     return PRE_ERR_HIP;
+  if (cfg->chunk) {
+    char *wc = ws + coff;
+    if (hipMemsetAsync(wc, 0, (size_t)Lc.total, st) != hipSuccess ||
+        hipMemcpyAsync(wc + Lc.layers, dl.data(), dl.size() * sizeof(DevLayer), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(wc + Lc.tasks, Tc.data(), Tc.size() * sizeof(Task), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(wc + Lc.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice, st) !=
+            hipSuccess)
+      return PRE_ERR_HIP;
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return PRE_ERR_HIP;
 
   pre_engine *e = new pre_engine();
   e->cfg = *cfg;
@@ -1860,6 +1924,11 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   e->drop_slot = -1;
   e->static_gen = static_gen;
   e->serving = 0;
+  e->has_chunk = cfg->chunk > 0;
+  e->Dc = Dc;
+  e->Lc = Lc;
+  e->coff = coff;
+  e->chunk_epoch = 0;
   e->lw.assign(w->layers, w->layers + D.L);
   *out = e;
   return PRE_OK;
@@ -1889,8 +1958,22 @@ extern "C" int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos) {
   return PRE_OK;
 }
 
+static void fill_kp_dims(const pre_engine *e, const Dims &D, const Layout &Lo, char *ws, KP &P, int persistent);
+
 static void fill_kp(const pre_engine *e, KP &P, int persistent) {
-  const Dims &D = e->D;
+  fill_kp_dims(e, e->D, e->Lo, e->ws, P, persistent);
+}
+
+// The chunk task set's arguments: its own table, flags and activations; the
+// engine's status word, cache (one sequence) and position array.
+static void fill_kp_chunk(const pre_engine *e, KP &P) {
+  fill_kp_dims(e, e->Dc, e->Lc, e->ws + e->coff, P, 1);
+  P.status = (DevStatus *)(e->ws + e->Lo.status);
+  P.Bc = 1;
+  P.chunk = 1;
+}
+
+static void fill_kp_dims(const pre_engine *e, const Dims &D, const Layout &Lo, char *ws, KP &P, int persistent) {
   std::memset(&P, 0, sizeof(P));
   P.L = D.L; P.h = D.h; P.Hq = D.Hq; P.Hkv = D.Hkv; P.d = D.d; P.ffn = D.ffn; P.V = D.V; P.B = D.B;
   P.max_ctx = D.max_ctx; P.E = D.E; P.top_k = D.top_k; P.n_shared = D.n_shared; P.effn = D.effn;
@@ -1901,8 +1984,6 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.nw = D.threads / 64;
   P.eps = D.eps;
   P.attn_scale = (float)(1.0 / std::sqrt((double)D.d));
-  char *ws = e->ws;
-  const Layout &Lo = e->Lo;
   P.layers = (const DevLayer *)(ws + Lo.layers);
   P.embed = (const uint16_t *)e->embed;
   P.final_norm = (const uint16_t *)e->final_norm;
@@ -1929,6 +2010,7 @@ static void fill_kp(const pre_engine *e, KP &P, int persistent) {
   P.ctx_len = e->ctx;
   P.drop_slot = e->drop_slot;
   P.mbst = D.mbst;
+  P.Bc = D.B;
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;
@@ -1971,6 +2053,51 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   if (err != hipSuccess) return PRE_ERR_HIP;
   e->epoch_base += (uint32_t)n_steps;
   return PRE_OK;
+}
+
+// One launch of the chunk task set over n tokens of the engine's sequence.
+static int chunk_launch(pre_engine *e, int32_t n, const int32_t *d_tokens, int32_t *d_out, const pre_check *chk,
+                        int32_t *d_accept, void *stream) {
+  KP P;
+  fill_kp_chunk(e, P);
+  const int C = e->Dc.B;
+  P.n_steps = (n + C - 1) / C;
+  P.chunk_n = n;
+  P.verify = d_accept != nullptr;
+  P.v_accept = d_accept;
+  P.epoch_base = e->chunk_epoch;
+  P.forced = d_tokens;
+  P.out_tok = d_out;
+  P.chk_logits = chk ? chk->logits : nullptr;
+  P.chk_hidden = chk ? chk->hidden : nullptr;
+  void *args[] = {&P};
+  if (hipLaunchCooperativeKernel((const void *)pre_persistent_mb, dim3(e->Dc.W), dim3(e->Dc.threads), args,
+                                 (unsigned)e->lds_dyn, (hipStream_t)stream) != hipSuccess)
+    return PRE_ERR_HIP;
+  e->chunk_epoch += (uint32_t)P.n_steps;
+  return PRE_OK;
+}
+
+extern "C" int pre_engine_prefill(pre_engine *e, int32_t n_tokens, const int32_t *d_tokens, int32_t *d_out_tokens,
+                                  const pre_check *chk, void *stream) {
+  if (!e || n_tokens < 0) return PRE_ERR_ARG;
+  if (n_tokens == 0) return PRE_OK;
+  if (!d_tokens || !d_out_tokens) return PRE_ERR_ARG;
+  if (!e->has_chunk) return PRE_ERR_UNSUPPORTED;
+  if (e->serving) return PRE_ERR_BUSY;
+  if (e->broken || static_taken_over(e)) return PRE_ERR_BROKEN;
+  if (n_tokens > e->D.max_ctx) return PRE_ERR_CONTEXT;
+  return chunk_launch(e, n_tokens, d_tokens, d_out_tokens, chk, nullptr, stream);
+}
+
+extern "C" int pre_engine_verify(pre_engine *e, int32_t n_draft, const int32_t *d_tokens, int32_t *d_out_tokens,
+                                 int32_t *d_accepted, const pre_check *chk, void *stream) {
+  if (!e || !d_tokens || !d_out_tokens || !d_accepted || n_draft < 1) return PRE_ERR_ARG;
+  if (!e->has_chunk) return PRE_ERR_UNSUPPORTED;
+  if (n_draft + 1 > e->Dc.B) return PRE_ERR_SHAPE;
+  if (e->serving) return PRE_ERR_BUSY;
+  if (e->broken || static_taken_over(e)) return PRE_ERR_BROKEN;
+  return chunk_launch(e, n_draft + 1, d_tokens, d_out_tokens, chk, d_accepted, stream);
 }
 
 extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
@@ -2058,7 +2185,11 @@ extern "C" int pre_engine_reset(pre_engine *e, void *stream) {
   if (hipMemsetAsync(e->ws + Lo.status, 0, sizeof(DevStatus), st) != hipSuccess ||
       hipMemsetAsync(e->ws + Lo.flags, 0, (size_t)(Lo.layers - Lo.flags), st) != hipSuccess)
     return PRE_ERR_HIP;
+  if (e->has_chunk &&
+      hipMemsetAsync(e->ws + e->coff + e->Lc.flags, 0, (size_t)(e->Lc.layers - e->Lc.flags), st) != hipSuccess)
+    return PRE_ERR_HIP;
   e->epoch_base = 0;
+  e->chunk_epoch = 0;
   e->broken = 0;
   return PRE_OK;
 }

@@ -445,7 +445,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
           const int gh = p / half, g = gh / (P.G + 2), hh = gh % (P.G + 2), jj = p % half;
           const float r = M.rs[b];
           float a = r * mb_y(ys, nb, nkp, jA, b, i), c = r * mb_y(ys, nb, nkp, jA + 1, b, i);
-          const int pos = toks[8 + b] + step;
+          const int pos = toks[8 + b];  // column b's position in this step
           if (hh <= P.G) {  // RoPE on q and k
             const float cs = P.rope[(int64_t)pos * half + jj];
             const float sn = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + jj];
@@ -456,10 +456,12 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
             float *qd = P.q + vec_off(P, l, b, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
             st_sc1(qd + jj, a);
             st_sc1(qd + jj + half, c);
-          } else {  // the layer's K or V cache of every sequence under one descriptor each
-            const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
-            const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
-            const uint32_t o0 = (uint32_t)((((int64_t)b * P.Hkv + g) * P.max_ctx + pos) * P.d + jj) * 2;
+          } else if (toks[16 + b]) {  // the layer's K or V cache of every sequence under one descriptor each
+            // (a padding column of a ragged chunk appends nothing)
+            const int64_t lbase = (int64_t)l * P.Bc * P.Hkv * P.max_ctx * P.d;
+            const uint32_t bytes = (uint32_t)((int64_t)P.Bc * P.Hkv * P.max_ctx * P.d * 2);
+            const int cs = P.chunk ? 0 : b;  // the column's sequence in the cache
+            const uint32_t o0 = (uint32_t)((((int64_t)cs * P.Hkv + g) * P.max_ctx + pos) * P.d + jj) * 2;
             if (hh == P.G) {
               const Rsrc rr = mkbuf(P.kc + lbase, bytes);
               st16<CP_SC1>(rr, o0, f2bf(a));
@@ -506,7 +508,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] += mb_y(ys, nb, nkp, j, b, 8 * o + i);
             st8_vec(P, (down ? P.x_out : P.xmid) + vec_off(P, l, 0, P.h), b, r0, x);
-            if (down && P.chk_hidden && l == P.L - 1) {
+            if (down && P.chk_hidden && l == P.L - 1 && toks[16 + b]) {
               float *hd = P.chk_hidden + ((int64_t)step * P.B + b) * P.h + r0;
 #pragma unroll
               for (int i = 0; i < 8; ++i) hd[i] = x[i];
@@ -536,7 +538,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
             const float y = M.rs[b] * mb_y(ys, nb, nkp, j, b, i);
             if (y != y) nan = true;
             else argmax_merge(bv, bi, y, row);
-            if (P.chk_logits) P.chk_logits[((int64_t)step * P.B + b) * P.V + row] = y;
+            if (P.chk_logits && toks[16 + b]) P.chk_logits[((int64_t)step * P.B + b) * P.V + row] = y;
           }
         }
         break;
@@ -627,7 +629,8 @@ __device__ __forceinline__ int64_t mb_share(int64_t N, int Tw, int i) { return (
 //    lane).
 template <int NQ, int NS>
 __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, int g, int t0, int cnt, int pos,
-                                            float *lds, const MbWaiter *wait, bool first, bool last, bool &ok) {
+                                            int pnew, float *lds, const MbWaiter *wait, bool first, bool last,
+                                            bool &ok) {
   constexpr int D = 32 * NQ;  // head dimension
   constexpr int PL = 16 / NQ;  // positions per K load
   constexpr int RA = 8;  // K loads in flight per wavefront
@@ -637,14 +640,15 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
   const int cpad = ((P.cmax + 63) / 64) * 64;
   float *qs = lds, *sc = qs + G * D, *ored = sc + G * cpad, *st = ored + nw * G * D;
   float *Or = st + 2 * G, *Mr = Or + G * D, *Lr = Mr + G;
-  const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * D;
+  const int64_t cbase = (((int64_t)l * P.Bc + (P.chunk ? 0 : b)) * P.Hkv + g) * P.max_ctx * D;
   const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * D * 2);
   const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * D * 2);
   // K load u: positions u * PL ..; this lane's row and 16 bytes.  Before the
-  // wait the row this step's QKV stage writes is left out (reloaded after).
+  // wait the rows this step's QKV stage writes (pnew .. pos: the newest one,
+  // or a chunk's rows up to this column) are left out (reloaded after).
   auto koff = [&](int u, bool pre) -> uint32_t {
     const int tt = u * PL + ii / NQ;
-    const bool in = tt < cnt && !(pre && t0 + tt == pos);
+    const bool in = tt < cnt && !(pre && t0 + tt >= pnew);
     return in ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + (uint32_t)((ii % NQ) * 64 + qg * 16) : OOB;
   };
   const int nL = (cnt + PL - 1) / PL;
@@ -653,12 +657,12 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
 #pragma unroll
   for (int s = 0; s < RA; ++s) ka[s] = ld128<CP_SC1>(kr, koff(wave + nw * s, true));
   if (wait && !(*wait)(P)) { ok = false; return; }
-  if (t0 <= pos && pos < t0 + cnt) {  // the newest row, now written
-    const int up = (pos - t0) / PL;
-    if (up % nw == wave && up / nw < RA) {
+  if (t0 <= pos && pnew < t0 + cnt) {  // the rows written this step, now complete
+    const int ulo = (max(pnew, t0) - t0) / PL, uhi = (pos - t0) / PL;
 #pragma unroll
-      for (int s = 0; s < RA; ++s)
-        if (s == up / nw) ka[s] = ld128<CP_SC1>(kr, koff(up, false));
+    for (int s = 0; s < RA; ++s) {
+      const int u = wave + nw * s;
+      if (u >= ulo && u <= uhi) ka[s] = ld128<CP_SC1>(kr, koff(u, false));
     }
   }
   // q as the score columns: set s, column j = (head s * 16 / NQ + j / NQ, quarter j % NQ)
@@ -842,25 +846,29 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
 __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int step, const int *toks, float *lds,
                                         const MbWaiter &wait) {
   const int g = t.aux, i = t.r0, Tw = t.r1;
-  const int *pos0v = toks + 8;
+  const int *posv = toks + 8;  // each column's position in this step
   int64_t N = 0;
-  for (int b = 0; b < P.B; ++b) N += pos0v[b] + step + 1;
+  for (int b = 0; b < P.B; ++b) N += posv[b] + 1;
   const int64_t f0 = mb_share(N, Tw, i), f1 = mb_share(N, Tw, i + 1);
   bool ok = true, first = true;
   int64_t pre = 0;
   for (int b = 0; b < P.B && ok; ++b) {
-    const int pos = pos0v[b] + step;
+    const int pos = posv[b];
+    const int pnew = P.chunk ? posv[0] : pos;  // a chunk's rows of this step start at column 0's
     const int64_t lo = max(f0, pre), hi = min(f1, pre + pos + 1);
     // the piece in sub-pieces of at most cmax positions
     for (int64_t c0 = lo; c0 < hi && ok; c0 += P.cmax) {
       const int n = (int)min((int64_t)P.cmax, hi - c0);
       const MbWaiter *wp = first ? &wait : nullptr;
       if (P.d == 64)
-        mb_attn_sub<2, 1>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, wp, c0 == lo, c0 + n == hi, ok);
+        mb_attn_sub<2, 1>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, pnew, lds, wp, c0 == lo, c0 + n == hi,
+                          ok);
       else if (P.G <= 4)
-        mb_attn_sub<4, 1>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, wp, c0 == lo, c0 + n == hi, ok);
+        mb_attn_sub<4, 1>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, pnew, lds, wp, c0 == lo, c0 + n == hi,
+                          ok);
       else
-        mb_attn_sub<4, 2>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, lds, wp, c0 == lo, c0 + n == hi, ok);
+        mb_attn_sub<4, 2>(P, t.layer, lam, b, g, (int)(c0 - pre), n, pos, pnew, lds, wp, c0 == lo, c0 + n == hi,
+                          ok);
       first = false;
     }
     pre += pos + 1;
@@ -877,18 +885,18 @@ __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int
 __device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const int *toks, const MbWaiter &wait) {
   if (!wait(P)) return false;
   const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = threadIdx.x;
-  const int *pos0v = toks + 8;
+  const int *posv = toks + 8;
   const int rec = d + PREC_O, gd = G * d;
   const int ngr = (t.r1 - t.r0) >> 3, gpp = P.nthr >> 5;
   int64_t N = 0;
-  for (int b = 0; b < P.B; ++b) N += pos0v[b] + step + 1;
+  for (int b = 0; b < P.B; ++b) N += posv[b] + 1;
   for (int q0 = 0; q0 < ngr; q0 += gpp) {
     const int grp = q0 + (tid >> 5), sub = tid & 31;
     const bool act = grp < ngr;
     const int e = t.r0 + 8 * grp, b = act ? e / gd : 0, k = e % gd, hh = k / d, j0 = k % d;
     int64_t pre = 0;
-    for (int bb = 0; bb < b; ++bb) pre += pos0v[bb] + step + 1;
-    const int64_t nb = pos0v[b] + step + 1;
+    for (int bb = 0; bb < b; ++bb) pre += posv[bb] + 1;
+    const int64_t nb = posv[b] + 1;
     // workgroups holding f = pre and f = pre + nb - 1
     const int i_lo = (int)(((pre + 1) * Tw - 1) / N), i_hi = (int)(((pre + nb) * Tw - 1) / N);
     // the layer's records under one descriptor; record (wg, b, hh) at a per-lane offset
@@ -971,7 +979,10 @@ __device__ __forceinline__ bool mb_run_task(const Task &t, int lam, int step, co
 extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
-  __shared__ int toks[16];  // [0, 8): the step's tokens; [8, 16): the sequences' positions at the call's start
+  // [0, 8): each column's token of this step; [8, 16): its position in this
+  // step; [16, 24): 1 if the column is a real token (0: padding of a ragged
+  // chunk); [24, 32): the columns' positions at the call's start
+  __shared__ int toks[32];
   const bool res = P.persistent != 0;
   const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
   const int tid = threadIdx.x;
@@ -983,22 +994,34 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
   }
   const int s_begin = res ? 0 : P.b_step, s_end = res ? P.n_steps : P.b_step + 1;
   const int si0 = res ? 0 : P.b_si, si1 = res ? P.n_si : P.b_si + 1;
-  if (tid < P.B) {  // the first step's tokens (the baseline: its step's)
-    const int s = s_begin;
-    toks[tid] = P.forced ? P.forced[(int64_t)s * P.B + tid] : (s == 0 ? P.in_tok[tid] : P.tok_slot[tid]);
-  }
+  if (tid < P.B && !P.chunk)  // the first step's tokens (the baseline: its step's)
+    toks[tid] = P.forced ? P.forced[(int64_t)s_begin * P.B + tid]
+                         : (s_begin == 0 ? P.in_tok[tid] : P.tok_slot[tid]);
   // every sequence's start position (workgroup 0 advances them after the
-  // last step); all workgroups see the same values and leave together on an
-  // error
-  for (int b = 0; b < P.B; ++b) {
+  // last step; a chunk of one sequence has one); all workgroups see the same
+  // values and leave together on an error
+  for (int b = 0; b < (P.chunk ? 1 : P.B); ++b) {
     const int p = call_position(P, b);
     if (p < 0) return;
-    if (tid == 0) toks[8 + b] = p;
+    if (tid == 0) toks[24 + b] = p;
   }
   __syncthreads();
   for (int s = s_begin; s < s_end; ++s) {
     const uint32_t ep = P.epoch_base + (uint32_t)s + 1u;
-    if (res && P.forced && tid < P.B) toks[tid] = P.forced[(int64_t)s * P.B + tid];
+    if (tid < P.B) {
+      if (P.chunk) {
+        // column b is token j = s * B + b of the chunked sequence; past the
+        // last token the padding repeats it and appends nothing
+        const int j = s * P.B + tid, jj = min(j, P.chunk_n - 1);
+        toks[tid] = P.forced[jj];
+        toks[8 + tid] = toks[24] + jj;
+        toks[16 + tid] = j < P.chunk_n;
+      } else {
+        if (res && P.forced) toks[tid] = P.forced[(int64_t)s * P.B + tid];
+        toks[8 + tid] = toks[24 + tid] + s;
+        toks[16 + tid] = 1;
+      }
+    }
     __syncthreads();
     int bad = 0, badtok = 0;
     for (int b = 0; b < P.B; ++b)
@@ -1023,18 +1046,38 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
     if (need) {
       const int s_lm = P.n_si - 1;
       if (!wait_slots(P, s_lm * P.W, (s_lm + 1) * P.W, ep, s, s_lm, sh)) return;
+      const int act = toks[16 + min(tid, P.B - 1)];
       mb_reduce(P, toks);
       for (int b = 0; b < P.B; ++b)
         if (toks[b] < 0) {
           if (tid == 0) latch_error(P, PRE_DEV_NAN, s, s_lm, -1, 0, 0);
           return;
         }
-      if (lam == 0 && tid < P.B) P.out_tok[(int64_t)s * P.B + tid] = toks[tid];
+      if (lam == 0 && tid < P.B && act) P.out_tok[(int64_t)s * P.B + tid] = toks[tid];
       __syncthreads();
     }
   }
-  if (res && lam == 0 && tid < P.B)
-    st_flag(reinterpret_cast<uint32_t *>(P.ctx_len) + tid, (uint32_t)(toks[8 + tid] + P.n_steps));
+  if (!res || lam != 0) return;
+  // Workgroup 0 has seen every workgroup's LM flag of the last step: every
+  // workgroup has read the start positions.  Commit the call's tokens.
+  if (!P.chunk) {
+    if (tid < P.B) st_flag(reinterpret_cast<uint32_t *>(P.ctx_len) + tid, (uint32_t)(toks[24 + tid] + P.n_steps));
+  } else if (tid == 0) {
+    int keep = P.chunk_n;
+    if (P.verify) {
+      // speculative verify (one step): column 0 is the current token and
+      // columns 1..k the drafts; column b's greedy token (toks[b]) is the
+      // model's successor of columns 0..b.  The drafts are accepted while each
+      // equals the greedy successor of the one before; the accepted tokens and
+      // the current one stay in the cache, the next input is the greedy
+      // token after the last accepted draft.
+      int a = 0;
+      while (a + 1 < P.chunk_n && P.forced[a + 1] == toks[a]) ++a;
+      P.v_accept[0] = a;
+      keep = a + 1;
+    }
+    st_flag(reinterpret_cast<uint32_t *>(P.ctx_len), (uint32_t)(toks[24] + keep));
+  }
 }
 
 // Baseline: each sequence's greedy token of step `step` (one workgroup).

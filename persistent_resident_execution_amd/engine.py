@@ -7,6 +7,7 @@ library has not been built -- there is no fallback path.
 from __future__ import annotations
 
 import ctypes as C
+import dataclasses
 import os
 
 import torch
@@ -35,7 +36,7 @@ class Config(C.Structure):
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "batch", "max_ctx")] + [("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [
         (n, C.c_int32) for n in ("n_experts", "top_k", "n_shared", "expert_ffn", "expert_dtype",
-                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local")]
+                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local", "chunk")]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "router",
@@ -81,7 +82,7 @@ EXPORTS = ["pre_workspace_size", "pre_engine_create", "pre_engine_create_static"
            "pre_engine_status", "pre_engine_reset", "pre_engine_set_watchdog",
            "pre_engine_set_trace", "pre_engine_destroy", "pre_strerror", "pre_plan_describe",
            "pre_plan_validate", "pre_step_bytes", "pre_serve_start", "pre_serve_submit", "pre_serve_poll",
-           "pre_serve_stop"]
+           "pre_serve_stop", "pre_engine_prefill", "pre_engine_verify"]
 
 
 def lib():
@@ -100,6 +101,8 @@ def lib():
         L.pre_engine_get_positions.argtypes = [vp, C.POINTER(i32)]
         for f in (L.pre_engine_decode, L.pre_baseline_decode):
             f.argtypes = [vp, i32, vp, vp, vp, C.POINTER(Check), vp]
+        L.pre_engine_prefill.argtypes = [vp, i32, vp, vp, C.POINTER(Check), vp]
+        L.pre_engine_verify.argtypes = [vp, i32, vp, vp, vp, C.POINTER(Check), vp]
         L.pre_engine_status.argtypes = [vp, C.POINTER(Status)]
         L.pre_engine_reset.argtypes = [vp, vp]
         L.pre_engine_set_watchdog.argtypes = [vp, C.c_uint32]
@@ -129,7 +132,7 @@ def lib():
     return _lib
 
 
-def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, xcd_local=0) -> Config:
+def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, xcd_local=0, chunk=0) -> Config:
     c = Config()
     for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
               "batch", "max_ctx", "n_experts", "top_k", "n_shared", "expert_ffn"):
@@ -139,6 +142,7 @@ def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, x
     c.expert_dtype = 1 if m.is_moe else 0
     c.grid_wgs, c.wg_threads, c.attn_splits = int(grid_wgs), int(wg_threads), int(attn_splits)
     c.xcd_local = int(xcd_local)
+    c.chunk = int(chunk)
     return c
 
 
@@ -279,7 +283,7 @@ class Engine:
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
                  wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None,
-                 static_workspace=False):
+                 static_workspace=False, chunk=0):
         """static_workspace: create with pre_engine_create_static (the
         library's static device workspace; no allocation) instead of a
         workspace tensor."""
@@ -290,7 +294,8 @@ class Engine:
         for t in [weights["embed"], v_cache] + ([ctx_len] if ctx_len is not None else []):
             _need(t.device == dev, f"every tensor must be on {dev}, found one on {t.device}")
         self.device = dev
-        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local)
+        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local, chunk)
+        self.chunk = int(chunk)
         L = lib()
         nbytes = C.c_size_t()
         _check(L.pre_workspace_size(C.byref(self.cfg), C.byref(nbytes)), "workspace_size")
@@ -359,6 +364,43 @@ class Engine:
         self._run(lib().pre_baseline_decode, n_steps, in_tokens, forced, out_tokens, logits,
                   hidden, stream)
         return out_tokens
+
+    def prefill(self, tokens, out_tokens=None, logits=None, hidden=None, stream=None):
+        """Prefill through the chunk task set (pre_engine_prefill): tokens
+        int32 [n] on the device; returns the greedy successor of each token
+        (int32 [n]; the last one is the first generated token)."""
+        _need(self.h is not None, "engine is closed")
+        n = int(tokens.numel())
+        if out_tokens is None:
+            out_tokens = torch.empty(n, dtype=torch.int32, device=self.device)
+        mm = dataclasses.replace(self.m, batch=1)
+        check_tensor(tokens, "tokens", torch.int32, numel=n)
+        check_decode_args(mm, n, None, tokens, out_tokens, logits, hidden)
+        for t in (tokens, out_tokens, logits, hidden):
+            _need(t is None or t.device == self.device, f"every buffer must be on {self.device}")
+        chk = Check(_ptr(logits), _ptr(hidden))
+        _check(lib().pre_engine_prefill(self.h, n, _ptr(tokens), _ptr(out_tokens), C.byref(chk), _stream(stream)),
+               "engine_prefill")
+        return out_tokens
+
+    def verify(self, tokens, out_tokens=None, accepted=None, logits=None, stream=None):
+        """Speculative verify (pre_engine_verify): tokens int32 [1 + k] on the
+        device (the current token, then k drafts); returns (greedy successors
+        [1 + k], accepted count [1]) as device tensors."""
+        _need(self.h is not None, "engine is closed")
+        n = int(tokens.numel())
+        if out_tokens is None:
+            out_tokens = torch.empty(n, dtype=torch.int32, device=self.device)
+        if accepted is None:
+            accepted = torch.empty(1, dtype=torch.int32, device=self.device)
+        mm = dataclasses.replace(self.m, batch=1)
+        check_tensor(tokens, "tokens", torch.int32, numel=n)
+        check_decode_args(mm, n, None, tokens, out_tokens, logits, None)
+        check_tensor(accepted, "accepted", torch.int32, numel=1)
+        chk = Check(_ptr(logits), None)
+        _check(lib().pre_engine_verify(self.h, n - 1, _ptr(tokens), _ptr(out_tokens), _ptr(accepted),
+                                       C.byref(chk), _stream(stream)), "engine_verify")
+        return out_tokens, accepted
 
     def status(self, raise_on_error=True):
         st = Status()
