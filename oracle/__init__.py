@@ -52,6 +52,11 @@ class OrcLayer(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in _LAYER_FIELDS]
 
 
+class OrcKV(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("k_scale", C.c_void_p), ("v_scale", C.c_void_p),
+                ("layer_stride", C.c_int64), ("scale_layer_stride", C.c_int64), ("fp8", C.c_int32)]
+
+
 class OrcWeights(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("lm_head", C.c_void_p),
                 ("layers", C.POINTER(OrcLayer))]
@@ -89,6 +94,13 @@ def lib():
         L.orc_forward_full.argtypes = [C.POINTER(OrcConfig), C.POINTER(OrcWeights), vp, i32, dp, dp]
         L.orc_prefill.restype = C.c_int
         L.orc_prefill.argtypes = [C.POINTER(OrcConfig), C.POINTER(OrcWeights), vp, vp, i64, vp, i32]
+        L.orc_float_to_fp8e4m3.restype = C.c_uint8
+        L.orc_float_to_fp8e4m3.argtypes = [C.c_float]
+        L.orc_quantize_row_fp8.argtypes = [vp, i32, vp, vp]
+        L.orc_attend_fp8.argtypes = [dp, vp, vp, vp, vp, i32, i32, dp]
+        L.orc_decode_step_kv.restype = C.c_int
+        L.orc_decode_step_kv.argtypes = [C.POINTER(OrcConfig), C.POINTER(OrcWeights), C.POINTER(OrcKV), i32,
+                                         i32, dp, dp]
         L.orc_num_threads.restype = C.c_int
         L.orc_set_num_threads.argtypes = [C.c_int]
         _lib = L
@@ -125,6 +137,31 @@ def fp8_to_f64(codes) -> np.ndarray:
     L = lib()
     c = np.asarray(codes, dtype=np.uint8).ravel()
     return np.array([L.orc_fp8e4m3_to_double(int(x)) for x in c], dtype=np.float64)
+
+
+def f32_to_fp8(vals) -> np.ndarray:
+    L = lib()
+    v = np.asarray(vals, dtype=np.float32).ravel()
+    return np.array([L.orc_float_to_fp8e4m3(float(x)) for x in v], dtype=np.uint8)
+
+
+def quantize_row_fp8(x):
+    """(codes uint8 [n], fp32 scale) of one cached row."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.size, np.uint8)
+    sc = np.empty(1, np.float32)
+    lib().orc_quantize_row_fp8(_vp(x), x.size, _vp(codes), _vp(sc))
+    return codes, float(sc[0])
+
+
+def attend_fp8(q, Kc, Ks, Vc, Vs):
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    Kc, Vc = np.ascontiguousarray(Kc, dtype=np.uint8), np.ascontiguousarray(Vc, dtype=np.uint8)
+    Ks, Vs = np.ascontiguousarray(Ks, dtype=np.float32), np.ascontiguousarray(Vs, dtype=np.float32)
+    n, d = Kc.shape
+    o = np.empty(d, dtype=np.float64)
+    lib().orc_attend_fp8(_dp(q), _vp(Kc), _vp(Ks), _vp(Vc), _vp(Vs), n, d, _dp(o))
+    return o
 
 
 def silu(z: float) -> float:
@@ -263,6 +300,30 @@ class OracleModel:
                                     C.c_void_p(vc.ctypes.data), stride, int(token), int(pos),
                                     _dp(lg) if lg is not None else None,
                                     _dp(hd) if hd is not None else None)
+        return tok, lg, hd
+
+    def new_cache_fp8(self):
+        """Zeroed fp8 caches: codes uint8 [n_layers][n_kv_heads][max_ctx][head_dim]
+        (K, V) and fp32 row scales [n_layers][n_kv_heads][max_ctx] (K, V)."""
+        c = self.cfg
+        shape = (c.n_layers, c.n_kv_heads, c.max_ctx, c.head_dim)
+        return (np.zeros(shape, np.uint8), np.zeros(shape, np.uint8), np.zeros(shape[:3], np.float32),
+                np.zeros(shape[:3], np.float32))
+
+    def decode_step_fp8(self, kc8, vc8, ks, vs, token, pos, want_logits=True, want_hidden=True):
+        """decode_step over an fp8 cache (codes [L][Hkv][max_ctx][d] uint8 and
+        fp32 row scales [L][Hkv][max_ctx]; inner dimensions contiguous)."""
+        c = self.cfg
+        assert kc8.dtype == np.uint8 and vc8.dtype == np.uint8 and ks.dtype == np.float32
+        assert kc8.shape[1:] == (c.n_kv_heads, c.max_ctx, c.head_dim) and ks.shape[1:] == (c.n_kv_heads, c.max_ctx)
+        assert kc8.strides == vc8.strides and kc8.strides[1:] == (c.max_ctx * c.head_dim, c.head_dim, 1)
+        assert ks.strides == vs.strides and ks.strides[1:] == (c.max_ctx * 4, 4)
+        kv = OrcKV(kc8.ctypes.data, vc8.ctypes.data, ks.ctypes.data, vs.ctypes.data, kc8.strides[0],
+                   ks.strides[0] // 4, 1)
+        lg = np.empty(c.vocab, np.float64) if want_logits else None
+        hd = np.empty(c.hidden, np.float64) if want_hidden else None
+        tok = lib().orc_decode_step_kv(C.byref(self.c), C.byref(self.w), C.byref(kv), int(token), int(pos),
+                                       _dp(lg) if lg is not None else None, _dp(hd) if hd is not None else None)
         return tok, lg, hd
 
     def prefill(self, kc, vc, tokens):

@@ -53,6 +53,40 @@ double orc_fp8e4m3_to_double(uint8_t c) {
   return s ? -v : v;
 }
 
+uint8_t orc_float_to_fp8e4m3(float x) {
+  /* OCP E4M3: magnitudes below 2^-6 are subnormal multiples of 2^-9; above,
+   * 3 mantissa bits under exponents -6..8; 448 = 1.75 * 2^8 is the largest
+   * finite value (S.1111.111 is NaN). */
+  if (isnan(x)) return 0x7F;
+  uint8_t s = signbit(x) ? 0x80 : 0x00;
+  float a = fabsf(x);
+  if (a >= 448.0f) return (uint8_t)(s | 0x7E);
+  if (a < 0x1p-6f) {
+    /* a * 2^9 is exact; rounding it to an integer (ties to even) gives the
+     * subnormal's mantissa, and 8 is the smallest normal, code 0x08 */
+    return (uint8_t)(s | (uint8_t)nearbyintf(a * 512.0f));
+  }
+  int e;
+  frexpf(a, &e); /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  float m = nearbyintf(ldexpf(a, 3 - E)); /* 1.mmm * 8, ties to even: 8..16 */
+  if (m == 16.0f) {
+    m = 8.0f;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && m > 14.0f)) return (uint8_t)(s | 0x7E);
+  return (uint8_t)(s | (uint8_t)(((E + 7) << 3) | ((int)m - 8)));
+}
+
+void orc_quantize_row_fp8(const float *x, int n, uint8_t *codes, float *scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i)
+    if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int i = 0; i < n; ++i) codes[i] = orc_float_to_fp8e4m3(x[i] / sc);
+  *scale = sc;
+}
+
 double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* ---- building blocks --------------------------------------------------- */
@@ -128,6 +162,26 @@ void orc_attend(const double *q, const uint16_t *K, const uint16_t *V, int n_pos
   for (int j = 0; j < d; ++j) o[j] = 0.0;
   for (int t = 0; t < n_pos; ++t)
     for (int j = 0; j < d; ++j) o[j] += p[t] * orc_bf16_to_double(V[(int64_t)t * d + j]);
+  free(s);
+  free(p);
+}
+
+void orc_attend_fp8(const double *q, const uint8_t *Kc, const float *Ks, const uint8_t *Vc,
+                    const float *Vs, int n_pos, int d, double *o) {
+  double *s = (double *)malloc(sizeof(double) * (size_t)n_pos);
+  double *p = (double *)malloc(sizeof(double) * (size_t)n_pos);
+  double scale = 1.0 / sqrt((double)d);
+  for (int t = 0; t < n_pos; ++t) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j)
+      acc += q[j] * (orc_fp8e4m3_to_double(Kc[(int64_t)t * d + j]) * (double)Ks[t]);
+    s[t] = acc * scale;
+  }
+  orc_softmax(s, n_pos, p);
+  for (int j = 0; j < d; ++j) o[j] = 0.0;
+  for (int t = 0; t < n_pos; ++t)
+    for (int j = 0; j < d; ++j)
+      o[j] += p[t] * (orc_fp8e4m3_to_double(Vc[(int64_t)t * d + j]) * (double)Vs[t]);
   free(s);
   free(p);
 }
@@ -248,7 +302,14 @@ static int lm_head(const orc_config *c, const orc_weights *w, const double *x,
 int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kc,
                     uint16_t *vc, int64_t layer_stride, int token, int pos,
                     double *logits_out, double *hidden_out) {
+  orc_kv kv = {kc, vc, NULL, NULL, layer_stride, 0, 0};
+  return orc_decode_step_kv(c, w, &kv, token, pos, logits_out, hidden_out);
+}
+
+int orc_decode_step_kv(const orc_config *c, const orc_weights *w, const orc_kv *kv, int token,
+                       int pos, double *logits_out, double *hidden_out) {
   int h = c->hidden, Hq = c->n_q_heads, Hkv = c->n_kv_heads, d = c->head_dim;
+  int64_t layer_stride = kv->layer_stride;
   if (token < 0 || token >= c->vocab || pos < 0 || pos >= c->max_ctx) return -1;
   double *x = (double *)malloc(sizeof(double) * (size_t)h);
   double *a = (double *)malloc(sizeof(double) * (size_t)h);
@@ -266,19 +327,42 @@ int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kc,
     orc_gemv_bf16(L->wv, Hkv * d, h, a, v);
     for (int hh = 0; hh < Hq; ++hh) orc_rope(q + hh * d, d, pos, c->rope_theta);
     for (int g = 0; g < Hkv; ++g) orc_rope(k + g * d, d, pos, c->rope_theta);
-    uint16_t *Kl = kc + (int64_t)l * layer_stride;
-    uint16_t *Vl = vc + (int64_t)l * layer_stride;
-    for (int g = 0; g < Hkv; ++g)
-      for (int j = 0; j < d; ++j) {
-        int64_t off = ((int64_t)g * c->max_ctx + pos) * d + j;
-        Kl[off] = orc_float_to_bf16((float)k[g * d + j]);
-        Vl[off] = orc_float_to_bf16((float)v[g * d + j]);
-      }
+    if (!kv->fp8) {
+      uint16_t *Kl = (uint16_t *)kv->k + (int64_t)l * layer_stride;
+      uint16_t *Vl = (uint16_t *)kv->v + (int64_t)l * layer_stride;
+      for (int g = 0; g < Hkv; ++g)
+        for (int j = 0; j < d; ++j) {
+          int64_t off = ((int64_t)g * c->max_ctx + pos) * d + j;
+          Kl[off] = orc_float_to_bf16((float)k[g * d + j]);
+          Vl[off] = orc_float_to_bf16((float)v[g * d + j]);
+        }
 #pragma omp parallel for schedule(static)
-    for (int hh = 0; hh < Hq; ++hh) {
-      int g = (int)(((int64_t)hh * Hkv) / Hq);
-      orc_attend(q + hh * d, Kl + (int64_t)g * c->max_ctx * d,
-                 Vl + (int64_t)g * c->max_ctx * d, pos + 1, d, o + hh * d);
+      for (int hh = 0; hh < Hq; ++hh) {
+        int g = (int)(((int64_t)hh * Hkv) / Hq);
+        orc_attend(q + hh * d, Kl + (int64_t)g * c->max_ctx * d,
+                   Vl + (int64_t)g * c->max_ctx * d, pos + 1, d, o + hh * d);
+      }
+    } else {
+      uint8_t *Kl = (uint8_t *)kv->k + (int64_t)l * layer_stride;
+      uint8_t *Vl = (uint8_t *)kv->v + (int64_t)l * layer_stride;
+      float *KSl = kv->k_scale + (int64_t)l * kv->scale_layer_stride;
+      float *VSl = kv->v_scale + (int64_t)l * kv->scale_layer_stride;
+      float *row = (float *)malloc(sizeof(float) * (size_t)d);
+      for (int g = 0; g < Hkv; ++g) {
+        int64_t r = (int64_t)g * c->max_ctx + pos;
+        for (int j = 0; j < d; ++j) row[j] = (float)k[g * d + j];
+        orc_quantize_row_fp8(row, d, Kl + r * d, KSl + r);
+        for (int j = 0; j < d; ++j) row[j] = (float)v[g * d + j];
+        orc_quantize_row_fp8(row, d, Vl + r * d, VSl + r);
+      }
+      free(row);
+#pragma omp parallel for schedule(static)
+      for (int hh = 0; hh < Hq; ++hh) {
+        int g = (int)(((int64_t)hh * Hkv) / Hq);
+        orc_attend_fp8(q + hh * d, Kl + (int64_t)g * c->max_ctx * d, KSl + (int64_t)g * c->max_ctx,
+                       Vl + (int64_t)g * c->max_ctx * d, VSl + (int64_t)g * c->max_ctx, pos + 1, d,
+                       o + hh * d);
+      }
     }
     orc_gemv_bf16(L->wo, h, Hq * d, o, dl);
     for (int i = 0; i < h; ++i) x[i] += dl[i];

@@ -24,7 +24,9 @@
  *     query head h reads KV head floor(h * Hkv / Hq);
  *   - rounding points: weights as given (bf16, or fp8 e4m3 times a bf16
  *     128x128 block scale); K and V rounded to bf16 (round to nearest even)
- *     from an fp32 value when appended; nothing else is rounded;
+ *     from an fp32 value when appended (or, with an fp8 cache, quantized per
+ *     row: an fp32 scale amax/448 and e4m3 codes of the fp32 quotients, ties
+ *     to even, saturating at 448); nothing else is rounded;
  *   - SwiGLU FFN: Wd (silu(Wg b) * (Wu b)), silu(z) = z / (1 + e^-z);
  *   - MoE: softmax over all router logits, the top-k probabilities (ties to
  *     the lower expert id) weight their experts without renormalisation,
@@ -72,6 +74,23 @@ typedef struct {
 double orc_bf16_to_double(uint16_t b);
 uint16_t orc_float_to_bf16(float f);
 double orc_fp8e4m3_to_double(uint8_t c);
+/* fp32 -> OCP E4M3 code: round to nearest, ties to even, magnitudes at or
+ * above 448 (the largest finite value) saturate to +-448, NaN -> 0x7F. */
+uint8_t orc_float_to_fp8e4m3(float x);
+/* One cached K or V row in fp8: scale = amax(|x|) / 448 in fp32 (1 for an
+ * all-zero row), codes[j] = e4m3(x[j] / scale) with the fp32 quotient. */
+void orc_quantize_row_fp8(const float *x, int n, uint8_t *codes, float *scale);
+
+/* The K/V cache of one sequence: bf16 rows, or fp8 e4m3 codes with one fp32
+ * scale per row.  k, v: [n_layers][n_kv_heads][max_ctx][head_dim] (layer
+ * distance layer_stride elements); k_scale, v_scale: [n_layers][n_kv_heads]
+ * [max_ctx] (layer distance scale_layer_stride) when fp8. */
+typedef struct {
+  void *k, *v;
+  float *k_scale, *v_scale;
+  int64_t layer_stride, scale_layer_stride;
+  int32_t fp8;
+} orc_kv;
 
 /* Building blocks (each a plain definition). */
 void orc_rmsnorm(const double *x, const uint16_t *g, int n, double eps, double *out);
@@ -82,6 +101,9 @@ void orc_rope(double *v, int d, int pos, double theta);
 void orc_softmax(const double *s, int n, double *p);
 void orc_attend(const double *q, const uint16_t *K, const uint16_t *V, int n_pos,
                 int d, double *o);
+/* The same over fp8 rows: K[t][j] = fp8dec(Kc[t][j]) * Ks[t] (V alike). */
+void orc_attend_fp8(const double *q, const uint8_t *Kc, const float *Ks, const uint8_t *Vc,
+                    const float *Vs, int n_pos, int d, double *o);
 int orc_argmax(const double *v, int n);
 void orc_topk(const double *p, int n, int k, int32_t *idx);
 double orc_silu(double z);
@@ -97,6 +119,12 @@ void orc_moe_ffn(const orc_config *c, const orc_layer *L, const double *b,
 int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kc,
                     uint16_t *vc, int64_t layer_stride, int token, int pos,
                     double *logits_out, double *hidden_out);
+
+/* The same step over either cache format (orc_kv): with fp8, the new K and V
+ * rows are quantized (orc_quantize_row_fp8 of their fp32 values) when
+ * appended, and attention reads the dequantized rows. */
+int orc_decode_step_kv(const orc_config *c, const orc_weights *w, const orc_kv *kv, int token,
+                       int pos, double *logits_out, double *hidden_out);
 
 /* The same model recomputed from scratch over tokens[0..n): layer by layer
  * over all positions, with its own K/V storage and no cache input.

@@ -169,3 +169,48 @@ def test_prefill_then_decode_matches_full(oracle_lib):
     # the greedy continuation recomputed from scratch
     for j in range(len(prompt), len(seq) - 1):
         assert m.forward_full(np.array(seq[: j + 1], np.int32))[0] == seq[j + 1]
+
+
+def _library_fp8_rows(x):
+    """Rows [..., d] quantized per row as the fp8 cache stores them, with the
+    library's cast: fp32 scale = amax / 448, saturating e4m3 of x / scale."""
+    xf = x.float()
+    amax = xf.abs().amax(dim=-1, keepdim=True)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (xf / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.double() * sc.double()
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, synth.SMALL_DENSE], ids=lambda c: c.name)
+def test_fp8_cache_decode_matches_library_model(oracle_lib, cfg):
+    """Decoding through the fp8 cache equals the library model whose K and V
+    rows are quantized with the library's own cast (per row and head)."""
+    W, m = _model(oracle_lib, cfg, seed=5)
+    toks = synth.gen_tokens(cfg.vocab, 12, seed=6).numpy()
+    kc8, vc8, ks, vs = m.new_cache_fp8()
+    lgs, hds = [], []
+    for t, tok in enumerate(toks):
+        _, lg, hd = m.decode_step_fp8(kc8, vc8, ks, vs, int(tok), t)
+        lgs.append(lg)
+        hds.append(hd)
+    n, h, d = len(toks), cfg.hidden, cfg.head_dim
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    pos = torch.arange(n)
+    x = W["embed"][torch.as_tensor(toks, dtype=torch.long)].double()
+    for L in W["layers"]:
+        a = F.rms_norm(x, (h,), weight=L["attn_norm"].double(), eps=cfg.rms_eps)
+        q = _rope_t((a @ L["wq"].double().T).view(n, Hq, d), pos, cfg.rope_theta)
+        k = _rope_t((a @ L["wk"].double().T).view(n, Hkv, d), pos, cfg.rope_theta)
+        v = (a @ L["wv"].double().T).view(n, Hkv, d)
+        k, v = _library_fp8_rows(k), _library_fp8_rows(v)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                           is_causal=True, enable_gqa=True)
+        x = x + o.transpose(0, 1).reshape(n, Hq * d) @ L["wo"].double().T
+        b = F.rms_norm(x, (h,), weight=L["ffn_norm"].double(), eps=cfg.rms_eps)
+        x = x + (F.silu(b @ L["wg"].double().T) * (b @ L["wu"].double().T)) @ L["wd"].double().T
+    y = F.rms_norm(x, (h,), weight=W["final_norm"].double(), eps=cfg.rms_eps)
+    np.testing.assert_allclose(np.array(hds), x.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(np.array(lgs), (y @ W["lm_head"].double().T).numpy(), rtol=1e-9, atol=1e-10)
+    # and the fp8 cache changes the result by about its quantization error only
+    _, lg16, _ = m.forward_full(toks)
+    assert np.abs(np.array(lgs) - lg16).max() < 0.05 * np.abs(lg16).max()

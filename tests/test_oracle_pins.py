@@ -257,3 +257,71 @@ def test_silu_closed_forms(oracle_lib):
     assert abs(oracle_lib.silu(-40.0)) < 1e-15
     for z in (-3.0, -0.5, 0.25, 2.0):
         assert abs(oracle_lib.silu(z) - float(F.silu(torch.tensor(z, dtype=torch.float64)))) < 1e-15
+
+
+# ----------------------------------------------------------------- fp8 K/V cache
+
+def _torch_fp8_sat(x):
+    """torch's float8_e4m3fn cast (round to nearest even) after clamping to
+    the largest finite magnitude, as bit patterns."""
+    t = torch.as_tensor(np.asarray(x, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_encode_matches_library_saturating_cast(oracle_lib):
+    g = torch.Generator().manual_seed(11)
+    x = (torch.randn(6000, generator=g) * torch.exp2(torch.randint(-14, 12, (6000,), generator=g).float()))
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle_lib.fp8_to_f64(codes)
+    finite = np.sort(np.unique(vals[~np.isnan(vals)]))
+    mids = (finite[1:] + finite[:-1]) / 2  # exact halfway points: ties to the even code
+    probe = np.concatenate([x.numpy(), finite, mids, mids * (1 + 2 ** -20), mids * (1 - 2 ** -20),
+                            [447.0, 448.0, 455.0, 464.0, 479.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -10]])
+    probe = np.concatenate([probe, -probe]).astype(np.float32)
+    ours = oracle_lib.f32_to_fp8(probe)
+    assert np.array_equal(ours, _torch_fp8_sat(probe))
+
+
+def test_fp8_encode_round_trips_every_finite_code(oracle_lib):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle_lib.fp8_to_f64(codes)
+    keep = ~np.isnan(vals) & (codes != 0x80)  # (-0 encodes back as 0x80 too: checked on its own)
+    assert np.array_equal(oracle_lib.f32_to_fp8(vals[keep]), codes[keep])
+    assert oracle_lib.f32_to_fp8([-0.0])[0] == 0x80
+    assert oracle_lib.f32_to_fp8([float("nan")])[0] == 0x7F
+
+
+def test_fp8_row_quantizer(oracle_lib):
+    g = torch.Generator().manual_seed(12)
+    for n, mag in ((128, 1.0), (64, 1e-3), (128, 300.0)):
+        x = (torch.randn(n, generator=g) * mag).numpy().astype(np.float32)
+        codes, sc = oracle_lib.quantize_row_fp8(x)
+        amax = np.float32(np.abs(x).max())
+        assert sc == np.float32(amax / np.float32(448.0))  # the fp32 quotient
+        i = int(np.argmax(np.abs(x)))
+        assert codes[i] in (0x7E, 0xFE)  # the largest element lands on +-448
+        deq = oracle_lib.fp8_to_f64(codes) * sc
+        # within half a step of the 3-bit mantissa (or of the subnormal step)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10)
+        assert np.all(np.abs(deq - x) <= bound * (1 + 1e-6))
+    codes, sc = oracle_lib.quantize_row_fp8(np.zeros(16, np.float32))
+    assert sc == 1.0 and not codes.any()
+
+
+def test_fp8_attention_matches_dequantized_bf16_free_path(oracle_lib):
+    """Attention over fp8 rows equals the plain attention over the rows'
+    dequantized values (computed here with the library)."""
+    g = torch.Generator().manual_seed(13)
+    n, d = 37, 64
+    Kc = torch.randint(0, 256, (n, d), generator=g, dtype=torch.int64).numpy().astype(np.uint8)
+    Vc = torch.randint(0, 256, (n, d), generator=g, dtype=torch.int64).numpy().astype(np.uint8)
+    Kc[(Kc & 0x7F) == 0x7F] = 0  # no NaN codes
+    Vc[(Vc & 0x7F) == 0x7F] = 0
+    Ks = (torch.rand(n, generator=g) * 0.01 + 1e-3).numpy().astype(np.float32)
+    Vs = (torch.rand(n, generator=g) * 0.01 + 1e-3).numpy().astype(np.float32)
+    q = torch.randn(d, generator=g, dtype=torch.float64).numpy() * 40
+    o = oracle_lib.attend_fp8(q, Kc, Ks, Vc, Vs)
+    K = torch.from_numpy(Kc).view(torch.float8_e4m3fn).double() * torch.from_numpy(Ks).double()[:, None]
+    V = torch.from_numpy(Vc).view(torch.float8_e4m3fn).double() * torch.from_numpy(Vs).double()[:, None]
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None, None, None], K[None, None], V[None, None])
+    np.testing.assert_allclose(o, ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-14)
