@@ -38,12 +38,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-CONFIG_ORDER = ["dense8b_ctx8192", "moe", "dense8b_mb8", "tiny"]
+CONFIG_ORDER = ["dense8b_ctx8192", "dense8b_ctx8192_kv8", "moe", "dense8b_mb8", "tiny"]
 # what each path computes in (the "dtype" of its line)
 DTYPE_B1 = ("bf16 weights and K/V cache; GEMV products and sums in fp32; attention scores and P.V on the "
             "matrix cores with q and p split into bf16 hi+lo parts (about 16 significant bits), fp32 accumulate")
 DTYPE_MOE = DTYPE_B1.replace("bf16 weights", "bf16 attention/router weights, fp8 e4m3 experts with bf16 "
                              "128x128 block scales (decoded exactly to fp32)")
+DTYPE_KV8 = DTYPE_B1.replace("bf16 weights and K/V cache", "bf16 weights, fp8 e4m3 K/V cache with an fp32 scale "
+                             "per row (codes decoded exactly to bf16 for the matrix cores, scales applied to the "
+                             "scores and to p)")
 DTYPE_MB = ("bf16 weights and K/V cache; every GEMM and attention product on the matrix cores with the "
             "activations split into bf16 hi+lo parts (about 16 significant bits), fp32 accumulate")
 
@@ -70,13 +73,15 @@ def setup(workload, W=None, device="cuda", seed=0, prefill="engine", **eng_kw):
         W = synth.gen_weights(m, seed=seed, device=device)
     pos = list(w.contexts)
     ctx = torch.zeros(m.batch, dtype=torch.int32, device=device)
-    if m.batch > 1 or prefill == "synthetic":
+    ks = vs = None
+    if m.kv_fp8:  # the engine fills its own fp8 cache
+        prefill = "engine"
+        kc, vc, ks, vs = synth.empty_kv_cache(m, device=device)
+    elif m.batch > 1 or prefill == "synthetic":
         kc, vc = synth.gen_kv_cache(m, max(pos), seed=seed + 1, device=device)
     else:
-        shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
-        kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-        vc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-    eng = E.Engine(m, W, kc, vc, ctx_len=ctx, **eng_kw)
+        kc, vc, _, _ = synth.empty_kv_cache(m, device=device)
+    eng = E.Engine(m, W, kc, vc, ctx_len=ctx, k_scale=ks, v_scale=vs, **eng_kw)
     if m.batch > 1:
         g0 = synth.gen_tokens(m.vocab, m.batch, seed=seed + 2, device=device)
         how = f"synthetic caches of contexts {pos}"
@@ -91,7 +96,7 @@ def setup(workload, W=None, device="cuda", seed=0, prefill="engine", **eng_kw):
         g0 = out[-1].contiguous()
         how = f"engine prefill of {pos[0]} tokens"
     log(f"[bench] {workload}: weights + {how} in {time.time() - t0:.1f}s")
-    return w, m, W, (kc, vc, ctx), eng, g0
+    return w, m, W, (kc, vc, ctx, ks, vs), eng, g0
 
 
 def launches_per_step_per_op(m):
@@ -154,20 +159,23 @@ def cpu_baseline(m, W, pos, budget_s=12.0, single_thread_steps=0):
     from persistent_resident_execution_amd import synth
     t0 = time.time()
     om = oracle.OracleModel(m, synth.weights_to_numpy(W))
-    kc_t, vc_t = synth.gen_kv_cache(m, max(pos), seed=1, device="cpu")
-    kc_all, vc_all = synth.to_bits(kc_t), synth.to_bits(vc_t)
-    del kc_t, vc_t
-    caches = [(np.ascontiguousarray(kc_all[:, b]), np.ascontiguousarray(vc_all[:, b])) for b in range(len(pos))]
-    del kc_all, vc_all
+    if m.kv_fp8:  # (zero codes and scales: the work does not depend on the values)
+        caches = [om.new_cache_fp8() for _ in pos]
+    else:
+        kc_t, vc_t = synth.gen_kv_cache(m, max(pos), seed=1, device="cpu")
+        kc_all, vc_all = synth.to_bits(kc_t), synth.to_bits(vc_t)
+        del kc_t, vc_t
+        caches = [(np.ascontiguousarray(kc_all[:, b]), np.ascontiguousarray(vc_all[:, b])) for b in range(len(pos))]
+        del kc_all, vc_all
     threads = oracle.num_threads()
     log(f"[bench] oracle set-up {time.time() - t0:.1f}s ({threads} threads)")
 
     def run(max_steps, budget):
         toks, steps, ts = [1] * len(pos), 0, time.time()
         while steps < max_steps:
-            for b, (kc, vc) in enumerate(caches):
-                toks[b], _, _ = om.decode_step(kc, vc, int(toks[b]), pos[b] + steps, want_logits=False,
-                                               want_hidden=False)
+            for b, c in enumerate(caches):
+                step = om.decode_step_fp8 if m.kv_fp8 else om.decode_step
+                toks[b], _, _ = step(*c, int(toks[b]), pos[b] + steps, want_logits=False, want_hidden=False)
             steps += 1
             if time.time() - ts >= budget:
                 break
@@ -227,7 +235,7 @@ def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps
                     "note": f"one launch of {K} greedy steps from the prefilled position(s)"},
          "tokens_per_s": round(K * m.batch / t_med, 1),
          "repeats_us_per_step": [round(t / K * 1e6, 2) for t in tp],
-         "dtype": DTYPE_MB if mb else (DTYPE_MOE if m.is_moe else DTYPE_B1),
+         "dtype": DTYPE_MB if mb else (DTYPE_MOE if m.is_moe else (DTYPE_KV8 if m.kv_fp8 else DTYPE_B1)),
          "roofline": roofline(m, pos, K, t_med, kern, workload)}
     if baseline:
         log(f"[bench] {workload}: the one-kernel-per-operator path")

@@ -104,7 +104,16 @@ extern "C" {
  * task set, the micro-batch tiles run over `chunk` consecutive tokens of the
  * engine's one sequence, used by pre_engine_prefill and pre_engine_verify
  * (hidden, ffn_dim and n_q_heads * head_dim multiples of 32; MoE returns
- * PRE_ERR_UNSUPPORTED). */
+ * PRE_ERR_UNSUPPORTED).
+ * kv_dtype: 0 = bf16 K/V cache; 1 = fp8 e4m3 K/V codes with one fp32 scale
+ * per cached row (layer, sequence, KV head, position): scale = amax(|row|) /
+ * 448 in fp32 (1 for an all-zero row), codes = e4m3 of row / scale (ties to
+ * even, saturating at 448); attention reads code x scale.  Batch-1 engines
+ * (the decode kernel, its per-operator path and the serving loop); a
+ * micro-batch or chunk task set returns PRE_ERR_UNSUPPORTED.  The pages
+ * name quantized KV inside a persistent kernel as open work ("Persistent
+ * execution paradigm" section 7.5; XL-Persistent-Kernel, future work) but
+ * fix no format: this is the reading taken. */
 typedef struct pre_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t batch, max_ctx;
@@ -113,6 +122,7 @@ typedef struct pre_config {
   int32_t grid_wgs, wg_threads, attn_splits;
   int32_t xcd_local;
   int32_t chunk;
+  int32_t kv_dtype;
 } pre_config;
 
 /* Per-layer weights (device pointers).  Dense: wg, wu [ffn][hidden], wd
@@ -147,10 +157,14 @@ typedef struct pre_weights {
  * (the pages' split of prefill and decode: a decode engine takes over a
  * cache that another engine filled -- SemiAnalysis TileRT digest, "PD
  * separation").  With NULL the engine keeps its own device array in the
- * workspace, starting at 0. */
+ * workspace, starting at 0.
+ * With kv_dtype 1, k and v hold one e4m3 code per element (uint8, same
+ * shape) and k_scale, v_scale (device, fp32 [n_layers][batch][n_kv_heads]
+ * [max_ctx], caller-owned) the rows' scales; NULL otherwise. */
 typedef struct pre_kv {
   void *k, *v;
   int32_t *d_ctx_len;
+  float *k_scale, *v_scale;
 } pre_kv;
 
 /* Optional per-call outputs for checking (device, may be NULL):

@@ -196,6 +196,41 @@ __device__ __forceinline__ void fp8x4(uint32_t w, float (&o)[4]) {
   o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
 }
 
+// fp32 -> OCP e4m3 code, round to nearest (ties to even), magnitudes at or
+// above 448 saturate to +-448.  Below 2^-6 the codes are multiples of 2^-9
+// (x * 512 rounded to an integer; 8 is the smallest normal); above, the
+// mantissa is x scaled into [8, 16) and rounded, carrying into the exponent
+// at 16.  Finite inputs only.
+__device__ __forceinline__ uint32_t f2e4m3(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(x);
+  if (a >= 448.0f) return s | 0x7Eu;
+  if (a < 0.015625f) return s | (uint32_t)__builtin_rintf(a * 512.0f);
+  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xffu) - 127;  // a in [2^E, 2^(E+1))
+  float m = __builtin_rintf(a * __builtin_bit_cast(float, (uint32_t)(127 + 3 - E) << 23));
+  if (m == 16.0f) { m = 8.0f; E += 1; }
+  if (E > 8 || (E == 8 && m > 14.0f)) return s | 0x7Eu;
+  return s | ((uint32_t)(E + 7) << 3) | ((uint32_t)m - 8u);
+}
+
+// Eight e4m3 codes (byte e = element e) as eight bf16 (exact: every e4m3
+// value is a bf16 value) in the layout of one 16-byte bf16 load.  (The
+// converted pairs are copied into scalars before their bit casts: a bit cast
+// of a vector element reads element 0 with this compiler.)
+__device__ __forceinline__ v4i fp8x8_bf16(v2i w) {
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int wi = w[i];
+    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(wi, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wi, true);
+    const float a = lo.x, b = lo.y, c = hi.x, d = hi.y;
+    r[2 * i] = (int)((__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xffff0000u));
+    r[2 * i + 1] = (int)((__builtin_bit_cast(uint32_t, c) >> 16) | (__builtin_bit_cast(uint32_t, d) & 0xffff0000u));
+  }
+  return r;
+}
+
 // Sixteen fp8 weights (one 16-byte load) dotted with sixteen activations.
 __device__ __forceinline__ float dot16_fp8(v4i w, const float *x) {
   float acc = 0.f, f[4];

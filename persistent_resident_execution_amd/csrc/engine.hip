@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/pre.h"
@@ -71,6 +72,9 @@ struct KP {
   int32_t chunk_n;       // chunk mode: tokens of the call (the last step may be ragged)
   int32_t verify;        // chunk mode, one step: accept the drafts, commit the accepted tokens
   int32_t *v_accept;     // verify: the number of accepted drafts
+  int32_t kv8;           // fp8 e4m3 cache: kc / vc hold codes, ksc / vsc one fp32 scale per row
+  float *ksc, *vsc;      // [L][B][Hkv][max_ctx]
+  float *kvnew;          // the step's new K and V rows in fp32 [L][B][2][Hkv][d]
   uint8_t *pk;           // packed GEMM inputs
   float *ssq;            // per-workgroup sums of squares of the normalised inputs
   // serving loop: the request ring (coherent host memory) and the
@@ -1046,6 +1050,10 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
           float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
           st_out(P, qd + j, a);
           st_out(P, qd + j + half, b);
+        } else if (P.kv8) {  // fp8 cache: the new row in fp32, quantized by the attention task owning it
+          float *kn = P.kvnew + ((((int64_t)l * P.B) * 2 + (hh == P.G ? 0 : 1)) * P.Hkv + g) * P.d;
+          st_out(P, kn + j, a);
+          st_out(P, kn + j + half, b);
         } else {  // the layer's K or V cache of every KV head under one descriptor each
           const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
           const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
@@ -1188,61 +1196,76 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(v4i a, v4i b, f32x4_t c) {
 // would otherwise arrive only after the scores.  Ends after a barrier; false
 // if the wait was aborted.  Phase marks 0-2 after the scores, the softmax
 // and the weighted sums.
-template <int NQ, int NS, bool VPRE, class WaitT>
+template <int NQ, int NS, bool VPRE, bool F8, class WaitT>
 __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int t0, int cnt, int pos, float *sc,
-                                          int cpad, float *ored, float *st, const WaitT *wait) {
+                                          int cpad, float *ored, float *st, float *ksl, float *vsl,
+                                          uint8_t *nrow, const WaitT *wait) {
   constexpr int D = 32 * NQ;  // head dimension
   constexpr int PL = 16 / NQ;  // positions per K load
   constexpr int RA = 8;  // K loads in flight per wavefront
+  constexpr int EB = F8 ? 1 : 2;  // bytes per cached element
   constexpr uint32_t OOB = 0x80000000u;
+  // a load of one lane: 8 elements (16 bytes of bf16, 8 bytes of fp8 codes)
+  using KV8 = typename std::conditional<F8, v2i, v4i>::type;
+  auto ld8e = [](Rsrc r, uint32_t off) -> KV8 {
+    if constexpr (F8) return ld64<CP_SC1>(r, off);
+    else return ld128<CP_SC1>(r, off);
+  };
+  auto as_bf16 = [](const KV8 &w) -> v4i {
+    if constexpr (F8) return fp8x8_bf16(w);
+    else return w;
+  };
   const int G = P.G;
   const int wave = wave_id(), nw = P.nw, lane = threadIdx.x & 63, ii = lane & 15, qg = lane >> 4;
   const int64_t cbase = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx * D;
-  const Rsrc kr = mkbuf(P.kc + cbase, (uint32_t)P.max_ctx * D * 2);
-  const Rsrc vr = mkbuf(P.vc + cbase, (uint32_t)P.max_ctx * D * 2);
-  // K load u: positions u * PL ..; this lane's row and 16 bytes.  Before the
-  // wait the row this step's QKV stage writes is left out (reloaded after).
+  const Rsrc kr = mkbuf(reinterpret_cast<const uint8_t *>(P.kc) + cbase * EB, (uint32_t)P.max_ctx * D * EB);
+  const Rsrc vr = mkbuf(reinterpret_cast<const uint8_t *>(P.vc) + cbase * EB, (uint32_t)P.max_ctx * D * EB);
+  // K load u: positions u * PL ..; this lane's row and 8 elements.  Before
+  // the wait the row this step's QKV stage writes is left out (reloaded after).
+  // (With the fp8 cache the newest row is never read back from memory: the
+  // task owning it quantizes it into LDS, nrow, and patches its operands.)
   auto koff = [&](int u, bool pre) -> uint32_t {
     const int tt = u * PL + ii / NQ;
-    const bool in = tt < cnt && !(pre && t0 + tt == pos);
-    return in ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + (uint32_t)((ii % NQ) * 64 + qg * 16) : OOB;
+    const bool in = tt < cnt && !((pre || F8) && t0 + tt == pos);
+    return in ? ((uint32_t)(t0 + tt) * (uint32_t)D + (uint32_t)((ii % NQ) * 32 + qg * 8)) * EB : OOB;
   };
   const int nL = (cnt + PL - 1) / PL;
   const int nk = nL > wave ? (nL - wave + nw - 1) / nw : 0;  // this wavefront's loads u = wave + nw * k
   // V chunk c (positions c * 32 ..): load r of this lane = position
   // c * 32 + 8 qg + r, dimensions 8 (ii % (D / 8)) ..
-  const uint32_t vcol = (uint32_t)(ii % (D / 8)) * 16u;
-  auto vload = [&](v4i (&x)[8], int c, bool pre) {
+  const uint32_t vcol = (uint32_t)(ii % (D / 8)) * 8u * EB;
+  auto vload = [&](KV8 (&x)[8], int c, bool pre) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int tt = c * 32 + 8 * qg + r;
-      const bool in = tt < cnt && !(pre && t0 + tt == pos);
-      x[r] = ld128<CP_SC1>(vr, in ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + vcol : OOB);
+      const bool in = tt < cnt && !((pre || F8) && t0 + tt == pos);
+      x[r] = ld8e(vr, in ? (uint32_t)(t0 + tt) * (uint32_t)(D * EB) + vcol : OOB);
     }
   };
   const int nC = (cnt + 31) >> 5;
   const int nkc = nC > wave ? (nC - wave + nw - 1) / nw : 0;  // this wavefront's chunks c = wave + nw * k
-  v4i ka[RA], va[8], vn[8];
+  KV8 ka[RA], va[8], vn[8];
 #pragma unroll
-  for (int s = 0; s < RA; ++s) ka[s] = ld128<CP_SC1>(kr, koff(wave + nw * s, true));
+  for (int s = 0; s < RA; ++s) ka[s] = ld8e(kr, koff(wave + nw * s, true));
   if (VPRE) vload(va, wave, true);
+  const int64_t srow = (((int64_t)l * P.B + b) * P.Hkv + g) * P.max_ctx;  // scale of row t: [srow + t]
+  if (F8) {
+    // the earlier rows' scales into LDS (0 past the piece, where p is 0 too)
+    for (int i = threadIdx.x; i < nC * 32; i += P.nthr) {
+      const bool in = i < cnt && t0 + i != pos;
+      ksl[i] = in ? ld_sc1(P.ksc + srow + t0 + i) : 0.f;
+      vsl[i] = in ? ld_sc1(P.vsc + srow + t0 + i) : 0.f;
+    }
+  }
   if (wait && !(*wait)(P)) return false;
-  if (t0 <= pos && pos < t0 + cnt) {  // the newest row, now written
-    const int up = (pos - t0) / PL;
-    if (up % nw == wave && up / nw < RA) {
-#pragma unroll
-      for (int s = 0; s < RA; ++s)
-        if (s == up / nw) ka[s] = ld128<CP_SC1>(kr, koff(up, false));
-    }
-    const int tp = pos - t0 - 32 * wave;  // in this wavefront's first V chunk: load (tp % 8) of every lane
-    if (VPRE && tp >= 0 && tp < 32) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r == (tp & 7)) {
-          const int tt = 32 * wave + 8 * qg + r;
-          va[r] = ld128<CP_SC1>(vr, tt < cnt ? (uint32_t)(t0 + tt) * (uint32_t)(D * 2) + vcol : OOB);
-        }
-    }
+  const bool own = t0 <= pos && pos < t0 + cnt;  // this piece holds the step's newest row
+  // fp8 cache: the newest row's fp32 K and V values, loaded together with q
+  // (one round trip for both)
+  float kx = 0.f, vx = 0.f;
+  if (F8 && own && threadIdx.x < D) {
+    const float *kn = P.kvnew + (((int64_t)l * P.B + b) * 2 * P.Hkv + g) * D;
+    kx = ld_sc1(kn + threadIdx.x);
+    vx = ld_sc1(kn + (int64_t)P.Hkv * D + threadIdx.x);
   }
   // q as the score columns: set s, column j = (head s * 16 / NQ + j / NQ, quarter j % NQ)
   v4i qh[NS], ql[NS];
@@ -1266,8 +1289,66 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
       }
     }
   }
-  // scores of K load u (positions u * PL ..) into sc
-  auto scores = [&](const v4i &a, int u) {
+  if (F8 && own) {
+    // Quantize the step's row from the fp32 values the QKV stage left
+    // (scale = amax / 448, e4m3 codes of x / scale) into LDS for this task's
+    // own products, and append it to the cache for the later steps (the
+    // stores complete before this task's flag).
+    const int tid = threadIdx.x;
+    if (tid < D) {
+      const float km = wave_max(__builtin_fabsf(kx)), vm = wave_max(__builtin_fabsf(vx));
+      if ((tid & 63) == 0) { st[2 * wave] = km; st[2 * wave + 1] = vm; }
+    }
+    __syncthreads();
+    float km = st[0], vm = st[1];
+    if (D > 64) { km = fmaxf(km, st[2]); vm = fmaxf(vm, st[3]); }
+    const float ks = km > 0.f ? km / 448.0f : 1.0f, vs = vm > 0.f ? vm / 448.0f : 1.0f;
+    if (tid < D) {
+      const uint32_t ck = f2e4m3(kx / ks), cv = f2e4m3(vx / vs), o = (uint32_t)(pos * D + tid);
+      nrow[tid] = (uint8_t)ck;
+      nrow[D + tid] = (uint8_t)cv;
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ck, kr, o, 0, CP_SC1);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)cv, vr, o, 0, CP_SC1);
+    }
+    if (tid == 0) {
+      st_sc1(P.ksc + srow + pos, ks);
+      st_sc1(P.vsc + srow + pos, vs);
+      ksl[pos - t0] = ks;
+      vsl[pos - t0] = vs;
+    }
+    __syncthreads();
+  } else if (F8) {
+    __syncthreads();  // the scales staged above
+  }
+  if (!F8 && own) {  // the newest row, now written
+    const int up = (pos - t0) / PL;
+    if (up % nw == wave && up / nw < RA) {
+#pragma unroll
+      for (int s = 0; s < RA; ++s)
+        if (s == up / nw) ka[s] = ld8e(kr, koff(up, false));
+    }
+    const int tp = pos - t0 - 32 * wave;  // in this wavefront's first V chunk: load (tp % 8) of every lane
+    if (VPRE && tp >= 0 && tp < 32) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r == (tp & 7)) {
+          const int tt = 32 * wave + 8 * qg + r;
+          va[r] = ld8e(vr, tt < cnt ? (uint32_t)(t0 + tt) * (uint32_t)(D * EB) + vcol : OOB);
+        }
+    }
+  }
+  // fp8: the newest row's lanes take their 8 codes from nrow
+  const int tnew = F8 && own ? pos - t0 : -1;
+  auto knew = [&](KV8 &a, int u) {
+    if constexpr (F8) {
+      if (u * PL + ii / NQ == tnew) a = *reinterpret_cast<const v2i *>(nrow + (ii % NQ) * 32 + qg * 8);
+    }
+  };
+  // scores of K load u (positions u * PL ..) into sc (fp8: of the codes; the
+  // rows' scales are applied in the softmax pass)
+  auto scores = [&](KV8 araw, int u) {
+    knew(araw, u);
+    const v4i a = as_bf16(araw);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       f32x4_t c = mfma_16x16x32(a, qh[s], f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -1296,20 +1377,30 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
 #pragma unroll
     for (int s = 0; s < RA; ++s) {
       if (k0 + s < nk) scores(ka[s], wave + nw * (k0 + s));
-      ka[s] = ld128<CP_SC1>(kr, koff(wave + nw * (k0 + s + RA), false));
+      ka[s] = ld8e(kr, koff(wave + nw * (k0 + s + RA), false));
     }
   }
   if (!VPRE) vload(va, wave, false);  // the first V chunk, during the softmax
   __syncthreads();
   if (wait) wait->mark(0);
+  // softmax per head; with the fp8 cache each score takes its K row's scale
+  // here, and the stored p its V row's (the sum stays unscaled), so the
+  // products below run on the codes as they are
   for (int hh = wave; hh < G; hh += nw) {
     float m = -INFINITY;
-    for (int i = lane; i < cnt; i += 64) m = fmaxf(m, sc[hh * cpad + i]);
+    for (int i = lane; i < cnt; i += 64) {
+      float v = sc[hh * cpad + i];
+      if (F8) {
+        v *= ksl[i];
+        sc[hh * cpad + i] = v;
+      }
+      m = fmaxf(m, v);
+    }
     m = wave_max(m);
     float sm = 0.f;
     for (int i = lane; i < cnt; i += 64) {
       const float e = expf(sc[hh * cpad + i] - m);
-      sc[hh * cpad + i] = e;
+      sc[hh * cpad + i] = F8 ? e * vsl[i] : e;
       sm += e;
     }
     for (int i = cnt + lane; i < nC * 32; i += 64) sc[hh * cpad + i] = 0.f;  // whole chunks
@@ -1321,8 +1412,9 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
   f32x4_t acc[D / 16];
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto pv = [&](const v4i (&x)[8], int c) {
+  auto pv = [&](const KV8 (&xr)[8], int c) {
     // A: row ii = (head ii / 2, part ii % 2) of p, positions c * 32 + 8 qg ..
+    // (with the fp8 cache, p already carries each row's V scale)
     const int hh = ii >> 1;
     float p[8];
     if (hh < G) {
@@ -1332,6 +1424,15 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = 0.f;
+    }
+    v4i x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      KV8 w = xr[r];
+      if constexpr (F8) {
+        if (c * 32 + 8 * qg + r == tnew) w = *reinterpret_cast<const v2i *>(nrow + D + vcol);
+      }
+      x[r] = as_bf16(w);
     }
     v4i pa;
 #pragma unroll
@@ -1383,6 +1484,7 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
 // One attention chunk task: chunk c of NC of (sequence b, KV head g)'s
 // positions, all G query heads, on the matrix cores; the record (m, l, -, -,
 // o[d]) per head goes to the O-projection task's combine.
+template <bool KV8>
 __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
                                            const Waiter &wait) {
   const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, c = t.r0, NC = t.r1;
@@ -1391,9 +1493,21 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
   const int cnt = max(0, min(n, t0 + C) - t0);
   const int cpad = ((P.cmax + 63) / 64) * 64;
   float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
-  const bool ok = d == 64    ? attn_core<2, 1, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait)
-                  : G <= 4 ? attn_core<4, 1, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait)
-                           : attn_core<4, 2, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, &wait);
+  // fp8 cache: the piece's row scales, and the newest row's codes (K then V)
+  float *ksl = st + 4 * G, *vsl = ksl + cpad;
+  uint8_t *nrow = reinterpret_cast<uint8_t *>(vsl + cpad);
+  bool ok;
+  if (KV8)
+    ok = d == 64 ? attn_core<2, 1, true, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait)
+         : G <= 4
+             ? attn_core<4, 1, true, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait)
+             : attn_core<4, 2, true, true>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait);
+  else
+    ok = d == 64
+             ? attn_core<2, 1, true, false>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait)
+         : G <= 4
+             ? attn_core<4, 1, true, false>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait)
+             : attn_core<4, 2, true, false>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait);
   if (!ok) return false;
   const int rec = d + PREC_O;
   float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * rec;
@@ -1457,12 +1571,17 @@ __device__ __forceinline__ const KP &kp_fresh() {
 }
 
 // Run one task of the table (both paths).
+// KV8: the attention tile of the fp8 cache; it is compiled into kernels of
+// its own (pre_persistent_kv8, pre_serve_kv8) so that the bf16 kernels keep
+// their register allocation (one kernel takes the budget of its heaviest
+// task).
+template <bool KV8>
 __device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int pos, int tok, float *lds,
                                          const Waiter &wait) {
   const KP &P = kp_fresh();
   switch (t.op) {
     case OP_NONE: return true;
-    case OP_ATTN: return attn_chunk(P, t, pos, lds, wait);
+    case OP_ATTN: return attn_chunk<KV8>(P, t, pos, lds, wait);
     case OP_EGU:
     case OP_EDOWN: return task_gemv<true>(P, t, lam, step, pos, tok, lds, wait);
     default: return task_gemv<false>(P, t, lam, step, pos, tok, lds, wait);
@@ -1477,7 +1596,8 @@ __device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int p
 // P.b_si for step P.b_step once, without waits or flags (stream order is the
 // only synchronisation).  Both modes go through the one call of run_task, so
 // the task code exists once in the binary.
-extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
+template <bool KV8>
+__device__ __forceinline__ void resident_body(KP &P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
   const bool res = P.persistent != 0;
@@ -1519,7 +1639,7 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
       const int tr = res && P.trace != nullptr;
       const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
       const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
-      if (!run_task(t, lam, s, pos, tok, lds, wait)) return;
+      if (!run_task<KV8>(t, lam, s, pos, tok, lds, wait)) return;
       if (res) {
         signal_slot(P, t.signal, ep, P.onexcd || (P.local && (t.op == OP_QKV || t.op == OP_ATTN)));
         if (tr) trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
@@ -1545,6 +1665,9 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) {
   // workgroup has read the start position: advance it.
   if (lam == 0 && threadIdx.x == 0) st_flag(reinterpret_cast<uint32_t *>(P.ctx_len), (uint32_t)(pos0 + P.n_steps));
 }
+
+extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) { resident_body<false>(P); }
+extern "C" __global__ void __launch_bounds__(512) pre_persistent_kv8(KP P) { resident_body<true>(P); }
 
 // the micro-batch task set and kernel
 #include "mb.h"
@@ -1609,6 +1732,12 @@ extern "C" __global__ void pre_k_lane_ops(const float *in, float *out) {
   if (lane == 0) { out[128] = ws; out[129] = wm; }
   out[192 + lane] = v + dpp<0x128>(v);
   out[256 + lane] = xrow_sum(v);
+}
+
+// Debug: encode n fp32 values with the fp8 cache's encoder (checks the format).
+extern "C" __global__ void pre_k_fp8_encode(const float *in, uint8_t *out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)f2e4m3(in[i]);
 }
 
 // Debug: decode n fp8 codes with the GEMV's unpacking (checks the format).
@@ -1819,6 +1948,8 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   int rc = derive_dims(cfg, cus, &D);
   if (rc != PRE_OK) return rc;
   if (!w->embed || !w->final_norm || !w->lm_head || !kv->k || !kv->v) return PRE_ERR_ARG;
+  if (D.kv8 && (!kv->k_scale || !kv->v_scale)) return PRE_ERR_ARG;
+  if (((uintptr_t)kv->k_scale & 3) || ((uintptr_t)kv->v_scale & 3)) return PRE_ERR_ALIGN;
   if (!al16(w->embed) || !al16(w->final_norm) || !al16(w->lm_head) || !al16(kv->k) || !al16(kv->v) ||
       !al16(d_workspace) || ((uintptr_t)kv->d_ctx_len & 3))
     return PRE_ERR_ALIGN;
@@ -1847,9 +1978,11 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   const int want = std::min(ldsm, 96 * 1024);
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
-  const void *kern = D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
-  if ((!D.mb && hipFuncSetAttribute((const void *)pre_serve, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
-                    hipSuccess) ||
+  const void *kern = D.mb    ? (const void *)pre_persistent_mb
+                     : D.kv8 ? (const void *)pre_persistent_kv8
+                             : (const void *)pre_persistent;
+  const void *serve_kern = D.kv8 ? (const void *)pre_serve_kv8 : (const void *)pre_serve;
+  if ((!D.mb && hipFuncSetAttribute(serve_kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess) ||
       hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
@@ -2011,6 +2144,10 @@ static void fill_kp_dims(const pre_engine *e, const Dims &D, const Layout &Lo, c
   P.drop_slot = e->drop_slot;
   P.mbst = D.mbst;
   P.Bc = D.B;
+  P.kv8 = D.kv8;
+  P.ksc = e->kv.k_scale;
+  P.vsc = e->kv.v_scale;
+  P.kvnew = D.kv8 ? (float *)(ws + Lo.kvnew) : nullptr;
   P.tok_slot = (int32_t *)(ws + Lo.tok);
   P.watchdog_ticks = (uint32_t)std::min<uint64_t>((uint64_t)e->watchdog_ms * 100000ull, 0xffffffffull);
   P.persistent = persistent;
@@ -2046,7 +2183,9 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   P.trace = e->trace;
   P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 32, 0xffffffffu);
   void *args[] = {&P};
-  const void *kern = e->D.mb ? (const void *)pre_persistent_mb : (const void *)pre_persistent;
+  const void *kern = e->D.mb    ? (const void *)pre_persistent_mb
+                     : e->D.kv8 ? (const void *)pre_persistent_kv8
+                                : (const void *)pre_persistent;
   const unsigned nblk = (unsigned)(e->D.W * (e->D.onexcd ? e->D.X : 1));  // one-XCD: 8 blocks per workgroup
   hipError_t err = hipLaunchCooperativeKernel(kern, dim3(nblk), dim3(e->D.threads), args, (unsigned)e->lds_dyn,
                                               (hipStream_t)stream);
@@ -2123,6 +2262,7 @@ extern "C" int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t
     P.b_si = si;
     P.b_step = s;
     if (D.mb) hipLaunchKernelGGL(pre_persistent_mb, dim3(D.W), blk, lds, st, P);
+    else if (D.kv8) hipLaunchKernelGGL(pre_persistent_kv8, dim3(D.W), blk, lds, st, P);
     else hipLaunchKernelGGL(pre_persistent, dim3(D.W), blk, lds, st, P);
   };
   for (int s = 0; s < n_steps && D.mb; ++s) {  // micro-batch: every stage is a task kernel
@@ -2261,7 +2401,8 @@ extern "C" int pre_serve_start(pre_engine *e, int32_t n_slots, int32_t max_promp
   void *args[] = {&P};
   const unsigned nblk = (unsigned)(e->D.W * (e->D.onexcd ? e->D.X : 1));
   if (hipMemsetAsync(P.cmd, 0, 64, st) != hipSuccess ||
-      hipLaunchCooperativeKernel((const void *)pre_serve, dim3(nblk), dim3(e->D.threads), args,
+      hipLaunchCooperativeKernel(e->D.kv8 ? (const void *)pre_serve_kv8 : (const void *)pre_serve, dim3(nblk),
+                                 dim3(e->D.threads), args,
                                  (unsigned)e->lds_dyn, st) != hipSuccess) {
     (void)hipHostFree(h);
     return PRE_ERR_HIP;
@@ -2371,6 +2512,14 @@ extern "C" int pre_debug_fp8_decode(const void *d_codes, float *d_out, int n, vo
   return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
 }
 
+// Debug entry: encode n fp32 values with the fp8 cache's encoder.
+extern "C" int pre_debug_fp8_encode(const float *d_in, void *d_out, int n, void *stream) {
+  if (!d_in || !d_out || n <= 0) return PRE_ERR_ARG;
+  const int th = 256, nb = (n + th - 1) / th;
+  hipLaunchKernelGGL(pre_k_fp8_encode, dim3(nb), dim3(th), 0, (hipStream_t)stream, d_in, (uint8_t *)d_out, n);
+  return hipGetLastError() == hipSuccess ? PRE_OK : PRE_ERR_HIP;
+}
+
 // Debug / tuning entry: time the streamed GEMV variants.  variant = 2 * i + c
 // with ring depth {2, 4, 8, 12}[i] row pairs and weight cache policy {default,
 // streaming}[c]; rows are split over `grid` workgroups of `threads` threads,
@@ -2418,13 +2567,13 @@ extern "C" int pre_debug_mfma(const void *d_a, const void *d_b, float *d_d, void
 
 // Debug: byte offsets of the workspace regions (status, flags, layers, tasks,
 // rope, xcc, x_out, pbuf, q, u, rl, part, lmp, x_emb, a_norm, tok, xmid, pk,
-// ssq, ctx, total) -- 21 int64 values.
+// ssq, ctx, kvnew, total) -- 22 int64 values.
 extern "C" int pre_debug_layout(const pre_engine *e, int64_t *out) {
   if (!e || !out) return PRE_ERR_ARG;
   const Layout &L = e->Lo;
-  const int64_t v[21] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u, L.rl,
-                         L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.xmid, L.pk, L.ssq, L.ctx, L.total};
-  for (int i = 0; i < 21; ++i) out[i] = v[i];
+  const int64_t v[22] = {L.status, L.flags, L.layers, L.tasks, L.rope, L.xcc, L.x_out, L.pbuf, L.q, L.u, L.rl,
+                         L.part, L.lmp, L.x_emb, L.a_norm, L.tok, L.xmid, L.pk, L.ssq, L.ctx, L.kvnew, L.total};
+  for (int i = 0; i < 22; ++i) out[i] = v[i];
   return PRE_OK;
 }
 

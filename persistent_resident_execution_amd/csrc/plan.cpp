@@ -34,6 +34,9 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if ((int64_t)c->batch * c->n_kv_heads * c->max_ctx * c->head_dim * 2 >= (1ll << 32)) return PRE_ERR_SHAPE;
   const bool moe = c->n_experts > 0;
   const bool mb = c->batch > 1;
+  if (c->kv_dtype != 0 && c->kv_dtype != 1) return PRE_ERR_SHAPE;
+  // the fp8 cache is built for the batch-1 attention tile
+  if (c->kv_dtype == 1 && mb) return PRE_ERR_UNSUPPORTED;
   // micro-batch: dense models whose GEMM inputs come in whole 32-column
   // blocks of the packed MFMA layout
   if (mb && (moe || c->hidden % 32 || c->ffn_dim % 32 || (c->n_q_heads * c->head_dim) % 32))
@@ -46,6 +49,7 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   } else {
     if (c->ffn_dim < 8 || c->ffn_dim % 8) return PRE_ERR_SHAPE;
   }
+  D->kv8 = c->kv_dtype == 1;
   D->L = c->n_layers; D->h = c->hidden; D->Hq = c->n_q_heads; D->Hkv = c->n_kv_heads;
   D->d = c->head_dim; D->ffn = c->ffn_dim; D->V = c->vocab; D->B = c->batch;
   D->max_ctx = c->max_ctx;
@@ -133,6 +137,8 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   int64_t gemv = (int64_t)D->segoff + 80 * 12;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
+  // the chunk's K and V row scales, the newest row's K and V codes
+  if (D->kv8) attn += 2 * (int64_t)pad_to(D->cmax, 64) + D->d / 2;
   if (mb) {
     // MFMA stages: per-wavefront partials (8 sequences x 16 rows), the
     // sequences' norm scales and sums, per-thread partials, and the packed
@@ -176,6 +182,7 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->ctx = take((int64_t)D.B * 4);
   Lo->cmd = take(64);
   Lo->req = take((int64_t)D.max_ctx * 4);
+  Lo->kvnew = D.kv8 ? take((int64_t)D.L * D.B * 2 * D.Hkv * D.d * f) : 0;
   if (D.mb) {
     // packed bf16 hi/lo GEMM inputs: 4 KB per 128 columns (whole steps, the
     // tail left zero); per layer the QKV input (plus the LM head's), the
@@ -604,7 +611,8 @@ int64_t step_bytes(const pre_config *c, const int32_t *pos) {
   int64_t total = w * L + (int64_t)c->vocab * h * 2 + h * 2;     // LM head + final norm
   for (int b = 0; b < c->batch; ++b) {
     total += h * 2;                                              // embedding row
-    const int64_t kv_row = (int64_t)c->n_kv_heads * d * 2;       // one position, K or V
+    // one position, K or V: bf16 rows, or fp8 codes plus an fp32 scale per head
+    const int64_t kv_row = c->kv_dtype == 1 ? (int64_t)c->n_kv_heads * (d + 4) : (int64_t)c->n_kv_heads * d * 2;
     total += L * 2 * kv_row * ((int64_t)pos[b] + 1);             // attend 0..pos
     total += L * 2 * kv_row;                                     // append at pos
   }

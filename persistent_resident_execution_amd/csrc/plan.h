@@ -70,6 +70,7 @@ struct Layout {
   int64_t pk, ssq;  // micro-batch: packed GEMM inputs, per-workgroup sums of squares
   int64_t ctx;      // the engine's own position array [B] (used when the caller passes none)
   int64_t cmd, req;  // serving loop: the scheduler's command words, the claimed prompt [max_ctx]
+  int64_t kvnew;     // fp8 cache: the step's new K and V rows in fp32 [L][B][2][Hkv][d]
   int64_t total;
 };
 
@@ -92,6 +93,7 @@ struct Dims {
   int32_t mbst;       // micro-batch: longest GEMM input staged in LDS (0: none)
   int32_t cmax;       // longest attention chunk (positions; micro-batch: longest piece of one workgroup)
   int32_t lds_bytes;  // dynamic LDS per workgroup
+  int32_t kv8;        // fp8 e4m3 K/V cache with an fp32 scale per cached row
   float eps, theta;
 };
 

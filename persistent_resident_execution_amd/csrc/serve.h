@@ -161,7 +161,8 @@ __device__ __forceinline__ bool serve_wait_cmd(const KP &P, uint32_t seq, int *s
   return r;
 }
 
-extern "C" __global__ void __launch_bounds__(512) pre_serve(KP P) {
+template <bool KV8>
+__device__ __forceinline__ void serve_body(KP &P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
   if (P.onexcd && blockIdx.x % P.X != 0) return;
@@ -203,7 +204,7 @@ extern "C" __global__ void __launch_bounds__(512) pre_serve(KP P) {
         const Task t = Q.tasks[(int64_t)si * Q.W + lam];
         if (t.op == OP_NONE) continue;
         const Waiter wait{1, t.wait_lo, t.wait_hi, s, si, ep, sh, 0};
-        if (!run_task(t, lam, s, pos, tok, lds, wait)) { alive = false; break; }
+        if (!run_task<KV8>(t, lam, s, pos, tok, lds, wait)) { alive = false; break; }
         const KP &R = kp_fresh();
         signal_slot(R, t.signal, ep, R.onexcd || (R.local && (t.op == OP_QKV || t.op == OP_ATTN)));
       }
@@ -255,3 +256,6 @@ extern "C" __global__ void __launch_bounds__(512) pre_serve(KP P) {
     st_sys(R.ring + 1, 2u);
   }
 }
+
+extern "C" __global__ void __launch_bounds__(512) pre_serve(KP P) { serve_body<false>(P); }
+extern "C" __global__ void __launch_bounds__(512) pre_serve_kv8(KP P) { serve_body<true>(P); }

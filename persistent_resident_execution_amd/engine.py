@@ -36,7 +36,7 @@ class Config(C.Structure):
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "batch", "max_ctx")] + [("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [
         (n, C.c_int32) for n in ("n_experts", "top_k", "n_shared", "expert_ffn", "expert_dtype",
-                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local", "chunk")]
+                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local", "chunk", "kv_dtype")]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "router",
@@ -54,7 +54,8 @@ class Weights(C.Structure):
 
 
 class KV(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("d_ctx_len", C.c_void_p)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("d_ctx_len", C.c_void_p), ("k_scale", C.c_void_p),
+                ("v_scale", C.c_void_p)]
 
 
 class Check(C.Structure):
@@ -124,7 +125,7 @@ def lib():
                  "pre_debug_lane_ops": [vp, vp, vp],
                  "pre_debug_gemv": [C.c_int, vp, C.c_int, C.c_int, vp, vp, C.c_int, C.c_int, C.c_int, vp],
                  "pre_debug_copy": [vp, vp, C.c_size_t, vp], "pre_debug_mfma": [vp, vp, vp, vp],
-                 "pre_debug_drop_signal": [vp, i32]}
+                 "pre_debug_drop_signal": [vp, i32], "pre_debug_fp8_encode": [vp, vp, C.c_int, vp]}
         for name, at in debug.items():
             if hasattr(L, name):
                 getattr(L, name).argtypes = at
@@ -143,6 +144,7 @@ def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, x
     c.grid_wgs, c.wg_threads, c.attn_splits = int(grid_wgs), int(wg_threads), int(attn_splits)
     c.xcd_local = int(xcd_local)
     c.chunk = int(chunk)
+    c.kv_dtype = 1 if getattr(m, "kv_fp8", False) else 0
     return c
 
 
@@ -234,8 +236,9 @@ def weight_shapes(m: synth.ModelConfig) -> dict:
 
 
 def check_model_args(m: synth.ModelConfig, weights: dict, k_cache, v_cache, ctx_len=None,
-                     device_type="cuda"):
-    """Weights, cache and position array of an engine, before create."""
+                     device_type="cuda", k_scale=None, v_scale=None):
+    """Weights, cache (and its row scales, for an fp8 cache) and position
+    array of an engine, before create."""
     ws = weight_shapes(m)
     for n, (dt, sh) in ws["top"].items():
         check_tensor(weights.get(n), n, dt, shape=sh, device_type=device_type)
@@ -244,8 +247,14 @@ def check_model_args(m: synth.ModelConfig, weights: dict, k_cache, v_cache, ctx_
         for n, (dt, sh) in ws["layer"].items():
             check_tensor(lw.get(n), f"layers[{l}].{n}", dt, shape=sh, device_type=device_type)
     kv_shape = (m.n_layers, m.batch, m.n_kv_heads, m.max_ctx, m.head_dim)
-    check_tensor(k_cache, "k_cache", torch.bfloat16, shape=kv_shape, device_type=device_type)
-    check_tensor(v_cache, "v_cache", torch.bfloat16, shape=kv_shape, device_type=device_type)
+    kv_dt = torch.uint8 if m.kv_fp8 else torch.bfloat16
+    check_tensor(k_cache, "k_cache", kv_dt, shape=kv_shape, device_type=device_type)
+    check_tensor(v_cache, "v_cache", kv_dt, shape=kv_shape, device_type=device_type)
+    if m.kv_fp8:
+        check_tensor(k_scale, "k_scale", torch.float32, shape=kv_shape[:4], device_type=device_type)
+        check_tensor(v_scale, "v_scale", torch.float32, shape=kv_shape[:4], device_type=device_type)
+    else:
+        _need(k_scale is None and v_scale is None, "k_scale / v_scale are for an fp8 cache only")
     if ctx_len is not None:
         check_tensor(ctx_len, "ctx_len", torch.int32, shape=(m.batch,), device_type=device_type)
 
@@ -283,13 +292,13 @@ class Engine:
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
                  wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None,
-                 static_workspace=False, chunk=0):
+                 static_workspace=False, chunk=0, k_scale=None, v_scale=None):
         """static_workspace: create with pre_engine_create_static (the
         library's static device workspace; no allocation) instead of a
         workspace tensor."""
         self.m = m
         self.h = None
-        check_model_args(m, weights, k_cache, v_cache, ctx_len)
+        check_model_args(m, weights, k_cache, v_cache, ctx_len, k_scale=k_scale, v_scale=v_scale)
         dev = k_cache.device
         for t in [weights["embed"], v_cache] + ([ctx_len] if ctx_len is not None else []):
             _need(t.device == dev, f"every tensor must be on {dev}, found one on {t.device}")
@@ -302,7 +311,7 @@ class Engine:
         self.workspace = None if static_workspace else torch.empty(int(nbytes.value), dtype=torch.uint8,
                                                                    device=dev)
         self.ctx_len = ctx_len
-        self._keep = [weights, k_cache, v_cache, ctx_len]
+        self._keep = [weights, k_cache, v_cache, ctx_len, k_scale, v_scale]
         self.layers = (LayerW * m.n_layers)()
         for l, lw in enumerate(weights["layers"]):
             for n in LAYER_FIELDS:
@@ -312,7 +321,9 @@ class Engine:
         self.w = Weights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
                          weights["lm_head"].data_ptr(), self.layers)
         self.kv = KV(k_cache.data_ptr(), v_cache.data_ptr(),
-                     ctx_len.data_ptr() if ctx_len is not None else None)
+                     ctx_len.data_ptr() if ctx_len is not None else None,
+                     k_scale.data_ptr() if k_scale is not None else None,
+                     v_scale.data_ptr() if v_scale is not None else None)
         h = C.c_void_p()
         if static_workspace:
             _check(L.pre_engine_create_static(C.byref(self.cfg), C.byref(self.w), C.byref(self.kv),
@@ -426,7 +437,7 @@ class Engine:
         _check(lib().pre_debug_drop_signal(self.h, int(slot)), "debug_drop_signal")
 
     LAYOUT = ["status", "flags", "layers", "tasks", "rope", "xcc", "x_out", "pbuf", "q", "u", "rl",
-              "part", "lmp", "x_emb", "a_norm", "tok", "xmid", "pk", "ssq", "ctx", "total"]
+              "part", "lmp", "x_emb", "a_norm", "tok", "xmid", "pk", "ssq", "ctx", "kvnew", "total"]
 
     def debug_slot(self, name, count, dtype=torch.float32, offset=0):
         """A view of a workspace region (debugging)."""
@@ -513,6 +524,16 @@ def fp8_decode_table(device="cuda"):
     codes = torch.arange(256, dtype=torch.uint8, device=device)
     out = torch.empty(256, dtype=torch.float32, device=device)
     _check(lib().pre_debug_fp8_decode(_ptr(codes), _ptr(out), 256, _stream()), "fp8_decode")
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def fp8_encode(values):
+    """The fp8 cache's e4m3 encoder applied on the device to fp32 values
+    (debug entry); returns the codes on the host."""
+    x = torch.as_tensor(values, dtype=torch.float32).to("cuda").contiguous()
+    out = torch.zeros(x.numel(), dtype=torch.uint8, device="cuda")
+    _check(lib().pre_debug_fp8_encode(_ptr(x), _ptr(out), x.numel(), _stream()), "fp8_encode")
     torch.cuda.synchronize()
     return out.cpu()
 

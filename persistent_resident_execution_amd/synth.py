@@ -41,6 +41,7 @@ class ModelConfig:
     top_k: int = 0
     n_shared: int = 0
     expert_ffn: int = 0
+    kv_fp8: bool = False  # K/V cache as fp8 e4m3 codes with one fp32 scale per row
 
     @property
     def is_moe(self) -> bool:
@@ -75,6 +76,9 @@ WORKLOADS = {
     "dense8b_mb8": Workload("dense8b_mb8", replace(DENSE8B, batch=8, max_ctx=8192 + 128),
                             (512, 1024, 1536, 2048, 3072, 4096, 6144, 8192), 128,
                             "8B-shape dense decoder, micro-batch 8, unequal contexts, 128 steps"),
+    "dense8b_ctx8192_kv8": Workload("dense8b_ctx8192_kv8", replace(DENSE8B, max_ctx=8192 + 256, kv_fp8=True),
+                                    (8192,), 256, "8B-shape dense decoder, batch 1, context 8192, fp8 e4m3 K/V "
+                                                  "cache (one fp32 scale per row), 256 steps"),
     "moe": Workload("moe", MOE, (4096,), 128,
                     "MoE decoder (128 experts top-8 + 1 shared, fp8 experts), context 4096, "
                     "128 greedy steps"),
@@ -201,6 +205,20 @@ def gen_tokens(vocab: int, n: int, seed: int = 0, seq: int = 0, device="cpu") ->
     g = _gen(seed, f"tokens.{seq}", device)
     return torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int64).to(
         torch.int32)
+
+
+def empty_kv_cache(cfg: ModelConfig, device="cpu"):
+    """A zeroed cache of cfg's format: (k, v, k_scale, v_scale); bf16
+    [n_layers][batch][n_kv_heads][max_ctx][head_dim] and no scales, or, for an
+    fp8 cache, uint8 codes of that shape and fp32 row scales
+    [n_layers][batch][n_kv_heads][max_ctx]."""
+    shape = (cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
+    if not cfg.kv_fp8:
+        return (torch.zeros(shape, dtype=torch.bfloat16, device=device),
+                torch.zeros(shape, dtype=torch.bfloat16, device=device), None, None)
+    return (torch.zeros(shape, dtype=torch.uint8, device=device), torch.zeros(shape, dtype=torch.uint8, device=device),
+            torch.zeros(shape[:4], dtype=torch.float32, device=device),
+            torch.zeros(shape[:4], dtype=torch.float32, device=device))
 
 
 def gen_kv_cache(cfg: ModelConfig, ctx: int, seed: int = 0, device="cpu"):

@@ -61,7 +61,8 @@ def compare_step(step, gpu_tok, gpu_logits, gpu_hidden, ref_tok, ref_logits, ref
     return rec
 
 
-def check_forced(om, kc, vc, P, first_in, gpu_toks, gpu_lgs, gpu_hds, free=None, say=None, inputs=None):
+def check_forced(om, kc, vc, P, first_in, gpu_toks, gpu_lgs, gpu_hds, free=None, say=None, inputs=None,
+                 fp8=None):
     """Teacher-forced comparison of len(gpu_toks) steps from position P.
 
     kc, vc: the oracle's cache [L][Hkv][max_ctx][d] holding positions < P (it
@@ -71,7 +72,8 @@ def check_forced(om, kc, vc, P, first_in, gpu_toks, gpu_lgs, gpu_hds, free=None,
     cache state and first input; used while the inputs agree.  gpu_lgs /
     gpu_hds entries may be None (not compared).  inputs: when the GPU run was
     itself teacher-forced, the token step s consumed (replaces the feedback).
-    Returns the records."""
+    fp8: (k_scale, v_scale) when kc, vc are an fp8 cache's codes.  Returns
+    the records."""
     recs, copied = [], False
     tok_in = int(first_in)
     use_free = free is not None
@@ -85,7 +87,12 @@ def check_forced(om, kc, vc, P, first_in, gpu_toks, gpu_lgs, gpu_hds, free=None,
         else:
             if not copied:
                 kc, vc, copied = kc.copy(), vc.copy(), True
-            rt, rl, rh = om.decode_step(kc, vc, tok_in, P + s)
+                if fp8 is not None:
+                    fp8 = (fp8[0].copy(), fp8[1].copy())
+            if fp8 is None:
+                rt, rl, rh = om.decode_step(kc, vc, tok_in, P + s)
+            else:
+                rt, rl, rh = om.decode_step_fp8(kc, vc, fp8[0], fp8[1], tok_in, P + s)
         rec = compare_step(s, int(gpu_toks[s]), None if gpu_lgs is None else gpu_lgs[s],
                            None if gpu_hds is None else gpu_hds[s], rt, rl, rh)
         recs.append(rec)
