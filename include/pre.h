@@ -190,14 +190,23 @@ typedef struct pre_engine pre_engine;
 
 /* Bytes of device workspace the engine needs for cfg (task table, ready
  * flags, activation slots, attention partials, RoPE table, status).  The
- * caller allocates it (16-byte aligned) and passes it to create. */
+ * caller allocates it (16-byte aligned) and passes it to create, so the
+ * caller's framework stays the only device allocator.  Source: the static
+ * task graph and its buffers are fixed before the run ("Persistent execution
+ * paradigm" sections 4 and 5.1, Fleet's precompiled task graph). */
 int pre_workspace_size(const pre_config *cfg, size_t *bytes);
 
 /* Validate cfg and the pointers, build and check the task table on the
  * host, and upload it, the RoPE cos/sin table and zeroed flags into the
- * workspace on `stream` (asynchronously).  Positions start at 0.  *out is an
- * opaque host handle.  Returns PRE_ERR_SHAPE / PRE_ERR_ALIGN /
- * PRE_ERR_WORKSPACE / PRE_ERR_HIP on failure, leaving *out NULL. */
+ * workspace on `stream` (asynchronously).  Positions come from kv->d_ctx_len
+ * (or start at 0).  *out is an opaque host handle.  Returns PRE_ERR_SHAPE /
+ * PRE_ERR_ALIGN / PRE_ERR_WORKSPACE / PRE_ERR_HIP on failure, leaving *out
+ * NULL.  Sources: the whole model unrolled ahead of time into one resident
+ * kernel's work (TileRT notes, "persistent engine kernel"); the task graph
+ * fixed at compile time with per-XCD placement ("Persistent execution
+ * paradigm" section 5.1; "TileRT speed scaling law", the compile-time tile
+ * routing table among its future directions); sampling and other knobs fixed
+ * when the engine is built ("Persistent execution paradigm" section 5.1). */
 int pre_engine_create(const pre_config *cfg, const pre_weights *w, const pre_kv *kv,
                       void *d_workspace, size_t ws_bytes, void *stream, pre_engine **out);
 
@@ -218,21 +227,37 @@ int pre_engine_create(const pre_config *cfg, const pre_weights *w, const pre_kv 
 int pre_engine_create_static(const pre_config *cfg, const pre_weights *w, const pre_kv *kv, void *stream,
                              pre_engine **out);
 
-/* Set / read the position each sequence decodes at next (host-side state:
- * h_pos[batch]).  A position is also the number of cached tokens. */
+/* Set / read the position each sequence decodes at next (h_pos[batch],
+ * host).  The positions live on the device (kv->d_ctx_len, or the engine's
+ * own array); these calls synchronise the device and copy them, and are
+ * only needed to move a sequence by hand -- decode, prefill and verify
+ * advance them on the device.  A position is also the number of cached
+ * tokens.  PRE_ERR_BUSY while a serving loop holds the engine.  Source: a
+ * decode engine that takes over a cache filled elsewhere (SemiAnalysis
+ * TileRT digest, "PD separation"). */
 int pre_engine_set_positions(pre_engine *e, const int32_t *h_pos);
 int pre_engine_get_positions(const pre_engine *e, int32_t *h_pos);
 
 /* Run n_steps decode steps in ONE persistent kernel launch on `stream`
- * (asynchronous).  Step s of sequence b decodes at position pos[b] + s: its
+ * (asynchronous).  Step s of sequence b decodes at position pos[b] + s, where
+ * pos[b] is read from the device positions when the kernel starts: its
  * input token is d_in_tokens[b] at s = 0 and the previous step's greedy
  * token after that, unless d_forced is non-NULL, in which case it is
  * d_forced[s * batch + b] (teacher forcing; used to fill a cache from a
  * prompt).  d_out_tokens[s * batch + b] receives the greedy token of step s.
- * Advances the host positions by n_steps.  n_steps == 0 returns PRE_OK at
- * once without reading any buffer.  Returns PRE_ERR_CONTEXT if a position
- * would pass max_ctx, PRE_ERR_BROKEN after a latched device error until
- * pre_engine_reset. */
+ * The kernel advances the device positions by n_steps at its end.
+ * n_steps == 0 returns PRE_OK at once without reading any buffer.  Returns
+ * PRE_ERR_CONTEXT if n_steps exceeds max_ctx; a position that would pass
+ * max_ctx is caught on the device (PRE_DEV_CONTEXT, nothing is written).
+ * PRE_ERR_BROKEN after a latched device error until pre_engine_reset.
+ * Sources: the host launches once and the GPU stays resident for the
+ * decode (TileRT notes, "persistent engine kernel"; SemiAnalysis TileRT
+ * digest, what TileRT is); tile tasks ordered on the device instead of by
+ * kernel boundaries (TileRT notes, "tile pipeline"; "Persistent execution
+ * paradigm" sections 1, 4 and 6.2); the per-token operator chain
+ * ("Persistent execution paradigm" section 1 and section 4's fused RMSNorm
+ * and projection; section 7.1's expert selection fused with gate/up and
+ * SiLU). */
 int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
                       const int32_t *d_forced, int32_t *d_out_tokens, const pre_check *chk,
                       void *stream);
@@ -269,32 +294,47 @@ int pre_engine_verify(pre_engine *e, int32_t n_draft, const int32_t *d_tokens, i
 /* The same decode as a conventional one-kernel-per-operator launch sequence
  * (seven launches per dense layer, eight per MoE layer, four per step),
  * using the same tile code and the same workspace, so that both paths can be
- * timed through identical calls. */
+ * timed through identical calls.  Source: the launch and boundary cost the
+ * resident kernel removes ("Persistent execution paradigm" sections 1 and
+ * 6.1: microseconds per launch and hundreds of launches per token);
+ * XL-Persistent-Kernel, benchmark modes (a host-driven decode next to the
+ * resident one). */
 int pre_baseline_decode(pre_engine *e, int32_t n_steps, const int32_t *d_in_tokens,
                         const int32_t *d_forced, int32_t *d_out_tokens, const pre_check *chk,
                         void *stream);
 
 /* Copy the latched device status to *out (synchronises the engine's
  * create stream).  Returns PRE_OK, or PRE_ERR_DEVICE if an error is latched
- * (the engine is then BROKEN until pre_engine_reset). */
+ * (the engine is then BROKEN until pre_engine_reset).  Source: a persistent
+ * kernel has no margin for a fault, one error ends the whole decode, so the
+ * device reports where it stopped ("Persistent execution paradigm" section
+ * 7.3). */
 int pre_engine_status(pre_engine *e, pre_status *out);
 
 /* Zero the ready flags, counters and status on `stream` and clear the
- * broken state.  Positions are kept. */
+ * broken state.  Positions are kept.  Source: as pre_engine_status
+ * ("Persistent execution paradigm" section 7.3). */
 int pre_engine_reset(pre_engine *e, void *stream);
 
 /* Watchdog for dependency waits, in milliseconds (default 2000; the
- * environment variable PRE_WATCHDOG_MS overrides the default). */
+ * environment variable PRE_WATCHDOG_MS overrides the default).  A wait that
+ * runs out latches PRE_DEV_TIMEOUT with the flag and epoch, and every
+ * workgroup leaves through the abort word.  Source: "Persistent execution
+ * paradigm" section 7.3 (a stuck resident kernel must end by itself). */
 int pre_engine_set_watchdog(pre_engine *e, uint32_t ms);
 
 /* Optional per-task timestamps.  d_buf receives, per (step, stage instance,
  * workgroup) executed, 8 uint32: {stage | wg << 16, t_begin, t_wait_end,
  * t_end, m0, m1, m2, m3} in 100 MHz realtime ticks (low 32 bits), where m*
  * are task phase marks (input staged, rows streamed, ...; stale where a task
- * kind sets fewer); records beyond `bytes` are dropped.  NULL disables. */
+ * kind sets fewer); records beyond `bytes` are dropped.  NULL disables.
+ * Source: CU busy and idle gaps as the measure of what a resident kernel
+ * recovers ("Persistent execution paradigm" section 6.1; SemiAnalysis TileRT
+ * digest, the gap between the bandwidth roofline and the measured rate). */
 int pre_engine_set_trace(pre_engine *e, void *d_buf, size_t bytes);
 
-/* Free the host-side state (no device memory is owned). */
+/* Free the host-side state (no device memory is owned: the caller owns the
+ * workspace, weights and cache, as pre_engine_create states). */
 int pre_engine_destroy(pre_engine *e);
 
 /* ---- the serving loop: one resident launch, requests through a ring ------
@@ -352,7 +392,8 @@ int pre_serve_poll(pre_server *s, int32_t slot, int32_t *h_tokens, int32_t max_t
  * ring and the server. */
 int pre_serve_stop(pre_server *s, pre_serve_stats *stats);
 
-/* Static description of an error code. */
+/* Static description of an error code (PRE_ERR_* or PRE_DEV_* kinds are
+ * told apart by sign: PRE_ERR_* are negative). */
 const char *pre_strerror(int code);
 
 /* ---- introspection (host only, no GPU needed) ------------------------- */
@@ -360,7 +401,10 @@ const char *pre_strerror(int code);
  * workgroups used, ready-flag slots, and the result of the table validator
  * (0 = every check passed, otherwise the number of the first failed check).
  * Also dumps up to max_tasks task records (8 int32 each: op, layer, r0, r1,
- * aux, wait_lo, wait_hi, signal) in table order when h_tasks is non-NULL. */
+ * aux, wait_lo, wait_hi, signal) in table order when h_tasks is non-NULL.
+ * Source: the compile-time task table with per-XCD placement ("Persistent
+ * execution paradigm" section 5.1; "TileRT speed scaling law", future
+ * directions). */
 typedef struct pre_plan_info {
   int32_t n_stage_inst, n_wgs, n_slots, n_tasks, attn_splits, validator;
   int32_t xcd_local;  /* 1: per-KV-head XCD-local hand-offs; 2: every workgroup on one XCD; 0: none */
@@ -371,12 +415,18 @@ int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int32_t *h_task
 
 /* Run the table validator on a caller-supplied table (n_tasks records of 8
  * int32 in the layout pre_plan_describe dumps).  Returns 0 if it passes, the
- * number of the first failed check otherwise, or a negative PRE_ERR_* code. */
+ * number of the first failed check otherwise, or a negative PRE_ERR_* code.
+ * Source: a task graph fixed ahead of time can be checked before it runs,
+ * where a fault inside the resident kernel could not be recovered from
+ * ("Persistent execution paradigm" sections 5.1 and 7.3). */
 int pre_plan_validate(const pre_config *cfg, const int32_t *h_tasks, int32_t n_tasks);
 
 /* Algorithmic bytes one decode step moves for sequences at the given
  * positions (h_pos[batch]): every weight read once (active experts only),
- * the attended K/V read once, the new K/V written.  For bandwidth figures. */
+ * the attended K/V read once, the new K/V written.  For bandwidth figures.
+ * Source: the bandwidth roofline, bytes per token over HBM bandwidth, as the
+ * score of a decode engine (SemiAnalysis TileRT digest, its roofline
+ * arithmetic; "TileRT speed scaling law", Fleet's Eq. (1)). */
 int64_t pre_step_bytes(const pre_config *cfg, const int32_t *h_pos);
 
 #ifdef __cplusplus
