@@ -32,6 +32,10 @@ constexpr int CP_NT = 2;
 constexpr int CP_SC1 = 16;
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+// LDS addresses as 32-bit byte offsets (what ds_* instructions and M0 take)
+typedef __attribute__((address_space(3))) void *LdsPtr;
+__device__ __forceinline__ LdsPtr lds_ptr(uint32_t a) { return (LdsPtr)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t lds_u32(const void *p) { return (uint32_t)(uintptr_t)(LdsPtr)(void *)p; }
 
 // A pointer every lane holds the same value of, as a scalar.  Buffer
 // descriptors must live in scalar registers; when the compiler cannot prove

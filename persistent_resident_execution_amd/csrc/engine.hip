@@ -36,6 +36,7 @@ struct KP {
   // shapes
   int32_t L, h, Hq, Hkv, d, ffn, V, B, max_ctx, E, top_k, n_shared, effn, moe, G, F, W, X, NC, Tg;
   int32_t n_si, spl, kmax, ymax, segoff, cmax, lds_floats;
+  int32_t npre, xsoff;  // GEMV: most units per wavefront loaded into LDS first; staged input offset
   int32_t nthr, nw;  // threads and wavefronts per workgroup (scalar: never re-read from the dispatch packet)
   float eps, attn_scale;
   // model
@@ -245,6 +246,21 @@ __device__ __forceinline__ void st_out(const KP &P, float *p, float v) {
   else
     st_sc1(p, v);
 }
+// A result whose every reader runs on this XCD (the QKV -> attention ->
+// O-projection hand-offs of one KV head with XCD-local placement): left in
+// the XCD's L2 like those stages' flags, so the readers' device-scope loads
+// find it there instead of in memory.
+__device__ __forceinline__ void st_xcd(const KP &P, float *p, float v) {
+  if (P.local || P.onexcd)
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    st_sc1(p, v);
+}
+__device__ __forceinline__ void st_xcd16(const KP &P, Rsrc r, uint32_t off, uint16_t v) {
+  if (P.local || P.onexcd) st16<CP_SC0>(r, off, v);
+  else st16<CP_SC1>(r, off, v);
+}
 __device__ __forceinline__ void st_out16(const KP &P, Rsrc r, uint32_t off, uint16_t v) {
   if (P.onexcd) st16<CP_SC0>(r, off, v);
   else st16<CP_SC1>(r, off, v);
@@ -442,6 +458,8 @@ struct PStream {
   // compute cursor
   int cg, cc;
   int nch, left, wave, nw;
+  int np;        // units of the span held in LDS (the span's first ones)
+  uint32_t pre;  // LDS byte address of this wavefront's units there
   float acc[2];
 };
 
@@ -480,8 +498,25 @@ __device__ __forceinline__ void seg_enter(PStream<FP8, D, CP> &S, const Seg *tab
   }
 }
 
+// Move the issue cursor to the next unit of the span.  Once the span is used
+// up every further issue reads nothing.
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_advance(PStream<FP8, D, CP> &S, const Seg *tab, const Geo &G) {
+  if (--S.left <= 0) {
+    S.rbA = 0;
+  } else if (++S.ic == S.nch) {
+    S.ic = 0;
+    if (++S.ig == S.segn) {
+      seg_enter(S, tab, G, ++S.is);
+    } else {
+      S.pa += G.pstride;
+      S.pb += G.pstride;
+      S.j += G.gstep;
+    }
+  }
+}
+
 // Issue the unit under the cursor into ring slot jj and advance the cursor.
-// Once the span is used up every further issue reads nothing.
 template <bool FP8, int D, int CP>
 __device__ __forceinline__ void st_issue(PStream<FP8, D, CP> &S, int jj, const Seg *tab, const Geo &G) {
   const int lane = threadIdx.x & 63;
@@ -499,24 +534,32 @@ __device__ __forceinline__ void st_issue(PStream<FP8, D, CP> &S, int jj, const S
         mkbuf64(S.sb + (uint64_t)((S.j + G.jb) >> 7) * G.srow, rbB ? G.srow : 0u), so, 0, CP_DEF));
     S.xo[jj] = S.segxo;
   }
-  if (--S.left <= 0) {
-    S.rbA = 0;
-  } else if (++S.ic == S.nch) {
-    S.ic = 0;
-    if (++S.ig == S.segn) {
-      seg_enter(S, tab, G, ++S.is);
-    } else {
-      S.pa += G.pstride;
-      S.pb += G.pstride;
-      S.j += G.gstep;
-    }
-  }
+  st_advance(S, tab, G);
+}
+
+// Issue the unit under the cursor (bf16) straight into LDS at byte address
+// dst: row A's 1 KB, then row B's (zeros past a task's last B row), lane i's
+// 16 bytes at 16 i; no register holds it.
+template <bool FP8, int D, int CP>
+__device__ __forceinline__ void st_issue_lds(PStream<FP8, D, CP> &S, uint32_t dst, const Seg *tab, const Geo &G) {
+  static_assert(!FP8, "the LDS head is for bf16 streams");
+  const int lane = threadIdx.x & 63;
+  const uint32_t off = ((uint32_t)S.ic * 512 + lane * 8) * 2;
+  const uint32_t rbB = S.ig < S.segnB ? S.rbA : 0u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(mkbuf64(S.pa, S.rbA), lds_ptr(dst), 16, off, 0, 0, CP);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(mkbuf64(S.pb, rbB), lds_ptr(dst + 1024), 16, off, 0, 0, CP);
+  st_advance(S, tab, G);
 }
 
 // This wavefront's span of the task's NG * nch units; issues its first D
 // units (reading nothing past the span).  Returns the span length.
+// With npre > 0 (bf16), the span's first min(npre, n) units go straight into
+// LDS at pre (2 KB each; the wavefront's own area) before the ring's D:
+// twice the bytes on their way while the task waits for its producers and
+// stages its input, without the registers a deeper ring would take.
 template <bool FP8, int D, int CP>
-__device__ __forceinline__ int st_begin(PStream<FP8, D, CP> &S, const Seg *tab, const Geo &G, int nw) {
+__device__ __forceinline__ int st_begin(PStream<FP8, D, CP> &S, const Seg *tab, const Geo &G, int nw,
+                                        int npre = 0, const float *pre = nullptr) {
   const int wave = wave_id();
   S.wave = wave;
   S.nw = nw;
@@ -543,6 +586,12 @@ __device__ __forceinline__ int st_begin(PStream<FP8, D, CP> &S, const Seg *tab, 
   S.pb += (uint64_t)g * G.pstride;
   S.j += g * G.gstep;
   if (n <= 0) S.rbA = 0;
+  S.np = 0;
+  if constexpr (!FP8) {
+    S.np = rfl(min(npre, n));
+    S.pre = lds_u32(pre);
+    for (int e = 0; e < S.np; ++e) st_issue_lds(S, S.pre + e * 2048, tab, G);
+  }
 #pragma unroll
   for (int jj = 0; jj < D; ++jj) st_issue(S, jj, tab, G);
   return n;
@@ -584,6 +633,26 @@ __device__ __forceinline__ void st_compute(PStream<FP8, D, CP> &S, int jj, bool 
 template <bool FP8, int D, int CP>
 __device__ __forceinline__ void st_run(PStream<FP8, D, CP> &S, int n, const Seg *tab, const Geo &G,
                                        const float *xs, float *ys) {
+  if constexpr (!FP8) {
+    // the units in LDS first.  Their loads were issued before the ring's,
+    // so once every load of this wavefront is complete (by now they have
+    // landed: the staging after them waited for its own) the LDS holds
+    // them; the wait and the reads share one asm block, which no memory
+    // access crosses.
+    for (int e = 0; e < S.np; ++e) {
+      v4i w0, w1;
+      asm volatile(
+          "s_waitcnt vmcnt(0)\n\t"
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %2 offset:1024\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w0), "=&v"(w1)
+          : "v"(S.pre + e * 2048 + (threadIdx.x & 63) * 16)
+          : "memory");
+      st_compute_w(S, 0, w0, w1, e == n - 1, xs, ys);
+    }
+    n -= S.np;
+  }
   const int m = n >= D ? (n - D) / D : 0;  // rounds whose every issue lies inside the span
   for (int q = 0; q < m; ++q) {
 #pragma unroll
@@ -675,8 +744,8 @@ struct GemvLds {
   Seg *seg;
 };
 __device__ __forceinline__ GemvLds gemv_lds(const KP &P, float *lds) {
-  float *ys = lds + P.kmax, *red = ys + P.ymax * P.nw;
-  return GemvLds{lds, ys, red, reinterpret_cast<Seg *>(lds + P.segoff)};
+  float *red = lds + SEGMAX * 12, *ys = red + 256;
+  return GemvLds{lds + P.xsoff, ys, red, reinterpret_cast<Seg *>(lds + P.segoff)};
 }
 
 // Best (value, lowest index) of two candidates.
@@ -953,7 +1022,15 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   G = geo_uniform(G);
   __syncthreads();
   PStream<FP8> S;
-  const int n = st_begin(S, M.seg, G, nw);
+  // this task's LDS units: past its staged input, as many as the LDS holds
+  int npre = 0;
+  const float *pre = nullptr;
+  if (!FP8 && P.npre) {
+    const int hoff = (P.xsoff + min(P.kmax, (G.K + 1023) & ~1023) + 63) & ~63;
+    npre = rfl(min(P.npre, (P.lds_floats - hoff) / (nw * 512)));
+    pre = lds + hoff + wave_id() * npre * 512;
+  }
+  const int n = st_begin(S, M.seg, G, nw, npre, pre);
   ys_clear(M.ys, G.NG, nw, P.nthr);
   // the post-attention residual was final before the gate/up stage this
   // workgroup passed: fetch it now
@@ -967,7 +1044,10 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     cos0 = P.rope[(int64_t)pos * half + j];
     sin0 = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + j];
   }
-  if (known && !wait(P)) return false;
+  if (known && !wait(P)) {
+    __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outlives the task
+    return false;
+  }
   bool normed = false;  // RMSNorm folded into the staging: results scale by norm_scale
   int Kst = 0;
   if (op == OP_OPROJ) {
@@ -1048,24 +1128,24 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         }
         if (hh < P.G) {
           float *qd = P.q + vec_off(P, l, 0, P.Hq * P.d) + (int64_t)(g * P.G + hh) * P.d;
-          st_out(P, qd + j, a);
-          st_out(P, qd + j + half, b);
+          st_xcd(P, qd + j, a);
+          st_xcd(P, qd + j + half, b);
         } else if (P.kv8) {  // fp8 cache: the new row in fp32, quantized by the attention task owning it
           float *kn = P.kvnew + ((((int64_t)l * P.B) * 2 + (hh == P.G ? 0 : 1)) * P.Hkv + g) * P.d;
-          st_out(P, kn + j, a);
-          st_out(P, kn + j + half, b);
+          st_xcd(P, kn + j, a);
+          st_xcd(P, kn + j + half, b);
         } else {  // the layer's K or V cache of every KV head under one descriptor each
           const int64_t lbase = (int64_t)l * P.B * P.Hkv * P.max_ctx * P.d;
           const uint32_t bytes = (uint32_t)((int64_t)P.B * P.Hkv * P.max_ctx * P.d * 2);
           const uint32_t o0 = (uint32_t)(((int64_t)g * P.max_ctx + pos) * P.d + j) * 2, o1 = o0 + (uint32_t)half * 2;
           if (hh == P.G) {
             const Rsrc r = mkbuf(P.kc + lbase, bytes);
-            st_out16(P, r, o0, f2bf(a));
-            st_out16(P, r, o1, f2bf(b));
+            st_xcd16(P, r, o0, f2bf(a));
+            st_xcd16(P, r, o1, f2bf(b));
           } else {
             const Rsrc r = mkbuf(P.vc + lbase, bytes);
-            st_out16(P, r, o0, f2bf(a));
-            st_out16(P, r, o1, f2bf(b));
+            st_xcd16(P, r, o0, f2bf(a));
+            st_xcd16(P, r, o1, f2bf(b));
           }
         }
       }
@@ -1519,11 +1599,11 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
     for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) s += ov[w];
-    st_out(P, pdst + hh * rec + PREC_O + j, s);
+    st_xcd(P, pdst + hh * rec + PREC_O + j, s);
   }
   for (int hh = tid; hh < G; hh += T) {
-    st_out(P, pdst + hh * rec, st[2 * hh]);
-    st_out(P, pdst + hh * rec + 1, st[2 * hh + 1]);
+    st_xcd(P, pdst + hh * rec, st[2 * hh]);
+    st_xcd(P, pdst + hh * rec + 1, st[2 * hh + 1]);
   }
   return true;
 }
@@ -2112,6 +2192,7 @@ static void fill_kp_dims(const pre_engine *e, const Dims &D, const Layout &Lo, c
   P.max_ctx = D.max_ctx; P.E = D.E; P.top_k = D.top_k; P.n_shared = D.n_shared; P.effn = D.effn;
   P.moe = D.moe; P.G = D.G; P.F = D.F; P.W = D.W; P.X = D.X; P.NC = D.NC; P.Tg = D.Tg; P.n_si = D.n_si;
   P.spl = D.stages_per_layer; P.kmax = D.kmax; P.ymax = D.ymax; P.segoff = D.segoff; P.cmax = D.cmax;
+  P.npre = D.npre; P.xsoff = D.xsoff;
   P.lds_floats = e->lds_dyn / 4;
   P.nthr = D.threads;
   P.nw = D.threads / 64;

@@ -129,12 +129,13 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
     else y = std::max(y, 2 * cdiv(D->ffn, W));
     D->ymax = pad_to(y, 64);
   }
-  // GEMV phase: staged input, per-row results, reduction scratch, segment
-  // table (80 entries of 12 words); the output projection's chunk combine
-  // writes its result into the staged input and needs no scratch.
+  // GEMV phase: segment table (80 entries of 12 words), reduction scratch,
+  // per-row results, then the staged input; the output projection's chunk
+  // combine writes its result into the staged input and needs no scratch.
   // Attention phase: q, scores, per-wave output partials, softmax stats.
-  D->segoff = (int32_t)pad_to((int64_t)D->kmax + (int64_t)D->ymax * waves + 256, 4);
-  int64_t gemv = (int64_t)D->segoff + 80 * 12;
+  D->segoff = 0;
+  D->xsoff = (int32_t)pad_to(80 * 12 + 256 + (int64_t)D->ymax * waves, 64);
+  int64_t gemv = (int64_t)D->xsoff + D->kmax;
   int64_t attn = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->cmax, 64) +
                  (int64_t)waves * D->G * D->d + 4 * D->G + 256;
   // the chunk's K and V row scales, the newest row's K and V codes
@@ -151,7 +152,15 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
     gemv = base + (int64_t)D->mbst * 8;
     attn += (int64_t)D->G * D->d + 4 * D->G;
   }
-  D->lds_bytes = (int32_t)(std::max(gemv, attn) * 4);
+  // The head of every batch-1 GEMV stream (up to PRE_UNITS units of 2 KB per
+  // wavefront) goes straight into LDS after the task's staged input, in
+  // what the CU's 160 KB leave; the workgroup then takes all of them.  Not
+  // on one XCD, where the streams are short and the hand-offs' latency is
+  // the whole cost.
+  const int64_t base = std::max(gemv, attn);
+  D->npre = (mb || D->onexcd) ? 0 : PRE_UNITS;
+  // (1 KB of the 160 KB stays for the kernels' static LDS)
+  D->lds_bytes = (int32_t)((D->npre ? std::max<int64_t>(base, 40704) : base) * 4);
   if (D->lds_bytes > 160 * 1024) return PRE_ERR_SHAPE;
   D->eps = c->rms_eps;
   D->theta = c->rope_theta;

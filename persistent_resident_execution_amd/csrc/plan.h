@@ -21,6 +21,12 @@
 
 namespace pre {
 
+// Most units (2 KB per wavefront) of a batch-1 GEMV stream loaded into LDS
+// ahead of the register ring (fewer where the task's own LDS leaves less).
+#ifndef PRE_UNITS
+#define PRE_UNITS 4
+#endif
+
 enum Op : int32_t {
   OP_NONE = 0,
   OP_QKV = 1,    // RMSNorm-folded QKV rows (RoPE pairs), K/V append
@@ -89,8 +95,11 @@ struct Dims {
   int32_t n_si, stages_per_layer, threads;
   int32_t kmax;       // longest GEMV input, padded
   int32_t ymax;       // most GEMV results one task produces (x waves: LDS partials)
-  int32_t segoff;     // LDS float offset of the GEMV segment table
+  int32_t segoff;     // LDS float offset of the GEMV segment table (0)
   int32_t mbst;       // micro-batch: longest GEMM input staged in LDS (0: none)
+  int32_t npre;       // GEMV: most units of each wavefront's stream loaded straight into LDS first
+  int32_t xsoff;      // LDS float offset of the staged GEMV input (segment table, reduction
+                      // scratch and partials come first; a task's LDS units follow its input)
   int32_t cmax;       // longest attention chunk (positions; micro-batch: longest piece of one workgroup)
   int32_t lds_bytes;  // dynamic LDS per workgroup
   int32_t kv8;        // fp8 e4m3 K/V cache with an fp32 scale per cached row
