@@ -226,7 +226,7 @@ def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps
     K = args.steps if args.steps > 0 else w.steps
     log(f"[bench] {workload}: timing {args.repeats} x {K} persistent steps from position(s) {pos}")
     tp, toks = time_calls(eng, eng.decode, K, g0, pos, args.repeats, args.warmup)
-    kern = "pre_persistent_mb" if mb else "pre_persistent"
+    kern = "pre_persistent_mb" if mb else ("pre_persistent_kv8" if m.kv_fp8 else "pre_persistent")
     t_med = statistics.median(tp)
     us = t_med / K * 1e6
     unit = "us/step" if mb else "us/token"

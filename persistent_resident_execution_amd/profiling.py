@@ -68,24 +68,35 @@ def _short(name, n=60):
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def summarize_stats(d, out, command, kernel=KERNEL):
+def summarize_stats(d, out, command, kernel=KERNEL, index=None, workload=None):
+    """index: the dispatch of `kernel` (in launch order) that ran `workload`
+    when one profiled process ran several workloads; its duration is then the
+    summary's mean_us."""
     rows = _csv(d, "kernel_stats.csv")
-    trace = _csv(d, "kernel_trace.csv")
+    trace = sorted(_csv(d, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
             if r["Kernel_Name"] == kernel]
-    lines = [f"# rocprofv3 kernel trace + stats", f"command: {command}", f"source_sha256: {source_hash()}", "",
+    lines = [f"# rocprofv3 kernel trace + stats", f"command: {command}", f"source_sha256: {source_hash()}"]
+    if workload is not None:
+        lines.append(f"workload: {workload}")
+    lines += ["",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>12s} {'min_us':>12s} {'max_us':>12s} {'pct':>6s}"]
     for r in rows:
         lines.append(f"{_short(r['Name']):60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} "
                      f"{float(r['MinNs']) / 1e3:12.1f} {float(r['MaxNs']) / 1e3:12.1f} "
                      f"{float(r['Percentage']):6.2f}")
-    lines += ["", f"{kernel} dispatches (us): " + ", ".join(f"{x:.1f}" for x in durs)]
-    if durs:
+    lines += ["", f"{kernel} dispatches (us, in launch order): " + ", ".join(f"{x:.1f}" for x in durs)]
+    if index is not None:
+        lines.append(f"{kernel} dispatch {index} ran {workload}: {durs[index]:.1f} us")
+        lines.append(f"{kernel} mean_us: {durs[index]:.1f}")
+    elif durs:
         lines.append(f"{kernel} mean_us: {statistics.mean(durs):.1f}")
     _write(out, lines)
 
 
-def _last_dispatch_value(rows, kernel, counter):
+def _last_dispatch_value(rows, kernel, counter, index=-1):
+    """The counter summed over its instances for one dispatch of kernel: the
+    index-th in dispatch order (default the last); and how many there were."""
     vals = {}
     for r in rows:
         if r["Counter_Name"] == counter and r["Kernel_Name"] == kernel:
@@ -93,13 +104,15 @@ def _last_dispatch_value(rows, kernel, counter):
             vals[did] = vals.get(did, 0.0) + float(r["Counter_Value"])
     if not vals:
         raise ValueError(f"no {counter} rows for {kernel}")
-    return vals[max(vals)], len(vals)
+    return vals[sorted(vals)[index]], len(vals)
 
 
-def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, steps, kernel=KERNEL):
+def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, steps, kernel=KERNEL,
+                      index=-1):
     fr, wr = _csv(fetch_dir, "counter_collection.csv"), _csv(write_dir, "counter_collection.csv")
-    f_k, nf = _last_dispatch_value(fr, kernel, "FETCH_SIZE")
-    w_k, nw = _last_dispatch_value(wr, kernel, "WRITE_SIZE")
+    f_k, nf = _last_dispatch_value(fr, kernel, "FETCH_SIZE", index)
+    w_k, nw = _last_dispatch_value(wr, kernel, "WRITE_SIZE", index)
+    which = "last" if index == -1 else f"dispatch {index}"
     f_c, _ = _last_dispatch_value(fr, COPY_KERNEL, "FETCH_SIZE")
     w_c, _ = _last_dispatch_value(wr, COPY_KERNEL, "WRITE_SIZE")
     ff, fw = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
@@ -111,8 +124,8 @@ def summarize_traffic(fetch_dir, write_dir, out, command, copy_bytes, workload, 
              f"copy_FETCH_SIZE_KiB: {f_c:.1f}", f"copy_WRITE_SIZE_KiB: {w_c:.1f}",
              f"fetch_scale: {ff:.4f}", f"write_scale: {fw:.4f}",
              f"kernel: {kernel}",
-             f"kernel_FETCH_SIZE_KiB: {f_k:.1f}  (last of {nf} {kernel} dispatches)",
-             f"kernel_WRITE_SIZE_KiB: {w_k:.1f}  (last of {nw} {kernel} dispatches)",
+             f"kernel_FETCH_SIZE_KiB: {f_k:.1f}  ({which} of {nf} {kernel} dispatches)",
+             f"kernel_WRITE_SIZE_KiB: {w_k:.1f}  ({which} of {nw} {kernel} dispatches)",
              f"fetch_bytes_per_launch: {fetch_b:.0f}", f"write_bytes_per_launch: {write_b:.0f}",
              f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
              f"traffic_bytes_per_step: {(fetch_b + write_b) / steps:.0f}"]
@@ -304,6 +317,8 @@ def main():
     a.add_argument("--out", required=True)
     a.add_argument("--command", required=True)
     a.add_argument("--kernel", default=KERNEL)
+    a.add_argument("--index", type=int, default=None, help="the dispatch that ran --workload")
+    a.add_argument("--workload", default=None)
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
@@ -313,6 +328,7 @@ def main():
     b.add_argument("--workload", required=True)
     b.add_argument("--steps", type=int, required=True)
     b.add_argument("--kernel", default=KERNEL)
+    b.add_argument("--index", type=int, default=-1, help="the dispatch that ran --workload (default: last)")
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--out", required=True)
@@ -325,10 +341,10 @@ def main():
     e.add_argument("--kernel", default=KERNEL)
     args = ap.parse_args()
     if args.cmd == "stats":
-        summarize_stats(args.dir, args.out, args.command, args.kernel)
+        summarize_stats(args.dir, args.out, args.command, args.kernel, args.index, args.workload)
     elif args.cmd == "traffic":
         summarize_traffic(args.fetch_dir, args.write_dir, args.out, args.command, args.copy_bytes,
-                          args.workload, args.steps, args.kernel)
+                          args.workload, args.steps, args.kernel, args.index)
     elif args.cmd == "l2xcd":
         summarize_l2_per_xcd(args.dir, args.out, args.command, args.kernel)
     else:
