@@ -449,7 +449,8 @@ __device__ __forceinline__ Geo geo_uniform(const Geo &g) {
 template <bool FP8, int D = RING, int CP = CP_W>
 struct PStream {
   v4i buf[D][2];
-  float sc[D][2];  // fp8: the block scale of each lane's 16 weights
+  uint16_t sc[D][2];  // fp8: the bf16 block scale of each lane's 16 weights, as loaded (widened where
+                      // used, so that issuing a unit never waits for its scale)
   int xo[D];       // fp8: input offset of the unit in each slot
   // issue cursor (wave-uniform)
   uint64_t pa, pb, sa, sb;
@@ -528,10 +529,10 @@ __device__ __forceinline__ void st_issue(PStream<FP8, D, CP> &S, int jj, const S
   if (FP8) {
     // this lane's 16 columns share one 128-wide block: one bf16 scale each
     const uint32_t so = (col >> 7) * 2;
-    S.sc[jj][0] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(
-        mkbuf64(S.sa + (uint64_t)(S.j >> 7) * G.srow, S.rbA ? G.srow : 0u), so, 0, CP_DEF));
-    S.sc[jj][1] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(
-        mkbuf64(S.sb + (uint64_t)((S.j + G.jb) >> 7) * G.srow, rbB ? G.srow : 0u), so, 0, CP_DEF));
+    S.sc[jj][0] = __builtin_amdgcn_raw_buffer_load_b16(
+        mkbuf64(S.sa + (uint64_t)(S.j >> 7) * G.srow, S.rbA ? G.srow : 0u), so, 0, CP_DEF);
+    S.sc[jj][1] = __builtin_amdgcn_raw_buffer_load_b16(
+        mkbuf64(S.sb + (uint64_t)((S.j + G.jb) >> 7) * G.srow, rbB ? G.srow : 0u), so, 0, CP_DEF);
     S.xo[jj] = S.segxo;
   }
   st_advance(S, tab, G);
@@ -606,8 +607,8 @@ __device__ __forceinline__ void st_compute_w(PStream<FP8, D, CP> &S, int jj, v4i
   const int lane = threadIdx.x & 63;
   const float *xb = xs + (FP8 ? S.xo[jj] + S.cc * 1024 + lane * 16 : S.cc * 512 + lane * 8);
   if (FP8) {
-    S.acc[0] = fmaf(S.sc[jj][0], dot16_fp8(w0, xb), S.acc[0]);
-    S.acc[1] = fmaf(S.sc[jj][1], dot16_fp8(w1, xb), S.acc[1]);
+    S.acc[0] = fmaf(bf16f(S.sc[jj][0]), dot16_fp8(w0, xb), S.acc[0]);
+    S.acc[1] = fmaf(bf16f(S.sc[jj][1]), dot16_fp8(w1, xb), S.acc[1]);
   } else {
     const float4 *x4 = reinterpret_cast<const float4 *>(xb);
     const float4 x0 = x4[0], x1 = x4[1];
@@ -1010,16 +1011,21 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   // kernel the down task of a layer runs on the workgroup that just routed
   // the same layer for its gate/up task, and the choice is still in LDS.
   const bool known = !FP8 || (P.persistent && op == OP_EDOWN);
+  // The resident kernel's expert gate/up task: its input (the post-attention
+  // residual, summed once by the router stage) is final once the router is,
+  // so it is copied into LDS before the routing reads the router's logits,
+  // and the weight loads follow the choice (late).
+  const bool late = FP8 && !known && P.persistent;
   if (FP8) {
     if (!known) {
       if (!wait(P)) return false;
-      route(P, l, sel, selw, M.xs);
+      if (!late) route(P, l, sel, selw, M.xs);
     }
-    G = segs_fp8(P, t, sel, M.seg);
+    if (!late) G = segs_fp8(P, t, sel, M.seg);
   } else {
     G = segs_bf16(P, t, M.seg);
   }
-  G = geo_uniform(G);
+  if (!late) G = geo_uniform(G);
   __syncthreads();
   PStream<FP8> S;
   // this task's LDS units: past its staged input, as many as the LDS holds
@@ -1030,8 +1036,11 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     npre = rfl(min(P.npre, (P.lds_floats - hoff) / (nw * 512)));
     pre = lds + hoff + wave_id() * npre * 512;
   }
-  const int n = st_begin(S, M.seg, G, nw, npre, pre);
-  ys_clear(M.ys, G.NG, nw, P.nthr);
+  int n = 0;
+  if (!late) {
+    n = st_begin(S, M.seg, G, nw, npre, pre);
+    ys_clear(M.ys, G.NG, nw, P.nthr);
+  }
   // the post-attention residual was final before the gate/up stage this
   // workgroup passed: fetch it now
   const bool down = op == OP_DOWN || op == OP_EDOWN;
@@ -1056,6 +1065,51 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     attn_combine(P, l, t.aux, M.xs);
     for (int i = G.K + tid; i < Kp; i += P.nthr) M.xs[i] = 0.f;
     __syncthreads();
+  } else if (late) {
+    // x = the post-attention residual into xs through LDS-destination loads
+    // (1 KB per instruction, no registers held while the routing runs; past
+    // K they write zeros) and this thread's gains into registers; then the
+    // routing (the partials' area as its scratch), the segments and the
+    // weight loads; then xs = x * g and the sums of squares for the folded
+    // RMSNorm.
+    const int K = P.h, n4 = K >> 2, T = P.nthr, lane = tid & 63, wave = wave_id(), nc = (K + 255) >> 8;
+    const Rsrc rx = mkbuf(uni_ptr(P.xmid + vec_off(P, l, 0, P.h)), (uint32_t)K * 4);
+    const Rsrc rg = mkbuf(uni_ptr(P.layers[l].ffn_norm), (uint32_t)K * 2);
+    const uint32_t xb = lds_u32(M.xs);
+    for (int c = wave; c < nc; c += nw)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_ptr(xb + c * 1024), 16, (uint32_t)(c * 256 + lane * 4) * 4,
+                                               0, 0, CP_SC1);
+    constexpr int GJ = 4;  // gains held for K <= 16 T (the rest read after)
+    v2i gv[GJ];
+#pragma unroll
+    for (int j = 0; j < GJ; ++j)
+      gv[j] = tid + j * T < n4 ? ld64<CP_DEF>(rg, (uint32_t)(tid + j * T) * 8) : v2i{0, 0};
+    route(P, l, sel, selw, M.ys);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's copies and gains
+    G = geo_uniform(segs_fp8(P, t, sel, M.seg));
+    __syncthreads();  // the segment table and every wavefront's copy of x
+    // xs = x * g and the sums of squares, then the weight loads: nothing in
+    // the staging waits behind them
+    float ss = 0.f;
+    float4 *x4 = reinterpret_cast<float4 *>(M.xs);
+    auto scale4 = [&](int i, v2i g) {
+      const float4 f = x4[i];
+      ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
+      ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
+      x4[i] = float4{f.x * bf_lo(g.x), f.y * bf_hi(g.x), f.z * bf_lo(g.y), f.w * bf_hi(g.y)};
+    };
+#pragma unroll
+    for (int j = 0; j < GJ; ++j)
+      if (tid + j * T < n4) scale4(tid + j * T, gv[j]);
+    for (int i = tid + GJ * T; i < n4; i += T) scale4(i, ld64<CP_DEF>(rg, (uint32_t)i * 8));
+    for (int i = nc * 256 + tid; i < P.kmax; i += T) M.xs[i] = 0.f;
+    const float w = wave_sum2_l63(ss, 0.f).x;
+    if (lane == 63) M.red[wave] = w;
+    ys_clear(M.ys, G.NG, nw, P.nthr);
+    __syncthreads();
+    n = st_begin(S, M.seg, G, nw, npre, pre);
+    normed = true;
+    Kst = K;
   } else {
     Src src{P.a_norm, nullptr, nullptr, 0, 0, nullptr};  // the baseline's normalised input
     int K = P.h;
