@@ -219,18 +219,18 @@ __device__ __forceinline__ uint32_t f2e4m3(float x) {
 }
 
 // Eight e4m3 codes (byte e = element e) as eight bf16 (exact: every e4m3
-// value is a bf16 value) in the layout of one 16-byte bf16 load.  (The
-// converted pairs are copied into scalars before their bit casts: a bit cast
-// of a vector element reads element 0 with this compiler.)
+// value is a bf16 value) in the layout of one 16-byte bf16 load.
 __device__ __forceinline__ v4i fp8x8_bf16(v2i w) {
   v4i r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int wi = w[i];
-    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(wi, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wi, true);
-    const float a = lo.x, b = lo.y, c = hi.x, d = hi.y;
-    r[2 * i] = (int)((__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xffff0000u));
-    r[2 * i + 1] = (int)((__builtin_bit_cast(uint32_t, c) >> 16) | (__builtin_bit_cast(uint32_t, d) & 0xffff0000u));
+    // gfx950's scaled conversion with scale 1: e4m3 values are bf16 values,
+    // so it is exact (checked against the f32 route on every code)
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wi, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wi, 1.0f, true);
+    r[2 * i] = (int)__builtin_bit_cast(uint32_t, lo);
+    r[2 * i + 1] = (int)__builtin_bit_cast(uint32_t, hi);
   }
   return r;
 }
