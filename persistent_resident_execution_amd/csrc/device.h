@@ -257,6 +257,18 @@ __device__ __forceinline__ float dot16_fp8(v4i w, const float *x) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int nwaves() { return __builtin_amdgcn_readfirstlane(blockDim.x >> 6); }
 
+// The thread index behind an empty asm statement, for code inlined into a
+// resident kernel's task loop.  Nothing derived from it can be hoisted out of
+// the loop: with the plain index the compiler computes dozens of lane
+// offsets once before the loop and keeps them live across every task, in
+// registers the heaviest task then lacks, or spilled to scratch.
+__device__ __forceinline__ int tid_task() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ int wave_task() { return __builtin_amdgcn_readfirstlane(tid_task() >> 6); }
+
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 __device__ __forceinline__ uint32_t xcc_id() {

@@ -171,7 +171,7 @@ template <bool STAGED, int DS, class AfterWait, class AfterStage>
 __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, int nb, int nrg, const uint8_t *act,
                                           float *lact, int K, const MbWaiter *wait, float *ys,
                                           const AfterWait &after_wait, const AfterStage &after_stage) {
-  const int lane = threadIdx.x & 63, wave = wave_id(), nw = P.nw;
+  const int lane = tid_task() & 63, wave = wave_task(), nw = P.nw;
   const int ii = lane & 15, q = lane >> 4, h = ii & 3;
   const int jr = wave % nb, kp = wave / nb, nkp = nw / nb;
   MbRg g{0, 0, 0, 0};
@@ -210,7 +210,7 @@ __device__ __forceinline__ bool mb_stream(const KP &P, const Task &t, int j0, in
     after_wait();  // loads of the producers' other results, in flight with the staging
     if (STAGED) {  // the packed input, once, into LDS (one round trip for the workgroup)
       const int n16 = nks * 256;
-      for (int i0 = threadIdx.x; i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
+      for (int i0 = tid_task(); i0 < n16; i0 += 16 * P.nthr) {  // 4096 columns: one round
         v4i x[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k)
@@ -311,7 +311,7 @@ __device__ __forceinline__ float mb_y(const float *ys, int nb, int nkp, int j, i
 // 1 / rms of each sequence's input from the producers' sums of squares
 // (wavefront b sums sequence b's W partials in workgroup order).
 __device__ __forceinline__ void mb_norm_scales(const KP &P, int idx, int K, float *rs) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wave = wave_task(), lane = tid_task() & 63;
   if (wave < P.B) {
     float s = 0.f;
     for (int w = lane; w < P.W; w += 64) s += ld_sc1(ssq_at(P, idx, w) + wave);
@@ -375,7 +375,7 @@ __device__ __forceinline__ MbLds mb_lds(const KP &P, float *lds) {
 // finished by its operator's epilogue.
 __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int step, const int *toks, float *lds,
                                         const MbWaiter &wait) {
-  const int l = t.layer, op = t.op, tid = threadIdx.x, T = P.nthr, nw = P.nw, B = P.B;
+  const int l = t.layer, op = t.op, tid = tid_task(), T = P.nthr, nw = P.nw, B = P.B;
   const MbLds M = mb_lds(P, lds);
   const int nrg = rfl(mb_nrg(P, t));
   const int nb = min(nw, nrg <= 1 ? 1 : nrg <= 2 ? 2 : nrg <= 4 ? 4 : 8);  // row groups per batch
@@ -394,7 +394,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
   float sq4[4] = {0.f, 0.f, 0.f, 0.f};
   const bool early_ss = nidx >= 0 && P.W <= 256 && K <= P.mbst;  // staged inputs only
   auto load_ss = [&]() {
-    const int wave = wave_id(), lane = tid & 63;
+    const int wave = wave_task(), lane = tid & 63;
     if (early_ss && wave < B) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -402,7 +402,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
     }
   };
   auto fold_ss = [&]() {
-    const int wave = wave_id(), lane = tid & 63;
+    const int wave = wave_task(), lane = tid & 63;
     if (early_ss && wave < B) {
       const float s = wave_sum(sq4[0] + sq4[1] + sq4[2] + sq4[3]);
       if (lane == 0) M.rs[wave] = 1.0f / sqrtf(s / (float)K + P.eps);
@@ -529,7 +529,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
         break;
       }
       default: {  // OP_LM: wavefront b keeps sequence b's best
-        const int wave = wave_id(), lane = tid & 63;
+        const int wave = wave_task(), lane = tid & 63;
         if (wave < B) {
           const int b = wave;
           for (int e = lane; e < nb * 16; e += 64) {
@@ -547,7 +547,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
     __syncthreads();  // ys is rewritten by the next batch
   }
   if (op == OP_LM) {
-    const int wave = wave_id(), lane = tid & 63;
+    const int wave = wave_task(), lane = tid & 63;
     if (wave < B) {
       wave_argmax_l63(bv, bi);
       const bool wn = __any(nan);
@@ -566,7 +566,7 @@ __device__ __forceinline__ bool mb_gemm(const KP &P, const Task &t, int lam, int
 // first layer's attention-norm gains) for the first QKV stage, with their
 // sums of squares.
 __device__ __forceinline__ bool mb_embed(const KP &P, const Task &t, int lam, const int *toks, float *lds) {
-  const int tid = threadIdx.x, B = P.B;
+  const int tid = tid_task(), B = P.B;
   const MbLds M = mb_lds(P, lds);
   const uint16_t *gain = (const uint16_t *)P.layers[0].attn_norm;
   const int n8 = (t.r1 - t.r0) >> 3;
@@ -635,8 +635,8 @@ __device__ __forceinline__ void mb_attn_sub(const KP &P, int l, int lam, int b, 
   constexpr int PL = 16 / NQ;  // positions per K load
   constexpr int RA = 8;  // K loads in flight per wavefront
   constexpr uint32_t OOB = 0x80000000u;
-  const int G = P.G, tid = threadIdx.x, T = P.nthr;
-  const int wave = wave_id(), nw = P.nw, lane = tid & 63, ii = lane & 15, qg = lane >> 4;
+  const int G = P.G, tid = tid_task(), T = P.nthr;
+  const int wave = wave_task(), nw = P.nw, lane = tid & 63, ii = lane & 15, qg = lane >> 4;
   const int cpad = ((P.cmax + 63) / 64) * 64;
   float *qs = lds, *sc = qs + G * D, *ored = sc + G * cpad, *st = ored + nw * G * D;
   float *Or = st + 2 * G, *Mr = Or + G * D, *Lr = Mr + G;
@@ -884,7 +884,7 @@ __device__ __forceinline__ bool mb_attn(const KP &P, const Task &t, int lam, int
 // group; lane 0 packs the 8 outputs for the O projection.
 __device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, const int *toks, const MbWaiter &wait) {
   if (!wait(P)) return false;
-  const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = threadIdx.x;
+  const int g = t.aux, Tw = P.Tg, G = P.G, d = P.d, l = t.layer, tid = tid_task();
   const int *posv = toks + 8;
   const int rec = d + PREC_O, gd = G * d;
   const int ngr = (t.r1 - t.r0) >> 3, gpp = P.nthr >> 5;
@@ -943,7 +943,7 @@ __device__ __forceinline__ bool mb_comb(const KP &P, const Task &t, int step, co
 // Each sequence's greedy token from the W partials (wavefront b reads
 // sequence b's); toks[b] = -1 on NaN.
 __device__ __forceinline__ void mb_reduce(const KP &P, int *toks) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wave = wave_task(), lane = tid_task() & 63;
   __syncthreads();
   if (wave < P.B) {
     float bv = -INFINITY;
@@ -985,7 +985,7 @@ extern "C" __global__ void __launch_bounds__(512) pre_persistent_mb(KP P) {
   __shared__ int toks[32];
   const bool res = P.persistent != 0;
   const int lam = res ? lambda_of_block(blockIdx.x, P.W, P.X) : blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = tid_task();
   if (res && tid == 0) {
     const uint32_t x = xcc_id();
     P.xcc[lam] = x;
