@@ -220,7 +220,7 @@ def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps
     """Everything reported for one workload; returns (entry, weights)."""
     import torch
     w, m, W, bufs, eng, g0 = setup(workload, W, grid_wgs=args.grid, prefill=args.prefill,
-                                   attn_splits=args.attn_splits)
+                                   attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
     mb = m.batch > 1
     pos = list(w.contexts)
     K = args.steps if args.steps > 0 else w.steps
@@ -372,17 +372,19 @@ def measure_chunk(args, W):
 
 def tiny_grids(args, entry):
     """The tiny decoder's persistent µs/token at a few grid sizes (its
-    default grid is one XCD's 32 CUs)."""
+    default grid is one XCD's 32 CUs), and at the default grid with the down
+    projection run as a stage of its own (the default folds it into the
+    gate/up stage)."""
     import torch
     from persistent_resident_execution_amd import engine as E
     w, m, W, bufs, eng, g0 = setup("tiny")
     eng.close()
     pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
     res = {}
-    for grid in (8, 16, 64):
-        e2 = E.Engine(m, W, bufs[0], bufs[1], grid_wgs=grid, ctx_len=bufs[2])
+    for grid, fold in ((8, 0), (16, 0), (64, 0), (0, -1)):
+        e2 = E.Engine(m, W, bufs[0], bufs[1], grid_wgs=grid, ctx_len=bufs[2], fold_ffn=fold)
         t, _ = time_calls(e2, e2.decode, K, g0, pos, args.repeats, 8)
-        res[str(grid)] = round(statistics.median(t) / K * 1e6, 2)
+        res[str(grid) if grid else "32, down stage not folded"] = round(statistics.median(t) / K * 1e6, 2)
         e2.close()
     res["32 (default)"] = entry["value"]
     del eng, bufs, W
@@ -398,9 +400,9 @@ def phases(args):
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import profiling
     w, m, W, bufs, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill,
-                                   attn_splits=args.attn_splits)
+                                   attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
     pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
-    info, _ = E.plan_describe(m, grid_wgs=args.grid, attn_splits=args.attn_splits)
+    info, _ = E.plan_describe(m, grid_wgs=args.grid, attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
     nsi, nW = info.n_stage_inst, info.n_wgs
     tr = torch.zeros(K * nsi * nW * 8, dtype=torch.int32, device="cuda")
     eng.set_trace(tr)
@@ -478,6 +480,8 @@ def main():
                          "ring and write the per-stage wait/busy/phase summary to this file")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--attn-splits", type=int, default=0, help="attention chunks per KV head (0: default)")
+    ap.add_argument("--fold-ffn", type=int, default=0,
+                    help="0: fold the down projection into the gate/up stage where supported; -1: never")
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first copy this many MiB with the library's copy kernel (counter calibration)")

@@ -85,6 +85,13 @@ struct KP {
   int32_t *req_tok;      // workspace: the claimed request's prompt [max_ctx]
   int32_t ring_slots, ring_prompt, ring_out, ring_words;
   uint32_t idle_ticks;   // the loop ends after this long without a request
+  // folded FFN (resident kernel): the gate/up tasks leave the down
+  // projection's partials, the down stage is skipped
+  int32_t fold;
+  float *dpart;          // [L][W][h]
+  // attention folded into the output projection (resident kernel): the
+  // attention stage is skipped, every O-projection task attends itself
+  int32_t inl, aoff;     // on; LDS float offset of the attention's scratch
 };
 
 
@@ -384,6 +391,64 @@ __device__ __forceinline__ float norm_scale(const KP &P, const float *red, int K
 #pragma unroll
   for (int w = 0; w < MAXW; ++w) tot += rw[w];
   return 1.0f / sqrtf(tot / (float)K + P.eps);
+}
+
+// Staging of the folded FFN's consumers (the next layer's QKV stage, the LM
+// head): x = base + the np partials of the down projection (vectors of K
+// floats, np <= 32), times the gains, RMSNorm folded as in stage_vec.  The 8
+// lanes of a group share one float4 slot: lane j adds partials j, j + 8, ...
+// (lane 0 starts from the base), the group's sums meet by a butterfly over
+// the 8 lanes (the same order on every run), and lane 0 writes the slot.
+// Float4s [d0, d1) of x (before the gains) also go to dump and, if given,
+// dump2.  All loads of a round are in flight together: one device round
+// trip for up to 32 partials.  Ends with a barrier.
+__device__ __forceinline__ void stage_fold(const KP &P, float *xs, float *red, const float *base,
+                                           const float *parts, int np, const uint16_t *gain, float *dump,
+                                           float *dump2, int d0, int d1, int K, int Kpad) {
+  const int tid = threadIdx.x, T = P.nthr, n4 = K >> 2, j = tid & 7, per = T >> 3;
+  constexpr uint32_t OOB = 0x80000000u;
+  const Rsrc rb = mkbuf(uni_ptr(base), (uint32_t)K * 4);
+  const Rsrc rp = mkbuf(uni_ptr(parts), (uint32_t)np * K * 4);
+  const Rsrc rg = mkbuf(uni_ptr(gain), (uint32_t)K * 2);
+  const Rsrc rd = mkbuf(uni_ptr(dump), dump ? (uint32_t)K * 4 : 0u);
+  const Rsrc rd2 = mkbuf(uni_ptr(dump2), dump2 ? (uint32_t)K * 4 : 0u);
+  float ss = 0.f;
+  for (int i0 = 0; i0 < n4; i0 += per) {
+    const int i = i0 + (tid >> 3);
+    const bool in = i < n4;
+    v4i a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = j + 8 * k;
+      a[k] = ld128<CP_SC1>(rp, in && p < np ? (uint32_t)(p * K + 4 * i) * 4 : OOB);
+    }
+    const v4i b = ld128<CP_SC1>(rb, in && j == 0 ? (uint32_t)i * 16 : OOB);
+    const v2i g = ld64<CP_DEF>(rg, in && j == 0 ? (uint32_t)i * 8 : OOB);
+    float4 f = __builtin_bit_cast(float4, b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 q = __builtin_bit_cast(float4, a[k]);
+      f.x += q.x; f.y += q.y; f.z += q.z; f.w += q.w;
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      f.x += __shfl_xor(f.x, m); f.y += __shfl_xor(f.y, m);
+      f.z += __shfl_xor(f.z, m); f.w += __shfl_xor(f.w, m);
+    }
+    if (in && j == 0) {
+      reinterpret_cast<float4 *>(xs)[i] = float4{f.x * bf_lo(g.x), f.y * bf_hi(g.x), f.z * bf_lo(g.y), f.w * bf_hi(g.y)};
+      ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
+      ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
+      if (i >= d0 && i < d1) {
+        if (dump) st_out128(P, rd, (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
+        if (dump2) st_out128(P, rd2, (uint32_t)i * 16, __builtin_bit_cast(v4i, f));
+      }
+    }
+  }
+  for (int i = K + tid; i < Kpad; i += T) xs[i] = 0.f;
+  const float w = wave_sum2_l63(ss, 0.f).x;
+  if ((tid & 63) == 63) red[wave_id()] = w;
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -1053,6 +1118,18 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     cos0 = P.rope[(int64_t)pos * half + j];
     sin0 = P.rope[(int64_t)P.max_ctx * half + (int64_t)pos * half + j];
   }
+  // folded FFN: this thread's Wd weights for the gate/up task's partial of
+  // the down projection (row tid, the task's columns in 16-byte units; a
+  // unit's columns past the task's are not used), fetched before the wait
+  const bool fold = !FP8 && P.fold && op == OP_GU;
+  v4i wdv[FOLD_U];
+  if (fold) {
+    const Rsrc rw = mkbuf(uni_ptr(P.layers[l].wd), (uint32_t)P.h * P.ffn * 2);
+#pragma unroll
+    for (int u = 0; u < FOLD_U; ++u)
+      wdv[u] = ld128<CP_DEF>(rw, tid < P.h && 8 * u < rows ? (uint32_t)((int64_t)tid * P.ffn + t.r0 + 8 * u) * 2
+                                                          : 0x80000000u);
+  }
   if (known && !wait(P)) {
     __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outlives the task
     return false;
@@ -1060,9 +1137,10 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   bool normed = false;  // RMSNorm folded into the staging: results scale by norm_scale
   int Kst = 0;
   if (op == OP_OPROJ) {
-    // combine into xs[0..K) and zero the padding of the last chunk
+    // combine into xs[0..K) and zero the padding of the last chunk (with the
+    // attention folded in, xs already holds the head group's output)
     const int Kp = (G.K + 511) & ~511;
-    attn_combine(P, l, t.aux, M.xs);
+    if (!P.inl) attn_combine(P, l, t.aux, M.xs);
     for (int i = G.K + tid; i < Kp; i += P.nthr) M.xs[i] = 0.f;
     __syncthreads();
   } else if (late) {
@@ -1119,7 +1197,19 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       K = P.F;
     } else if (P.persistent) {
       const DevLayer &Lw = P.layers[l];
-      if (op == OP_QKV) {
+      if (P.fold && (op == OP_LM || (op == OP_QKV && l > 0))) {
+        // folded FFN: the previous layer's output is its post-attention
+        // residual plus the gate/up tasks' partials of the down projection,
+        // summed here; this task's share of it is kept (the next gate/up
+        // stage's residual, the checked hidden state)
+        const int lp = op == OP_LM ? P.L - 1 : l - 1, n4 = P.h >> 2;
+        float *hid = (op == OP_LM && P.chk_hidden) ? P.chk_hidden + (int64_t)step * P.B * P.h : nullptr;
+        stage_fold(P, M.xs, M.red, P.xmid + vec_off(P, lp, 0, P.h), P.dpart + (int64_t)lp * P.W * P.h, P.W,
+                   op == OP_LM ? P.final_norm : (const uint16_t *)Lw.attn_norm, P.x_out + vec_off(P, lp, 0, P.h),
+                   hid, (int)((int64_t)n4 * lam / P.W), (int)((int64_t)n4 * (lam + 1) / P.W), K,
+                   min(P.kmax, (K + 1023) & ~1023));
+        src.f32 = nullptr;
+      } else if (op == OP_QKV) {
         src = layer_input(P, l, tok, (const uint16_t *)Lw.attn_norm);
       } else if (op == OP_LM) {
         src = Src{P.x_out + vec_off(P, P.L - 1, 0, P.h), nullptr, nullptr, 0, 0, P.final_norm};
@@ -1128,7 +1218,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
         src = Src{P.xmid + vec_off(P, l, 0, P.h), nullptr, nullptr, 0, 0, (const uint16_t *)Lw.ffn_norm};
       } else {
         src = mid_input(P, l, tok, (const uint16_t *)Lw.ffn_norm);
-        if (op == OP_ROUTER) {  // sum the residual once for the expert stages: this task's share
+        if (op == OP_ROUTER || fold) {  // sum the residual once for the expert stages (folded FFN: for
+                                        // the next layer's input): this task's share
           const int n4 = P.h >> 2;
           src.dump = P.xmid + vec_off(P, l, 0, P.h);
           src.d0 = (int)((int64_t)n4 * lam / P.W);
@@ -1138,8 +1229,12 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     }
     // zero padding up to what the stream reads: whole 512-column chunks
     // (fp8 expert slots start at their own offsets: up to kmax)
-    stage_vec(P, M.xs, M.red, src, K, FP8 ? P.kmax : min(P.kmax, (K + 1023) & ~1023));
-    normed = src.gain != nullptr;
+    if (src.f32 || src.bf16) {
+      stage_vec(P, M.xs, M.red, src, K, FP8 ? P.kmax : min(P.kmax, (K + 1023) & ~1023));
+      normed = src.gain != nullptr;
+    } else {
+      normed = true;  // staged by stage_fold
+    }
     Kst = K;
   }
   wait.mark(0);
@@ -1213,8 +1308,29 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     }
     case OP_GU: {
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
-      for (int i = tid; i < rows; i += P.nthr)
-        st_out(P, u + i, silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw)));
+      for (int i = tid; i < rows; i += P.nthr) {
+        const float v = silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw));
+        st_out(P, u + i, v);
+        if (fold) M.xs[i] = v;  // (every wavefront is past the stream: xs is free)
+      }
+      if (fold) {
+        // the down projection's partial over this task's columns: row tid of
+        // Wd times u[r0 .. r1), in column order
+        __syncthreads();
+        if (tid < P.h) {
+          float y = 0.f;
+#pragma unroll
+          for (int u = 0; u < FOLD_U; ++u) {
+            const int w4[4] = {wdv[u].x, wdv[u].y, wdv[u].z, wdv[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int c = 8 * u + e;
+              if (c < rows) y = fmaf((e & 1) ? bf_hi(w4[e >> 1]) : bf_lo(w4[e >> 1]), M.xs[c], y);
+            }
+          }
+          st_out(P, P.dpart + ((int64_t)l * P.W + lam) * P.h + tid, y);
+        }
+      }
       return true;
     }
     case OP_DOWN: {
@@ -1618,14 +1734,17 @@ __device__ __forceinline__ bool attn_core(const KP &P, int l, int b, int g, int 
 // One attention chunk task: chunk c of NC of (sequence b, KV head g)'s
 // positions, all G query heads, on the matrix cores; the record (m, l, -, -,
 // o[d]) per head goes to the O-projection task's combine.
+// xo != NULL (the attention folded into the output projection): one piece
+// over every position, its normalised output o / l per head written to xo
+// (LDS) instead of a record.
 template <bool KV8>
 __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, float *lds,
-                                           const Waiter &wait) {
+                                           const Waiter &wait, float *xo = nullptr) {
   const int l = t.layer, bg = t.aux, b = bg / P.Hkv, g = bg % P.Hkv, c = t.r0, NC = t.r1;
   const int G = P.G, d = P.d, tid = threadIdx.x, T = P.nthr, nw = P.nw;
   const int n = pos + 1, C = (n + NC - 1) / NC, t0 = c * C;
   const int cnt = max(0, min(n, t0 + C) - t0);
-  const int cpad = ((P.cmax + 63) / 64) * 64;
+  const int cpad = (((xo ? P.max_ctx : P.cmax) + 63) / 64) * 64;
   float *qs = lds, *sc = qs + G * d, *ored = sc + G * cpad, *st = ored + nw * G * d;
   // fp8 cache: the piece's row scales, and the newest row's codes (K then V)
   float *ksl = st + 4 * G, *vsl = ksl + cpad;
@@ -1643,6 +1762,20 @@ __device__ __forceinline__ bool attn_chunk(const KP &P, const Task &t, int pos, 
              ? attn_core<4, 1, true, false>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait)
              : attn_core<4, 2, true, false>(P, l, b, g, t0, cnt, pos, sc, cpad, ored, st, ksl, vsl, nrow, &wait);
   if (!ok) return false;
+  if (xo) {
+    for (int i = tid; i < G * d; i += T) {
+      const int hh = i / d, j = i % d;
+      float s = 0.f;
+      float ov[MAXW];
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) ov[w] = w < nw ? ored[(w * G + hh) * d + j] : 0.f;
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) s += ov[w];
+      xo[i] = s / st[2 * hh + 1];
+    }
+    __syncthreads();
+    return true;
+  }
   const int rec = d + PREC_O;
   float *pdst = P.part + ((((int64_t)l * P.B + b) * P.Hkv + g) * NC + c) * G * rec;
   for (int i = tid; i < G * d; i += T) {
@@ -1713,13 +1846,50 @@ template <bool KV8>
 __device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int pos, int tok, float *lds,
                                          const Waiter &wait) {
   const KP &P = kp_fresh();
-  switch (t.op) {
-    case OP_NONE: return true;
-    case OP_ATTN: return attn_chunk<KV8>(P, t, pos, lds, wait);
-    case OP_EGU:
-    case OP_EDOWN: return task_gemv<true>(P, t, lam, step, pos, tok, lds, wait);
-    default: return task_gemv<false>(P, t, lam, step, pos, tok, lds, wait);
+  if (t.op == OP_NONE) return true;
+  // attention folded into the output projection: the task's KV head over
+  // every position (its wait is the head's QKV producers), the output
+  // straight into the projection's staged input, then the projection with
+  // nothing left to wait for
+  const bool inl = !KV8 && P.inl && t.op == OP_OPROJ;
+  if (t.op == OP_ATTN || inl) {
+    Task a = t;
+    if (inl) { a.r0 = 0; a.r1 = 1; }
+    if (!attn_chunk<KV8>(P, a, pos, inl ? lds + P.aoff : lds, wait, inl ? lds + P.xsoff : nullptr)) return false;
+    if (!inl) return true;
   }
+  if (t.op == OP_EGU || t.op == OP_EDOWN) return task_gemv<true>(P, t, lam, step, pos, tok, lds, wait);
+  Waiter w = wait;
+  if (inl) w.lo = w.hi;
+  return task_gemv<false>(P, t, lam, step, pos, tok, lds, w);
+}
+
+// The folded stages of the resident kernel.  The folded FFN: the down
+// stage's tasks are skipped,
+// and the stages that waited for them (the next layer's QKV, the LM head)
+// wait for the gate/up stage of the same layer instead -- the stage right
+// before, whose tasks now leave the down projection's partials.  False: skip
+// the task.
+// With the attention folded into the output projection, the attention
+// stage's tasks are skipped and each O-projection task waits for what the
+// first attention task of its (sequence, KV head) would have: that head's
+// QKV producers.
+__device__ __forceinline__ bool fold_task(const KP &P, Task &t, int si) {
+  if (P.inl) {
+    if (t.op == OP_ATTN) return false;
+    if (t.op == OP_OPROJ) {
+      const Task a = P.tasks[(int64_t)(si - 1) * P.W + t.aux * P.Tg];
+      t.wait_lo = a.wait_lo;
+      t.wait_hi = a.wait_hi;
+    }
+  }
+  if (!P.fold) return true;
+  if (t.op == OP_DOWN) return false;
+  if ((t.op == OP_QKV && t.layer > 0) || t.op == OP_LM) {
+    t.wait_lo -= P.W;
+    t.wait_hi -= P.W;
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1768,8 +1938,8 @@ __device__ __forceinline__ void resident_body(KP &P) {
       if (!token_ok(P, tok, s)) return;
     }
     for (int si = si0; si < si1; ++si) {
-      const Task t = P.tasks[(int64_t)si * P.W + lam];
-      if (t.op == OP_NONE) continue;
+      Task t = P.tasks[(int64_t)si * P.W + lam];
+      if (t.op == OP_NONE || !fold_task(P, t, si)) continue;
       const int tr = res && P.trace != nullptr;
       const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
       const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
@@ -2288,6 +2458,10 @@ static void fill_kp_dims(const pre_engine *e, const Dims &D, const Layout &Lo, c
   P.persistent = persistent;
   P.local = D.local;
   P.onexcd = persistent ? D.onexcd : 0;  // the per-operator launches spread over every XCD
+  P.fold = persistent ? D.fold : 0;      // the per-operator path runs the down stage
+  P.dpart = D.fold ? (float *)(ws + Lo.dpart) : nullptr;
+  P.inl = persistent ? D.inl : 0;        // the per-operator path runs the attention stage
+  P.aoff = D.aoff;
 }
 
 static int check_call(const pre_engine *e, int32_t n_steps, const int32_t *d_in, const int32_t *d_forced,

@@ -18,6 +18,7 @@ namespace pre {
 static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 static int32_t pad_to(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
 static int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+static inline void split(int64_t n, int W, int t, int32_t *lo, int32_t *hi);
 
 int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   if (!c || !D) return PRE_ERR_ARG;
@@ -105,6 +106,23 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // micro-batch: wavefronts split a batch's row groups evenly (a power of
   // two), and the LM head keeps one wavefront per sequence
   if (mb && ((D->threads & (D->threads - 1)) || D->threads < 64 * D->B)) return PRE_ERR_SHAPE;
+  // Folded FFN (small one-XCD dense engines, resident kernel only): each
+  // gate/up task also forms its slice's partial of the down projection, so
+  // the down stage and its hand-off drop out.  Thread t of the task holds
+  // row t of Wd's columns [r0, r1) in registers, in 16-byte units (so r0 is
+  // a multiple of 8 and there are at most FOLD_U units); every workgroup
+  // must produce QKV pairs, so that the output projection's waits cover
+  // every workgroup's share of the residual it writes while staging.
+  if (c->fold_ffn >= 0 && !moe && !mb && D->onexcd && D->h <= D->threads && D->qkv_pairs >= D->W &&
+      D->W <= 32) {
+    bool ok = true;
+    for (int lam = 0; lam < D->W && ok; ++lam) {
+      int32_t r0, r1;
+      split(D->ffn, D->W, lam, &r0, &r1);
+      ok = r0 % 8 == 0 && r1 - r0 <= 8 * FOLD_U;
+    }
+    D->fold = ok;
+  }
   D->stages_per_layer = (moe || mb) ? 6 : 5;
   // micro-batch: an embedding stage first, then per layer QKV, ATTN, COMB,
   // OPROJ, GU, DOWN, then the LM head
@@ -157,7 +175,21 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // what the CU's 160 KB leave; the workgroup then takes all of them.  Not
   // on one XCD, where the streams are short and the hand-offs' latency is
   // the whole cost.
-  const int64_t base = std::max(gemv, attn);
+  int64_t base = std::max(gemv, attn);
+  // Attention folded into the output projection (small one-XCD batch-1
+  // engines, bf16 cache, resident kernel only): each O-projection task runs
+  // its KV head's attention over every position before its own stream, with
+  // the scores of the whole context in LDS past the staged input.
+  if (c->fold_attn >= 0 && !mb && !D->kv8 && D->B == 1 && D->onexcd) {
+    const int64_t aoff = pad_to(D->xsoff + (int64_t)D->kmax, 64);
+    const int64_t need = (int64_t)D->G * D->d + (int64_t)D->G * pad_to(D->max_ctx, 64) +
+                         (int64_t)waves * D->G * D->d + 4 * D->G + 256;
+    if ((aoff + need) * 4 <= 150 * 1024) {
+      D->inl = 1;
+      D->aoff = (int32_t)aoff;
+      base = std::max(base, aoff + need);
+    }
+  }
   D->npre = (mb || D->onexcd) ? 0 : PRE_UNITS;
   // (1 KB of the 160 KB stays for the kernels' static LDS)
   D->lds_bytes = (int32_t)((D->npre ? std::max<int64_t>(base, 40704) : base) * 4);
@@ -192,6 +224,7 @@ void build_layout(const Dims &D, Layout *Lo) {
   Lo->cmd = take(64);
   Lo->req = take((int64_t)D.max_ctx * 4);
   Lo->kvnew = D.kv8 ? take((int64_t)D.L * D.B * 2 * D.Hkv * D.d * f) : 0;
+  Lo->dpart = D.fold ? take((int64_t)D.L * D.W * D.h * f) : 0;
   if (D.mb) {
     // packed bf16 hi/lo GEMM inputs: 4 KB per 128 columns (whole steps, the
     // tail left zero); per layer the QKV input (plus the LM head's), the
@@ -647,6 +680,8 @@ extern "C" int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int3
   out->attn_splits = D.NC;
   out->validator = pre::validate(D, T);
   out->xcd_local = D.local ? 1 : D.onexcd ? 2 : 0;
+  out->fold_ffn = D.fold;
+  out->fold_attn = D.inl;
   out->workspace_bytes = Lo.total;
   if (h_tasks)
     for (int32_t i = 0; i < max_tasks && i < (int32_t)T.size(); ++i)

@@ -27,6 +27,10 @@ namespace pre {
 #define PRE_UNITS 4
 #endif
 
+// Folded FFN: most 16-byte units of Wd (8 columns each) one thread of a
+// gate/up task holds for its row of the down projection's partial.
+#define FOLD_U 4
+
 enum Op : int32_t {
   OP_NONE = 0,
   OP_QKV = 1,    // RMSNorm-folded QKV rows (RoPE pairs), K/V append
@@ -77,6 +81,7 @@ struct Layout {
   int64_t ctx;      // the engine's own position array [B] (used when the caller passes none)
   int64_t cmd, req;  // serving loop: the scheduler's command words, the claimed prompt [max_ctx]
   int64_t kvnew;     // fp8 cache: the step's new K and V rows in fp32 [L][B][2][Hkv][d]
+  int64_t dpart;     // folded FFN: each gate/up task's partial of the down projection [L][W][h]
   int64_t total;
 };
 
@@ -103,6 +108,9 @@ struct Dims {
   int32_t cmax;       // longest attention chunk (positions; micro-batch: longest piece of one workgroup)
   int32_t lds_bytes;  // dynamic LDS per workgroup
   int32_t kv8;        // fp8 e4m3 K/V cache with an fp32 scale per cached row
+  int32_t fold;       // resident kernel: the down projection folded into the gate/up stage
+  int32_t inl;        // resident kernel: each O-projection task computes its head's attention itself
+  int32_t aoff;       // inline attention: LDS float offset of its scratch (past the staged input)
   float eps, theta;
 };
 

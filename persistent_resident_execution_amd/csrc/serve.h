@@ -201,8 +201,8 @@ __device__ __forceinline__ void serve_body(KP &P) {
       const uint32_t ep = ep_base + (uint32_t)s + 1u;
       const int pos = pos0 + s;
       for (int si = 0; si < Q.n_si && alive; ++si) {
-        const Task t = Q.tasks[(int64_t)si * Q.W + lam];
-        if (t.op == OP_NONE) continue;
+        Task t = Q.tasks[(int64_t)si * Q.W + lam];
+        if (t.op == OP_NONE || !fold_task(Q, t, si)) continue;
         const Waiter wait{1, t.wait_lo, t.wait_hi, s, si, ep, sh, 0};
         if (!run_task<KV8>(t, lam, s, pos, tok, lds, wait)) { alive = false; break; }
         const KP &R = kp_fresh();

@@ -36,7 +36,8 @@ class Config(C.Structure):
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "batch", "max_ctx")] + [("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [
         (n, C.c_int32) for n in ("n_experts", "top_k", "n_shared", "expert_ffn", "expert_dtype",
-                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local", "chunk", "kv_dtype")]
+                                 "grid_wgs", "wg_threads", "attn_splits", "xcd_local", "chunk", "kv_dtype",
+                                 "fold_ffn", "fold_attn")]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd", "router",
@@ -73,7 +74,8 @@ class ServeStats(C.Structure):
 
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_stage_inst", "n_wgs", "n_slots", "n_tasks",
-                                         "attn_splits", "validator", "xcd_local")] + [
+                                         "attn_splits", "validator", "xcd_local", "fold_ffn",
+                                         "fold_attn")] + [
         ("workspace_bytes", C.c_int64)]
 
 
@@ -133,7 +135,8 @@ def lib():
     return _lib
 
 
-def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, xcd_local=0, chunk=0) -> Config:
+def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, xcd_local=0, chunk=0,
+                fold_ffn=0, fold_attn=0) -> Config:
     c = Config()
     for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
               "batch", "max_ctx", "n_experts", "top_k", "n_shared", "expert_ffn"):
@@ -145,6 +148,8 @@ def make_config(m: synth.ModelConfig, grid_wgs=0, wg_threads=0, attn_splits=0, x
     c.xcd_local = int(xcd_local)
     c.chunk = int(chunk)
     c.kv_dtype = 1 if getattr(m, "kv_fp8", False) else 0
+    c.fold_ffn = int(fold_ffn)
+    c.fold_attn = int(fold_attn)
     return c
 
 
@@ -292,10 +297,15 @@ class Engine:
 
     def __init__(self, m: synth.ModelConfig, weights: dict, k_cache, v_cache, grid_wgs=0,
                  wg_threads=0, attn_splits=0, stream=None, xcd_local=0, ctx_len=None,
-                 static_workspace=False, chunk=0, k_scale=None, v_scale=None):
+                 static_workspace=False, chunk=0, k_scale=None, v_scale=None, fold_ffn=0,
+                 fold_attn=0):
         """static_workspace: create with pre_engine_create_static (the
         library's static device workspace; no allocation) instead of a
-        workspace tensor."""
+        workspace tensor.  fold_ffn: 0 = fold the down projection into the
+        gate/up stage where the engine supports it (small one-XCD dense
+        models), -1 = never.  fold_attn: 0 = each output-projection task
+        computes its KV head's attention itself where supported (small
+        one-XCD batch-1 engines, bf16 cache), -1 = never."""
         self.m = m
         self.h = None
         check_model_args(m, weights, k_cache, v_cache, ctx_len, k_scale=k_scale, v_scale=v_scale)
@@ -303,7 +313,7 @@ class Engine:
         for t in [weights["embed"], v_cache] + ([ctx_len] if ctx_len is not None else []):
             _need(t.device == dev, f"every tensor must be on {dev}, found one on {t.device}")
         self.device = dev
-        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local, chunk)
+        self.cfg = make_config(m, grid_wgs, wg_threads, attn_splits, xcd_local, chunk, fold_ffn, fold_attn)
         self.chunk = int(chunk)
         L = lib()
         nbytes = C.c_size_t()

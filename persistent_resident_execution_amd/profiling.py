@@ -260,8 +260,13 @@ def phase_table(rec, stage_names, n_layers, stages_per_layer, first, phases=None
             pm = np.mean(np.array(ph), axis=0) / 100.0
             line += "  | " + "  ".join(f"{n} {v:.2f}" for (n, _), v in zip(phases[nm], pm))
         lines.append(line)
-    # d[j]: latest end of stage instance j + 1 minus that of instance j
+    # d[j]: latest end of stage instance j + 1 minus that of instance j (a
+    # stage that ran no task -- the down stage of a folded FFN -- ends where
+    # the one before it did, so its delta is 0)
     ends = np.array([[a[s, si][:, 3].max() for si in range(nsi)] for s in range(1, steps)], dtype=np.float64)
+    for j in range(1, nsi):
+        empty = ends[:, j] == 0
+        ends[empty, j] = ends[empty, j - 1]
     d = np.diff(ends, axis=1).mean(axis=0) / 100.0
     per = []
     for k in range(stages_per_layer):

@@ -146,6 +146,24 @@ def test_persistent_equals_baseline_tokens(tiny):
     assert np.max(np.abs(l1 - l2)) < 1e-3
 
 
+@pytest.mark.parametrize("fold_ffn,fold_attn", [(0, 0), (0, -1), (-1, 0)])
+def test_tiny_folded_stages_match_unfolded(tiny, fold_ffn, fold_attn):
+    """The tiny engine can fold the down projection into the gate/up stage
+    (per-workgroup partials added by the next stage) and the attention into
+    the output projection (every O-projection task attends its KV head over
+    all positions).  Against the resident kernel with neither: both streams
+    follow the oracle (64 steps, logits and hidden state), the tokens agree,
+    and the logits differ only by the order of additions."""
+    S, prompt, ref = tiny
+    _say(f"[test] tiny folded stages fold_ffn={fold_ffn} fold_attn={fold_attn} vs neither")
+    info, _ = E.plan_describe(S.m, fold_ffn=fold_ffn, fold_attn=fold_attn)
+    assert (info.fold_ffn, info.fold_attn) == (int(fold_ffn == 0), int(fold_attn == 0))
+    _, t1, l1 = _check_run(S, prompt, ref, baseline=False, fold_ffn=fold_ffn, fold_attn=fold_attn)
+    _, t2, l2 = _check_run(S, prompt, ref, baseline=False, fold_ffn=-1, fold_attn=-1)
+    assert np.array_equal(t1, t2)
+    assert np.max(np.abs(l1 - l2)) < 1e-3
+
+
 def test_bad_token_is_latched_and_reset_clears_it(tiny):
     S, _, _ = tiny
     _say("[test] out-of-range token -> device error, reset")

@@ -6,6 +6,8 @@ independent count from the shapes."""
 import os
 import re
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -269,6 +271,48 @@ def test_xcd_local_mode_only_where_each_head_fits_one_xcd(lib, m, grid, flag, wa
                 if op == 0 or lo >= hi or k == 0:
                     continue
                 assert all((s % W) // per == lam // per for s in range(lo, hi)), (layer, k, lam)
+
+
+@pytest.mark.parametrize("m,kw,want", [
+    (synth.TINY, {}, 1), (synth.TINY, {"fold_ffn": -1}, 0), (synth.TINY, {"xcd_local": -1}, 0),
+    (synth.TINY, {"grid_wgs": 64}, 0), (synth.TINY, {"grid_wgs": 16}, 0), (synth.TINY, {"grid_wgs": 24}, 1),
+    (synth.DENSE8B, {}, 0), (synth.MOE, {}, 0), (synth.SMALL_MB, {}, 0), (synth.SMALL_GQA8, {"grid_wgs": 12}, 0)],
+    ids=lambda v: str(getattr(v, "name", v)))
+def test_ffn_fold_only_on_small_one_xcd_dense_engines(lib, m, kw, want):
+    """The down projection is folded into the gate/up stage only for batch-1
+    dense engines on one XCD whose hidden size fits the workgroup (one Wd row
+    per thread) and whose gate/up tasks start at a multiple of 8 rows and hold
+    at most 32 (tiny at its default 32 workgroups: 24; at 24 workgroups 32;
+    at 16 workgroups 48 do not fit; hidden 640 does not fit 512 threads).
+    The task table stays the unfolded one (the per-operator path runs it as
+    it is), and the workspace gains the partials [L][W][hidden]."""
+    info, _ = E.plan_describe(m, **kw)
+    assert info.fold_ffn == want
+    assert info.validator == 0
+    if want:
+        off, _ = E.plan_describe(m, **dict(kw, fold_ffn=-1))
+        assert off.fold_ffn == 0 and off.n_tasks == info.n_tasks
+        assert info.workspace_bytes - off.workspace_bytes >= m.n_layers * info.n_wgs * m.hidden * 4
+
+
+@pytest.mark.parametrize("m,kw,want", [
+    (synth.TINY, {}, 1), (synth.TINY, {"fold_attn": -1}, 0), (synth.TINY, {"xcd_local": -1}, 0),
+    (synth.TINY, {"grid_wgs": 64}, 0), (synth.TINY, {"grid_wgs": 16}, 1), (synth.SMALL_DENSE, {}, 0),
+    (synth.SMALL_DENSE, {"grid_wgs": 16, "wg_threads": 256}, 1), (synth.SMALL_MHA, {}, 1),
+    (replace(synth.TINY, kv_fp8=True), {}, 0), (replace(synth.TINY, max_ctx=32768), {}, 0),
+    (synth.DENSE8B, {}, 0), (synth.MOE, {}, 0), (synth.SMALL_MB, {}, 0)],
+    ids=lambda v: str(getattr(v, "name", v)))
+def test_attention_fold_only_on_small_one_xcd_bf16_engines(lib, m, kw, want):
+    """Each output-projection task attends itself (the attention stage is
+    skipped) only in batch-1 engines on one XCD with a bf16 cache whose whole
+    context's scores fit the LDS; the table keeps its attention stage for
+    the per-operator path."""
+    info, T = E.plan_describe(m, with_tasks=True, **kw)
+    assert info.fold_attn == want
+    assert info.validator == 0
+    if want:
+        W = info.n_wgs
+        assert (T[W:2 * W, 0] != 0).any()  # the attention stage is still in the table
 
 
 def test_kv_descriptor_size_bound(lib):
