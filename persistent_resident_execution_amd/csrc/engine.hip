@@ -1320,8 +1320,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       float *u = P.u + vec_off(P, l, 0, P.F) + t.r0;
       for (int i = tid; i < rows; i += P.nthr) {
         const float v = silu(rs * ys_get(ys, i, 0, nw)) * (rs * ys_get(ys, i, 1, nw));
-        st_out(P, u + i, v);
-        if (fold) M.xs[i] = v;  // (every wavefront is past the stream: xs is free)
+        if (fold) M.xs[i] = v;  // (every wavefront is past the stream: xs is free; u has no reader)
+        else st_out(P, u + i, v);
       }
       if (fold) {
         // the down projection's partial over this task's columns: row tid of
