@@ -301,15 +301,9 @@ constexpr int PREC_O = 4;    // attention chunk record: m, l, two unused words, 
 // results by norm_scale() -- W (x * g) / rms(x) equals W (x * g / rms(x)) --
 // so staging needs neither a second pass nor a barrier before it.  The gains
 // are fetched together with the data: staging costs one device round trip.
-// rot: the workgroup's starting point in the vector (float4s are visited
-// from slot (rot * 64) mod n4 on, wrapping), so the workgroups that stage
-// the same vector at once start on different cache lines; the sums per
-// element are the same.
 __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, const Src &s, int K,
-                                          int Kpad, int rot = 0) {
+                                          int Kpad) {
   const int tid = threadIdx.x, T = P.nthr, n4 = K >> 2;
-  const int r0 = (int)(((uint32_t)rot * 64u) % (uint32_t)max(n4, 1));
-  auto slot = [&](int i) { const int v = i + r0; return v >= n4 ? v - n4 : v; };  // i < n4
   float ss = 0.f;
   const Rsrc rg = mkbuf(uni_ptr(s.gain), s.gain ? (uint32_t)K * 2 : 0u);
   auto scaled = [](float4 f, v2i g) {
@@ -325,16 +319,15 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
         a[j] = v4i{0, 0, 0, 0};
         g[j] = v2i{0, 0};
         if (i + j * T < n4) {
-          const int q = slot(i + j * T);
-          a[j] = ld128<CP_SC1>(r, (uint32_t)q * 16);
-          if (s.gain) g[j] = ld64<CP_DEF>(rg, (uint32_t)q * 8);
+          a[j] = ld128<CP_SC1>(r, (uint32_t)(i + j * T) * 16);
+          if (s.gain) g[j] = ld64<CP_DEF>(rg, (uint32_t)(i + j * T) * 8);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (i + j * T < n4) {
           const float4 f = __builtin_bit_cast(float4, a[j]);
-          reinterpret_cast<float4 *>(xs)[slot(i + j * T)] = s.gain ? scaled(f, g[j]) : f;
+          reinterpret_cast<float4 *>(xs)[i + j * T] = s.gain ? scaled(f, g[j]) : f;
           ss = fmaf(f.x, f.x, ss); ss = fmaf(f.y, f.y, ss);
           ss = fmaf(f.z, f.z, ss); ss = fmaf(f.w, f.w, ss);
         }
@@ -349,8 +342,7 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
       v2i g[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        // past n4 the buffers return 0 (slots past the input keep their index)
-        const int i = i0 + k * T < n4 ? slot(i0 + k * T) : i0 + k * T;
+        const int i = i0 + k * T;  // past n4 the buffers return 0
 #pragma unroll
         for (int p = 0; p < MAXPARTS; ++p)
           if (p < s.nparts) pv[k][p] = ld128<CP_SC1>(rp, (uint32_t)(p * s.pstride + 4 * i) * 4);
@@ -364,8 +356,8 @@ __device__ __forceinline__ void stage_vec(const KP &P, float *xs, float *red, co
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        if (i0 + k * T >= n4) break;
-        const int i = slot(i0 + k * T);
+        const int i = i0 + k * T;
+        if (i >= n4) break;
         float4 f = __builtin_bit_cast(float4, bv[k]);
 #pragma unroll
         for (int p = 0; p < MAXPARTS; ++p)
@@ -1071,7 +1063,9 @@ __device__ __forceinline__ void attn_combine(const KP &P, int l, int bg, float *
 //   LM     LM-head rows; epilogue: logits (check mode) and the task's
 //          (max, lowest index) partial, NaN if any logit is NaN
 
-template <bool FP8>
+// SM: the small-model kernel, which can fold stages (the large models'
+// kernels are compiled without that code).
+template <bool FP8, bool SM>
 __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, int step, int pos, int tok,
                                           float *lds, const Waiter &wait) {
   const int l = t.layer, rows = t.r1 - t.r0, tid = threadIdx.x, nw = P.nw, op = t.op;
@@ -1129,7 +1123,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
   // folded FFN: this thread's Wd weights for the gate/up task's partial of
   // the down projection (row tid, the task's columns in 16-byte units; a
   // unit's columns past the task's are not used), fetched before the wait
-  const bool fold = !FP8 && P.fold && op == OP_GU;
+  const bool fold = SM && !FP8 && P.fold && op == OP_GU;
   v4i wdv[FOLD_U];
   if (fold) {
     const Rsrc rw = mkbuf(uni_ptr(P.layers[l].wd), (uint32_t)P.h * P.ffn * 2);
@@ -1148,7 +1142,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     // combine into xs[0..K) and zero the padding of the last chunk (with the
     // attention folded in, xs already holds the head group's output)
     const int Kp = (G.K + 511) & ~511;
-    if (!P.inl) attn_combine(P, l, t.aux, M.xs);
+    if (!(SM && P.inl)) attn_combine(P, l, t.aux, M.xs);
     for (int i = G.K + tid; i < Kp; i += P.nthr) M.xs[i] = 0.f;
     __syncthreads();
   } else if (late) {
@@ -1205,7 +1199,7 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
       K = P.F;
     } else if (P.persistent) {
       const DevLayer &Lw = P.layers[l];
-      if (P.fold && (op == OP_LM || (op == OP_QKV && l > 0))) {
+      if (SM && P.fold && (op == OP_LM || (op == OP_QKV && l > 0))) {
         // folded FFN: the previous layer's output is its post-attention
         // residual plus the gate/up tasks' partials of the down projection,
         // summed here; this task's share of it is kept (the next gate/up
@@ -1237,10 +1231,8 @@ __device__ __forceinline__ bool task_gemv(const KP &P, const Task &t, int lam, i
     }
     // zero padding up to what the stream reads: whole 512-column chunks
     // (fp8 expert slots start at their own offsets: up to kmax)
-    if (src.f32 || src.bf16) {
-      // (the start rotated per workgroup in MoE engines, where it measured 1%
-      // faster; the dense 8B step measured 0.25% slower with it)
-      stage_vec(P, M.xs, M.red, src, K, FP8 ? P.kmax : min(P.kmax, (K + 1023) & ~1023), P.moe ? lam : 0);
+    if (!SM || src.f32 || src.bf16) {
+      stage_vec(P, M.xs, M.red, src, K, FP8 ? P.kmax : min(P.kmax, (K + 1023) & ~1023));
       normed = src.gain != nullptr;
     } else {
       normed = true;  // staged by stage_fold
@@ -1852,26 +1844,36 @@ __device__ __forceinline__ const KP &kp_fresh() {
 // its own (pre_persistent_kv8, pre_serve_kv8) so that the bf16 kernels keep
 // their register allocation (one kernel takes the budget of its heaviest
 // task).
-template <bool KV8>
+template <bool KV8, bool SM>
 __device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int pos, int tok, float *lds,
                                          const Waiter &wait) {
   const KP &P = kp_fresh();
-  if (t.op == OP_NONE) return true;
-  // attention folded into the output projection: the task's KV head over
-  // every position (its wait is the head's QKV producers), the output
-  // straight into the projection's staged input, then the projection with
-  // nothing left to wait for
-  const bool inl = !KV8 && P.inl && t.op == OP_OPROJ;
-  if (t.op == OP_ATTN || inl) {
-    Task a = t;
-    if (inl) { a.r0 = 0; a.r1 = 1; }
-    if (!attn_chunk<KV8>(P, a, pos, inl ? lds + P.aoff : lds, wait, inl ? lds + P.xsoff : nullptr)) return false;
-    if (!inl) return true;
+  if constexpr (!SM) {
+    switch (t.op) {
+      case OP_NONE: return true;
+      case OP_ATTN: return attn_chunk<KV8>(P, t, pos, lds, wait);
+      case OP_EGU:
+      case OP_EDOWN: return task_gemv<true, false>(P, t, lam, step, pos, tok, lds, wait);
+      default: return task_gemv<false, false>(P, t, lam, step, pos, tok, lds, wait);
+    }
+  } else {
+    if (t.op == OP_NONE) return true;
+    // attention folded into the output projection: the task's KV head over
+    // every position (its wait is the head's QKV producers), the output
+    // straight into the projection's staged input, then the projection with
+    // nothing left to wait for
+    const bool inl = !KV8 && P.inl && t.op == OP_OPROJ;
+    if (t.op == OP_ATTN || inl) {
+      Task a = t;
+      if (inl) { a.r0 = 0; a.r1 = 1; }
+      if (!attn_chunk<KV8>(P, a, pos, inl ? lds + P.aoff : lds, wait, inl ? lds + P.xsoff : nullptr)) return false;
+      if (!inl) return true;
+    }
+    if (t.op == OP_EGU || t.op == OP_EDOWN) return task_gemv<true, true>(P, t, lam, step, pos, tok, lds, wait);
+    Waiter w = wait;
+    if (inl) w.lo = w.hi;
+    return task_gemv<false, true>(P, t, lam, step, pos, tok, lds, w);
   }
-  if (t.op == OP_EGU || t.op == OP_EDOWN) return task_gemv<true>(P, t, lam, step, pos, tok, lds, wait);
-  Waiter w = wait;
-  if (inl) w.lo = w.hi;
-  return task_gemv<false>(P, t, lam, step, pos, tok, lds, w);
 }
 
 // The folded stages of the resident kernel.  The folded FFN: the down
@@ -1910,7 +1912,7 @@ __device__ __forceinline__ bool fold_task(const KP &P, Task &t, int si) {
 // P.b_si for step P.b_step once, without waits or flags (stream order is the
 // only synchronisation).  Both modes go through the one call of run_task, so
 // the task code exists once in the binary.
-template <bool KV8>
+template <bool KV8, bool SM>
 __device__ __forceinline__ void resident_body(KP &P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ int sh[8];
@@ -1949,11 +1951,14 @@ __device__ __forceinline__ void resident_body(KP &P) {
     }
     for (int si = si0; si < si1; ++si) {
       Task t = P.tasks[(int64_t)si * P.W + lam];
-      if (t.op == OP_NONE || !fold_task(P, t, si)) continue;
+      if (t.op == OP_NONE) continue;
+      if constexpr (SM) {
+        if (!fold_task(P, t, si)) continue;
+      }
       const int tr = res && P.trace != nullptr;
       const uint32_t tw = tr ? (uint32_t)now_ticks() : 0u;
       const Waiter wait{res ? 1 : 0, t.wait_lo, t.wait_hi, s, si, ep, sh, tr};
-      if (!run_task<KV8>(t, lam, s, pos, tok, lds, wait)) return;
+      if (!run_task<KV8, SM>(t, lam, s, pos, tok, lds, wait)) return;
       if (res) {
         signal_slot(P, t.signal, ep, P.onexcd || (P.local && (t.op == OP_QKV || t.op == OP_ATTN)));
         if (tr) trace_rec(P, s, si, lam, tw, (uint32_t)sh[3], (uint32_t)now_ticks(), sh);
@@ -1980,8 +1985,11 @@ __device__ __forceinline__ void resident_body(KP &P) {
   if (lam == 0 && threadIdx.x == 0) st_flag(reinterpret_cast<uint32_t *>(P.ctx_len), (uint32_t)(pos0 + P.n_steps));
 }
 
-extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) { resident_body<false>(P); }
-extern "C" __global__ void __launch_bounds__(512) pre_persistent_kv8(KP P) { resident_body<true>(P); }
+extern "C" __global__ void __launch_bounds__(512) pre_persistent(KP P) { resident_body<false, false>(P); }
+extern "C" __global__ void __launch_bounds__(512) pre_persistent_kv8(KP P) { resident_body<true, false>(P); }
+// Small one-XCD engines whose stages are folded (bf16 cache): a kernel of its
+// own, so that the large models' kernel keeps its code and register budget.
+extern "C" __global__ void __launch_bounds__(512) pre_persistent_small(KP P) { resident_body<false, true>(P); }
 
 // the micro-batch task set and kernel
 #include "mb.h"
@@ -2292,12 +2300,15 @@ static int create_engine(const pre_config *cfg, const pre_weights *w, const pre_
   const int want = std::min(ldsm, 96 * 1024);
   if (want > dyn && want > ldsm / 2) dyn = want;
   if (dyn > ldsm) return PRE_ERR_SHAPE;
-  const void *kern = D.mb    ? (const void *)pre_persistent_mb
-                     : D.kv8 ? (const void *)pre_persistent_kv8
-                             : (const void *)pre_persistent;
+  const void *kern = D.mb                 ? (const void *)pre_persistent_mb
+                     : D.kv8              ? (const void *)pre_persistent_kv8
+                     : (D.fold || D.inl) ? (const void *)pre_persistent_small
+                                          : (const void *)pre_persistent;
   const void *serve_kern = D.kv8 ? (const void *)pre_serve_kv8 : (const void *)pre_serve;
   if ((!D.mb && hipFuncSetAttribute(serve_kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess) ||
       hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess ||
+      hipFuncSetAttribute((const void *)pre_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
+          hipSuccess ||
       hipFuncSetAttribute((const void *)pre_k_norm, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
           hipSuccess)
     return PRE_ERR_HIP;
@@ -2502,9 +2513,10 @@ extern "C" int pre_engine_decode(pre_engine *e, int32_t n_steps, const int32_t *
   P.trace = e->trace;
   P.trace_cap = (uint32_t)std::min<size_t>(e->trace_bytes / 32, 0xffffffffu);
   void *args[] = {&P};
-  const void *kern = e->D.mb    ? (const void *)pre_persistent_mb
-                     : e->D.kv8 ? (const void *)pre_persistent_kv8
-                                : (const void *)pre_persistent;
+  const void *kern = e->D.mb                    ? (const void *)pre_persistent_mb
+                     : e->D.kv8                 ? (const void *)pre_persistent_kv8
+                     : (e->D.fold || e->D.inl) ? (const void *)pre_persistent_small
+                                                : (const void *)pre_persistent;
   const unsigned nblk = (unsigned)(e->D.W * (e->D.onexcd ? e->D.X : 1));  // one-XCD: 8 blocks per workgroup
   hipError_t err = hipLaunchCooperativeKernel(kern, dim3(nblk), dim3(e->D.threads), args, (unsigned)e->lds_dyn,
                                               (hipStream_t)stream);
@@ -2707,6 +2719,7 @@ extern "C" int pre_serve_start(pre_engine *e, int32_t n_slots, int32_t max_promp
   }
   KP P;
   fill_kp(e, P, 1);
+  P.fold = P.inl = 0;  // the serving loop runs every stage (its kernels carry no folded stages)
   P.epoch_base = e->epoch_base;
   P.ring = (uint32_t *)d;
   P.cmd = (int32_t *)(e->ws + e->Lo.cmd);

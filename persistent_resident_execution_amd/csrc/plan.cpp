@@ -106,15 +106,16 @@ int derive_dims(const pre_config *c, int n_cus, Dims *D) {
   // micro-batch: wavefronts split a batch's row groups evenly (a power of
   // two), and the LM head keeps one wavefront per sequence
   if (mb && ((D->threads & (D->threads - 1)) || D->threads < 64 * D->B)) return PRE_ERR_SHAPE;
-  // Folded FFN (small one-XCD dense engines, resident kernel only): each
+  // Folded FFN (small one-XCD dense engines with a bf16 cache, resident
+  // kernel only): each
   // gate/up task also forms its slice's partial of the down projection, so
   // the down stage and its hand-off drop out.  Thread t of the task holds
   // row t of Wd's columns [r0, r1) in registers, in 16-byte units (so r0 is
   // a multiple of 8 and there are at most FOLD_U units); every workgroup
   // must produce QKV pairs, so that the output projection's waits cover
   // every workgroup's share of the residual it writes while staging.
-  if (c->fold_ffn >= 0 && !moe && !mb && D->onexcd && D->h <= D->threads && D->qkv_pairs >= D->W &&
-      D->W <= 32) {
+  if (c->fold_ffn >= 0 && !moe && !mb && !D->kv8 && D->onexcd && D->h <= D->threads &&
+      D->qkv_pairs >= D->W && D->W <= 32) {
     bool ok = true;
     for (int lam = 0; lam < D->W && ok; ++lam) {
       int32_t r0, r1;

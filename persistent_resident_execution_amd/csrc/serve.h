@@ -201,10 +201,10 @@ __device__ __forceinline__ void serve_body(KP &P) {
       const uint32_t ep = ep_base + (uint32_t)s + 1u;
       const int pos = pos0 + s;
       for (int si = 0; si < Q.n_si && alive; ++si) {
-        Task t = Q.tasks[(int64_t)si * Q.W + lam];
-        if (t.op == OP_NONE || !fold_task(Q, t, si)) continue;
+        const Task t = Q.tasks[(int64_t)si * Q.W + lam];
+        if (t.op == OP_NONE) continue;
         const Waiter wait{1, t.wait_lo, t.wait_hi, s, si, ep, sh, 0};
-        if (!run_task<KV8>(t, lam, s, pos, tok, lds, wait)) { alive = false; break; }
+        if (!run_task<KV8, false>(t, lam, s, pos, tok, lds, wait)) { alive = false; break; }
         const KP &R = kp_fresh();
         signal_slot(R, t.signal, ep, R.onexcd || (R.local && (t.op == OP_QKV || t.op == OP_ATTN)));
       }
