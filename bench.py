@@ -200,6 +200,17 @@ def cpu_baseline(m, W, pos, budget_s=12.0, single_thread_steps=0):
     return res
 
 
+def kernel_of(m, **kw):
+    """The resident kernel the library launches for this model and options."""
+    from persistent_resident_execution_amd import engine as E
+    if m.batch > 1:
+        return "pre_persistent_mb"
+    if m.kv_fp8:
+        return "pre_persistent_kv8"
+    info, _ = E.plan_describe(m, **kw)
+    return "pre_persistent_small" if (info.fold_ffn or info.fold_attn) else "pre_persistent"
+
+
 def roofline(m, pos, K, t_med, kernel, workload):
     """Algorithmic bytes of one launch of K steps from positions pos over its
     HIP-event time, against the 8 TB/s peak; HBM traffic from the committed
@@ -219,14 +230,14 @@ def roofline(m, pos, K, t_med, kernel, workload):
 def measure(workload, args, W=None, baseline=True, cpu=True, single_thread_steps=0):
     """Everything reported for one workload; returns (entry, weights)."""
     import torch
-    w, m, W, bufs, eng, g0 = setup(workload, W, grid_wgs=args.grid, prefill=args.prefill,
-                                   attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
+    kw = dict(grid_wgs=args.grid, attn_splits=args.attn_splits, fold_ffn=args.fold_ffn, fold_attn=args.fold_attn)
+    w, m, W, bufs, eng, g0 = setup(workload, W, prefill=args.prefill, **kw)
     mb = m.batch > 1
     pos = list(w.contexts)
     K = args.steps if args.steps > 0 else w.steps
     log(f"[bench] {workload}: timing {args.repeats} x {K} persistent steps from position(s) {pos}")
     tp, toks = time_calls(eng, eng.decode, K, g0, pos, args.repeats, args.warmup)
-    kern = "pre_persistent_mb" if mb else ("pre_persistent_kv8" if m.kv_fp8 else "pre_persistent")
+    kern = kernel_of(m, **kw)
     t_med = statistics.median(tp)
     us = t_med / K * 1e6
     unit = "us/step" if mb else "us/token"
@@ -372,9 +383,9 @@ def measure_chunk(args, W):
 
 def tiny_grids(args, entry):
     """The tiny decoder's persistent µs/token at a few grid sizes (its
-    default grid is one XCD's 32 CUs), and at the default grid with the down
-    projection run as a stage of its own (the default folds it into the
-    gate/up stage)."""
+    default grid is one XCD's 32 CUs), and at the default grid with every
+    stage run as a stage of its own (the default folds the down projection
+    into the gate/up stage and the attention into the output projection)."""
     import torch
     from persistent_resident_execution_amd import engine as E
     w, m, W, bufs, eng, g0 = setup("tiny")
@@ -382,9 +393,9 @@ def tiny_grids(args, entry):
     pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
     res = {}
     for grid, fold in ((8, 0), (16, 0), (64, 0), (0, -1)):
-        e2 = E.Engine(m, W, bufs[0], bufs[1], grid_wgs=grid, ctx_len=bufs[2], fold_ffn=fold)
+        e2 = E.Engine(m, W, bufs[0], bufs[1], grid_wgs=grid, ctx_len=bufs[2], fold_ffn=fold, fold_attn=fold)
         t, _ = time_calls(e2, e2.decode, K, g0, pos, args.repeats, 8)
-        res[str(grid) if grid else "32, down stage not folded"] = round(statistics.median(t) / K * 1e6, 2)
+        res[str(grid) if grid else "32, no folded stages"] = round(statistics.median(t) / K * 1e6, 2)
         e2.close()
     res["32 (default)"] = entry["value"]
     del eng, bufs, W
@@ -399,10 +410,10 @@ def phases(args):
     import torch
     from persistent_resident_execution_amd import engine as E
     from persistent_resident_execution_amd import profiling
-    w, m, W, bufs, eng, g0 = setup(args.workload, grid_wgs=args.grid, prefill=args.prefill,
-                                   attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
+    kw = dict(grid_wgs=args.grid, attn_splits=args.attn_splits, fold_ffn=args.fold_ffn, fold_attn=args.fold_attn)
+    w, m, W, bufs, eng, g0 = setup(args.workload, prefill=args.prefill, **kw)
     pos, K = list(w.contexts), (args.steps if args.steps > 0 else w.steps)
-    info, _ = E.plan_describe(m, grid_wgs=args.grid, attn_splits=args.attn_splits, fold_ffn=args.fold_ffn)
+    info, _ = E.plan_describe(m, **kw)
     nsi, nW = info.n_stage_inst, info.n_wgs
     tr = torch.zeros(K * nsi * nW * 8, dtype=torch.int32, device="cuda")
     eng.set_trace(tr)
@@ -482,6 +493,8 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=0, help="attention chunks per KV head (0: default)")
     ap.add_argument("--fold-ffn", type=int, default=0,
                     help="0: fold the down projection into the gate/up stage where supported; -1: never")
+    ap.add_argument("--fold-attn", type=int, default=0,
+                    help="0: fold the attention into the output projection where supported; -1: never")
     ap.add_argument("--prefill", choices=("engine", "synthetic"), default="engine")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first copy this many MiB with the library's copy kernel (counter calibration)")
