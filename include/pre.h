@@ -114,23 +114,23 @@ extern "C" {
  * name quantized KV inside a persistent kernel as open work ("Persistent
  * execution paradigm" section 7.5; XL-Persistent-Kernel, future work) but
  * fix no format: this is the reading taken.
- * fold_ffn: 0 = in the resident kernel of a small one-XCD dense engine
- * (hidden <= wg_threads; every gate/up task's rows start at a multiple of 8
- * and number at most 32; every workgroup a QKV producer) each gate/up task
- * also multiplies its slice of the SwiGLU
- * output by the matching columns of Wd and leaves that split-K partial of
- * the down projection; the next layer's QKV stage (or the LM head) adds the
- * partials while it stages its input, so a layer takes one hand-off fewer
- * (the pages' fusion of adjacent operators into one task to remove
- * synchronisation points, "Persistent execution paradigm" sections 4 and
- * 6.1); -1 = never.  The per-operator path always runs the down stage.
- * fold_attn: 0 = in the resident kernel of a small one-XCD batch-1 engine
+ * fold_ffn: 0 = in the decode kernel of a small one-XCD dense engine with
+ * a bf16 cache (hidden <= wg_threads; every gate/up task's rows start at a
+ * multiple of 8 and number at most 32; every workgroup a QKV producer), each
+ * gate/up task also multiplies its slice of the SwiGLU output by the
+ * matching columns of Wd and leaves that split-K partial of the down
+ * projection; the next layer's QKV stage (or the LM head) adds the partials
+ * while it stages its input, so a layer takes one hand-off fewer (the pages'
+ * fusion of adjacent operators into one task to remove synchronisation
+ * points, "Persistent execution paradigm" sections 4 and 6.1); -1 = never.
+ * The per-operator path and the serving loop always run the down stage.
+ * fold_attn: 0 = in the decode kernel of a small one-XCD batch-1 engine
  * with a bf16 cache (when the whole context's scores fit the LDS beside the
- * projection's input) every output-projection task computes its KV head's
+ * projection's input), every output-projection task computes its KV head's
  * attention over all positions itself, in place of the attention stage and
  * its hand-off (each of the head's workgroups repeats it: the cache is read
- * from the XCD's L2); -1 = never.  The per-operator path always runs the
- * attention stage. */
+ * from the XCD's L2); -1 = never.  The per-operator path and the serving
+ * loop always run the attention stage. */
 typedef struct pre_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t batch, max_ctx;
@@ -427,8 +427,8 @@ const char *pre_strerror(int code);
 typedef struct pre_plan_info {
   int32_t n_stage_inst, n_wgs, n_slots, n_tasks, attn_splits, validator;
   int32_t xcd_local;  /* 1: per-KV-head XCD-local hand-offs; 2: every workgroup on one XCD; 0: none */
-  int32_t fold_ffn;   /* 1: the resident kernel folds the down projection into the gate/up stage */
-  int32_t fold_attn;  /* 1: the resident kernel folds the attention into the output projection */
+  int32_t fold_ffn;   /* 1: the decode kernel folds the down projection into the gate/up stage */
+  int32_t fold_attn;  /* 1: the decode kernel folds the attention into the output projection */
   int64_t workspace_bytes;
 } pre_plan_info;
 int pre_plan_describe(const pre_config *cfg, pre_plan_info *out, int32_t *h_tasks,

@@ -85,11 +85,11 @@ struct KP {
   int32_t *req_tok;      // workspace: the claimed request's prompt [max_ctx]
   int32_t ring_slots, ring_prompt, ring_out, ring_words;
   uint32_t idle_ticks;   // the loop ends after this long without a request
-  // folded FFN (resident kernel): the gate/up tasks leave the down
+  // folded FFN (small-model kernel): the gate/up tasks leave the down
   // projection's partials, the down stage is skipped
   int32_t fold;
   float *dpart;          // [L][W][h]
-  // attention folded into the output projection (resident kernel): the
+  // attention folded into the output projection (small-model kernel): the
   // attention stage is skipped, every O-projection task attends itself
   int32_t inl, aoff;     // on; LDS float offset of the attention's scratch
 };
@@ -1876,16 +1876,14 @@ __device__ __forceinline__ bool run_task(const Task &t, int lam, int step, int p
   }
 }
 
-// The folded stages of the resident kernel.  The folded FFN: the down
-// stage's tasks are skipped,
-// and the stages that waited for them (the next layer's QKV, the LM head)
-// wait for the gate/up stage of the same layer instead -- the stage right
-// before, whose tasks now leave the down projection's partials.  False: skip
-// the task.
-// With the attention folded into the output projection, the attention
-// stage's tasks are skipped and each O-projection task waits for what the
-// first attention task of its (sequence, KV head) would have: that head's
-// QKV producers.
+// The folded stages of the small-model kernel, applied to the task table as
+// it is read (false: skip the task).  Folded FFN: the down stage's tasks are
+// skipped, and the stages that waited for them (the next layer's QKV, the LM
+// head) wait for the gate/up stage of the same layer instead -- the stage
+// right before, whose tasks now leave the down projection's partials.
+// Attention folded into the output projection: the attention stage's tasks
+// are skipped, and each O-projection task waits for what the first attention
+// task of its (sequence, KV head) would have: that head's QKV producers.
 __device__ __forceinline__ bool fold_task(const KP &P, Task &t, int si) {
   if (P.inl) {
     if (t.op == OP_ATTN) return false;
