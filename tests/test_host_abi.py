@@ -315,6 +315,69 @@ def test_attention_fold_only_on_small_one_xcd_bf16_engines(lib, m, kw, want):
         assert (T[W:2 * W, 0] != 0).any()  # the attention stage is still in the table
 
 
+def _folded_reading(T, W, Tg, fold, inl):
+    """The table as the small-model kernel reads it (the device's fold_task):
+    {(stage instance, workgroup): task} of the tasks it runs, waits re-pointed."""
+    out = {}
+    for si in range(len(T) // W):
+        for lam in range(W):
+            op, layer, r0, r1, aux, lo, hi, sig = (int(v) for v in T[si * W + lam])
+            if op == 0:
+                continue
+            if inl and op == 2:
+                continue
+            if inl and op == 3:
+                a = T[(si - 1) * W + aux * Tg]
+                lo, hi = int(a[5]), int(a[6])
+            if fold and op == 5:
+                continue
+            if fold and ((op == 1 and layer > 0) or op == 9):
+                lo, hi = lo - W, hi - W
+            out[(si, lam)] = (op, layer, r0, r1, aux, lo, hi, sig)
+    return out
+
+
+@pytest.mark.parametrize("m,kw", [(synth.TINY, {}), (synth.TINY, {"grid_wgs": 24}), (synth.SMALL_MHA, {}),
+                                  (synth.SMALL_DENSE, {"grid_wgs": 16, "wg_threads": 256})],
+                         ids=lambda v: str(getattr(v, "name", v)))
+def test_folded_reading_keeps_every_dependency(lib, m, kw):
+    """The folded stages skip the down and attention tasks and re-point their
+    consumers' waits.  Read that way, the table must still order every hand-off:
+    each wait names only slots that a task which still runs sets in an earlier
+    stage; the next layer's QKV and the LM head wait for the whole gate/up
+    stage (which now leaves the down partials); each output projection waits
+    for every QKV task holding its KV head's pairs; and every QKV task is
+    waited for by some output projection, so the residual shares it writes
+    are ordered before the gate/up stage that reads them."""
+    info, T = E.plan_describe(m, with_tasks=True, **kw)
+    W, fold, inl = info.n_wgs, info.fold_ffn, info.fold_attn
+    assert fold or inl
+    Tg = W // (m.batch * m.n_kv_heads)
+    R = _folded_reading(T, W, Tg, fold, inl)
+    setters = {t[7]: si for (si, lam), t in R.items()}
+    for (si, lam), t in R.items():
+        for slot in range(t[5], t[6]):
+            assert slot in setters and setters[slot] < si, (si, lam, slot)
+    spl, pg = 5, m.head_dim // 2 * (m.n_q_heads // m.n_kv_heads + 2)  # RoPE pairs per KV head
+    waited_qkv = set()
+    for (si, lam), t in R.items():
+        op, layer, lo, hi = t[0], t[1], t[5], t[6]
+        if fold and ((op == 1 and layer > 0) or op == 9):
+            gu = (layer - 1 if op == 1 else m.n_layers - 1) * spl + 3
+            assert lo <= gu * W and hi >= (gu + 1) * W, (si, lam)
+        if inl and op == 3:
+            g, q = t[4] % m.n_kv_heads, layer * spl
+            for w in range(W):
+                r0, r1 = int(T[q * W + w][2]), int(T[q * W + w][3])
+                if r0 < r1 and r0 < (g + 1) * pg and r1 > g * pg:
+                    assert lo <= q * W + w < hi, (si, lam, w)
+                    waited_qkv.add((layer, w))
+    if fold and inl:
+        assert waited_qkv == {(l, w) for l in range(m.n_layers) for w in range(W)}
+    kept_ops = {t[0] for t in R.values()}
+    assert (5 not in kept_ops) == bool(fold) and (2 not in kept_ops) == bool(inl)
+
+
 def test_kv_descriptor_size_bound(lib):
     """The K/V append addresses a layer's whole cache with a 32-bit buffer
     size: a configuration whose layer cache reaches 4 GiB is refused, the
