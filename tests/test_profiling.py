@@ -48,3 +48,30 @@ def test_phase_table_microbatch_layout():
     assert "stream 0.99  epi 0.51" in lines[1]  # ends at mark 1, then the task end
     assert lines[-1] == ("critical-path deltas per layer (us): qkv 1.00  attn 1.00  comb 1.00  oproj 1.00  "
                          "gu 1.00  down 1.00")
+
+
+def test_phase_table_with_folded_stages():
+    # the small-model kernel skips the attention and down stages: their
+    # records stay zero; they report no line and a zero delta, and the stage
+    # after each is measured from the stage before it
+    L, spl, W = 2, 5, 4
+    rec = _records(3, L * spl + 1, W)
+    for l in range(L):
+        rec[:, l * spl + 1] = 0  # attention
+        rec[:, l * spl + 4] = 0  # down
+    lines = pf.phase_table(rec, ["qkv", "attn", "oproj", "gu", "down", "lm"], L, spl, 0)
+    kinds = [ln.split()[0] for ln in lines[:-1]]
+    assert kinds == ["qkv", "oproj", "gu", "lm"]
+    assert lines[-1].endswith("qkv 6.00  attn 0.00  oproj 6.00  gu 3.00  down 0.00")
+
+
+def test_bench_names_the_kernel_each_engine_launches():
+    import bench
+    from persistent_resident_execution_amd import synth
+    from dataclasses import replace
+    assert bench.kernel_of(synth.TINY) == "pre_persistent_small"
+    assert bench.kernel_of(synth.TINY, fold_ffn=-1, fold_attn=-1) == "pre_persistent"
+    assert bench.kernel_of(synth.DENSE8B) == "pre_persistent"
+    assert bench.kernel_of(synth.MOE) == "pre_persistent"
+    assert bench.kernel_of(replace(synth.TINY, kv_fp8=True)) == "pre_persistent_kv8"
+    assert bench.kernel_of(synth.SMALL_MB) == "pre_persistent_mb"
